@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the ReplaySSM decode hot path on one MI355X.
+
+Workload: the Nemotron-3-style Mamba-2 layer (batch 256, nheads 128, headdim
+64, dstate 128, ngroups 8; FP32 state 4 MiB per sequence), window L = 16, bf16
+x/B/C and fp32 dt, seeded synthetic inputs, steady state (every sequence starts
+with L committed records, so one call in 16 flushes).  One step = one
+replayssm_decode_step call over the whole batch, flush included when due.
+
+Prints one JSON line: value = achieved algorithmic HBM GB/s of the decode step
+(ms_per_step carries the time), the roofline of the replay kernel, the
+in-library conventional kernel on the same inputs, the streaming-probe ceiling
+and the fp64 CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "Mamba-2 layer decode-step µs + achieved HBM GB/s at batch 256, L=16"
+PEAK_GBS = 8000.0
+COUNTERS = ROOT / "profiles" / "replay_decode_batch256_L16_counters.json"
+KERNEL_SOURCES = ["mamba_state_replay_amd/csrc/replay.hip", "mamba_state_replay_amd/csrc/common.h"]
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update((ROOT / p).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--window", type=int, default=16)
+    ap.add_argument("--read-copy", choices=["none", "bf16", "e4m3"], default="none")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-conventional", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU sample")
+    return ap.parse_args()
+
+
+def timed_launches(fn, steps, torch):
+    """Run fn(i) for i < steps with an event pair around each launch.
+
+    Returns (total ms of the region, list of per-launch ms)."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    region0.record()
+    for i in range(steps):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    region1.record()
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return region0.elapsed_time(region1), per
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the decode path shards by sequence or head group with no "
+              "exchange, so only --gpus 1 is run here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mamba_state_replay_amd import binding as rb
+    from mamba_state_replay_amd import staging, synth, traffic
+
+    dev = torch.device("cuda", 0)
+    L = args.window
+    read_copy = None if args.read_copy == "none" else args.read_copy
+    shape = synth.LayerShape(batch=args.batch, nheads=128, headdim=64, dstate=128, ngroups=8, window=L)
+    ntok = 64
+    work = synth.decode_workload(shape, ntok, seed=1001, n0=L)
+    cfg = staging.config(shape, read_copy=read_copy)
+    st = staging.replay_state(cfg, work, dev)
+    p = staging.params(work, dev)
+    toks = staging.TokenStream(work.steps, dev)
+    y = torch.empty((shape.batch, 1, shape.nheads, shape.headdim), device=dev)
+    if read_copy:
+        rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST)
+
+    W, K = args.warmup, args.steps
+    for i in range(W):
+        rb.replayssm_decode_step(cfg, st, p, toks.call(i % ntok), y)
+    torch.cuda.synchronize()
+
+    sched, n_end = traffic.decode_schedule(work.n0, L, W + K)
+    sz = traffic.sizes(128, 64, 128, 8, 2, read_copy)
+    timed_sched = sched[W:]
+    bytes_per_launch = [traffic.decode_step_bytes(sz, n, f) for n, f in timed_sched]
+    folds = sum(int(f.any()) for _, f in timed_sched)
+
+    total_ms, per_ms = timed_launches(
+        lambda i: rb.replayssm_decode_step(cfg, st, p, toks.call((W + i) % ntok), y), K, torch)
+    meta = st.meta.cpu().numpy()
+    assert np.array_equal(meta[:, 1], n_end), "ring pointers disagree with the flush schedule"
+    assert int(st.status.cpu()[0]) == 0 and bool(torch.isfinite(y).all())
+
+    total_bytes = sum(bytes_per_launch)
+    us_step = total_ms * 1e3 / K
+    gbs = total_bytes / (total_ms * 1e-3) / 1e9
+    kernel_ms = float(np.mean(per_ms))
+    achieved = (total_bytes / K) / (kernel_ms * 1e-3) / 1e9
+    fold_ms = [t for t, (_, f) in zip(per_ms, timed_sched) if f.any()]
+    nonfold_ms = [t for t, (_, f) in zip(per_ms, timed_sched) if not f.any()]
+
+    traffic_bytes = None
+    if COUNTERS.exists():
+        c = json.loads(COUNTERS.read_text())
+        if c.get("source_hash") == source_hash(KERNEL_SOURCES) and c.get("batch") == shape.batch:
+            traffic_bytes = c.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(total_ms / K, 6),
+        "us_per_step": round(us_step, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"Nemotron-3-style Mamba-2 layer decode (ReplaySSM), batch {shape.batch}, "
+                        f"nheads 128, headdim 64, dstate 128, ngroups 8, L={L}, bf16 x/B/C, fp32 dt, "
+                        f"FP32 checkpoint" + (f" + {read_copy} read copy" if read_copy else "") +
+                        ", steady state (L committed records at start)",
+            "batch": shape.batch, "window": L, "read_copy": read_copy or "none",
+            "flush_launches_timed": folds,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "replay_kernel",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": traffic_bytes,
+            "algorithmic_bytes_per_launch": int(total_bytes / K),
+            "avg_launch_us": round(kernel_ms * 1e3, 2),
+            "nonflush_launch_us": round(float(np.mean(nonfold_ms)) * 1e3, 2) if nonfold_ms else None,
+            "flush_launch_us": round(float(np.mean(fold_ms)) * 1e3, 2) if fold_ms else None,
+        },
+    }
+
+    if not args.no_conventional:
+        states = staging.conventional_states(cfg, work.h0, 1, dev)
+        for i in range(W):
+            rb.conventional_state_update(cfg, states, p, toks.call(i % ntok), y)
+        ctot, cper = timed_launches(
+            lambda i: rb.conventional_state_update(cfg, states, p, toks.call((W + i) % ntok), y), K, torch)
+        cbytes = traffic.conventional_step_bytes(sz, shape.batch)
+        c_us = ctot * 1e3 / K
+        result["conventional"] = {
+            "us_per_step": round(c_us, 2),
+            "gbs": round(cbytes / (c_us * 1e-6) / 1e9, 1),
+            "avg_launch_us": round(float(np.mean(cper)) * 1e3, 2),
+            "frac": round(cbytes / (float(np.mean(cper)) * 1e-3) / 1e9 / PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": cbytes,
+        }
+        result["speedup_vs_conventional"] = round(c_us / us_step, 3)
+        del states
+
+    if not args.no_probe:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_()
+        dst = torch.empty_like(src)
+        sink = torch.zeros(rb.probe_sink_elems(nbytes), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            rb.rssm_probe_read(src, sink)
+            rb.rssm_probe_copy(dst, src)
+        rt, rper = timed_launches(lambda i: rb.rssm_probe_read(src, sink), 10, torch)
+        ct, cper = timed_launches(lambda i: rb.rssm_probe_copy(dst, src), 10, torch)
+        read_gbs = nbytes / (float(np.median(rper)) * 1e-3) / 1e9
+        copy_gbs = 2 * nbytes / (float(np.median(cper)) * 1e-3) / 1e9
+        result["probe"] = {"read_gbs": round(read_gbs, 1), "copy_gbs": round(copy_gbs, 1),
+                           "bytes": nbytes}
+        result["roofline"]["frac_of_probe_read"] = round(achieved / read_gbs, 4)
+        del src, dst, sink
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(work, total_bytes / K, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(work, gpu_bytes_per_step, target_s):
+    """The fp64 oracle on a bounded sample of the same workload, scaled to GB/s.
+
+    The oracle steps every sequence (all heads) of the workload through its 64
+    decode tokens, repeated until about `target_s` seconds have passed; the
+    value is the GPU step's algorithmic bytes divided by the oracle's time per
+    step (so the GPU/CPU value ratio is the step-rate ratio)."""
+    from oracle import oracle as orc
+    o = orc.default()
+    cores = o.num_threads()
+    batch = work.shape.batch
+    seqs = np.arange(batch)
+    nsteps = work.steps.steps
+    t0 = time.perf_counter()
+    elapsed, passes = 0.0, 0
+    while passes == 0 or (time.perf_counter() - t0 < target_s and passes < 50):
+        elapsed += orc.time_decode(work, seqs, nsteps)
+        passes += 1
+    step_s = elapsed / (passes * nsteps)
+    return {
+        "value": round(gpu_bytes_per_step / step_s / 1e9, 4),
+        "unit": "GB/s",
+        "us_per_step": round(step_s * 1e6, 1),
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"all {batch} sequences x 128 heads x {nsteps} decode tokens of the same workload, "
+                  f"{passes} pass(es), {elapsed:.1f} s inside the oracle (fp64 conventional recurrence, "
+                  f"OpenMP over sequence/head pairs)",
+        "host_cpu": platform.processor() or platform.machine(),
+    }
+
+
+if __name__ == "__main__":
+    main()

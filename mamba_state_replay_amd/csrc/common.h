@@ -1,0 +1,228 @@
+// Device helpers shared by the ReplaySSM kernels: tile geometry, number
+// formats and wave-level reductions for gfx950 (wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rssm {
+
+// Native 16-byte vector types (usable with the nontemporal builtins).
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Tile geometry.
+//
+// A (sequence, head) tile is HD rows x DS columns, row-major.  A workgroup of
+// NT threads streams it with 16-byte vector loads: a row is LPR consecutive
+// lanes (one 16-byte vector each), so each load instruction of a wave covers
+// 64/LPR whole rows and every byte of every 128-byte line it touches.  Thread
+// t owns NI consecutive rows (rows rgrp*NI .. rgrp*NI+NI-1, rgrp = t / LPR) at
+// vector column t % LPR; its columns stay fixed across rows, so the C values
+// it multiplies by are loaded once.  EB is the element size of the tile's
+// storage type (4 fp32, 2 bf16, 1 e4m3).
+// ---------------------------------------------------------------------------
+template <int HD, int DS, int NT, int EB>
+struct TileGeo {
+    static constexpr int EPV = 16 / EB;             // elements per 16-byte vector
+    static constexpr int LPR = DS / EPV;            // lanes per row
+    static constexpr int RPI = NT / LPR;            // rows per load instruction (whole WG)
+    static constexpr int NI = HD >= RPI ? HD / RPI : 1;  // rows per thread
+    static constexpr int ACTIVE = HD >= RPI ? NT : HD * LPR;  // threads that own data
+    static_assert(DS % EPV == 0, "row must be a whole number of 16-byte vectors");
+    static_assert(LPR >= 1 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "lanes per row: power of two <= 32");
+    static_assert(NI <= 16, "too many rows per thread");
+    static_assert(NI <= LPR || LPR == 1, "transposed reduction needs NI <= LPR");
+    static_assert(HD % NI == 0, "rows must split evenly");
+};
+
+// ---------------------------------------------------------------------------
+// Number formats.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// fp32 -> OCP e4m3fn, round to nearest even, saturating to +-448; NaN -> 0x7F.
+// Normal codes (exponent field 1..15, bias 7) get their 3 mantissa bits by
+// rounding the fp32 mantissa; the subnormal range (|v| < 2^-6) is a multiple
+// of 2^-9, and a rounded multiple of 8 is exactly the smallest normal code.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fabsf(f);
+    if (!(a == a)) return 0x7Fu;
+    uint32_t code;
+    if (a >= 448.0f) {
+        code = 0x7Eu;
+    } else if (a < 0.015625f) {
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        uint32_t ua = __float_as_uint(a);
+        ua += 0x7FFFFu + ((ua >> 20) & 1u);
+        code = (((ua >> 23) - 120u) << 3) | ((ua >> 20) & 7u);
+        if (code > 0x7Eu) code = 0x7Eu;
+    }
+    return sign | code;
+}
+
+// Four e4m3 codes (bytes of w, low byte first) -> fp32, with the hardware
+// converter (gfx950 reads OCP e4m3fn).
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float out[4]) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    out[0] = lo[0];
+    out[1] = lo[1];
+    out[2] = hi[0];
+    out[3] = hi[1];
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane exchange within 32-lane halves: DPP quad permutes for xor 1 and
+// xor 2, ds_swizzle (bit-mask mode) for xor 4, 8 and 16.
+// ---------------------------------------------------------------------------
+template <int MASK>
+__device__ __forceinline__ float xor_shfl(float v) {
+    const int iv = __float_as_int(v);
+    int r;
+    if constexpr (MASK == 1) {
+        r = __builtin_amdgcn_update_dpp(iv, iv, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (MASK == 2) {
+        r = __builtin_amdgcn_update_dpp(iv, iv, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (MASK == 4 || MASK == 8 || MASK == 16) {
+        r = __builtin_amdgcn_ds_swizzle(iv, (MASK << 10) | 0x1F);
+    } else {
+        static_assert(MASK == 32, "unsupported lane mask");
+        r = __shfl_xor(iv, 32);
+    }
+    return __int_as_float(r);
+}
+
+template <int MASK>
+__device__ __forceinline__ float xor_max(float v) {
+    return fmaxf(v, xor_shfl<MASK>(v));
+}
+
+// Sum v over groups of W consecutive lanes (W a power of two <= 64); every
+// lane of a group gets the group's sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (W >= 2) v += xor_shfl<1>(v);
+    if constexpr (W >= 4) v += xor_shfl<2>(v);
+    if constexpr (W >= 8) v += xor_shfl<4>(v);
+    if constexpr (W >= 16) v += xor_shfl<8>(v);
+    if constexpr (W >= 32) v += xor_shfl<16>(v);
+    if constexpr (W >= 64) v += xor_shfl<32>(v);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+    if constexpr (W >= 2) v = xor_max<1>(v);
+    if constexpr (W >= 4) v = xor_max<2>(v);
+    if constexpr (W >= 8) v = xor_max<4>(v);
+    if constexpr (W >= 16) v = xor_max<8>(v);
+    if constexpr (W >= 32) v = xor_max<16>(v);
+    if constexpr (W >= 64) v = xor_max<32>(v);
+    return v;
+}
+
+// One halving stage of the transposed reduction: lanes whose MASK bit is set
+// keep the upper half of their N values and hand the lower half to their
+// partner, which does the opposite; each then adds what it receives.
+template <int MASK, int N>
+__device__ __forceinline__ void halve(float (&v)[16], bool upper) {
+    constexpr int H = N / 2;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        const float keep = upper ? v[i + H] : v[i];
+        const float send = upper ? v[i] : v[i + H];
+        v[i] = keep + xor_shfl<MASK>(send);
+    }
+}
+
+// Reduce N values per lane over groups of W consecutive lanes (N <= W, both
+// powers of two) with log2(N) halving stages followed by log2(W/N) plain
+// butterfly stages.  Returns the sum of value index `idx` over the group;
+// lanes with (lane % W) < N hold distinct indices (idx is then lane % W read
+// with its bits reversed into the stage order below).
+template <int N, int W>
+__device__ __forceinline__ float transpose_reduce(float (&v)[16], int lane, int& idx) {
+    static_assert(N <= W, "need at least as many lanes as values");
+    idx = 0;
+    if constexpr (N >= 2) { const bool u = lane & 1; halve<1, N>(v, u); idx += u ? N / 2 : 0; }
+    if constexpr (N >= 4) { const bool u = lane & 2; halve<2, N / 2>(v, u); idx += u ? N / 4 : 0; }
+    if constexpr (N >= 8) { const bool u = lane & 4; halve<4, N / 4>(v, u); idx += u ? N / 8 : 0; }
+    if constexpr (N >= 16) { const bool u = lane & 8; halve<8, N / 8>(v, u); idx += u ? N / 16 : 0; }
+    float s = v[0];
+    if constexpr (W > N) {
+        if constexpr (N <= 1 && W >= 2) s += xor_shfl<1>(s);
+        if constexpr (N <= 2 && W >= 4) s += xor_shfl<2>(s);
+        if constexpr (N <= 4 && W >= 8) s += xor_shfl<4>(s);
+        if constexpr (N <= 8 && W >= 16) s += xor_shfl<8>(s);
+        if constexpr (N <= 16 && W >= 32) s += xor_shfl<16>(s);
+    }
+    return s;
+}
+
+// Remap the linear workgroup id so that each of the 8 XCDs (which receive
+// workgroups round-robin) processes one contiguous block of tiles; the heads
+// of a group then share B/C records through that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
+    if ((nwg & 7) != 0) return wg;
+    return (wg & 7) * (nwg >> 3) + (wg >> 3);
+}
+
+}  // namespace rssm
+
+namespace rssm {
+
+// Threads per workgroup for each compiled tile shape: every thread of the
+// large shapes owns 8 rows x one 16-byte fp32 vector (128 bytes of the tile).
+template <int HD, int DS>
+struct ShapeNT;
+template <>
+struct ShapeNT<16, 16> { static constexpr int NT = 64; };
+template <>
+struct ShapeNT<64, 64> { static constexpr int NT = 128; };
+template <>
+struct ShapeNT<64, 128> { static constexpr int NT = 256; };
+template <>
+struct ShapeNT<128, 128> { static constexpr int NT = 512; };
+
+// Token / record element type: fp32, or bf16 carried as its 16-bit pattern.
+template <typename InT>
+struct InTraits;
+template <>
+struct InTraits<float> { static constexpr int EPV = 4; };
+template <>
+struct InTraits<uint16_t> { static constexpr int EPV = 8; };
+
+// Widen one 16-byte vector of InT elements to fp32.
+template <typename InT>
+__device__ __forceinline__ void widen16(const uint4 v, float* out) {
+    if constexpr (InTraits<InT>::EPV == 4) {
+        out[0] = __uint_as_float(v.x);
+        out[1] = __uint_as_float(v.y);
+        out[2] = __uint_as_float(v.z);
+        out[3] = __uint_as_float(v.w);
+    } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+}
+
+}  // namespace rssm

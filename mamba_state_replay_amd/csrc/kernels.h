@@ -1,0 +1,76 @@
+// Host-side launch interface between api.cpp (argument checks) and the
+// kernel files.  Internal to the library; not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rssm {
+
+enum Mode : int32_t { MODE_DECODE = 0, MODE_VERIFY = 1, MODE_FLUSH = 2 };
+enum InType : int32_t { IN_F32 = 0, IN_BF16 = 1 };
+enum ReadMode : int32_t { READ_F32 = 0, READ_BF16 = 1, READ_E4M3 = 2 };
+
+constexpr uint32_t kStatusMeta = 1u;
+constexpr uint32_t kStatusAccept = 2u;
+constexpr uint32_t kStatusSlot = 4u;
+constexpr int32_t kFlushForceCast = 1;
+
+struct ReplayArgs {
+    float* ckpt;
+    void* ckpt_read;
+    float* ckpt_scale;
+    void* buf_x;
+    void* buf_B;
+    float* buf_dt;
+    int32_t* meta;
+    int32_t* arrive;
+    int32_t* status;
+    const void* x;
+    const void* B;
+    const void* C;
+    const float* dt;
+    const float* A;
+    const float* D;
+    float* y;
+    int32_t batch, nheads, ngroups;
+    int32_t L, cap, T;
+    int32_t mode, flags;
+};
+
+struct ConvArgs {
+    float* states;
+    const int32_t* slot;
+    int32_t* status;
+    const void* x;
+    const void* B;
+    const void* C;
+    const float* dt;
+    const float* A;
+    const float* D;
+    float* y;
+    int32_t batch, nheads, ngroups, nslots, T;
+};
+
+struct CommitArgs {
+    int32_t* meta;      // replay: [batch][2]
+    int32_t* slot;      // conventional: [batch]
+    const int32_t* accepted;
+    int32_t* status;
+    int32_t batch, T, cap, nslots;
+};
+
+// Dynamic LDS bytes of the replay kernel for a shape, ring capacity and T.
+size_t replay_lds_bytes(int hd, int ds, int cap, int T);
+size_t conventional_lds_bytes(int hd, int ds, int T);
+
+// Each returns hipSuccess or the launch error; -1 cast to hipError_t never
+// happens because api.cpp only passes shapes that replay_shape_supported accepts.
+bool shape_supported(int hd, int ds);
+hipError_t launch_replay(const ReplayArgs& a, int hd, int ds, int in_type, int read_mode,
+                         hipStream_t stream);
+hipError_t launch_conventional(const ConvArgs& a, int hd, int ds, int in_type, hipStream_t stream);
+hipError_t launch_replay_commit(const CommitArgs& a, hipStream_t stream);
+hipError_t launch_conventional_commit(const CommitArgs& a, hipStream_t stream);
+
+}  // namespace rssm

@@ -1,0 +1,72 @@
+// HBM streaming probes: a read-only and a copy kernel with the access pattern
+// of one 32 KiB checkpoint tile per 256-thread workgroup (8 x 16-byte loads
+// per thread, whole rows per wave instruction).
+#include <hip/hip_runtime.h>
+
+#include "../../include/replayssm.h"
+#include "../../include/replayssm_probe.h"
+#include "common.h"
+
+namespace rssm {
+namespace {
+
+constexpr int kBlock = 32768;
+constexpr int kThreads = 256;
+constexpr int kVec = kBlock / 16 / kThreads;  // 8
+
+__global__ __launch_bounds__(kThreads) void probe_read_kernel(const v4u* src, float* sink) {
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const v4u* p = src + (size_t)wg * (kBlock / 16);
+    v4u r[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) r[i] = __builtin_nontemporal_load(p + i * kThreads + threadIdx.x);
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) acc ^= r[i].x ^ r[i].y ^ r[i].z ^ r[i].w;
+    float v = __uint_as_float(acc & 0x007FFFFFu);
+    v = group_sum<64>(v);
+    if ((threadIdx.x & 63) == 0) atomicAdd(sink + wg, v);
+}
+
+__global__ __launch_bounds__(kThreads) void probe_copy_kernel(v4u* dst, const v4u* src) {
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const size_t off = (size_t)wg * (kBlock / 16);
+    v4u r[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) r[i] = __builtin_nontemporal_load(src + off + i * kThreads + threadIdx.x);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) __builtin_nontemporal_store(r[i], dst + off + i * kThreads + threadIdx.x);
+}
+
+int check(size_t bytes) {
+    if (bytes % kBlock != 0 || bytes / kBlock > 0x7FFFFFFF) return RSSM_ERR_SHAPE;
+    return RSSM_OK;
+}
+
+}  // namespace
+}  // namespace rssm
+
+extern "C" {
+
+size_t rssm_probe_sink_elems(size_t bytes) { return bytes / rssm::kBlock; }
+
+int rssm_probe_read(const void* src, size_t bytes, float* sink, void* stream) {
+    if (!src || !sink) return RSSM_ERR_NULL;
+    if (rssm::check(bytes)) return RSSM_ERR_SHAPE;
+    if (bytes == 0) return RSSM_OK;
+    hipLaunchKernelGGL(rssm::probe_read_kernel, dim3(bytes / rssm::kBlock), dim3(rssm::kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const rssm::v4u*>(src), sink);
+    return hipGetLastError() == hipSuccess ? RSSM_OK : RSSM_ERR_HIP;
+}
+
+int rssm_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (!src || !dst) return RSSM_ERR_NULL;
+    if (rssm::check(bytes)) return RSSM_ERR_SHAPE;
+    if (bytes == 0) return RSSM_OK;
+    hipLaunchKernelGGL(rssm::probe_copy_kernel, dim3(bytes / rssm::kBlock), dim3(rssm::kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<rssm::v4u*>(dst),
+                       static_cast<const rssm::v4u*>(src));
+    return hipGetLastError() == hipSuccess ? RSSM_OK : RSSM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+"""Algorithmic HBM bytes of the decode-path kernels (measurement accounting).
+
+Counts what each call must move at minimum, per sequence:
+
+  S    = nheads*headdim*dstate*4          FP32 checkpoint (or state) bytes
+  S_r  = bytes of the tile a non-flush call reads: S, S/2 (bf16 copy) or
+         S/4 + nheads*4 (e4m3 copy + per-tile scales)
+  S_c  = read-copy bytes a flush writes (0 without a copy)
+  R    = nheads*headdim*e + ngroups*dstate*e + nheads*4   one record (x, B, dt)
+  TOK  = R + ngroups*dstate*e                             one token's inputs (+ C)
+  Y    = nheads*headdim*4                                 one token's outputs
+
+  replay decode, non-flush, n records: S_r + n*R + TOK + R + Y
+  replay decode, flush of n records:   S + n*R + TOK + S + S_c + R + Y
+  replay verify of T drafts:           S_r + n*R + T*(TOK + R + Y)   (+ S + S_c, S_r -> S on a flush)
+  conventional step:                   2*S + TOK + Y
+  snapshot verify of T drafts:         (1 + T)*S + T*(TOK + Y)
+
+e is the input element size (2 for bf16).  The 1 KiB of per-head A and D and
+the 8-byte ring pointers are ignored.  The realized schedule (which calls
+flush, and how many records each reads) is replayed here with the same
+integer rule as the kernels: a call that starts with n >= L flushes first.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Sizes:
+    S: int
+    S_r: int
+    S_c: int
+    R: int
+    TOK: int
+    Y: int
+
+
+def sizes(nheads, headdim, dstate, ngroups, in_bytes=2, read_copy=None) -> Sizes:
+    S = nheads * headdim * dstate * 4
+    if read_copy is None:
+        S_r, S_c = S, 0
+    elif read_copy == "bf16":
+        S_r = S_c = S // 2
+    elif read_copy == "e4m3":
+        S_r = S_c = S // 4 + nheads * 4
+    else:
+        raise ValueError(read_copy)
+    R = nheads * headdim * in_bytes + ngroups * dstate * in_bytes + nheads * 4
+    TOK = R + ngroups * dstate * in_bytes
+    Y = nheads * headdim * 4
+    return Sizes(S, S_r, S_c, R, TOK, Y)
+
+
+def decode_schedule(n0: np.ndarray, L: int, steps: int):
+    """Per step: (records read n [batch], flushed [batch]) under flush-at-start."""
+    n = np.array(n0, np.int64).copy()
+    out = []
+    for _ in range(steps):
+        fold = n >= L
+        out.append((n.copy(), fold.copy()))
+        n = np.where(fold, 0, n) + 1
+    return out, n
+
+
+def decode_step_bytes(sz: Sizes, n: np.ndarray, fold: np.ndarray) -> int:
+    """Algorithmic bytes of one replay decode call over the batch."""
+    nonfold = sz.S_r + n * sz.R + sz.TOK + sz.R + sz.Y
+    folded = sz.S + n * sz.R + sz.TOK + sz.S + sz.S_c + sz.R + sz.Y
+    return int(np.where(fold, folded, nonfold).sum())
+
+
+def conventional_step_bytes(sz: Sizes, batch: int) -> int:
+    return batch * (2 * sz.S + sz.TOK + sz.Y)
+
+
+def verify_bytes(sz: Sizes, n: np.ndarray, fold: np.ndarray, T: int) -> int:
+    base = n * sz.R + T * (sz.TOK + sz.R + sz.Y)
+    return int(np.where(fold, base + 2 * sz.S + sz.S_c, base + sz.S_r).sum())
+
+
+def snapshot_verify_bytes(sz: Sizes, batch: int, T: int) -> int:
+    return batch * ((1 + T) * sz.S + T * (sz.TOK + sz.Y))

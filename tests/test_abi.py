@@ -1,0 +1,112 @@
+"""The C-ABI library loads and exports every function include/*.h declares;
+host-side checks reject bad arguments before anything reaches the GPU."""
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+import torch
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADERS = sorted((ROOT / "include").glob("*.h"))
+
+
+@pytest.fixture(scope="module")
+def rb():
+    from mamba_state_replay_amd import binding
+    if not binding.LIBRARY.exists():
+        from mamba_state_replay_amd import _build
+        _build.build()
+    binding.lib()
+    return binding
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", h.read_text(), flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M):
+            if not m.group(0).lstrip().startswith(("#", "typedef", "return")):
+                names.add(m.group(1))
+    return sorted(names)
+
+
+def test_headers_declare_the_entry_points():
+    names = declared_functions()
+    for required in ["replayssm_decode_step", "replayssm_flush", "replayssm_verify_drafts",
+                     "replayssm_commit", "conventional_state_update", "conventional_commit",
+                     "replayssm_sizes", "replayssm_capacity", "replayssm_last_error"]:
+        assert required in names, required
+
+
+def test_library_exports_every_declared_symbol(rb):
+    out = subprocess.run(["nm", "-D", "--defined-only", str(rb.LIBRARY)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    handle = ctypes.CDLL(str(rb.LIBRARY))
+    for n in declared_functions():
+        getattr(handle, n)
+
+
+def test_sizes_and_capacity(rb):
+    cfg = rb.Config(batch=256, nheads=128, headdim=64, dstate=128, ngroups=8, window=16, max_drafts=1)
+    assert rb.replayssm_capacity(cfg) == 17
+    sz = rb.replayssm_sizes(cfg)
+    assert sz[rb.BUF_CKPT] == 256 * 128 * 64 * 128 * 4 == 1 << 30   # 4 MiB per sequence
+    assert sz[rb.BUF_CKPT_READ] == 0 and sz[rb.BUF_CKPT_SCALE] == 0
+    assert sz[rb.BUF_X] == 256 * 128 * 17 * 64 * 2
+    assert sz[rb.BUF_B] == 256 * 8 * 17 * 128 * 2
+    assert sz[rb.BUF_DT] == 256 * 128 * 17 * 4
+    assert sz[rb.BUF_META] == 256 * 8 and sz[rb.BUF_ARRIVE] == 256 * 4
+    e4 = rb.Config(256, 128, 64, 128, 8, 16, 3, "bf16", "e4m3")
+    assert rb.replayssm_capacity(e4) == 21
+    sz = rb.replayssm_sizes(e4)
+    assert sz[rb.BUF_CKPT_READ] == 1 << 28 and sz[rb.BUF_CKPT_SCALE] == 256 * 128 * 4
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(headdim=32), -2), (dict(ngroups=3), -2), (dict(window=0), -2), (dict(window=65), -2),
+    (dict(max_drafts=9), -2), (dict(max_drafts=0), -2), (dict(batch=-1), -2),
+])
+def test_config_rejections(rb, bad, code):
+    base = dict(batch=4, nheads=128, headdim=64, dstate=128, ngroups=8, window=16, max_drafts=1)
+    base.update(bad)
+    with pytest.raises(rb.ReplaySSMError) as e:
+        rb.replayssm_sizes(rb.Config(**base))
+    assert e.value.code == code
+
+
+def test_null_pointers_rejected_before_launch(rb):
+    L = rb.lib()
+    c = rb.Config(4, 128, 64, 128, 8).c()
+    s = rb.rssm_state()          # all NULL
+    p = rb.rssm_params()
+    t = rb.rssm_tokens(None, None, None, None, 1)
+    assert L.replayssm_decode_step(ctypes.byref(c), ctypes.byref(s), ctypes.byref(p), ctypes.byref(t),
+                                   None, None) == -1
+    assert "required" in rb.replayssm_last_error()
+    assert L.replayssm_flush(ctypes.byref(c), ctypes.byref(s), ctypes.byref(p), 0, None) == -1
+    assert L.replayssm_flush(ctypes.byref(c), ctypes.byref(s), ctypes.byref(p), 8, None) == -2
+    assert L.replayssm_commit(ctypes.byref(c), ctypes.byref(s), None, 2, None) == -4
+    assert L.replayssm_commit(ctypes.byref(c), ctypes.byref(s), None, 1, None) == -1
+    assert L.conventional_state_update(ctypes.byref(c), None, 1, None, None, ctypes.byref(p),
+                                       ctypes.byref(t), None, None) == -1
+    assert L.conventional_commit(ctypes.byref(c), None, 1, None, 1, None, None) == -2
+    assert L.replayssm_decode_step(None, None, None, None, None, None) == -1
+    bad = rb.Config(4, 128, 64, 128, 8, in_dtype="bf16").c()
+    bad.in_dtype = 7
+    assert L.replayssm_sizes(ctypes.byref(bad), (ctypes.c_size_t * 8)()) == -3
+
+
+def test_binding_checks_tensors_on_host(rb):
+    cfg = rb.Config(2, 8, 16, 16, 2, window=4, max_drafts=1, in_dtype="f32")
+    # CPU tensors are refused before the library is called
+    st = rb.State(*[torch.zeros(1)] * 9)
+    p = rb.Params(torch.zeros(8), torch.zeros(8))
+    tok = rb.Tokens(torch.zeros(2, 1, 8, 16), torch.zeros(2, 1, 2, 16), torch.zeros(2, 1, 2, 16),
+                    torch.zeros(2, 1, 8))
+    with pytest.raises(ValueError):
+        rb.replayssm_decode_step(cfg, st, p, tok, torch.zeros(2, 1, 8, 16))
