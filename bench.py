@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-conventional", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU sample")
+    ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
+                    help="summarise rocprofv3 output of the counter runs into profiles/ and exit")
     return ap.parse_args()
 
 
@@ -78,6 +80,9 @@ def timed_launches(fn, steps, torch):
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the decode path shards by sequence or head group with no "
               "exchange, so only --gpus 1 is run here.", file=sys.stderr)
@@ -154,6 +159,7 @@ def main():
             "batch": shape.batch, "window": L, "read_copy": read_copy or "none",
             "flush_launches_timed": folds,
         },
+        "kernel_source_hash": source_hash(KERNEL_SOURCES),
         "roofline": {
             "bound": "hbm",
             "kernel": "replay_kernel",
@@ -240,6 +246,97 @@ def cpu_baseline(work, gpu_bytes_per_step, target_s):
                   f"OpenMP over sequence/head pairs)",
         "host_cpu": platform.processor() or platform.machine(),
     }
+
+
+PROFILE_CMDS = {
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
+             "python -u bench.py --no-cpu --no-conventional --steps 16 --warmup 16",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- "
+             "python -u bench.py --no-cpu --no-conventional --steps 16 --warmup 16",
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof -o trace -- "
+             "python -u bench.py --no-cpu --steps 32 --warmup 16",
+}
+
+
+def ingest_counters(fetch_dir, write_dir, trace_dir):
+    """Turn the rocprofv3 CSVs of PROFILE_CMDS into profiles/ summaries.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read
+    for the 1 GiB copy probe in the same run (its true traffic is 1 GiB read +
+    1 GiB written), then averaged over the replay kernel's dispatches."""
+    import csv
+    from mamba_state_replay_amd import traffic
+
+    def counters(d, name):
+        rows = list(csv.DictReader(open(next(Path(d).glob("*counter_collection.csv")))))
+        rep = [float(r["Counter_Value"]) for r in rows
+               if "replay_kernel" in r["Kernel_Name"] and r["Counter_Name"] == name]
+        cp = [float(r["Counter_Value"]) for r in rows
+              if "probe_copy_kernel" in r["Kernel_Name"] and r["Counter_Name"] == name]
+        return rep, cp
+
+    def bench_line(d):
+        log = Path(d).parent / (Path(d).name + ".log")
+        for line in reversed(log.read_text().splitlines()):
+            if line.startswith("{"):
+                return json.loads(line)
+        raise ValueError(f"no bench JSON line in {log}")
+
+    f_rep, f_cp = counters(fetch_dir, "FETCH_SIZE")
+    w_rep, w_cp = counters(write_dir, "WRITE_SIZE")
+    line = bench_line(fetch_dir)
+    assert bench_line(write_dir)["kernel_source_hash"] == line["kernel_source_hash"]
+    gib_kib = (1 << 30) / 1024
+    ff = gib_kib / float(np.mean(f_cp))
+    wf = gib_kib / float(np.mean(w_cp))
+    fetch_b = float(np.mean(f_rep)) * ff * 1024
+    write_b = float(np.mean(w_rep)) * wf * 1024
+    L, batch = line["config"]["window"], line["config"]["batch"]
+    sched, _ = traffic.decode_schedule(np.full(batch, L), L, len(f_rep))
+    sz = traffic.sizes(128, 64, 128, 8, 2, None)
+    alg = float(np.mean([traffic.decode_step_bytes(sz, n, f) for n, f in sched]))
+    out = {
+        "kernel": "replay_kernel<64, 128, 256, bf16 inputs, FP32 checkpoint read>",
+        "batch": batch, "window": L, "dispatches": len(f_rep),
+        "source_hash": line["kernel_source_hash"],
+        "fetch_kib_per_dispatch": round(float(np.mean(f_rep)), 1),
+        "write_kib_per_dispatch": round(float(np.mean(w_rep)), 1),
+        "copy_probe_fetch_kib": round(float(np.mean(f_cp)), 1),
+        "copy_probe_write_kib": round(float(np.mean(w_cp)), 1),
+        "fetch_scale": round(ff, 4), "write_scale": round(wf, 4),
+        "bytes_per_launch": int(fetch_b + write_b),
+        "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
+        "algorithmic_bytes_per_launch": int(alg),
+        "traffic_over_algorithmic": round((fetch_b + write_b) / alg, 4),
+        "commands": [PROFILE_CMDS["fetch"], PROFILE_CMDS["write"]],
+    }
+    COUNTERS.write_text(json.dumps(out, indent=1) + "\n")
+
+    rows = list(csv.DictReader(open(next(Path(trace_dir).glob("*kernel_stats.csv")))))
+    md = ["# replay decode, batch 256, L = 16 (Nemotron-3-style Mamba-2 layer): kernel trace and HBM counters", "",
+          "Kernel trace (one MI355X):", "", "```", PROFILE_CMDS["trace"], "```", "",
+          "| kernel | calls | average us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        if "rssm::" not in r["Name"]:
+            continue
+        name = r["Name"].replace("void ", "").replace("rssm::(anonymous namespace)::", "").split("(")[0]
+        md.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    md += ["", "Template arguments: `<headdim, dstate, threads, input type (unsigned short = bf16 bits), "
+           "read mode (0 = FP32 checkpoint)>`. The replay average mixes non-flush and flush launches "
+           "(one in 16 flushes); min is a non-flush launch, max a flush launch.", "",
+           "HBM counters (separate runs, one counter each):", "", "```", PROFILE_CMDS["fetch"],
+           PROFILE_CMDS["write"], "```", "",
+           f"| | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch |", "|---|---|---|",
+           f"| replay_kernel (average of {len(f_rep)} dispatches) | {np.mean(f_rep):.1f} | {np.mean(w_rep):.1f} |",
+           f"| probe_copy_kernel, 1 GiB read + 1 GiB written | {np.mean(f_cp):.1f} | {np.mean(w_cp):.1f} |", "",
+           f"Scale factors from the copy probe: FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {wf:.4f}.",
+           f"Replay kernel: {fetch_b / 1e9:.4f} GB fetched + {write_b / 1e9:.4f} GB written = "
+           f"{(fetch_b + write_b) / 1e9:.4f} GB per launch, against {alg / 1e9:.4f} GB algorithmic "
+           f"(ratio {(fetch_b + write_b) / alg:.4f}).",
+           f"Kernel source hash {line['kernel_source_hash']}."]
+    (ROOT / "profiles" / "replay_decode_batch256_L16.md").write_text("\n".join(md) + "\n")
+    print(json.dumps(out))
 
 
 if __name__ == "__main__":

@@ -20,8 +20,9 @@ extern "C" {
 /* Number of floats `sink` must hold for rssm_probe_read of `bytes` bytes. */
 size_t rssm_probe_sink_elems(size_t bytes);
 
-/* Read `bytes` (a multiple of 32768) from src; one float per 32 KiB block goes
- * to sink so the loads cannot be removed. */
+/* Read `bytes` (a multiple of 32768) from src.  sink (one float per 32 KiB
+ * block) is only written if a block's words xor to a fixed pattern, which
+ * keeps the loads alive without adding traffic. */
 int rssm_probe_read(const void *src, size_t bytes, float *sink, void *stream);
 
 /* Copy `bytes` (a multiple of 32768) from src to dst (non-overlapping). */

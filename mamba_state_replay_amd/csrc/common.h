@@ -52,27 +52,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return u >> 16;
 }
 
-// fp32 -> OCP e4m3fn, round to nearest even, saturating to +-448; NaN -> 0x7F.
-// Normal codes (exponent field 1..15, bias 7) get their 3 mantissa bits by
-// rounding the fp32 mantissa; the subnormal range (|v| < 2^-6) is a multiple
-// of 2^-9, and a rounded multiple of 8 is exactly the smallest normal code.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const float a = fabsf(f);
-    if (!(a == a)) return 0x7Fu;
-    uint32_t code;
-    if (a >= 448.0f) {
-        code = 0x7Eu;
-    } else if (a < 0.015625f) {
-        code = (uint32_t)__builtin_rintf(a * 512.0f);
-    } else {
-        uint32_t ua = __float_as_uint(a);
-        ua += 0x7FFFFu + ((ua >> 20) & 1u);
-        code = (((ua >> 23) - 120u) << 3) | ((ua >> 20) & 7u);
-        if (code > 0x7Eu) code = 0x7Eu;
-    }
-    return sign | code;
+// Four fp32 -> four OCP e4m3fn codes (low byte = a), round to nearest even,
+// saturating: inputs are clamped to +-448 (the largest finite e4m3fn value)
+// and converted by gfx950's fp8 converter; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+    const float lim = 448.0f;
+    a = __builtin_amdgcn_fmed3f(a, -lim, lim);
+    b = __builtin_amdgcn_fmed3f(b, -lim, lim);
+    c = __builtin_amdgcn_fmed3f(c, -lim, lim);
+    d = __builtin_amdgcn_fmed3f(d, -lim, lim);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
 }
 
 // Four e4m3 codes (bytes of w, low byte first) -> fp32, with the hardware

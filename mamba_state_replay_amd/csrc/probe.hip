@@ -23,9 +23,9 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const v4u* src, fl
     uint32_t acc = 0;
 #pragma unroll
     for (int i = 0; i < kVec; ++i) acc ^= r[i].x ^ r[i].y ^ r[i].z ^ r[i].w;
-    float v = __uint_as_float(acc & 0x007FFFFFu);
-    v = group_sum<64>(v);
-    if ((threadIdx.x & 63) == 0) atomicAdd(sink + wg, v);
+    // a store the compiler cannot prove dead keeps the loads; it never happens
+    // for data whose words do not xor to this pattern
+    if (acc == 0x9E3779B9u) sink[wg] = 1.0f;
 }
 
 __global__ __launch_bounds__(kThreads) void probe_copy_kernel(v4u* dst, const v4u* src) {

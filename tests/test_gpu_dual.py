@@ -1,0 +1,212 @@
+"""GPU tests of the dual-precision mode: FP32 checkpoint + bf16 / e4m3 read copy.
+
+* the kernels' e4m3 decoding of every finite code, and their bf16 / e4m3
+  encoding on the cast-only and the flush paths, against host encoders written
+  from the format definitions (tests/formats.py);
+* outputs read from the copy stay within the stated bound of the fp64 oracle;
+* the copy never enters the recurrence: the FP32 checkpoint is bit-identical
+  to an FP32-only run, and a NaN-poisoned copy leaves every flush unchanged
+  (blog section "Benefit 3: Limit error accumulation with separate
+  precisions").
+"""
+import numpy as np
+import pytest
+import torch
+
+from mamba_state_replay_amd import binding as rb
+from mamba_state_replay_amd import staging, synth
+from oracle import oracle as orc_mod
+from tests import formats
+from tests.gpu_util import assert_rows_close, device, head_err, host, say
+
+pytestmark = pytest.mark.gpu
+
+NEMO = dict(nheads=128, headdim=64, dstate=128, ngroups=8)
+UNIT = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -4}   # relative rounding bound of one read
+
+
+def test_e4m3_decode_every_code():
+    """Tile (16 x 16) holding all 256 codes (NaN codes replaced by 0), scale 1,
+    x = 0, dt = 0, C = unit vectors: each output is exactly one decoded code."""
+    dev = device()
+    T = 8
+    cfg = rb.Config(1, 4, 16, 16, 1, window=4, max_drafts=T, in_dtype="f32", read_copy="e4m3")
+    st = rb.State.allocate(cfg, dev)
+    codes = np.arange(256, dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    st.ckpt_read[0, 0].copy_(torch.from_numpy(codes.reshape(16, 16)))
+    st.ckpt_scale.fill_(1.0)
+    p = rb.Params(torch.full((4,), -1.0, device=dev), torch.zeros(4, device=dev))
+    got = np.zeros((16, 16))
+    say("e4m3 decode of every code")
+    for j0 in (0, 8):
+        C = torch.zeros((1, T, 1, 16), device=dev)
+        for q in range(T):
+            C[0, q, 0, j0 + q] = 1.0
+        tok = rb.Tokens(torch.zeros((1, T, 4, 16), device=dev), torch.zeros((1, T, 1, 16), device=dev),
+                        C, torch.zeros((1, T, 4), device=dev))
+        y = torch.empty((1, T, 4, 16), device=dev)
+        rb.replayssm_verify_drafts(cfg, st, p, tok, y)
+        torch.cuda.synchronize()
+        got[:, j0:j0 + T] = host(y)[0, :, 0, :].T
+    expect = formats.decode_e4m3fn(codes).reshape(16, 16)
+    assert np.array_equal(got, expect)
+
+
+def _crafted_values(g, n):
+    """Every finite e4m3 value, every tie between neighbours, values next to the
+    ties, and random magnitudes over the whole range, all within +-448."""
+    val, nan = formats.e4m3fn_table()
+    fin = np.unique(val[~nan])
+    mids = (fin[1:] + fin[:-1]) / 2
+    pool = np.concatenate([fin, mids, np.nextafter(mids, -1e9), np.nextafter(mids, 1e9),
+                           np.exp(g.uniform(-16, 6, n)) * g.choice([-1.0, 1.0], n)])
+    pool = np.clip(pool, -448, 448).astype(np.float32)
+    return g.choice(pool, n)
+
+
+@pytest.mark.parametrize("copy", ["bf16", "e4m3"])
+def test_cast_only_encoding(copy):
+    """flush(FORCE_CAST) with nothing to fold: copy = encode(checkpoint)."""
+    dev = device()
+    g = np.random.default_rng(21)
+    cfg = rb.Config(2, 8, 64, 128, 8, window=16, max_drafts=1, in_dtype="bf16", read_copy=copy)
+    st = rb.State.allocate(cfg, dev)
+    h = _crafted_values(g, 2 * 8 * 64 * 128).reshape(2, 8, 64, 128)
+    h[:, :, 0, 0] = 448.0          # absmax 448 in every tile: e4m3 scale is exactly 1
+    h[:, :, 0, 1] = -448.0
+    st.ckpt.copy_(torch.from_numpy(h))
+    p = rb.Params(torch.full((8,), -1.0, device=dev), torch.zeros(8, device=dev))
+    say(f"cast-only flush {copy}")
+    rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST)
+    torch.cuda.synchronize()
+    assert torch.equal(st.ckpt.cpu(), torch.from_numpy(h)), "cast-only flush changed the FP32 checkpoint"
+    if copy == "bf16":
+        ref = torch.from_numpy(h).to(torch.bfloat16)
+        assert torch.equal(st.ckpt_read.cpu().view(torch.int16), ref.view(torch.int16))
+    else:
+        assert np.all(host(st.ckpt_scale) == 1.0)
+        got = host(st.ckpt_read)
+        assert np.all(formats.same_code(got, formats.encode_e4m3fn(h)))
+
+
+@pytest.mark.parametrize("copy", ["bf16", "e4m3"])
+def test_flush_encoding_and_scale(copy):
+    """A real flush (5 committed records): the copy is the encoding of the new
+    FP32 checkpoint, with scale absmax/448 per tile for e4m3."""
+    dev = device()
+    shape = synth.LayerShape(batch=3, window=16, **NEMO)
+    work = synth.decode_workload(shape, 0, seed=1010, n0=5)
+    cfg = staging.config(shape, read_copy=copy)
+    st = staging.replay_state(cfg, work, dev)
+    p = staging.params(work, dev)
+    say(f"flush encoding {copy}")
+    rb.replayssm_flush(cfg, st, p)
+    torch.cuda.synchronize()
+    H = host(st.ckpt)
+    assert np.all(host(st.meta)[:, 1] == 0)
+    if copy == "bf16":
+        ref = torch.from_numpy(H).to(torch.bfloat16)
+        assert torch.equal(st.ckpt_read.cpu().view(torch.int16), ref.view(torch.int16))
+    else:
+        amax = np.abs(H).max(axis=(-1, -2)).astype(np.float32)
+        sc = (amax / np.float32(448.0)).astype(np.float32)
+        assert np.array_equal(host(st.ckpt_scale), sc)
+        inv = (np.float32(1.0) / sc).astype(np.float32)
+        x = (H * inv[:, :, None, None]).astype(np.float32)
+        assert np.all(formats.same_code(host(st.ckpt_read), formats.encode_e4m3fn(x)))
+
+
+def _run_dual(cfg, work, dev, steps, poison_before=()):
+    st = staging.replay_state(cfg, work, dev)
+    p = staging.params(work, dev)
+    stream = staging.TokenStream(work.steps, dev)
+    if cfg.read_copy:
+        rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST)
+    y = torch.empty((steps, cfg.batch, 1, cfg.nheads, cfg.headdim), device=dev)
+    scales = {}
+    for t in range(steps):
+        if t in poison_before:
+            if cfg.read_copy == "bf16":
+                st.ckpt_read.view(torch.int16).fill_(0x7FC0)
+            else:
+                st.ckpt_read.fill_(0x7F)
+        rb.replayssm_decode_step(cfg, st, p, stream.call(t), y[t])
+        if cfg.read_copy == "e4m3":
+            scales[t] = st.ckpt_scale.clone()
+    torch.cuda.synchronize()
+    return host(y)[:, :, 0], st, {k: host(v) for k, v in scales.items()}
+
+
+@pytest.mark.parametrize("copy", ["bf16", "e4m3"])
+def test_dual_precision_error_bound(copy):
+    """Outputs of non-flush steps read the copy; per element
+    |y - y_ref| <= d_q sum_j |C_q[j]| (u |H_s[i,j]| + delta) + 1e-4 * (head output scale),
+    u = 2^-8 (bf16) or 2^-4 (e4m3), delta = 0 (bf16) or s 2^-10 (e4m3, half the
+    subnormal step scaled), H_s the oracle state at the last flush, d_q the decay
+    since then.  Flushing steps read FP32 registers and meet the FP32 tolerance.
+    The FP32 checkpoint must be bit-identical to an FP32-only run."""
+    dev = device()
+    L, steps = 16, 72
+    shape = synth.LayerShape(batch=4, window=L, **NEMO)
+    work = synth.decode_workload(shape, steps, seed=1011, n0=L)
+    say(f"dual precision {copy}, 72 steps")
+    cfg32 = staging.config(shape)
+    y32, st32, _ = _run_dual(cfg32, work, dev, steps)
+    cfgc = staging.config(shape, read_copy=copy)
+    yc, stc, scales = _run_dual(cfgc, work, dev, steps)
+    assert torch.equal(st32.ckpt, stc.ckpt), "read copy changed the FP32 recurrence"
+    assert torch.equal(st32.meta, stc.meta)
+
+    yref, _ = orc_mod.decode(work, nsteps=steps)
+    # the explicit FORCE_CAST flush folds the L pre-filled records; then a
+    # flush happens at the start of steps L, 2L, ...
+    flush_steps = set(range(L, steps, L))
+    hs = {}
+    for tf in [0] + sorted(flush_steps):
+        _, hs[tf] = orc_mod.decode(work, nsteps=tf)
+    scale = np.abs(yref).max(axis=(0, 3))      # per (seq, head) output scale
+    worst_ratio, per_window = 0.0, []
+    for tf in sorted(hs):
+        win = [t for t in range(tf, min(tf + L, steps)) if t not in flush_steps]
+        Hs = hs[tf]
+        werr = 0.0
+        for t in win:
+            dec = np.exp(work.A[None, :] * work.steps.dt[tf:t + 1].astype(np.float64).sum(0))  # [b][h]
+            Cg = np.repeat(work.steps.C[t].astype(np.float64), shape.nheads // shape.ngroups, axis=1)  # [b][h][ds]
+            if copy == "bf16":
+                delta = 0.0
+            else:
+                sc = scales[max(x for x in [0] + sorted(flush_steps) if x <= t)]
+                delta = (sc.astype(np.float64) * 2.0 ** -10)[:, :, None, None] * 1.001
+            term = UNIT[copy] * np.abs(Hs) + delta                      # [b][h][hd][ds]
+            bound = dec[:, :, None] * np.einsum("bhij,bhj->bhi", term, np.abs(Cg)) + 1e-4 * scale[:, :, None]
+            err = np.abs(yc[t] - yref[t])
+            worst_ratio = max(worst_ratio, float((err / bound).max()))
+            werr = max(werr, float((err / scale[:, :, None]).max()))
+        per_window.append(werr)
+    print(f"[gpu] {copy}: worst error/bound {worst_ratio:.3f}; max normalized error per window {per_window}")
+    assert worst_ratio <= 1.0
+    # read error does not grow with length: every window's error is of the same size as the first's
+    assert max(per_window) <= 4 * per_window[0] + 1e-4
+    fl = sorted(flush_steps)
+    assert_rows_close(yc[fl], yref[fl], what=f"{copy} flushing-step outputs")
+
+
+@pytest.mark.parametrize("copy", ["bf16", "e4m3"])
+def test_poisoned_copy_never_enters_recurrence(copy):
+    """NaN-fill the copy right before a flushing step: that step's outputs (read
+    from FP32 registers) and the checkpoint it writes are unchanged, and later
+    steps read the freshly written copy."""
+    dev = device()
+    L, steps = 8, 20
+    shape = synth.LayerShape(batch=3, window=L, **NEMO)
+    work = synth.decode_workload(shape, steps, seed=1012, n0=L)
+    cfg = staging.config(shape, read_copy=copy)
+    say(f"poisoned {copy} copy")
+    y_clean, st_clean, _ = _run_dual(cfg, work, dev, steps)
+    y_pois, st_pois, _ = _run_dual(cfg, work, dev, steps, poison_before=(L, 2 * L))
+    assert np.all(np.isfinite(y_pois))
+    assert np.array_equal(y_clean, y_pois)
+    assert torch.equal(st_clean.ckpt, st_pois.ckpt)
+    assert torch.equal(st_clean.ckpt_read, st_pois.ckpt_read)
