@@ -25,9 +25,11 @@
  *   - Return value: RSSM_OK or a negative RSSM_ERR_* code; the message is in
  *     replayssm_last_error() (per calling thread).  On an error nothing is
  *     enqueued.
- *   - Errors a kernel finds in the data (a corrupt buffer pointer, an accepted
+ *   - Errors a kernel finds in the data (a corrupt ring pointer, an accepted
  *     count out of range) OR a bit into *status (when status is not NULL),
- *     leave that sequence's state untouched and write NaN to its outputs.
+ *     leave the state of the heads concerned untouched and write NaN to their
+ *     outputs.
+ *   - batch == 0: only the config is checked and nothing is enqueued.
  *   - Calls that share buffers must be ordered on one stream.
  *   - Tile shapes compiled in: (headdim, dstate) = (16, 16), (64, 64),
  *     (64, 128), (128, 128).  nheads % ngroups == 0.  Pointers to tiles,
@@ -59,7 +61,7 @@ extern "C" {
 #define RSSM_ERR_HIP (-5)    /* the HIP runtime refused the launch */
 
 /* Sticky device status bits, OR-ed into *status. */
-#define RSSM_STATUS_META 1u   /* {start, len} out of range: sequence skipped */
+#define RSSM_STATUS_META 1u   /* {start, len} out of range or copies disagree: heads skipped */
 #define RSSM_STATUS_ACCEPT 2u /* accepted count outside 0..T: sequence skipped */
 #define RSSM_STATUS_SLOT 4u   /* conventional: slot index out of range */
 
@@ -80,7 +82,10 @@ typedef struct {
 /*
  * Per-layer decode state.  cap = window + 2*max_drafts - 1 record slots per
  * sequence, used as a ring: record k of the window lives in slot
- * (start + k) % cap.
+ * (start + k) % cap.  Every head keeps its own copy of the ring pointer
+ * {start, len}; all copies of a sequence hold the same values (initialise them
+ * together; the library keeps them equal).  A workgroup then reads and writes
+ * only the copies of the heads it owns and never waits on another workgroup.
  */
 typedef struct {
     float *ckpt;        /* [batch][nheads][headdim][dstate] fp32 checkpoint H_s */
@@ -89,8 +94,7 @@ typedef struct {
     void *buf_x;        /* [batch][nheads][cap][headdim] in_dtype */
     void *buf_B;        /* [batch][ngroups][cap][dstate] in_dtype */
     float *buf_dt;      /* [batch][nheads][cap] fp32 (after softplus) */
-    int32_t *meta;      /* [batch][2] = {ring start, committed length}; start 0 <= start < cap */
-    int32_t *arrive;    /* [batch] zero-initialised once; every call leaves it at zero */
+    int32_t *meta;      /* [batch][nheads][2] = {ring start, committed length}, 0 <= start < cap */
     int32_t *status;    /* one int32 of sticky RSSM_STATUS_* bits, or NULL */
 } rssm_state;
 
@@ -116,8 +120,7 @@ typedef struct {
 #define RSSM_BUF_B 4
 #define RSSM_BUF_DT 5
 #define RSSM_BUF_META 6
-#define RSSM_BUF_ARRIVE 7
-#define RSSM_NUM_BUFS 8
+#define RSSM_NUM_BUFS 7
 
 /* Host only.  Ring capacity cap = window + 2*max_drafts - 1 (or an error code). */
 int replayssm_capacity(const rssm_config *cfg);

@@ -21,9 +21,8 @@ RSSM_F32, RSSM_BF16, RSSM_FP8_E4M3, RSSM_NONE = 0, 1, 2, 3
 RSSM_FLUSH_FORCE_CAST = 1
 RSSM_STATUS_META, RSSM_STATUS_ACCEPT, RSSM_STATUS_SLOT = 1, 2, 4
 RSSM_MAX_DRAFTS, RSSM_MAX_WINDOW = 8, 64
-(BUF_CKPT, BUF_CKPT_READ, BUF_CKPT_SCALE, BUF_X, BUF_B, BUF_DT, BUF_META,
- BUF_ARRIVE) = range(8)
-NUM_BUFS = 8
+(BUF_CKPT, BUF_CKPT_READ, BUF_CKPT_SCALE, BUF_X, BUF_B, BUF_DT, BUF_META) = range(7)
+NUM_BUFS = 7
 
 _DTYPES = {"f32": RSSM_F32, "bf16": RSSM_BF16, "e4m3": RSSM_FP8_E4M3, None: RSSM_NONE,
            "none": RSSM_NONE}
@@ -40,8 +39,7 @@ class rssm_state(ctypes.Structure):
     _fields_ = [("ckpt", ctypes.c_void_p), ("ckpt_read", ctypes.c_void_p),
                 ("ckpt_scale", ctypes.c_void_p), ("buf_x", ctypes.c_void_p),
                 ("buf_B", ctypes.c_void_p), ("buf_dt", ctypes.c_void_p),
-                ("meta", ctypes.c_void_p), ("arrive", ctypes.c_void_p),
-                ("status", ctypes.c_void_p)]
+                ("meta", ctypes.c_void_p), ("status", ctypes.c_void_p)]
 
 
 class rssm_tokens(ctypes.Structure):
@@ -166,8 +164,7 @@ class State:
     buf_x: torch.Tensor
     buf_B: torch.Tensor
     buf_dt: torch.Tensor
-    meta: torch.Tensor
-    arrive: torch.Tensor
+    meta: torch.Tensor          # [batch][nheads][2] {start, len}, one copy per head
     status: torch.Tensor | None
 
     @classmethod
@@ -184,12 +181,11 @@ class State:
             buf_x=z((b, nh, cap, hd), cfg.in_torch),
             buf_B=z((b, ng, cap, ds), cfg.in_torch),
             buf_dt=z((b, nh, cap), torch.float32),
-            meta=z((b, 2), torch.int32),
-            arrive=z((b,), torch.int32),
+            meta=z((b, nh, 2), torch.int32),
             status=z((1,), torch.int32) if status else None,
         )
         for i, t in enumerate([st.ckpt, st.ckpt_read, st.ckpt_scale, st.buf_x, st.buf_B, st.buf_dt,
-                               st.meta, st.arrive]):
+                               st.meta]):
             nbytes = 0 if t is None else t.numel() * t.element_size()
             assert nbytes == sizes[i], (i, nbytes, sizes[i])
         return st
@@ -211,16 +207,14 @@ class State:
         _expect("buf_x", self.buf_x, (b, nh, cap, hd), cfg.in_torch, dev)
         _expect("buf_B", self.buf_B, (b, ng, cap, ds), cfg.in_torch, dev)
         _expect("buf_dt", self.buf_dt, (b, nh, cap), torch.float32, dev)
-        _expect("meta", self.meta, (b, 2), torch.int32, dev)
-        _expect("arrive", self.arrive, (b,), torch.int32, dev)
+        _expect("meta", self.meta, (b, nh, 2), torch.int32, dev)
         if self.status is not None:
             _expect("status", self.status, (1,), torch.int32, dev)
         return dev
 
     def c(self) -> rssm_state:
         return rssm_state(*[_ptr(t) for t in (self.ckpt, self.ckpt_read, self.ckpt_scale, self.buf_x,
-                                              self.buf_B, self.buf_dt, self.meta, self.arrive,
-                                              self.status)])
+                                              self.buf_B, self.buf_dt, self.meta, self.status)])
 
 
 @dataclass

@@ -49,7 +49,8 @@ int check_config(const rssm_config* c, bool need_window) {
         if (c->read_copy != RSSM_NONE && c->read_copy != RSSM_BF16 && c->read_copy != RSSM_FP8_E4M3)
             return fail(RSSM_ERR_DTYPE, "read_copy must be RSSM_NONE, RSSM_BF16 or RSSM_FP8_E4M3");
         const int cap = c->window + 2 * c->max_drafts - 1;
-        if (rssm::replay_lds_bytes(c->headdim, c->dstate, cap, c->max_drafts) > kMaxLds)
+        if (rssm::replay_lds_bytes(c->headdim, c->dstate, cap, c->max_drafts, c->in_dtype == RSSM_BF16 ? 2 : 4) >
+            kMaxLds)
             return fail(RSSM_ERR_SHAPE, "window/max_drafts need more than 64 KiB of LDS");
     }
     return RSSM_OK;
@@ -63,8 +64,8 @@ int read_mode(const rssm_config* c) {
 
 int check_state(const rssm_config* c, const rssm_state* s) {
     if (!s) return fail(RSSM_ERR_NULL, "state is NULL");
-    if (!s->ckpt || !s->buf_x || !s->buf_B || !s->buf_dt || !s->meta || !s->arrive)
-        return fail(RSSM_ERR_NULL, "state: ckpt, buf_x, buf_B, buf_dt, meta and arrive are required");
+    if (!s->ckpt || !s->buf_x || !s->buf_B || !s->buf_dt || !s->meta)
+        return fail(RSSM_ERR_NULL, "state: ckpt, buf_x, buf_B, buf_dt and meta are required");
     if ((c->read_copy == RSSM_NONE) != (s->ckpt_read == nullptr))
         return fail(RSSM_ERR_NULL, "state: ckpt_read must be set iff read_copy != RSSM_NONE");
     if ((c->read_copy == RSSM_FP8_E4M3) != (s->ckpt_scale != nullptr))
@@ -72,7 +73,7 @@ int check_state(const rssm_config* c, const rssm_state* s) {
     if (!aligned(s->ckpt, 16) || !aligned(s->buf_x, 16) || !aligned(s->buf_B, 16) ||
         (s->ckpt_read && !aligned(s->ckpt_read, 16)))
         return fail(RSSM_ERR_SHAPE, "state: ckpt, ckpt_read, buf_x and buf_B must be 16-byte aligned");
-    if (!aligned(s->buf_dt, 4) || !aligned(s->meta, 8) || !aligned(s->arrive, 4) ||
+    if (!aligned(s->buf_dt, 4) || !aligned(s->meta, 8) ||
         (s->ckpt_scale && !aligned(s->ckpt_scale, 4)) || (s->status && !aligned(s->status, 4)))
         return fail(RSSM_ERR_SHAPE, "state: misaligned scalar buffer");
     return RSSM_OK;
@@ -100,7 +101,6 @@ rssm::ReplayArgs replay_args(const rssm_config* c, const rssm_state* s, const rs
     a.buf_B = s->buf_B;
     a.buf_dt = s->buf_dt;
     a.meta = s->meta;
-    a.arrive = s->arrive;
     a.status = s->status;
     a.A = p ? p->A : nullptr;
     a.D = p ? p->D : nullptr;
@@ -164,8 +164,7 @@ int replayssm_sizes(const rssm_config* c, size_t bytes[RSSM_NUM_BUFS]) {
     bytes[RSSM_BUF_X] = tiles * cap * c->headdim * in_bytes;
     bytes[RSSM_BUF_B] = (size_t)c->batch * c->ngroups * cap * c->dstate * in_bytes;
     bytes[RSSM_BUF_DT] = tiles * cap * 4;
-    bytes[RSSM_BUF_META] = (size_t)c->batch * 2 * 4;
-    bytes[RSSM_BUF_ARRIVE] = (size_t)c->batch * 4;
+    bytes[RSSM_BUF_META] = tiles * 2 * 4;
     g_err[0] = '\0';
     return RSSM_OK;
 }
@@ -219,6 +218,7 @@ int replayssm_commit(const rssm_config* cfg, const rssm_state* st, const int32_t
     a.accepted = accepted;
     a.status = st->status;
     a.batch = cfg->batch;
+    a.nheads = cfg->nheads;
     a.T = T;
     a.cap = cfg->window + 2 * cfg->max_drafts - 1;
     return launched(rssm::launch_replay_commit(a, static_cast<hipStream_t>(stream)), "replayssm_commit");

@@ -44,12 +44,13 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN -> canonical quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two fp32 -> two bf16 (low half = a), round to nearest even, with gfx950's
+// packed converter (v_cvt_pk_bf16_f32); NaN stays NaN.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Four fp32 -> four OCP e4m3fn codes (low byte = a), round to nearest even,

@@ -153,17 +153,19 @@ hipError_t conv_shape(const ConvArgs& a, int in_type, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Commit kernels: one thread per sequence.
+// Commit kernels.  Replay: one thread per (sequence, head) copy of the ring
+// pointer; conventional: one thread per sequence.
 __global__ void replay_commit_kernel(const CommitArgs a) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= a.batch) return;
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= a.batch * a.nheads) return;
+    const int b = t / a.nheads;
     const int acc = a.accepted[b];
-    const int n = a.meta[2 * b + 1];
+    const int n = a.meta[2 * t + 1];
     if (acc < 0 || acc > a.T || n < 0 || n + acc > a.cap) {
         if (a.status) atomicOr(a.status, (int)kStatusAccept);
         return;
     }
-    a.meta[2 * b + 1] = n + acc;
+    a.meta[2 * t + 1] = n + acc;
 }
 
 __global__ void conventional_commit_kernel(const CommitArgs a) {
@@ -193,7 +195,8 @@ hipError_t launch_conventional(const ConvArgs& a, int hd, int ds, int in_type, h
 }
 
 hipError_t launch_replay_commit(const CommitArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(replay_commit_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, stream, a);
+    const int n = a.batch * a.nheads;
+    hipLaunchKernelGGL(replay_commit_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

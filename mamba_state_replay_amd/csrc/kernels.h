@@ -23,8 +23,7 @@ struct ReplayArgs {
     void* buf_x;
     void* buf_B;
     float* buf_dt;
-    int32_t* meta;
-    int32_t* arrive;
+    int32_t* meta;      // [batch][nheads][2]
     int32_t* status;
     const void* x;
     const void* B;
@@ -53,15 +52,15 @@ struct ConvArgs {
 };
 
 struct CommitArgs {
-    int32_t* meta;      // replay: [batch][2]
+    int32_t* meta;      // replay: [batch][nheads][2]
     int32_t* slot;      // conventional: [batch]
     const int32_t* accepted;
     int32_t* status;
-    int32_t batch, T, cap, nslots;
+    int32_t batch, nheads, T, cap, nslots;
 };
 
 // Dynamic LDS bytes of the replay kernel for a shape, ring capacity and T.
-size_t replay_lds_bytes(int hd, int ds, int cap, int T);
+size_t replay_lds_bytes(int hd, int ds, int cap, int T, int in_bytes);
 size_t conventional_lds_bytes(int hd, int ds, int T);
 
 // Each returns hipSuccess or the launch error; -1 cast to hipError_t never

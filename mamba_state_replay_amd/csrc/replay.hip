@@ -26,7 +26,9 @@
 //      of each row; the lane that ends up with row i's sum writes
 //      y_q[i] = d_q u_q[i] + sum_{c<=m} w[q][c] s[q][c] x_c[i] + D x_q[i]
 //      (output-only evaluation: no intermediate state is formed);
-//   6. the last workgroup of the sequence to finish advances {start, n}.
+//   6. write the head's new ring pointer.  Every head keeps its own copy of
+//      {start, n} (all copies of a sequence are equal), read and written only
+//      by the workgroup that owns the head, so no workgroup waits on another.
 #include "common.h"
 #include "kernels.h"
 
@@ -275,8 +277,8 @@ __global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs 
     const int T = a.T;
     const size_t tile = (size_t)b * a.nheads + h;
 
-    const int start = a.meta[2 * b];
-    const int n = a.meta[2 * b + 1];
+    const int start = a.meta[2 * tile];
+    const int n = a.meta[2 * tile + 1];
 
     if (!(start >= 0 && start < cap && n >= 0 && n + T <= cap)) {
         if (tid == 0 && h == 0 && a.status) atomicOr(a.status, (int)kStatusMeta);
@@ -438,9 +440,8 @@ __global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs 
                 uint2* out = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.ckpt_read) + tile * HD * DS);
 #pragma unroll
                 for (int s = 0; s < G32::NI; ++s) {
-                    const uint32_t lo = f32_to_bf16(f[s][0]) | (f32_to_bf16(f[s][1]) << 16);
-                    const uint32_t hi = f32_to_bf16(f[s][2]) | (f32_to_bf16(f[s][3]) << 16);
-                    out[(size_t)(row0 + s) * G32::LPR + colv] = make_uint2(lo, hi);
+                    out[(size_t)(row0 + s) * G32::LPR + colv] =
+                        make_uint2(f32x2_to_bf16x2(f[s][0], f[s][1]), f32x2_to_bf16x2(f[s][2], f[s][3]));
                 }
             }
             if constexpr (RM == READ_E4M3) {
@@ -483,16 +484,12 @@ __global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs 
         }
     }
 
-    // ---- 6. advance the sequence's ring pointer (last workgroup of b) ----------------
+    // ---- 6. advance this head's ring pointer -----------------------------------------
     const int new_start = fold && n > 0 ? (start + n) % cap : start;
     const int new_n = (fold ? 0 : n) + (a.mode == MODE_DECODE ? 1 : 0);
     if ((new_start != start || new_n != n) && tid == 0) {
-        const int old = atomicAdd(a.arrive + b, 1);
-        if (old == a.nheads - 1) {
-            a.arrive[b] = 0;
-            a.meta[2 * b] = new_start;
-            a.meta[2 * b + 1] = new_n;
-        }
+        a.meta[2 * tile] = new_start;
+        a.meta[2 * tile + 1] = new_n;
     }
 }
 
@@ -525,7 +522,7 @@ hipError_t launch_shape(const ReplayArgs& a, int in_type, int read_mode, hipStre
 
 }  // namespace
 
-size_t replay_lds_bytes(int hd, int ds, int cap, int T) {
+size_t replay_lds_bytes(int hd, int ds, int cap, int T, int /*in_bytes: records are widened to fp32*/) {
     return (size_t)lds_plan(hd, ds, cap, T).total * sizeof(float);
 }
 

@@ -75,7 +75,8 @@ def config(shape: synth.LayerShape, in_dtype="bf16", read_copy=None, window=None
 
 
 def replay_state(cfg: rb.Config, work: synth.Workload, device) -> rb.State:
-    """State with ckpt = h0 and the n0[b] pre-committed records in slots 0..n0[b]-1."""
+    """State with ckpt = h0 and the n0[b] pre-committed records in slots 0..n0[b]-1
+    (ring pointer {0, n0[b]} in every head's copy)."""
     if int(work.n0.max(initial=0)) > cfg.cap:
         raise ValueError("pre-committed records exceed the ring capacity")
     st = rb.State.allocate(cfg, device)
@@ -95,8 +96,8 @@ def replay_state(cfg: rb.Config, work: synth.Workload, device) -> rb.State:
         st.buf_x.copy_(_dev(bx, "cpu", xdt))
         st.buf_B.copy_(_dev(bB, "cpu", xdt))
         st.buf_dt.copy_(torch.from_numpy(bdt))
-    meta = np.stack([np.zeros_like(work.n0), work.n0], axis=1).astype(np.int32)
-    st.meta.copy_(torch.from_numpy(meta))
+    meta = np.stack([np.zeros_like(work.n0), work.n0], axis=1).astype(np.int32)   # [batch][2]
+    st.meta.copy_(torch.from_numpy(np.repeat(meta[:, None, :], cfg.nheads, axis=1)))
     return st
 
 

@@ -60,7 +60,7 @@ def test_sizes_and_capacity(rb):
     assert sz[rb.BUF_X] == 256 * 128 * 17 * 64 * 2
     assert sz[rb.BUF_B] == 256 * 8 * 17 * 128 * 2
     assert sz[rb.BUF_DT] == 256 * 128 * 17 * 4
-    assert sz[rb.BUF_META] == 256 * 8 and sz[rb.BUF_ARRIVE] == 256 * 4
+    assert sz[rb.BUF_META] == 256 * 128 * 8 and len(sz) == 7
     e4 = rb.Config(256, 128, 64, 128, 8, 16, 3, "bf16", "e4m3")
     assert rb.replayssm_capacity(e4) == 21
     sz = rb.replayssm_sizes(e4)
@@ -104,7 +104,7 @@ def test_null_pointers_rejected_before_launch(rb):
 def test_binding_checks_tensors_on_host(rb):
     cfg = rb.Config(2, 8, 16, 16, 2, window=4, max_drafts=1, in_dtype="f32")
     # CPU tensors are refused before the library is called
-    st = rb.State(*[torch.zeros(1)] * 9)
+    st = rb.State(*[torch.zeros(1)] * 8)
     p = rb.Params(torch.zeros(8), torch.zeros(8))
     tok = rb.Tokens(torch.zeros(2, 1, 8, 16), torch.zeros(2, 1, 2, 16), torch.zeros(2, 1, 2, 16),
                     torch.zeros(2, 1, 8))

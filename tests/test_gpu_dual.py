@@ -104,7 +104,7 @@ def test_flush_encoding_and_scale(copy):
     rb.replayssm_flush(cfg, st, p)
     torch.cuda.synchronize()
     H = host(st.ckpt)
-    assert np.all(host(st.meta)[:, 1] == 0)
+    assert np.all(host(st.meta)[:, :, 1] == 0)
     if copy == "bf16":
         ref = torch.from_numpy(H).to(torch.bfloat16)
         assert torch.equal(st.ckpt_read.cpu().view(torch.int16), ref.view(torch.int16))
