@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--no-conventional", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU sample")
+    ap.add_argument("--config", choices=["decode", "verify", "sweep", "dual"], default="decode",
+                    help="decode: the headline line (default); verify: speculative rounds at batch 512, "
+                         "T=3; sweep: batch x window grid; dual: FP32 / bf16 / e4m3 read copies over "
+                         "4096 steps with error drift against the oracle")
     ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                     help="summarise rocprofv3 output of the counter runs into profiles/ and exit")
     return ap.parse_args()
@@ -87,6 +91,9 @@ def main():
         print("bench.py measures one GPU: the decode path shards by sequence or head group with no "
               "exchange, so only --gpus 1 is run here.", file=sys.stderr)
         sys.exit(2)
+    if args.config != "decode":
+        {"verify": bench_verify, "sweep": bench_sweep, "dual": bench_dual}[args.config](args)
+        return
 
     import torch
     from mamba_state_replay_amd import binding as rb
@@ -246,6 +253,199 @@ def cpu_baseline(work, gpu_bytes_per_step, target_s):
                   f"OpenMP over sequence/head pairs)",
         "host_cpu": platform.processor() or platform.machine(),
     }
+
+
+def _device():
+    import torch
+    return torch, torch.device("cuda", 0)
+
+
+def bench_verify(args):
+    """Speculative verification: batch 512, T = 3 drafts, accepted ~ U{0..3},
+    64 rounds, initial fill U{0..L-1}.  Replay: verify_drafts + commit (pointer
+    move).  Baseline: the conventional kernel writing one FP32 snapshot per
+    draft (4 slots per sequence) + slot-select commit.  Same inputs and
+    acceptance for both."""
+    torch, dev = _device()
+    from mamba_state_replay_amd import binding as rb
+    from mamba_state_replay_amd import staging, synth, traffic
+    T, L, batch, rounds = 3, 16, 512, 64
+    shape = synth.LayerShape(batch=batch, nheads=128, headdim=64, dstate=128, ngroups=8, window=L,
+                             max_drafts=T)
+    work = synth.verify_workload(shape, rounds, T, seed=1003)
+    cfg = staging.config(shape)
+    st = staging.replay_state(cfg, work, dev)
+    p = staging.params(work, dev)
+    toks = staging.TokenStream(work.steps, dev, T=T)
+    acc = torch.from_numpy(work.extra["accepted"]).to(dev)
+    y = torch.empty((batch, T, 128, 64), device=dev)
+    sz = traffic.sizes(128, 64, 128, 8, 2, None)
+    n = work.n0.astype(np.int64).copy()
+    rbytes = []
+    for r in range(rounds):
+        fold = n >= L
+        rbytes.append(traffic.verify_bytes(sz, n, fold, T))
+        n = np.where(fold, 0, n) + work.extra["accepted"][r]
+
+    def replay_round(r):
+        rb.replayssm_verify_drafts(cfg, st, p, toks.call(r), y)
+        rb.replayssm_commit(cfg, st, acc[r], T)
+    ms, per = timed_launches(replay_round, rounds, torch)
+    meta = st.meta.cpu().numpy()
+    assert np.all(meta[:, :, 1] == n[:, None]) and int(st.status.cpu()[0]) == 0
+    replay_us = ms * 1e3 / rounds
+    del st
+    states = staging.conventional_states(cfg, work.h0, T + 1, dev)
+    slot = torch.zeros(batch, dtype=torch.int32, device=dev)
+
+    def snapshot_round(r):
+        rb.conventional_state_update(cfg, states, p, toks.call(r), y, slot=slot)
+        rb.conventional_commit(cfg, slot, T + 1, acc[r], T)
+    cms, cper = timed_launches(snapshot_round, rounds, torch)
+    snap_us = cms * 1e3 / rounds
+    sbytes = traffic.snapshot_verify_bytes(sz, batch, T)
+    ring = batch * 128 * cfg.cap * (64 * 2 + 4) + batch * 8 * cfg.cap * 128 * 2
+    out = {
+        "metric": "speculative verify round us (T=3 drafts, batch 512) + achieved HBM GB/s",
+        "config": {"workload": "Nemotron-3-style Mamba-2 layer, batch 512, T=3 drafts per round, accepted "
+                               "U{0..3}, 64 rounds, L=16, initial fill U{0..15}", "batch": batch, "T": T},
+        "replay": {"us_per_round": round(replay_us, 2), "gbs": round(np.mean(rbytes) / (replay_us * 1e-6) / 1e9, 1),
+                   "algorithmic_bytes_per_round": int(np.mean(rbytes)),
+                   "state_bytes": batch * sz.S + ring},
+        "snapshot_baseline": {"us_per_round": round(snap_us, 2),
+                              "gbs": round(sbytes / (snap_us * 1e-6) / 1e9, 1),
+                              "algorithmic_bytes_per_round": sbytes,
+                              "state_bytes": (T + 1) * batch * sz.S},
+        "speedup": round(snap_us / replay_us, 3),
+        "data": "synthetic", "n_gpus": 1,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_sweep(args):
+    """Batch x window grid of the same layer, 128 decode steps each, steady
+    state (L committed records at start).  Per point: replay amortised us per
+    step, its non-flush and flush launches, and the conventional step.  Points
+    whose FP32 state fits the 256 MB Infinity Cache are labelled as such."""
+    torch, dev = _device()
+    from mamba_state_replay_amd import binding as rb
+    from mamba_state_replay_amd import staging, synth, traffic
+    steps, ntok = 128, 32
+    rows = []
+    for batch in (1, 16, 64, 256, 512):
+        for L in (4, 8, 16, 32):
+            shape = synth.LayerShape(batch=batch, nheads=128, headdim=64, dstate=128, ngroups=8, window=L)
+            work = synth.decode_workload(shape, ntok, seed=1002, n0=L)
+            cfg = staging.config(shape)
+            st = staging.replay_state(cfg, work, dev)
+            p = staging.params(work, dev)
+            toks = staging.TokenStream(work.steps, dev)
+            y = torch.empty((batch, 1, 128, 64), device=dev)
+            for i in range(2 * L):
+                rb.replayssm_decode_step(cfg, st, p, toks.call(i % ntok), y)
+            sched, _ = traffic.decode_schedule(work.n0, L, 2 * L + steps)
+            sched = sched[2 * L:]
+            sz = traffic.sizes(128, 64, 128, 8, 2, None)
+            rbytes = sum(traffic.decode_step_bytes(sz, n, f) for n, f in sched)
+            ms, per = timed_launches(
+                lambda i: rb.replayssm_decode_step(cfg, st, p, toks.call(i % ntok), y), steps, torch)
+            folds = np.array([f.any() for _, f in sched])
+            per = np.array(per)
+            states = staging.conventional_states(cfg, work.h0, 1, dev)
+            for i in range(4):
+                rb.conventional_state_update(cfg, states, p, toks.call(i % ntok), y)
+            cms, cper = timed_launches(
+                lambda i: rb.conventional_state_update(cfg, states, p, toks.call(i % ntok), y), steps, torch)
+            cbytes = traffic.conventional_step_bytes(sz, batch)
+            r_us, c_us = ms * 1e3 / steps, cms * 1e3 / steps
+            rows.append({"batch": batch, "L": L, "replay_us": round(r_us, 2),
+                         "replay_nonflush_us": round(float(per[~folds].mean()) * 1e3, 2),
+                         "replay_flush_us": round(float(per[folds].mean()) * 1e3, 2) if folds.any() else None,
+                         "replay_gbs": round(rbytes / steps / (r_us * 1e-6) / 1e9, 1),
+                         "conventional_us": round(c_us, 2),
+                         "conventional_gbs": round(cbytes / (c_us * 1e-6) / 1e9, 1),
+                         "speedup": round(c_us / r_us, 3),
+                         "state_fits_infinity_cache": batch * sz.S <= 256 * 2 ** 20})
+            del st, states
+            torch.cuda.empty_cache()
+    print(json.dumps({"metric": "decode-step us, replay vs conventional, batch x L sweep",
+                      "config": {"workload": "Nemotron-3-style Mamba-2 layer, 128 decode steps per point, "
+                                             "steady state"},
+                      "points": rows, "data": "synthetic", "n_gpus": 1}), flush=True)
+
+
+def bench_dual(args):
+    """Dual precision: FP32 checkpoint with no copy, a bf16 copy or an e4m3
+    copy.  Throughput: batch 256, L = 16, 4096 decode steps (token inputs cycle
+    through 64 seeded steps).  Accuracy: 8 sequences x all heads over 4096
+    fresh seeded steps against the fp64 oracle, reported per window of L steps
+    (windows start at a flush)."""
+    torch, dev = _device()
+    from mamba_state_replay_amd import binding as rb
+    from mamba_state_replay_amd import staging, synth, traffic
+    from oracle import oracle as orc
+    L, steps = 16, 4096
+    res = {}
+    shape = synth.LayerShape(batch=256, nheads=128, headdim=64, dstate=128, ngroups=8, window=L)
+    work = synth.decode_workload(shape, 64, seed=1004, n0=L)
+    for mode in (None, "bf16", "e4m3"):
+        cfg = staging.config(shape, read_copy=mode)
+        st = staging.replay_state(cfg, work, dev)
+        p = staging.params(work, dev)
+        toks = staging.TokenStream(work.steps, dev)
+        y = torch.empty((256, 1, 128, 64), device=dev)
+        rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST)
+        n0 = np.zeros(256, np.int64)
+        sched, _ = traffic.decode_schedule(n0, L, steps)
+        sz = traffic.sizes(128, 64, 128, 8, 2, mode)
+        tot = sum(traffic.decode_step_bytes(sz, n, f) for n, f in sched)
+        ms, per = timed_launches(lambda i: rb.replayssm_decode_step(cfg, st, p, toks.call(i % 64), y),
+                                 steps, torch)
+        per = np.array(per)
+        folds = np.array([f.any() for _, f in sched])
+        res[mode or "fp32"] = {"us_per_step": round(ms * 1e3 / steps, 2),
+                               "gbs": round(tot / (ms * 1e-3) / 1e9, 1),
+                               "nonflush_launch_us": round(float(per[~folds].mean()) * 1e3, 2),
+                               "flush_launch_us": round(float(per[folds].mean()) * 1e3, 2)}
+        del st
+        torch.cuda.empty_cache()
+    # accuracy over 4096 fresh steps on 8 sequences
+    ashape = synth.LayerShape(batch=8, nheads=128, headdim=64, dstate=128, ngroups=8, window=L)
+    awork = synth.decode_workload(ashape, steps, seed=1005, n0=L)
+    yref, _ = orc.decode(awork, nsteps=steps)
+    for mode in (None, "bf16", "e4m3"):
+        cfg = staging.config(ashape, read_copy=mode)
+        st = staging.replay_state(cfg, awork, dev)
+        p = staging.params(awork, dev)
+        toks = staging.TokenStream(awork.steps, dev)
+        yall = torch.empty((steps, 8, 1, 128, 64), device=dev)
+        rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST)
+        for t in range(steps):
+            rb.replayssm_decode_step(cfg, st, p, toks.call(t), yall[t])
+        torch.cuda.synchronize()
+        yg = yall.cpu().numpy()[:, :, 0].astype(np.float64)
+        per_window = []
+        for w in range(steps // L):
+            sl = slice(w * L + 1, (w + 1) * L)        # non-flush steps of the window
+            ref = yref[sl]
+            scale = np.abs(ref).max(axis=(0, 3))
+            err = np.abs(yg[sl] - ref).max(axis=(0, 3)) / scale
+            per_window.append(float(err.max()))
+        pw = np.array(per_window)
+        q = len(pw) // 4
+        res[mode or "fp32"].update({
+            "max_error_per_window_first_quarter": float(pw[:q].max()),
+            "max_error_per_window_last_quarter": float(pw[-q:].max()),
+            "max_error": float(pw.max()),
+            "mean_error_per_window": float(pw.mean()),
+        })
+        del st, yall
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "dual-precision decode: us per step, HBM GB/s and output error drift "
+                                "vs the fp64 oracle (batch 256, L=16, 4096 steps)",
+                      "config": {"workload": "Nemotron-3-style Mamba-2 layer, batch 256 (throughput) and 8 "
+                                             "sequences x 128 heads (accuracy), L=16, 4096 decode steps"},
+                      "modes": res, "data": "synthetic", "n_gpus": 1}), flush=True)
 
 
 PROFILE_CMDS = {
