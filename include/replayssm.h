@@ -181,6 +181,20 @@ int replayssm_commit(const rssm_config *cfg, const rssm_state *st, const int32_t
                      int32_t T, void *stream);
 
 /*
+ * replayssm_commit(accepted_prev, T_prev) followed by
+ * replayssm_verify_drafts(tok), in one launch: each head's workgroup advances
+ * its own copy of the ring pointer by accepted_prev[b] before it verifies the
+ * new drafts, so a speculative round costs one launch instead of two.  Same
+ * results, bit for bit, as the two calls (blog section "Benefit 2": rollback
+ * is only the pointer move).  An accepted count outside 0..T_prev sets
+ * RSSM_STATUS_ACCEPT, writes NaN outputs and leaves that sequence's state
+ * untouched.
+ */
+int replayssm_commit_verify(const rssm_config *cfg, const rssm_state *st, const rssm_params *p,
+                            const int32_t *accepted_prev, int32_t T_prev, const rssm_tokens *tok,
+                            float *y, void *stream);
+
+/*
  * Baseline: the conventional Mamba-2 decode step, which loads the full state,
  * decays it, adds the rank-1 update, reads the output and stores the state
  * (blog section "Why SSM layers can become a decoding bottleneck"), and its

@@ -66,6 +66,10 @@ _SIGS = {
                                                ctypes.c_void_p, ctypes.c_void_p]),
     "replayssm_commit": (ctypes.c_int, [ctypes.POINTER(rssm_config), ctypes.POINTER(rssm_state),
                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    "replayssm_commit_verify": (ctypes.c_int, [ctypes.POINTER(rssm_config), ctypes.POINTER(rssm_state),
+                                               ctypes.POINTER(rssm_params), ctypes.c_void_p, ctypes.c_int32,
+                                               ctypes.POINTER(rssm_tokens), ctypes.c_void_p,
+                                               ctypes.c_void_p]),
     "conventional_state_update": (ctypes.c_int, [ctypes.POINTER(rssm_config), ctypes.c_void_p,
                                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                                  ctypes.POINTER(rssm_params),
@@ -313,6 +317,19 @@ def replayssm_commit(cfg: Config, state: State, accepted: torch.Tensor, T: int, 
     c, s = cfg.c(), state.c()
     _check("replayssm_commit", lib().replayssm_commit(
         ctypes.byref(c), ctypes.byref(s), _ptr(accepted), int(T), _stream(stream)))
+
+
+def replayssm_commit_verify(cfg: Config, state: State, params: Params, accepted_prev: torch.Tensor,
+                            T_prev: int, tokens: Tokens, y: torch.Tensor, stream=None) -> None:
+    dev = state.validate(cfg)
+    params.validate(cfg, dev)
+    tokens.validate(cfg, dev)
+    _expect("accepted_prev", accepted_prev, (cfg.batch,), torch.int32, dev)
+    _expect("y", y, (cfg.batch, tokens.T, cfg.nheads, cfg.headdim), torch.float32, dev)
+    c, s, p, t = cfg.c(), state.c(), params.c(), tokens.c()
+    _check("replayssm_commit_verify", lib().replayssm_commit_verify(
+        ctypes.byref(c), ctypes.byref(s), ctypes.byref(p), _ptr(accepted_prev), int(T_prev),
+        ctypes.byref(t), _ptr(y), _stream(stream)))
 
 
 def conventional_state_update(cfg: Config, states: torch.Tensor, params: Params, tokens: Tokens,

@@ -119,8 +119,11 @@ int launched(hipError_t e, const char* what) {
 }
 
 int run_replay(const rssm_config* c, const rssm_state* s, const rssm_params* p, const rssm_tokens* t,
-               float* y, int mode, int flags, void* stream, const char* what) {
+               float* y, int mode, int flags, void* stream, const char* what,
+               const int32_t* accepted_prev = nullptr, int32_t T_prev = 0) {
     rssm::ReplayArgs a = replay_args(c, s, p);
+    a.accepted_prev = accepted_prev;
+    a.T_prev = T_prev;
     if (t) {
         a.x = t->x;
         a.B = t->B;
@@ -201,6 +204,23 @@ int replayssm_verify_drafts(const rssm_config* cfg, const rssm_state* st, const 
     if (!rc) rc = check_tokens(tok, p, y, 1, cfg->max_drafts);
     if (rc) return rc;
     return run_replay(cfg, st, p, tok, y, rssm::MODE_VERIFY, 0, stream, "replayssm_verify_drafts");
+}
+
+int replayssm_commit_verify(const rssm_config* cfg, const rssm_state* st, const rssm_params* p,
+                            const int32_t* accepted_prev, int32_t T_prev, const rssm_tokens* tok, float* y,
+                            void* stream) {
+    int rc = check_config(cfg, true);
+    if (rc) return rc;
+    if (T_prev < 1 || T_prev > cfg->max_drafts)
+        return fail(RSSM_ERR_DRAFTS, "T_prev = %d outside 1..%d", T_prev, cfg->max_drafts);
+    if (cfg->batch == 0) return RSSM_OK;
+    if (!accepted_prev) return fail(RSSM_ERR_NULL, "accepted_prev is required");
+    if (!aligned(accepted_prev, 4)) return fail(RSSM_ERR_SHAPE, "misaligned accepted_prev");
+    rc = check_state(cfg, st);
+    if (!rc) rc = check_tokens(tok, p, y, 1, cfg->max_drafts);
+    if (rc) return rc;
+    return run_replay(cfg, st, p, tok, y, rssm::MODE_VERIFY, 0, stream, "replayssm_commit_verify",
+                      accepted_prev, T_prev);
 }
 
 int replayssm_commit(const rssm_config* cfg, const rssm_state* st, const int32_t* accepted, int32_t T,

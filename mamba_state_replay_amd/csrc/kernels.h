@@ -32,8 +32,9 @@ struct ReplayArgs {
     const float* A;
     const float* D;
     float* y;
+    const int32_t* accepted_prev;   // fused commit of the previous verification, or null
     int32_t batch, nheads, ngroups;
-    int32_t L, cap, T;
+    int32_t L, cap, T, T_prev;
     int32_t mode, flags;
 };
 

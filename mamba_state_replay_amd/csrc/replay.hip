@@ -245,6 +245,7 @@ __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& 
             const int row = row0 + idx;
             const int m = w.n + q;
             float acc = lds[L.DQ + q] * (u * scale);
+#pragma unroll 4
             for (int cc = w.first; cc <= m; ++cc)
                 acc = fmaf(lds[L.W + q * w.cap + cc] * lds[L.S + q * w.cap + cc], lds[L.X + cc * HD + row], acc);
             acc = fmaf(Dh, lds[L.X + m * HD + row], acc);
@@ -278,10 +279,18 @@ __global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs 
     const size_t tile = (size_t)b * a.nheads + h;
 
     const int start = a.meta[2 * tile];
-    const int n = a.meta[2 * tile + 1];
+    const int n_stored = a.meta[2 * tile + 1];
+    // Fused commit of the previous verification: len += accepted_prev[b].
+    int acc_prev = 0;
+    bool acc_ok = true;
+    if (a.accepted_prev) {
+        acc_prev = a.accepted_prev[b];
+        acc_ok = acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap;
+    }
+    const int n = n_stored + acc_prev;
 
-    if (!(start >= 0 && start < cap && n >= 0 && n + T <= cap)) {
-        if (tid == 0 && h == 0 && a.status) atomicOr(a.status, (int)kStatusMeta);
+    if (!(acc_ok && start >= 0 && start < cap && n >= 0 && n + T <= cap)) {
+        if (tid == 0 && h == 0 && a.status) atomicOr(a.status, (int)(acc_ok ? kStatusMeta : kStatusAccept));
         for (int o = tid; o < T * HD; o += NT) {
             const int q = o / HD, i = o - q * HD;
             a.y[((size_t)(b * T + q) * a.nheads + h) * HD + i] = __builtin_nanf("");
@@ -375,12 +384,14 @@ __global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs 
             const int m = n + q;
             if (c >= first && c <= m) {
                 float s = 0.f;
+#pragma unroll 4
                 for (int i = c + 1; i <= m; ++i) s += lds[L.AA + i];
                 lds[L.W + q * cap + c] = lds[L.DT + c] * expf(s);
                 if (c == first) lds[L.DQ + q] = expf(s + lds[L.AA + c]);
             }
         } else if (fold && c < n) {
             float s = 0.f;
+#pragma unroll 4
             for (int i = c + 1; i < n; ++i) s += lds[L.AA + i];
             lds[L.WF + c] = lds[L.DT + c] * expf(s);
             if (c == 0) lds[L.DQ + T] = expf(s + lds[L.AA + 0]);
@@ -487,7 +498,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs 
     // ---- 6. advance this head's ring pointer -----------------------------------------
     const int new_start = fold && n > 0 ? (start + n) % cap : start;
     const int new_n = (fold ? 0 : n) + (a.mode == MODE_DECODE ? 1 : 0);
-    if ((new_start != start || new_n != n) && tid == 0) {
+    if ((new_start != start || new_n != n_stored) && tid == 0) {
         a.meta[2 * tile] = new_start;
         a.meta[2 * tile + 1] = new_n;
     }

@@ -96,6 +96,10 @@ def test_null_pointers_rejected_before_launch(rb):
                                        ctypes.byref(t), None, None) == -1
     assert L.conventional_commit(ctypes.byref(c), None, 1, None, 1, None, None) == -2
     assert L.replayssm_decode_step(None, None, None, None, None, None) == -1
+    assert L.replayssm_commit_verify(ctypes.byref(c), ctypes.byref(s), ctypes.byref(p), None, 1,
+                                     ctypes.byref(t), None, None) == -1
+    assert L.replayssm_commit_verify(ctypes.byref(c), ctypes.byref(s), ctypes.byref(p), None, 0,
+                                     ctypes.byref(t), None, None) == -4
     bad = rb.Config(4, 128, 64, 128, 8, in_dtype="bf16").c()
     bad.in_dtype = 7
     assert L.replayssm_sizes(ctypes.byref(bad), (ctypes.c_size_t * 8)()) == -3

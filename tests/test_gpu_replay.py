@@ -264,3 +264,57 @@ def test_zero_batch_is_noop():
     rb.replayssm_decode_step(cfg, st, p, tok, y)
     rb.replayssm_flush(cfg, st, p)
     torch.cuda.synchronize()
+
+
+def test_commit_verify_equals_commit_then_verify_bitwise():
+    """replayssm_commit_verify(a_prev, drafts) == commit(a_prev) then verify_drafts(drafts)."""
+    dev = device()
+    T, rounds = 3, 20
+    shape = synth.LayerShape(batch=6, window=8, max_drafts=T, **NEMO)
+    work = synth.verify_workload(shape, rounds, T, seed=1008)
+    cfg = staging.config(shape)
+    st1 = staging.replay_state(cfg, work, dev)
+    st2 = staging.replay_state(cfg, work, dev)
+    p = staging.params(work, dev)
+    stream = staging.TokenStream(work.steps, dev, T=T)
+    acc = torch.from_numpy(work.extra["accepted"]).to(dev)
+    y1 = torch.empty((shape.batch, T, cfg.nheads, cfg.headdim), device=dev)
+    y2 = torch.empty_like(y1)
+    say("commit_verify vs commit + verify")
+    for r in range(rounds):
+        if r == 0:
+            rb.replayssm_verify_drafts(cfg, st1, p, stream.call(r), y1)
+            rb.replayssm_verify_drafts(cfg, st2, p, stream.call(r), y2)
+        else:
+            rb.replayssm_commit(cfg, st1, acc[r - 1], T)
+            rb.replayssm_verify_drafts(cfg, st1, p, stream.call(r), y1)
+            rb.replayssm_commit_verify(cfg, st2, p, acc[r - 1], T, stream.call(r), y2)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), f"round {r}"
+        assert torch.equal(st1.meta, st2.meta), f"round {r}"
+    rb.replayssm_commit(cfg, st1, acc[rounds - 1], T)
+    rb.replayssm_commit(cfg, st2, acc[rounds - 1], T)
+    rb.replayssm_flush(cfg, st1, p)
+    rb.replayssm_flush(cfg, st2, p)
+    torch.cuda.synchronize()
+    assert torch.equal(st1.ckpt, st2.ckpt) and torch.equal(st1.meta, st2.meta)
+    assert host(st1.status)[0] == 0 and host(st2.status)[0] == 0
+
+
+def test_commit_verify_rejects_bad_accepted_count():
+    dev = device()
+    T = 2
+    shape = synth.LayerShape(batch=3, window=4, max_drafts=T, **NEMO)
+    work = synth.verify_workload(shape, 1, T, seed=1009, n0=1)
+    cfg = staging.config(shape)
+    st = staging.replay_state(cfg, work, dev)
+    p = staging.params(work, dev)
+    tok = staging.TokenStream(work.steps, dev, T=T).call(0)
+    y = torch.zeros((3, T, cfg.nheads, cfg.headdim), device=dev)
+    say("commit_verify with accepted > T")
+    rb.replayssm_commit_verify(cfg, st, p, torch.tensor([1, 3, 0], dtype=torch.int32, device=dev), T, tok, y)
+    torch.cuda.synchronize()
+    assert host(st.status)[0] & rb.RSSM_STATUS_ACCEPT
+    assert torch.isnan(y[1]).all() and torch.isfinite(y[0]).all() and torch.isfinite(y[2]).all()
+    meta = host(st.meta)
+    assert np.all(meta[0, :, 1] == 2) and np.all(meta[1, :, 1] == 1) and np.all(meta[2, :, 1] == 1)
