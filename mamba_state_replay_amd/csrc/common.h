@@ -14,27 +14,37 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // Tile geometry.
 //
-// A (sequence, head) tile is HD rows x DS columns, row-major.  A workgroup of
-// NT threads streams it with 16-byte vector loads: a row is LPR consecutive
-// lanes (one 16-byte vector each), so each load instruction of a wave covers
-// 64/LPR whole rows and every byte of every 128-byte line it touches.  Thread
-// t owns NI consecutive rows (rows rgrp*NI .. rgrp*NI+NI-1, rgrp = t / LPR) at
-// vector column t % LPR; its columns stay fixed across rows, so the C values
-// it multiplies by are loaded once.  EB is the element size of the tile's
-// storage type (4 fp32, 2 bf16, 1 e4m3).
+// A (sequence, head) tile is HD rows x DS columns, row-major, streamed by a
+// workgroup of NT threads with 16-byte vector loads.  A row of VPR vectors is
+// shared by W consecutive lanes (W = 8 where the row has 8 or more vectors):
+// lane j of the row group holds vector columns j, j + W, j + 2W, ... (VPL of
+// them), and the group holds NI consecutive rows.  Thread t's vector s is
+//     row (t / W) * NI + s / VPL,  vector column t % W + W * (s % VPL),
+// so each load instruction (fixed s) of a wave reads whole 128-byte lines,
+// and a row's dot product needs a reduction over only W lanes.  EB is the
+// element size of the tile's storage type (4 fp32, 2 bf16, 1 e4m3).
 // ---------------------------------------------------------------------------
 template <int HD, int DS, int NT, int EB>
 struct TileGeo {
-    static constexpr int EPV = 16 / EB;             // elements per 16-byte vector
-    static constexpr int LPR = DS / EPV;            // lanes per row
-    static constexpr int RPI = NT / LPR;            // rows per load instruction (whole WG)
-    static constexpr int NI = HD >= RPI ? HD / RPI : 1;  // rows per thread
-    static constexpr int ACTIVE = HD >= RPI ? NT : HD * LPR;  // threads that own data
-    static_assert(DS % EPV == 0, "row must be a whole number of 16-byte vectors");
-    static_assert(LPR >= 1 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "lanes per row: power of two <= 32");
-    static_assert(NI <= 16, "too many rows per thread");
-    static_assert(NI <= LPR || LPR == 1, "transposed reduction needs NI <= LPR");
-    static_assert(HD % NI == 0, "rows must split evenly");
+    static constexpr int EPV = 16 / EB;                  // elements per 16-byte vector
+    static constexpr int VPR = DS / EPV;                 // vectors per row
+    static constexpr int W = VPR < 8 ? VPR : 8;          // lanes per row
+    static constexpr int VPL = VPR / W;                  // vectors per lane per row
+    static constexpr int TV = HD * VPR;                  // vectors per tile
+    static constexpr int NV = TV >= NT ? TV / NT : 1;    // vectors per thread
+    static constexpr int ACTIVE = TV >= NT ? NT : TV;    // threads that own data
+    static constexpr int NI = NV / VPL;                  // rows per thread
+    static_assert(DS % EPV == 0 && VPR % W == 0, "row must be whole vectors split evenly over W lanes");
+    static_assert((W & (W - 1)) == 0 && W >= 1 && W <= 8, "lanes per row: power of two <= 8");
+    static_assert(NI >= 1 && NI * VPL == NV && NV <= 8, "thread share: whole rows, at most 8 vectors");
+    static_assert(NI <= W, "transposed reduction needs NI <= W");
+    static_assert(ACTIVE * NV == TV, "tile must split evenly over the workgroup");
+
+    __device__ static __forceinline__ int row0(int t) { return (t / W) * NI; }
+    // Offset of thread t's vector s from the tile base, in 16-byte vectors.
+    __device__ static __forceinline__ int vec(int t, int s) {
+        return (row0(t) + s / VPL) * VPR + (t % W) + W * (s % VPL);
+    }
 };
 
 // ---------------------------------------------------------------------------
@@ -87,9 +97,9 @@ __device__ __forceinline__ float xor_shfl(float v) {
     const int iv = __float_as_int(v);
     int r;
     if constexpr (MASK == 1) {
-        r = __builtin_amdgcn_update_dpp(iv, iv, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+        r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
     } else if constexpr (MASK == 2) {
-        r = __builtin_amdgcn_update_dpp(iv, iv, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+        r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
     } else if constexpr (MASK == 4 || MASK == 8 || MASK == 16) {
         r = __builtin_amdgcn_ds_swizzle(iv, (MASK << 10) | 0x1F);
     } else {
@@ -129,16 +139,24 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 // One halving stage of the transposed reduction: lanes whose MASK bit is set
-// keep the upper half of their N values and hand the lower half to their
-// partner, which does the opposite; each then adds what it receives.
+// end with the sums of the upper half of their N values with their partner's,
+// the others with the sums of the lower half.  For the DPP masks (1, 2) the
+// exchange folds into the add, so both halves are summed and one is kept; for
+// the others each lane sends the half it gives away.
 template <int MASK, int N>
 __device__ __forceinline__ void halve(float (&v)[16], bool upper) {
     constexpr int H = N / 2;
 #pragma unroll
     for (int i = 0; i < H; ++i) {
-        const float keep = upper ? v[i + H] : v[i];
-        const float send = upper ? v[i] : v[i + H];
-        v[i] = keep + xor_shfl<MASK>(send);
+        if constexpr (MASK <= 2) {
+            const float lo = v[i] + xor_shfl<MASK>(v[i]);
+            const float hi = v[i + H] + xor_shfl<MASK>(v[i + H]);
+            v[i] = upper ? hi : lo;
+        } else {
+            const float keep = upper ? v[i + H] : v[i];
+            const float send = upper ? v[i] : v[i + H];
+            v[i] = keep + xor_shfl<MASK>(send);
+        }
     }
 }
 
@@ -179,7 +197,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
 namespace rssm {
 
 // Threads per workgroup for each compiled tile shape: every thread of the
-// large shapes owns 8 rows x one 16-byte fp32 vector (128 bytes of the tile).
+// large shapes owns 128 bytes of the FP32 tile (8 16-byte vectors).
 template <int HD, int DS>
 struct ShapeNT;
 template <>

@@ -9,9 +9,9 @@
 // picked afterwards.
 //
 // One workgroup per (sequence, head) tile, the same streaming layout as the
-// replay kernel: each thread holds NI rows x one 16-byte vector of the tile in
-// registers, updates them in place for every token, writes them out, and
-// reduces the output rows across the lanes of each row.
+// replay kernel (TileGeo): each thread holds NI rows x VPL 16-byte vectors of
+// the tile in registers, updates them in place for every token, writes them
+// out, and reduces the output rows across the W lanes of each row.
 #include "common.h"
 #include "kernels.h"
 
@@ -67,15 +67,14 @@ __global__ __launch_bounds__(NT) void conventional_kernel(const ConvArgs a) {
     };
 
     // Issue the tile loads first; the token staging below overlaps them.
-    const int colv = tid % G::LPR;
-    const int row0 = (tid / G::LPR) * G::NI;
+    const int j = tid % G::W;
+    const int row0 = G::row0(tid);
     const bool active = tid < G::ACTIVE;
-    v4f f[G::NI];
+    v4f f[G::NV];
     if (active) {
         const v4f* src = reinterpret_cast<const v4f*>(state_ptr(s0));
 #pragma unroll
-        for (int s = 0; s < G::NI; ++s)
-            f[s] = __builtin_nontemporal_load(src + (size_t)(row0 + s) * G::LPR + colv);
+        for (int s = 0; s < G::NV; ++s) f[s] = __builtin_nontemporal_load(src + G::vec(tid, s));
     }
 
     const ConvLds L = conv_plan(HD, DS, T);
@@ -109,26 +108,32 @@ __global__ __launch_bounds__(NT) void conventional_kernel(const ConvArgs a) {
         for (int q = 0; q < T; ++q) {
             const float dec = lds[L.DEC + q];
             const float dtq = lds[L.DTS + q];
-            const float4 bv = *reinterpret_cast<const float4*>(lds + L.B + q * DS + colv * 4);
-            const float4 cv = *reinterpret_cast<const float4*>(lds + L.C + q * DS + colv * 4);
             float v[16];
 #pragma unroll
-            for (int s = 0; s < G::NI; ++s) {
-                const float xs = dtq * lds[L.X + q * HD + row0 + s];
-                f[s].x = fmaf(dec, f[s].x, xs * bv.x);
-                f[s].y = fmaf(dec, f[s].y, xs * bv.y);
-                f[s].z = fmaf(dec, f[s].z, xs * bv.z);
-                f[s].w = fmaf(dec, f[s].w, xs * bv.w);
-                v[s] = fmaf(f[s].x, cv.x, fmaf(f[s].y, cv.y, fmaf(f[s].z, cv.z, f[s].w * cv.w)));
+            for (int r = 0; r < G::NI; ++r) v[r] = 0.f;
+#pragma unroll
+            for (int k = 0; k < G::VPL; ++k) {
+                const int col = (j + G::W * k) * 4;
+                const float4 bv = *reinterpret_cast<const float4*>(lds + L.B + q * DS + col);
+                const float4 cv = *reinterpret_cast<const float4*>(lds + L.C + q * DS + col);
+#pragma unroll
+                for (int r = 0; r < G::NI; ++r) {
+                    const float xs = dtq * lds[L.X + q * HD + row0 + r];
+                    v4f& fv = f[r * G::VPL + k];
+                    fv.x = fmaf(dec, fv.x, xs * bv.x);
+                    fv.y = fmaf(dec, fv.y, xs * bv.y);
+                    fv.z = fmaf(dec, fv.z, xs * bv.z);
+                    fv.w = fmaf(dec, fv.w, xs * bv.w);
+                    v[r] = fmaf(fv.x, cv.x, fmaf(fv.y, cv.y, fmaf(fv.z, cv.z, fmaf(fv.w, cv.w, v[r]))));
+                }
             }
             const int dst = nslots == 1 ? 0 : (s0 + 1 + q) % nslots;
             v4f* out = reinterpret_cast<v4f*>(state_ptr(dst));
 #pragma unroll
-            for (int s = 0; s < G::NI; ++s)
-                __builtin_nontemporal_store(f[s], out + (size_t)(row0 + s) * G::LPR + colv);
+            for (int s = 0; s < G::NV; ++s) __builtin_nontemporal_store(f[s], out + G::vec(tid, s));
             int idx;
-            const float u = transpose_reduce<G::NI, G::LPR>(v, lane, idx);
-            if ((lane % G::LPR) < G::NI) lds[L.U + q * HD + row0 + idx] = u;
+            const float u = transpose_reduce<G::NI, G::W>(v, lane, idx);
+            if ((lane % G::W) < G::NI) lds[L.U + q * HD + row0 + idx] = u;
         }
     }
     __syncthreads();

@@ -14,18 +14,20 @@
 //   2. stage the n records and the T query tokens in LDS as fp32 and append
 //      the queries' records to the ring (x and dt by every head, B by the
 //      first head of the group);
-//   3. decay weights w[q][c] = dt_c exp(sum_{c<i<=m_q} a_i) (one thread per
-//      (query, record) pair, segment sums, never ratios of exponentials) and
-//      the group scores s[q][c] = B_c . C_q (one wave per pair);
+//   3. per (query, record) pair, one 8-lane group forms the coefficient
+//      co[q][c] = dt_c exp(sum_{c<i<=m_q} a_i) (B_c . C_q) (+ D_h when c is
+//      the query's own record), splitting both the segment sum (never ratios
+//      of exponentials) and the score over its lanes; the same groups form
+//      the flush weights dt_c exp(sum_{c<i<n} a_i);
 //   4. flush: H = exp(sum a) H_s + sum_k dt_k exp(sum_{k<i<n} a_i) x_k B_k^T,
 //      the rank-n update applied to the tile in registers, written once, with
 //      the read copy cast from the same registers (section "Benefit 3": the
 //      copy is never read back into the recurrence);
-//   5. per query, u_q = H C_q from the same registers (section "Benefit 2":
-//      the checkpoint is read once for all queries), reduced across the lanes
-//      of each row; the lane that ends up with row i's sum writes
-//      y_q[i] = d_q u_q[i] + sum_{c<=m} w[q][c] s[q][c] x_c[i] + D x_q[i]
-//      (output-only evaluation: no intermediate state is formed);
+//   5. per query, every thread forms its share of d_q (H C_q)[i] plus its
+//      share of sum_c co[q][c] x_c[i] for each of its rows (section "Benefit
+//      2": the checkpoint is read once for all queries; output-only
+//      evaluation: no intermediate state is formed), and one reduction over
+//      the W lanes of each row gives y_q[i];
 //   6. write the head's new ring pointer.  Every head keeps its own copy of
 //      {start, n} (all copies of a sequence are equal), read and written only
 //      by the workgroup that owns the head, so no workgroup waits on another.
@@ -36,21 +38,23 @@ namespace rssm {
 
 namespace {
 
-// LDS plan in floats.
+// LDS plan in floats.  x rows are padded to XS = HD + 4 floats so that the
+// lanes of a row group, each reading a different record's x rows in step 5,
+// fall on different banks.
 struct Lds {
-    int X, K, Cq, DT, AA, W, S, DQ, WF, RED, total;
+    int X, XS, K, Cq, DT, AA, CO, DQ, WF, RED, total;
 };
 
 __host__ __device__ inline Lds lds_plan(int HD, int DS, int cap, int T) {
     Lds l;
     int o = 0;
-    l.X = o;  o += cap * HD;   // x of records then queries, window order
+    l.XS = HD + 4;
+    l.X = o;  o += cap * l.XS; // x of records then queries, window order
     l.K = o;  o += cap * DS;   // B of records then queries
     l.Cq = o; o += T * DS;     // C of the queries
     l.DT = o; o += cap;        // dt, window order
     l.AA = o; o += cap;        // a = dt * A
-    l.W = o;  o += T * cap;    // w[q][c] = dt_c exp(sum_{c<i<=m_q} a_i)
-    l.S = o;  o += T * cap;    // s[q][c] = B_c . C_q
+    l.CO = o; o += T * cap;    // co[q][c] = dt_c exp(sum_{c<i<=m_q} a_i) (B_c . C_q) [+ D at c = m_q]
     l.DQ = o; o += T + 1;      // d_q = exp(sum_{first<=i<=m_q} a_i); [T] = flush decay
     l.WF = o; o += cap;        // flush weights dt_c exp(sum_{c<i<n} a_i)
     l.RED = o; o += 16;        // cross-wave reductions
@@ -59,93 +63,68 @@ __host__ __device__ inline Lds lds_plan(int HD, int DS, int cap, int T) {
 }
 
 // This thread's share of a tile held as raw 16-byte vectors (issued in step
-// 1, consumed in step 4): NI vectors of the tile's element size EB, in one
-// register array sized for the FP32 tile so the FP32 and read-copy paths
-// share it.  widen() gives fp32 rows: f[s][e] is element (row0 + s,
-// colv*EPV + e) of the thread's rows.
+// 1, consumed in steps 4 and 5): NV vectors of the tile's element size EB,
+// laid out as TileGeo describes, in one register array sized for the FP32
+// tile so the FP32 and read-copy paths share it.
 template <int HD, int DS, int NT>
 struct TileRegs {
-    static constexpr int NMAX = TileGeo<HD, DS, NT, 4>::NI;
+    static constexpr int NMAX = TileGeo<HD, DS, NT, 4>::NV;
     v4u raw[NMAX];
 
     template <int EB>
     __device__ __forceinline__ void load(const void* tile, int tid) {
         using G = TileGeo<HD, DS, NT, EB>;
-        static_assert(G::NI <= NMAX, "copy tile needs more vectors than the FP32 tile");
+        static_assert(G::NV <= NMAX, "copy tile needs more vectors than the FP32 tile");
         if (tid >= G::ACTIVE) return;
-        const int colv = tid % G::LPR;
-        const int row0 = (tid / G::LPR) * G::NI;
         const v4u* base = reinterpret_cast<const v4u*>(tile);
 #pragma unroll
-        for (int s = 0; s < G::NI; ++s)
-            raw[s] = __builtin_nontemporal_load(base + (size_t)(row0 + s) * G::LPR + colv);
+        for (int s = 0; s < G::NV; ++s) raw[s] = __builtin_nontemporal_load(base + G::vec(tid, s));
     }
 
-    // Row s of this thread's share, widened to fp32 (16 / EB values).
+    // v[r] += (vector k of row r) . ck for each of the thread's NI rows; ck
+    // holds the EPV columns of C under that vector.  Low-precision words are
+    // widened one at a time, next to their use, so such a row never occupies
+    // a full set of fp32 registers.
     template <int EB>
-    __device__ __forceinline__ void widen_row(int s, float* f) const {
-        const uint32_t w[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
-        if constexpr (EB == 4) {
+    __device__ __forceinline__ void dot_vec(int k, const float* ck, float* v) const {
+        using G = TileGeo<HD, DS, NT, EB>;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(w[e]);
-        } else if constexpr (EB == 2) {
+        for (int r = 0; r < G::NI; ++r) {
+            const v4u rv = raw[r * G::VPL + k];
+            const uint32_t w[4] = {rv.x, rv.y, rv.z, rv.w};
+            float acc = v[r];
+            if constexpr (EB == 4) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                f[2 * e] = __uint_as_float(w[e] << 16);
-                f[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+                for (int e = 0; e < 4; ++e) acc = fmaf(__uint_as_float(w[e]), ck[e], acc);
+            } else if constexpr (EB == 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t we = w[e];
+                    asm volatile("" : "+v"(we));   // keep the widening inside the query loop
+                    acc = fmaf(__uint_as_float(we << 16), ck[2 * e], acc);
+                    acc = fmaf(__uint_as_float(we & 0xFFFF0000u), ck[2 * e + 1], acc);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t we = w[e];
+                    asm volatile("" : "+v"(we));   // decode next to its use, per query
+                    float f[4];
+                    e4m3x4_to_f32(we, f);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc = fmaf(f[i], ck[4 * e + i], acc);
+                }
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) e4m3x4_to_f32(w[e], f + 4 * e);
+            v[r] = acc;
         }
     }
 
-    // sum_e row_s[e] * c[e] over this thread's 16 / EB columns of row s; c
-    // points at those columns of C in LDS.  Widens and multiplies one 32-bit
-    // word at a time so a low-precision row never occupies 16 fp32 registers.
-    template <int EB>
-    __device__ __forceinline__ float dot_row(int s, const float* c) const {
-        const uint32_t w[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
-        float acc = 0.f;
-        if constexpr (EB == 4) {
-            const float4 cv = *reinterpret_cast<const float4*>(c);
-            acc = fmaf(__uint_as_float(w[0]), cv.x, acc);
-            acc = fmaf(__uint_as_float(w[1]), cv.y, acc);
-            acc = fmaf(__uint_as_float(w[2]), cv.z, acc);
-            acc = fmaf(__uint_as_float(w[3]), cv.w, acc);
-        } else if constexpr (EB == 2) {
-#pragma unroll
-            for (int e = 0; e < 4; e += 2) {
-                uint32_t w0 = w[e], w1 = w[e + 1];
-                // keep the widening next to its use (not hoisted out of the query loop)
-                asm volatile("" : "+v"(w0), "+v"(w1));
-                const float4 cv = *reinterpret_cast<const float4*>(c + 2 * e);
-                acc = fmaf(__uint_as_float(w0 << 16), cv.x, acc);
-                acc = fmaf(__uint_as_float(w0 & 0xFFFF0000u), cv.y, acc);
-                acc = fmaf(__uint_as_float(w1 << 16), cv.z, acc);
-                acc = fmaf(__uint_as_float(w1 & 0xFFFF0000u), cv.w, acc);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t we = w[e];
-                asm volatile("" : "+v"(we));   // decode next to its use, per query
-                const float4 cv = *reinterpret_cast<const float4*>(c + 4 * e);
-                float f[4];
-                e4m3x4_to_f32(we, f);
-                acc = fmaf(f[0], cv.x, acc);
-                acc = fmaf(f[1], cv.y, acc);
-                acc = fmaf(f[2], cv.z, acc);
-                acc = fmaf(f[3], cv.w, acc);
-            }
-        }
-        return acc;
-    }
-
-    // All NMAX rows as fp32 (FP32 tile only).
+    // All NMAX vectors as fp32 (FP32 tile only).
     __device__ __forceinline__ void widen(float (&f)[NMAX][4]) const {
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s) widen_row<4>(s, f[s]);
+        for (int s = 0; s < NMAX; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[s][e] = __uint_as_float(raw[s][e]);
     }
 
     __device__ __forceinline__ void set(const float (&f)[NMAX][4]) {
@@ -171,7 +150,7 @@ struct StageMap {
     const void* Bt;
     const void* Ct;
     int start, n, cap, T, b, h, g, nheads, ngroups, nx, nb;
-    int ldsX, ldsK, ldsC;
+    int ldsX, ldsXS, ldsK, ldsC;
     bool append_x, append_B;
 };
 
@@ -200,7 +179,7 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
                     ((size_t)(m.b * m.T + c - m.n) * m.nheads + m.h) * VR + cv;
             if (m.append_x) j.app = const_cast<uint4*>(ring);
         }
-        j.dst = m.ldsX + c * HD + cv * EPVIN;
+        j.dst = m.ldsX + c * m.ldsXS + cv * EPVIN;
     } else if (v < m.nx + m.nb) {
         const int u = v - m.nx;
         const int c = u / VS, cv = u - c * VS;
@@ -222,35 +201,65 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
     return j;
 }
 
-// Step 5 for one tile held in registers with element size EB: for every
-// query, reduce u_q over the lanes of each row, then the lane holding row i's
-// sum writes y_q[i].  Rows are widened to fp32 one at a time, inside the query
-// loop, so a low-precision tile never needs a full fp32 copy in registers.
+// Step 5 for one tile held in registers with element size EB.  For query q
+// the thread forms, for each of its NI rows, d_q * (its columns' share of
+// H C_q) plus its share of the record terms: lane j of a row group takes the
+// records c = first + j, first + j + W, ... and adds co[q][c] x_c[row] (the
+// D x_q term rides on co[q][m_q]).  One transposed reduction over the row's
+// W lanes then leaves y_q[row] on one lane, which stores it.
 template <int HD, int DS, int NT, int EB>
 __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& t, const float* lds,
-                                                    const Lds& L, const Window& w, float scale, float Dh,
+                                                    const Lds& L, const Window& w, float scale,
                                                     float* y_head, size_t y_qstride, int tid) {
     using G = TileGeo<HD, DS, NT, EB>;
-    const int colv = tid % G::LPR;
-    const int row0 = (tid / G::LPR) * G::NI;
+    const int j = tid % G::W;
+    const int row0 = G::row0(tid);
     const int lane = tid & 63;
     for (int q = 0; q < w.T; ++q) {
-        const float* c = lds + L.Cq + q * DS + colv * G::EPV;
         float v[16];
 #pragma unroll
-        for (int s = 0; s < G::NI; ++s) v[s] = t.template dot_row<EB>(s, c);
-        int idx;
-        const float u = transpose_reduce<G::NI, G::LPR>(v, lane, idx);
-        if ((lane % G::LPR) < G::NI) {
-            const int row = row0 + idx;
-            const int m = w.n + q;
-            float acc = lds[L.DQ + q] * (u * scale);
-#pragma unroll 4
-            for (int cc = w.first; cc <= m; ++cc)
-                acc = fmaf(lds[L.W + q * w.cap + cc] * lds[L.S + q * w.cap + cc], lds[L.X + cc * HD + row], acc);
-            acc = fmaf(Dh, lds[L.X + m * HD + row], acc);
-            y_head[q * y_qstride + row] = acc;
+        for (int r = 0; r < G::NI; ++r) v[r] = 0.f;
+#pragma unroll
+        for (int k = 0; k < G::VPL; ++k) {
+            float c[G::EPV];
+#pragma unroll
+            for (int e = 0; e < G::EPV; e += 4) {
+                const float4 cv =
+                    *reinterpret_cast<const float4*>(lds + L.Cq + q * DS + (j + G::W * k) * G::EPV + e);
+                c[e] = cv.x;
+                c[e + 1] = cv.y;
+                c[e + 2] = cv.z;
+                c[e + 3] = cv.w;
+            }
+            t.template dot_vec<EB>(k, c, v);
         }
+        const float dq = lds[L.DQ + q] * scale;
+#pragma unroll
+        for (int r = 0; r < G::NI; ++r) v[r] *= dq;
+        const int m = w.n + q;
+        for (int cc = w.first + j; cc <= m; cc += G::W) {
+            const float co = lds[L.CO + q * w.cap + cc];
+            const float* xr = lds + L.X + cc * L.XS + row0;
+            if constexpr (G::NI % 4 == 0) {
+#pragma unroll
+                for (int r = 0; r < G::NI; r += 4) {
+                    const float4 xv = *reinterpret_cast<const float4*>(xr + r);
+                    v[r] = fmaf(co, xv.x, v[r]);
+                    v[r + 1] = fmaf(co, xv.y, v[r + 1]);
+                    v[r + 2] = fmaf(co, xv.z, v[r + 2]);
+                    v[r + 3] = fmaf(co, xv.w, v[r + 3]);
+                }
+            } else if constexpr (G::NI == 2) {
+                const float2 xv = *reinterpret_cast<const float2*>(xr);
+                v[0] = fmaf(co, xv.x, v[0]);
+                v[1] = fmaf(co, xv.y, v[1]);
+            } else {
+                v[0] = fmaf(co, xr[0], v[0]);
+            }
+        }
+        int idx;
+        const float u = transpose_reduce<G::NI, G::W>(v, lane, idx);
+        if ((lane % G::W) < G::NI) y_head[q * y_qstride + row0 + idx] = u;
     }
 }
 
@@ -321,7 +330,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs 
     const int nv = nx + nb + nc;
 
     const StageMap sm{bx, bB, xt, Bt, Ct, start, n, cap, T, b, h, g, a.nheads, a.ngroups,
-                      nx, nb, L.X, L.K, L.Cq, append, append && writer};
+                      nx, nb, L.X, L.XS, L.K, L.Cq, append, append && writer};
     uint4 jv[JOBS];
 #pragma unroll
     for (int j = 0; j < JOBS; ++j) {
@@ -377,32 +386,53 @@ __global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs 
     }
     __syncthreads();
 
-    // ---- 3. decay weights and scores ------------------------------------------------
-    for (int p = tid; p < (T + 1) * cap; p += NT) {
-        const int q = p / cap, c = p - q * cap;
-        if (q < T) {
-            const int m = n + q;
-            if (c >= first && c <= m) {
-                float s = 0.f;
-#pragma unroll 4
-                for (int i = c + 1; i <= m; ++i) s += lds[L.AA + i];
-                lds[L.W + q * cap + c] = lds[L.DT + c] * expf(s);
-                if (c == first) lds[L.DQ + q] = expf(s + lds[L.AA + c]);
+    // ---- 3. coefficients: one 8-lane group per (query, record) pair ---------------
+    // Pairs (q, c), c = first .. m_q, give co[q][c]; when the call folds, the n
+    // pairs (T, c), c < n, give the flush weights.  The group's lanes split the
+    // segment sum of a over (c, m] and the score B_c . C_q, and reduce both.
+    {
+        constexpr int NG = NT / 8;
+        const int sub = tid & 7;
+        const int per0 = n - first + 1;                      // pairs of query 0
+        const int nflush = fold ? n : 0;
+        const int npairs = nflush + T * per0 + T * (T - 1) / 2;
+        for (int p = tid >> 3; p < npairs; p += NG) {
+            int q, c;
+            if (p < nflush) {
+                q = T;
+                c = p;
+            } else {
+                int r = p - nflush;
+                q = 0;
+                while (r >= per0 + q) r -= per0 + q++;
+                c = first + r;
             }
-        } else if (fold && c < n) {
-            float s = 0.f;
-#pragma unroll 4
-            for (int i = c + 1; i < n; ++i) s += lds[L.AA + i];
-            lds[L.WF + c] = lds[L.DT + c] * expf(s);
-            if (c == 0) lds[L.DQ + T] = expf(s + lds[L.AA + 0]);
-        }
-    }
-    for (int q = 0; q < T; ++q) {
-        for (int c = first + wave; c <= n + q; c += NW) {
-            float p = 0.f;
-            for (int j = lane; j < DS; j += 64) p = fmaf(lds[L.K + c * DS + j], lds[L.Cq + q * DS + j], p);
-            p = group_sum<64>(p);
-            if (lane == 0) lds[L.S + q * cap + c] = p;
+            const int m = q < T ? n + q : n - 1;             // last record the weight spans
+            float seg = 0.f;
+            for (int i = c + 1 + sub; i <= m; i += 8) seg += lds[L.AA + i];
+            float sc = 0.f;
+            if (q < T) {
+                for (int j4 = sub; j4 < DS / 4; j4 += 8) {
+                    const float4 kb = *reinterpret_cast<const float4*>(lds + L.K + c * DS + 4 * j4);
+                    const float4 cq = *reinterpret_cast<const float4*>(lds + L.Cq + q * DS + 4 * j4);
+                    sc = fmaf(kb.x, cq.x, sc);
+                    sc = fmaf(kb.y, cq.y, sc);
+                    sc = fmaf(kb.z, cq.z, sc);
+                    sc = fmaf(kb.w, cq.w, sc);
+                }
+                sc = group_sum<8>(sc);
+            }
+            seg = group_sum<8>(seg);
+            if (sub == 0) {
+                const float wgt = lds[L.DT + c] * expf(seg);
+                if (q < T) {
+                    lds[L.CO + q * cap + c] = fmaf(wgt, sc, c == m ? Dh : 0.f);
+                    if (c == first) lds[L.DQ + q] = expf(seg + lds[L.AA + c]);
+                } else {
+                    lds[L.WF + c] = wgt;
+                    if (c == 0) lds[L.DQ + T] = expf(seg + lds[L.AA + 0]);
+                }
+            }
         }
     }
     __syncthreads();
@@ -412,10 +442,10 @@ __global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs 
     float* y_head = a.y ? a.y + ((size_t)b * T * a.nheads + h) * HD : nullptr;
     const size_t y_qstride = (size_t)a.nheads * HD;
     if (fold) {
-        float f[G32::NI][4];
+        float f[G32::NV][4];
         const bool active = tid < G32::ACTIVE;
-        const int colv = tid % G32::LPR;
-        const int row0 = (tid / G32::LPR) * G32::NI;
+        const int j = tid % G32::W;
+        const int row0 = G32::row0(tid);
         float* ck = a.ckpt + tile * HD * DS;
         float amax = 0.f;
         if (active) {
@@ -423,41 +453,44 @@ __global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs 
             if (n > 0) {
                 const float df = lds[L.DQ + T];
 #pragma unroll
-                for (int s = 0; s < G32::NI; ++s)
+                for (int s = 0; s < G32::NV; ++s)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) f[s][e] *= df;
                 for (int c = 0; c < n; ++c) {
                     const float wf = lds[L.WF + c];
-                    const float4 kb = *reinterpret_cast<const float4*>(lds + L.K + c * DS + colv * 4);
                     float xs[G32::NI];
 #pragma unroll
-                    for (int s = 0; s < G32::NI; ++s) xs[s] = lds[L.X + c * HD + row0 + s] * wf;
+                    for (int r = 0; r < G32::NI; ++r) xs[r] = lds[L.X + c * L.XS + row0 + r] * wf;
 #pragma unroll
-                    for (int s = 0; s < G32::NI; ++s) {
-                        f[s][0] = fmaf(xs[s], kb.x, f[s][0]);
-                        f[s][1] = fmaf(xs[s], kb.y, f[s][1]);
-                        f[s][2] = fmaf(xs[s], kb.z, f[s][2]);
-                        f[s][3] = fmaf(xs[s], kb.w, f[s][3]);
+                    for (int k = 0; k < G32::VPL; ++k) {
+                        const float4 kb = *reinterpret_cast<const float4*>(lds + L.K + c * DS + (j + G32::W * k) * 4);
+#pragma unroll
+                        for (int r = 0; r < G32::NI; ++r) {
+                            float* fv = f[r * G32::VPL + k];
+                            fv[0] = fmaf(xs[r], kb.x, fv[0]);
+                            fv[1] = fmaf(xs[r], kb.y, fv[1]);
+                            fv[2] = fmaf(xs[r], kb.z, fv[2]);
+                            fv[3] = fmaf(xs[r], kb.w, fv[3]);
+                        }
                     }
                 }
                 v4f* out = reinterpret_cast<v4f*>(ck);
 #pragma unroll
-                for (int s = 0; s < G32::NI; ++s) {
+                for (int s = 0; s < G32::NV; ++s) {
                     const v4f val = {f[s][0], f[s][1], f[s][2], f[s][3]};
-                    __builtin_nontemporal_store(val, out + (size_t)(row0 + s) * G32::LPR + colv);
+                    __builtin_nontemporal_store(val, out + G32::vec(tid, s));
                 }
             }
             if constexpr (RM == READ_BF16) {
                 uint2* out = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.ckpt_read) + tile * HD * DS);
 #pragma unroll
-                for (int s = 0; s < G32::NI; ++s) {
-                    out[(size_t)(row0 + s) * G32::LPR + colv] =
+                for (int s = 0; s < G32::NV; ++s)
+                    out[G32::vec(tid, s)] =
                         make_uint2(f32x2_to_bf16x2(f[s][0], f[s][1]), f32x2_to_bf16x2(f[s][2], f[s][3]));
-                }
             }
             if constexpr (RM == READ_E4M3) {
 #pragma unroll
-                for (int s = 0; s < G32::NI; ++s)
+                for (int s = 0; s < G32::NV; ++s)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(f[s][e]));
             }
@@ -474,24 +507,22 @@ __global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs 
             if (active) {
                 uint32_t* out = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.ckpt_read) + tile * HD * DS);
 #pragma unroll
-                for (int s = 0; s < G32::NI; ++s) {
-                    out[(size_t)(row0 + s) * G32::LPR + colv] =
-                        f32x4_to_e4m3(f[s][0] * inv, f[s][1] * inv, f[s][2] * inv, f[s][3] * inv);
-                }
+                for (int s = 0; s < G32::NV; ++s)
+                    out[G32::vec(tid, s)] = f32x4_to_e4m3(f[s][0] * inv, f[s][1] * inv, f[s][2] * inv, f[s][3] * inv);
             }
             if (tid == 0) a.ckpt_scale[tile] = sc;
         }
         if (active && T > 0) {
             treg.set(f);
-            queries_and_outputs<HD, DS, NT, 4>(treg, lds, L, win, 1.0f, Dh, y_head, y_qstride, tid);
+            queries_and_outputs<HD, DS, NT, 4>(treg, lds, L, win, 1.0f, y_head, y_qstride, tid);
         }
     } else if constexpr (RM == READ_F32) {
         if (tid < G32::ACTIVE)
-            queries_and_outputs<HD, DS, NT, 4>(treg, lds, L, win, 1.0f, Dh, y_head, y_qstride, tid);
+            queries_and_outputs<HD, DS, NT, 4>(treg, lds, L, win, 1.0f, y_head, y_qstride, tid);
     } else {
         if (tid < TileGeo<HD, DS, NT, EBC>::ACTIVE) {
             const float sc = RM == READ_E4M3 ? a.ckpt_scale[tile] : 1.0f;
-            queries_and_outputs<HD, DS, NT, EBC>(treg, lds, L, win, sc, Dh, y_head, y_qstride, tid);
+            queries_and_outputs<HD, DS, NT, EBC>(treg, lds, L, win, sc, y_head, y_qstride, tid);
         }
     }
 
