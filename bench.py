@@ -53,10 +53,12 @@ def parse():
     ap.add_argument("--no-conventional", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU sample")
-    ap.add_argument("--config", choices=["decode", "verify", "sweep", "dual"], default="decode",
+    ap.add_argument("--config", choices=["decode", "verify", "verify_sweep", "sweep", "dual"], default="decode",
                     help="decode: the headline line (default); verify: speculative rounds at batch 512, "
-                         "T=3; sweep: batch x window grid; dual: FP32 / bf16 / e4m3 read copies over "
-                         "4096 steps with error drift against the oracle")
+                         "T=3; verify_sweep: the same for T in 1, 2, 3, 4, 8; sweep: batch x window grid; "
+                         "dual: FP32 / bf16 / e4m3 read copies over 4096 steps")
+    ap.add_argument("--summarize-configs", nargs="+", metavar="LOG",
+                    help="write the tables of bench logs of the non-default configs into profiles/ and exit")
     ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                     help="summarise rocprofv3 output of the counter runs into profiles/ and exit")
     return ap.parse_args()
@@ -87,12 +89,16 @@ def main():
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters)
         return
+    if args.summarize_configs:
+        summarize_configs(args.summarize_configs)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the decode path shards by sequence or head group with no "
               "exchange, so only --gpus 1 is run here.", file=sys.stderr)
         sys.exit(2)
     if args.config != "decode":
-        {"verify": bench_verify, "sweep": bench_sweep, "dual": bench_dual}[args.config](args)
+        {"verify": bench_verify, "verify_sweep": bench_verify_sweep, "sweep": bench_sweep,
+         "dual": bench_dual}[args.config](args)
         return
 
     import torch
@@ -260,19 +266,19 @@ def _device():
     return torch, torch.device("cuda", 0)
 
 
-def bench_verify(args):
-    """Speculative verification: batch 512, T = 3 drafts, accepted ~ U{0..3},
-    64 rounds, initial fill U{0..L-1}.  Replay: verify_drafts + commit (pointer
-    move).  Baseline: the conventional kernel writing one FP32 snapshot per
-    draft (4 slots per sequence) + slot-select commit.  Same inputs and
+def _verify_point(T, batch=512, L=16, rounds=64, seed=1003, snapshots=True):
+    """One speculative-verification workload: T drafts per round, accepted ~
+    U{0..T}, initial fill U{0..L-1}.  Replay: verify_drafts + commit (pointer
+    move), and the same rounds with the commit fused into the next
+    verification.  Baseline: the conventional kernel writing one FP32 snapshot
+    per draft (T + 1 slots per sequence) + slot-select commit.  Same inputs and
     acceptance for both."""
     torch, dev = _device()
     from mamba_state_replay_amd import binding as rb
     from mamba_state_replay_amd import staging, synth, traffic
-    T, L, batch, rounds = 3, 16, 512, 64
     shape = synth.LayerShape(batch=batch, nheads=128, headdim=64, dstate=128, ngroups=8, window=L,
                              max_drafts=T)
-    work = synth.verify_workload(shape, rounds, T, seed=1003)
+    work = synth.verify_workload(shape, rounds, T, seed=seed)
     cfg = staging.config(shape)
     st = staging.replay_state(cfg, work, dev)
     p = staging.params(work, dev)
@@ -311,75 +317,115 @@ def bench_verify(args):
     meta = st.meta.cpu().numpy()
     assert np.all(meta[:, :, 1] == n[:, None]) and int(st.status.cpu()[0]) == 0
     fused_us = fms * 1e3 / rounds
-    del st
-    states = staging.conventional_states(cfg, work.h0, T + 1, dev)
-    slot = torch.zeros(batch, dtype=torch.int32, device=dev)
-
-    def snapshot_round(r):
-        rb.conventional_state_update(cfg, states, p, toks.call(r), y, slot=slot)
-        rb.conventional_commit(cfg, slot, T + 1, acc[r], T)
-    for r in range(8):
-        snapshot_round(r)
-    slot.zero_()
-    cms, cper = timed_launches(snapshot_round, rounds, torch)
-    snap_us = cms * 1e3 / rounds
-    sbytes = traffic.snapshot_verify_bytes(sz, batch, T)
     ring = batch * 128 * cfg.cap * (64 * 2 + 4) + batch * 8 * cfg.cap * 128 * 2
+    del st
+    torch.cuda.empty_cache()
     out = {
-        "metric": "speculative verify round us (T=3 drafts, batch 512) + achieved HBM GB/s",
-        "config": {"workload": "Nemotron-3-style Mamba-2 layer, batch 512, T=3 drafts per round, accepted "
-                               "U{0..3}, 64 rounds, L=16, initial fill U{0..15}", "batch": batch, "T": T},
+        "T": T,
         "replay": {"us_per_round": round(replay_us, 2), "gbs": round(np.mean(rbytes) / (replay_us * 1e-6) / 1e9, 1),
                    "algorithmic_bytes_per_round": int(np.mean(rbytes)),
                    "state_bytes": batch * sz.S + ring},
         "replay_fused_commit": {"us_per_round": round(fused_us, 2),
                                 "gbs": round(np.mean(rbytes) / (fused_us * 1e-6) / 1e9, 1),
                                 "launches_per_round": 1},
-        "snapshot_baseline": {"us_per_round": round(snap_us, 2),
-                              "gbs": round(sbytes / (snap_us * 1e-6) / 1e9, 1),
-                              "algorithmic_bytes_per_round": sbytes,
-                              "state_bytes": (T + 1) * batch * sz.S},
-        "speedup": round(snap_us / replay_us, 3),
-        "speedup_fused": round(snap_us / fused_us, 3),
+        "mean_accepted": float(work.extra["accepted"].mean()),
+    }
+    if snapshots:
+        states = staging.conventional_states(cfg, work.h0, T + 1, dev)
+        slot = torch.zeros(batch, dtype=torch.int32, device=dev)
+
+        def snapshot_round(r):
+            rb.conventional_state_update(cfg, states, p, toks.call(r), y, slot=slot)
+            rb.conventional_commit(cfg, slot, T + 1, acc[r], T)
+        for r in range(8):
+            snapshot_round(r)
+        slot.zero_()
+        cms, cper = timed_launches(snapshot_round, rounds, torch)
+        snap_us = cms * 1e3 / rounds
+        sbytes = traffic.snapshot_verify_bytes(sz, batch, T)
+        del states
+        torch.cuda.empty_cache()
+        out["snapshot_baseline"] = {"us_per_round": round(snap_us, 2),
+                                    "gbs": round(sbytes / (snap_us * 1e-6) / 1e9, 1),
+                                    "algorithmic_bytes_per_round": sbytes,
+                                    "state_bytes": (T + 1) * batch * sz.S}
+        out["speedup"] = round(snap_us / replay_us, 3)
+        out["speedup_fused"] = round(snap_us / fused_us, 3)
+    return out
+
+
+def bench_verify(args):
+    """Speculative verification at batch 512, T = 3, 64 rounds."""
+    pt = _verify_point(3)
+    out = {
+        "metric": "speculative verify round us (T=3 drafts, batch 512) + achieved HBM GB/s",
+        "config": {"workload": "Nemotron-3-style Mamba-2 layer, batch 512, T=3 drafts per round, accepted "
+                               "U{0..3}, 64 rounds, L=16, initial fill U{0..15}", "batch": 512, "T": 3},
+        **{k: v for k, v in pt.items() if k != "T"},
         "data": "synthetic", "n_gpus": 1,
     }
     print(json.dumps(out), flush=True)
 
 
+def bench_verify_sweep(args):
+    """Speculative verification at batch 512, L = 16, for T in {1, 2, 3, 4, 8}
+    drafts per round (32 rounds each), replay against FP32 snapshots."""
+    pts = []
+    for T in (1, 2, 3, 4, 8):
+        pts.append(_verify_point(T, rounds=32))
+        print(json.dumps({"progress": f"T={T} done", "replay_us": pts[-1]["replay"]["us_per_round"]}), flush=True)
+    print(json.dumps({"metric": "speculative verify round us vs drafts per round (batch 512, L=16)",
+                      "config": {"workload": "Nemotron-3-style Mamba-2 layer, batch 512, L=16, accepted U{0..T}, "
+                                             "32 rounds per point, initial fill U{0..15}"},
+                      "points": pts, "data": "synthetic", "n_gpus": 1}), flush=True)
+
+
 def bench_sweep(args):
-    """Batch x window grid of the same layer, 128 decode steps each, steady
-    state (L committed records at start).  Per point: replay amortised us per
-    step, its non-flush and flush launches, and the conventional step.  Points
-    whose FP32 state fits the 256 MB Infinity Cache are labelled as such."""
+    """Batch x window grid of the same layer, steady state (L committed records
+    at start).  Per point: replay amortised us per step, its non-flush and
+    flush launches, and the conventional step.  Where one copy of the FP32 state
+    would fit the 256 MB Infinity Cache (batch <= 64), R independent replicas of
+    the whole layer state (checkpoint, ring, pointers; conventional states) are
+    allocated so that R copies exceed 768 MiB, and consecutive launches rotate
+    through them: every launch then streams its state from HBM.  Each replica
+    runs a whole number of windows inside the timed region."""
     torch, dev = _device()
     from mamba_state_replay_amd import binding as rb
     from mamba_state_replay_amd import staging, synth, traffic
-    steps, ntok = 128, 32
+    ntok = 32
     rows = []
+    sz = traffic.sizes(128, 64, 128, 8, 2, None)
     for batch in (1, 16, 64, 256, 512):
+        state = batch * sz.S
+        R = 1 if state > 256 * 2 ** 20 else -(-(768 * 2 ** 20) // state)
         for L in (4, 8, 16, 32):
+            steps = 128 if R == 1 else R * L * -(-128 // (R * L))
             shape = synth.LayerShape(batch=batch, nheads=128, headdim=64, dstate=128, ngroups=8, window=L)
             work = synth.decode_workload(shape, ntok, seed=1002, n0=L)
             cfg = staging.config(shape)
-            st = staging.replay_state(cfg, work, dev)
+            sts = [staging.replay_state(cfg, work, dev) for _ in range(R)]
             p = staging.params(work, dev)
             toks = staging.TokenStream(work.steps, dev)
             y = torch.empty((batch, 1, 128, 64), device=dev)
-            for i in range(2 * L):
-                rb.replayssm_decode_step(cfg, st, p, toks.call(i % ntok), y)
-            sched, _ = traffic.decode_schedule(work.n0, L, 2 * L + steps)
-            sched = sched[2 * L:]
-            sz = traffic.sizes(128, 64, 128, 8, 2, None)
+            for j in range(2 * L):
+                for st in sts:
+                    rb.replayssm_decode_step(cfg, st, p, toks.call(j % ntok), y)
+            sched, _ = traffic.decode_schedule(work.n0, L, 2 * L + steps // R)
+            sched = [sched[2 * L + i // R] for i in range(steps)]
             rbytes = sum(traffic.decode_step_bytes(sz, n, f) for n, f in sched)
             ms, per = timed_launches(
-                lambda i: rb.replayssm_decode_step(cfg, st, p, toks.call(i % ntok), y), steps, torch)
+                lambda i: rb.replayssm_decode_step(cfg, sts[i % R], p, toks.call((2 * L + i // R) % ntok), y),
+                steps, torch)
             folds = np.array([f.any() for _, f in sched])
             per = np.array(per)
-            states = staging.conventional_states(cfg, work.h0, 1, dev)
+            del sts
+            torch.cuda.empty_cache()
+            states = [staging.conventional_states(cfg, work.h0, 1, dev) for _ in range(R)]
             for i in range(4):
-                rb.conventional_state_update(cfg, states, p, toks.call(i % ntok), y)
+                rb.conventional_state_update(cfg, states[i % R], p, toks.call(i % ntok), y)
             cms, cper = timed_launches(
-                lambda i: rb.conventional_state_update(cfg, states, p, toks.call(i % ntok), y), steps, torch)
+                lambda i: rb.conventional_state_update(cfg, states[i % R], p, toks.call((i // R) % ntok), y),
+                steps, torch)
             cbytes = traffic.conventional_step_bytes(sz, batch)
             r_us, c_us = ms * 1e3 / steps, cms * 1e3 / steps
             rows.append({"batch": batch, "L": L, "replay_us": round(r_us, 2),
@@ -389,25 +435,25 @@ def bench_sweep(args):
                          "conventional_us": round(c_us, 2),
                          "conventional_gbs": round(cbytes / (c_us * 1e-6) / 1e9, 1),
                          "speedup": round(c_us / r_us, 3),
-                         "state_fits_infinity_cache": batch * sz.S <= 256 * 2 ** 20})
-            del st, states
+                         "state_replicas": R, "steps": steps})
+            del states
             torch.cuda.empty_cache()
+        print(json.dumps({"progress": f"batch {batch} done"}), flush=True)
     print(json.dumps({"metric": "decode-step us, replay vs conventional, batch x L sweep",
-                      "config": {"workload": "Nemotron-3-style Mamba-2 layer, 128 decode steps per point, "
-                                             "steady state"},
+                      "config": {"workload": "Nemotron-3-style Mamba-2 layer, >= 128 decode steps per point, "
+                                             "steady state; batch <= 64 rotates state replicas past the "
+                                             "Infinity Cache"},
                       "points": rows, "data": "synthetic", "n_gpus": 1}), flush=True)
 
 
 def bench_dual(args):
     """Dual precision: FP32 checkpoint with no copy, a bf16 copy or an e4m3
     copy.  Throughput: batch 256, L = 16, 4096 decode steps (token inputs cycle
-    through 64 seeded steps).  Accuracy: 8 sequences x all heads over 4096
-    fresh seeded steps against the fp64 oracle, reported per window of L steps
-    (windows start at a flush)."""
+    through 64 seeded steps).  The accuracy of the same modes over 4096 steps is
+    a GPU test (tests/test_gpu_dual.py), not part of this timing."""
     torch, dev = _device()
     from mamba_state_replay_amd import binding as rb
     from mamba_state_replay_amd import staging, synth, traffic
-    from oracle import oracle as orc
     L, steps = 16, 4096
     res = {}
     shape = synth.LayerShape(batch=256, nheads=128, headdim=64, dstate=128, ngroups=8, window=L)
@@ -433,42 +479,8 @@ def bench_dual(args):
                                "flush_launch_us": round(float(per[folds].mean()) * 1e3, 2)}
         del st
         torch.cuda.empty_cache()
-    # accuracy over 4096 fresh steps on 8 sequences
-    ashape = synth.LayerShape(batch=8, nheads=128, headdim=64, dstate=128, ngroups=8, window=L)
-    awork = synth.decode_workload(ashape, steps, seed=1005, n0=L)
-    yref, _ = orc.decode(awork, nsteps=steps)
-    for mode in (None, "bf16", "e4m3"):
-        cfg = staging.config(ashape, read_copy=mode)
-        st = staging.replay_state(cfg, awork, dev)
-        p = staging.params(awork, dev)
-        toks = staging.TokenStream(awork.steps, dev)
-        yall = torch.empty((steps, 8, 1, 128, 64), device=dev)
-        rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST)
-        for t in range(steps):
-            rb.replayssm_decode_step(cfg, st, p, toks.call(t), yall[t])
-        torch.cuda.synchronize()
-        yg = yall.cpu().numpy()[:, :, 0].astype(np.float64)
-        per_window = []
-        for w in range(steps // L):
-            sl = slice(w * L + 1, (w + 1) * L)        # non-flush steps of the window
-            ref = yref[sl]
-            scale = np.abs(ref).max(axis=(0, 3))
-            err = np.abs(yg[sl] - ref).max(axis=(0, 3)) / scale
-            per_window.append(float(err.max()))
-        pw = np.array(per_window)
-        q = len(pw) // 4
-        res[mode or "fp32"].update({
-            "max_error_per_window_first_quarter": float(pw[:q].max()),
-            "max_error_per_window_last_quarter": float(pw[-q:].max()),
-            "max_error": float(pw.max()),
-            "mean_error_per_window": float(pw.mean()),
-        })
-        del st, yall
-        torch.cuda.empty_cache()
-    print(json.dumps({"metric": "dual-precision decode: us per step, HBM GB/s and output error drift "
-                                "vs the fp64 oracle (batch 256, L=16, 4096 steps)",
-                      "config": {"workload": "Nemotron-3-style Mamba-2 layer, batch 256 (throughput) and 8 "
-                                             "sequences x 128 heads (accuracy), L=16, 4096 decode steps"},
+    print(json.dumps({"metric": "dual-precision decode: us per step and HBM GB/s (batch 256, L=16, 4096 steps)",
+                      "config": {"workload": "Nemotron-3-style Mamba-2 layer, batch 256, L=16, 4096 decode steps"},
                       "modes": res, "data": "synthetic", "n_gpus": 1}), flush=True)
 
 
@@ -480,6 +492,75 @@ PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof -o trace -- "
              "python -u bench.py --no-cpu --steps 32 --warmup 16",
 }
+
+
+CONFIG_SUMMARY = ROOT / "profiles" / "bench_configs_verify_sweep_dual.md"
+
+
+def summarize_configs(logs):
+    """Write the tables of the verify / verify_sweep / sweep / dual bench lines
+    (the last JSON line of each log, in any order) to profiles/."""
+    lines = {}
+    for path in logs:
+        for line in reversed(Path(path).read_text().splitlines()):
+            if line.startswith("{") and '"metric"' in line:
+                d = json.loads(line)
+                key = ("verify_sweep" if "drafts per round" in d["metric"] else
+                       "verify" if "verify" in d["metric"] else
+                       "sweep" if "sweep" in d["metric"] else "dual")
+                lines[key] = d
+                break
+    md = ["# Bench configurations beyond the headline decode step (one MI355X)", "",
+          "Commands (from the repository root):", "", "```"]
+    md += [f"python -u bench.py --config {k}" for k in ("verify", "verify_sweep", "sweep", "dual") if k in lines]
+    md += ["```", "", "Times are HIP events around the launches on the launch stream; GB/s are algorithmic "
+           "bytes (mamba_state_replay_amd/traffic.py) over that time.", ""]
+    if "verify" in lines:
+        v = lines["verify"]
+        md += ["## Speculative verification: batch 512, T = 3, accepted U{0..3}, 64 rounds, L = 16", "",
+               "| | us per round | algorithmic GB/s | bytes per round | state + buffer bytes |",
+               "|---|---|---|---|---|",
+               f"| replay: verify_drafts + commit | {v['replay']['us_per_round']} | {v['replay']['gbs']} | "
+               f"{v['replay']['algorithmic_bytes_per_round']:,} | {v['replay']['state_bytes']:,} |",
+               f"| replay: commit fused into the next verification | {v['replay_fused_commit']['us_per_round']} | "
+               f"{v['replay_fused_commit']['gbs']} | same | same |",
+               f"| conventional with one FP32 snapshot per draft + slot commit | "
+               f"{v['snapshot_baseline']['us_per_round']} | {v['snapshot_baseline']['gbs']} | "
+               f"{v['snapshot_baseline']['algorithmic_bytes_per_round']:,} | "
+               f"{v['snapshot_baseline']['state_bytes']:,} |", "",
+               f"Speed-up of a verification round: {v['speedup']}x (fused commit: {v['speedup_fused']}x).", ""]
+    if "verify_sweep" in lines:
+        md += ["## Verification vs drafts per round: batch 512, L = 16, accepted U{0..T}, 32 rounds per point", "",
+               "| T | replay us/round | fused us/round | replay GB/s | snapshot us/round | snapshot GB/s | speed-up | "
+               "replay state bytes | snapshot state bytes |", "|---|---|---|---|---|---|---|---|---|"]
+        for pt in lines["verify_sweep"]["points"]:
+            sb = pt["snapshot_baseline"]
+            md.append(f"| {pt['T']} | {pt['replay']['us_per_round']} | {pt['replay_fused_commit']['us_per_round']} | "
+                      f"{pt['replay']['gbs']} | {sb['us_per_round']} | {sb['gbs']} | {pt['speedup']} | "
+                      f"{pt['replay']['state_bytes']:,} | {sb['state_bytes']:,} |")
+        md.append("")
+    if "sweep" in lines:
+        md += ["## Batch x window sweep, steady state", "",
+               "| batch | L | replay us/step | non-flush launch us | flush launch us | conventional us/step | "
+               "speed-up | replay GB/s | conventional GB/s | state replicas rotated | steps |",
+               "|---|---|---|---|---|---|---|---|---|---|---|"]
+        for pt in lines["sweep"]["points"]:
+            md.append(f"| {pt['batch']} | {pt['L']} | {pt['replay_us']} | {pt['replay_nonflush_us']} | "
+                      f"{pt['replay_flush_us']} | {pt['conventional_us']} | {pt['speedup']} | {pt['replay_gbs']} | "
+                      f"{pt['conventional_gbs']} | {pt['state_replicas']} | {pt['steps']} |")
+        md += ["", "Where one copy of the FP32 state fits the 256 MB Infinity Cache (batch <= 64), launches rotate "
+               "through enough independent replicas of the layer state to exceed 768 MiB, so every launch "
+               "streams its state from HBM.", ""]
+    if "dual" in lines:
+        md += ["## Dual precision: batch 256, L = 16, 4096 decode steps", "",
+               "| checkpoint / read copy | us per step | algorithmic GB/s | non-flush launch us | flush launch us |",
+               "|---|---|---|---|---|"]
+        for k, m in lines["dual"]["modes"].items():
+            md.append(f"| {k} | {m['us_per_step']} | {m['gbs']} | {m['nonflush_launch_us']} | "
+                      f"{m['flush_launch_us']} |")
+        md.append("")
+    CONFIG_SUMMARY.write_text("\n".join(md) + "\n")
+    print(f"wrote {CONFIG_SUMMARY}")
 
 
 def ingest_counters(fetch_dir, write_dir, trace_dir):

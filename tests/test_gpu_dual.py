@@ -17,11 +17,17 @@ from mamba_state_replay_amd import binding as rb
 from mamba_state_replay_amd import staging, synth
 from oracle import oracle as orc_mod
 from tests import formats
-from tests.gpu_util import assert_rows_close, device, head_err, host, say
+from tests.gpu_util import TOL, assert_rows_close, device, head_err, host, say
 
 pytestmark = pytest.mark.gpu
 
 NEMO = dict(nheads=128, headdim=64, dstate=128, ngroups=8)
+SHAPES = {
+    "16x16": dict(nheads=4, headdim=16, dstate=16, ngroups=1),
+    "64x64": dict(nheads=16, headdim=64, dstate=64, ngroups=2),
+    "64x128": NEMO,
+    "128x128": dict(nheads=8, headdim=128, dstate=128, ngroups=1),
+}
 UNIT = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -4}   # relative rounding bound of one read
 
 
@@ -138,8 +144,9 @@ def _run_dual(cfg, work, dev, steps, poison_before=()):
     return host(y)[:, :, 0], st, {k: host(v) for k, v in scales.items()}
 
 
+@pytest.mark.parametrize("tile", ["64x128", "16x16", "64x64", "128x128"])
 @pytest.mark.parametrize("copy", ["bf16", "e4m3"])
-def test_dual_precision_error_bound(copy):
+def test_dual_precision_error_bound(copy, tile):
     """Outputs of non-flush steps read the copy; per element
     |y - y_ref| <= d_q sum_j |C_q[j]| (u |H_s[i,j]| + delta) + 1e-4 * (head output scale),
     u = 2^-8 (bf16) or 2^-4 (e4m3), delta = 0 (bf16) or s 2^-10 (e4m3, half the
@@ -148,9 +155,9 @@ def test_dual_precision_error_bound(copy):
     The FP32 checkpoint must be bit-identical to an FP32-only run."""
     dev = device()
     L, steps = 16, 72
-    shape = synth.LayerShape(batch=4, window=L, **NEMO)
+    shape = synth.LayerShape(batch=4, window=L, **SHAPES[tile])
     work = synth.decode_workload(shape, steps, seed=1011, n0=L)
-    say(f"dual precision {copy}, 72 steps")
+    say(f"dual precision {copy} {tile}, 72 steps")
     cfg32 = staging.config(shape)
     y32, st32, _ = _run_dual(cfg32, work, dev, steps)
     cfgc = staging.config(shape, read_copy=copy)
@@ -210,3 +217,86 @@ def test_poisoned_copy_never_enters_recurrence(copy):
     assert np.array_equal(y_clean, y_pois)
     assert torch.equal(st_clean.ckpt, st_pois.ckpt)
     assert torch.equal(st_clean.ckpt_read, st_pois.ckpt_read)
+
+
+def test_dual_4096_steps_bound_and_no_drift():
+    """4096 decode steps, 8 sequences x 128 heads, L = 16, all three modes run
+    side by side, window by window, against the fp64 oracle stepped over the
+    same window:
+    * FP32-only outputs within the FP32 tolerance in every window;
+    * read-copy outputs within the per-element bound of the dual-precision
+      test above in every window (flushing steps read FP32 registers and meet
+      the FP32 tolerance);
+    * the copy never enters the recurrence: after 4096 steps the FP32
+      checkpoints of the three modes are bit-identical;
+    * the read error does not grow: the largest normalized error of the last
+      quarter of windows is no more than twice that of the first quarter."""
+    dev = device()
+    L, steps = 16, 4096
+    shape = synth.LayerShape(batch=8, window=L, **NEMO)
+    work = synth.decode_workload(shape, steps, seed=1005, n0=L)
+    modes = (None, "bf16", "e4m3")
+    cfgs = {m: staging.config(shape, read_copy=m) for m in modes}
+    sts = {m: staging.replay_state(cfgs[m], work, dev) for m in modes}
+    p = staging.params(work, dev)
+    stream = staging.TokenStream(work.steps, dev)
+    say("dual precision, 4096 steps, 8 sequences, three modes")
+    for m in modes[1:]:
+        rb.replayssm_flush(cfgs[m], sts[m], p, rb.RSSM_FLUSH_FORCE_CAST)
+    rb.replayssm_flush(cfgs[None], sts[None], p)
+    H = orc_mod.committed_state(work)                 # H_s of window 0
+    A = work.A.astype(np.float64)
+    hpg = shape.nheads // shape.ngroups
+    y = {m: torch.empty((L, 8, 1, 128, 64), device=dev) for m in modes}
+    per_window = {m: [] for m in modes}
+    worst_ratio = {m: 0.0 for m in modes[1:]}
+    for w in range(steps // L):
+        t0 = w * L
+        scales = {}
+        for t in range(t0, t0 + L):
+            for m in modes:
+                rb.replayssm_decode_step(cfgs[m], sts[m], p, stream.call(t), y[m][t - t0])
+            if t == t0:
+                scales = host(sts["e4m3"].ckpt_scale).astype(np.float64)
+        torch.cuda.synchronize()
+        tok = work.steps
+        Hs = H
+        H, yref = orc_mod.default().conventional(Hs, tok.x[t0:t0 + L], tok.B[t0:t0 + L], tok.C[t0:t0 + L],
+                                                 tok.dt[t0:t0 + L], work.A, work.D)
+        scale = np.abs(yref).max(axis=(0, 3))                       # per (seq, head)
+        # steps of this window that read the copy (step t0 flushes, except in window 0)
+        copy_rows = np.arange(L) if w == 0 else np.arange(1, L)
+        dsum = np.cumsum(tok.dt[t0:t0 + L].astype(np.float64), axis=0)      # [L][b][h]
+        dec = np.exp(A[None, None, :] * dsum)                        # decay since H_s, [L][b][h]
+        Cabs = torch.from_numpy(np.repeat(np.abs(tok.C[t0:t0 + L].astype(np.float64)), hpg, axis=2))  # [L][b][h][ds]
+        Habs = torch.from_numpy(np.abs(Hs))                           # [b][h][hd][ds]
+        HC = torch.einsum("bhij,tbhj->tbhi", Habs, Cabs).numpy()     # [L][b][h][hd]
+        Csum = Cabs.sum(-1).numpy()                                   # [L][b][h]
+        for m in modes:
+            got = host(y[m])[:, :, 0].astype(np.float64)
+            err = np.abs(got - yref)
+            if m is None:
+                per_window[m].append(float((err.max(axis=(0, 3)) / scale).max()))
+                assert per_window[m][-1] <= TOL, f"fp32 window {w}: {per_window[m][-1]:.3e}"
+                continue
+            per_window[m].append(float((err[copy_rows].max(axis=(0, 3)) / scale).max()))
+            read = UNIT[m] * HC                                       # u sum_j |H_s[i,j]| |C_q[j]|
+            if m == "e4m3":
+                read = read + (scales * 2.0 ** -10 * 1.001)[None, :, :, None] * Csum[..., None]
+            bound = dec[..., None] * read + TOL * scale[None, :, :, None]
+            ratio = float((err[copy_rows] / bound[copy_rows]).max())
+            worst_ratio[m] = max(worst_ratio[m], ratio)
+            assert ratio <= 1.0, f"{m} window {w}: error / bound {ratio:.3f}"
+            if w > 0:
+                fl = float((err[0].max(axis=-1) / scale).max())
+                assert fl <= TOL, f"{m} flushing step of window {w}: {fl:.3e}"
+    for m in modes[1:]:
+        assert torch.equal(sts[m].ckpt, sts[None].ckpt), f"{m}: read copy changed the FP32 recurrence"
+    q = len(per_window[None]) // 4
+    for m in modes:
+        pw = np.array(per_window[m])
+        print(f"[gpu] {m or 'fp32'}: max error per window first quarter {pw[:q].max():.3e}, "
+              f"last quarter {pw[-q:].max():.3e}, mean {pw.mean():.3e}"
+              + (f", worst error/bound {worst_ratio[m]:.3f}" if m else ""), flush=True)
+        if m:
+            assert pw[-q:].max() <= 2 * pw[:q].max(), f"{m}: read error grows over the run"

@@ -137,6 +137,48 @@ def test_verify_commit_matches_oracle(batch, rounds):
     assert host(st.status)[0] == 0
 
 
+SHAPES = {
+    "16x16": dict(nheads=4, headdim=16, dstate=16, ngroups=1),
+    "64x64": dict(nheads=16, headdim=64, dstate=64, ngroups=2),
+    "64x128": NEMO,
+    "128x128": dict(nheads=8, headdim=128, dstate=128, ngroups=1),
+}
+
+
+@pytest.mark.parametrize("tile,in_dtype,L,T,batch,rounds", [
+    ("16x16", "f32", 4, 8, 3, 12),       # most drafts, window shorter than the drafts
+    ("64x64", "bf16", 16, 4, 3, 12),
+    ("128x128", "f32", 8, 2, 3, 16),
+    ("64x128", "bf16", 16, 8, 4, 10),     # most drafts at the layer shape
+    ("64x128", "bf16", 64, 4, 3, 40),     # longest window at the layer shape (cap 71)
+    ("128x128", "bf16", 32, 3, 2, 24),
+])
+def test_verify_shapes_and_limits(tile, in_dtype, L, T, batch, rounds):
+    """Every compiled tile shape, fp32 and bf16 inputs, up to the largest draft
+    count and window: verify + commit outputs and the state after a final flush
+    against the oracle stepping through the same drafts."""
+    dev = device()
+    shape = synth.LayerShape(batch=batch, window=L, max_drafts=T, **SHAPES[tile])
+    work = synth.verify_workload(shape, rounds, T, seed=1006, in_dtype=in_dtype)
+    cfg = staging.config(shape, in_dtype=in_dtype)
+    st = staging.replay_state(cfg, work, dev)
+    p = staging.params(work, dev)
+    stream = staging.TokenStream(work.steps, dev, T=T)
+    acc = torch.from_numpy(work.extra["accepted"]).to(dev)
+    y = torch.empty((rounds, batch, T, cfg.nheads, cfg.headdim), device=dev)
+    say(f"verify {tile} {in_dtype} L={L} T={T} batch={batch} rounds={rounds}")
+    for r in range(rounds):
+        rb.replayssm_verify_drafts(cfg, st, p, stream.call(r), y[r])
+        rb.replayssm_commit(cfg, st, acc[r], T)
+    torch.cuda.synchronize()
+    yref, Href = orc_mod.verify_rounds(work)
+    assert_rows_close(np.swapaxes(host(y), 1, 2), yref, what=f"verify outputs {tile} L={L} T={T}")
+    rb.replayssm_flush(cfg, st, p)
+    torch.cuda.synchronize()
+    assert tile_err(host(st.ckpt), Href).max() <= TOL
+    assert host(st.status)[0] == 0
+
+
 def test_snapshot_baseline_matches_oracle():
     """Conventional speculative baseline: one snapshot per draft, slot-select commit."""
     dev = device()
