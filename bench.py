@@ -84,6 +84,27 @@ def timed_launches(fn, steps, torch):
     return region0.elapsed_time(region1), per
 
 
+def graph_time(fn, steps, torch):
+    """Capture fn(0) .. fn(steps-1) in one HIP graph (torch.cuda.graph) and time
+    one replay after a warm one: GPU time of the launches without the host's
+    per-launch cost.  Returns ms for all steps."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1)
+
+
 def main():
     args = parse()
     if args.ingest_counters:
@@ -413,9 +434,9 @@ def bench_sweep(args):
             sched, _ = traffic.decode_schedule(work.n0, L, 2 * L + steps // R)
             sched = [sched[2 * L + i // R] for i in range(steps)]
             rbytes = sum(traffic.decode_step_bytes(sz, n, f) for n, f in sched)
-            ms, per = timed_launches(
-                lambda i: rb.replayssm_decode_step(cfg, sts[i % R], p, toks.call((2 * L + i // R) % ntok), y),
-                steps, torch)
+            rstep = lambda i: rb.replayssm_decode_step(cfg, sts[i % R], p, toks.call((2 * L + i // R) % ntok), y)
+            ms, per = timed_launches(rstep, steps, torch)
+            gms = graph_time(rstep, steps, torch)      # each replica runs whole windows: same phase
             folds = np.array([f.any() for _, f in sched])
             per = np.array(per)
             del sts
@@ -423,11 +444,12 @@ def bench_sweep(args):
             states = [staging.conventional_states(cfg, work.h0, 1, dev) for _ in range(R)]
             for i in range(4):
                 rb.conventional_state_update(cfg, states[i % R], p, toks.call(i % ntok), y)
-            cms, cper = timed_launches(
-                lambda i: rb.conventional_state_update(cfg, states[i % R], p, toks.call((i // R) % ntok), y),
-                steps, torch)
+            cstep = lambda i: rb.conventional_state_update(cfg, states[i % R], p, toks.call((i // R) % ntok), y)
+            cms, cper = timed_launches(cstep, steps, torch)
+            cgms = graph_time(cstep, steps, torch)
             cbytes = traffic.conventional_step_bytes(sz, batch)
             r_us, c_us = ms * 1e3 / steps, cms * 1e3 / steps
+            rg_us, cg_us = gms * 1e3 / steps, cgms * 1e3 / steps
             rows.append({"batch": batch, "L": L, "replay_us": round(r_us, 2),
                          "replay_nonflush_us": round(float(per[~folds].mean()) * 1e3, 2),
                          "replay_flush_us": round(float(per[folds].mean()) * 1e3, 2) if folds.any() else None,
@@ -435,6 +457,9 @@ def bench_sweep(args):
                          "conventional_us": round(c_us, 2),
                          "conventional_gbs": round(cbytes / (c_us * 1e-6) / 1e9, 1),
                          "speedup": round(c_us / r_us, 3),
+                         "replay_graph_us": round(rg_us, 2), "conventional_graph_us": round(cg_us, 2),
+                         "speedup_graph": round(cg_us / rg_us, 3),
+                         "replay_graph_gbs": round(rbytes / steps / (rg_us * 1e-6) / 1e9, 1),
                          "state_replicas": R, "steps": steps})
             del states
             torch.cuda.empty_cache()
@@ -541,13 +566,17 @@ def summarize_configs(logs):
         md.append("")
     if "sweep" in lines:
         md += ["## Batch x window sweep, steady state", "",
+               "Eager: one Python call per launch, events around each launch. Graph: the same launches captured "
+               "in one HIP graph, one replay timed (GPU time without the host's per-launch cost).", "",
                "| batch | L | replay us/step | non-flush launch us | flush launch us | conventional us/step | "
-               "speed-up | replay GB/s | conventional GB/s | state replicas rotated | steps |",
-               "|---|---|---|---|---|---|---|---|---|---|---|"]
+               "speed-up | replay GB/s | graph: replay us/step | graph: conventional us/step | graph: speed-up | "
+               "graph: replay GB/s | state replicas rotated | steps |",
+               "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
         for pt in lines["sweep"]["points"]:
             md.append(f"| {pt['batch']} | {pt['L']} | {pt['replay_us']} | {pt['replay_nonflush_us']} | "
                       f"{pt['replay_flush_us']} | {pt['conventional_us']} | {pt['speedup']} | {pt['replay_gbs']} | "
-                      f"{pt['conventional_gbs']} | {pt['state_replicas']} | {pt['steps']} |")
+                      f"{pt.get('replay_graph_us')} | {pt.get('conventional_graph_us')} | {pt.get('speedup_graph')} | "
+                      f"{pt.get('replay_graph_gbs')} | {pt['state_replicas']} | {pt['steps']} |")
         md += ["", "Where one copy of the FP32 state fits the 256 MB Infinity Cache (batch <= 64), launches rotate "
                "through enough independent replicas of the layer state to exceed 768 MiB, so every launch "
                "streams its state from HBM.", ""]
