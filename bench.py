@@ -269,6 +269,9 @@ def cpu_baseline(work, gpu_bytes_per_step, target_s):
         elapsed += orc.time_decode(work, seqs, nsteps)
         passes += 1
     step_s = elapsed / (passes * nsteps)
+    # one thread, 8 sequences (all heads), scaled to the whole batch
+    few = np.arange(min(8, batch))
+    one_s = orc.time_decode(work, few, nsteps, threads=1) / nsteps * batch / len(few)
     return {
         "value": round(gpu_bytes_per_step / step_s / 1e9, 4),
         "unit": "GB/s",
@@ -278,8 +281,22 @@ def cpu_baseline(work, gpu_bytes_per_step, target_s):
         "sample": f"all {batch} sequences x 128 heads x {nsteps} decode tokens of the same workload, "
                   f"{passes} pass(es), {elapsed:.1f} s inside the oracle (fp64 conventional recurrence, "
                   f"OpenMP over sequence/head pairs)",
-        "host_cpu": platform.processor() or platform.machine(),
+        "cores_available": orc.available_cores(),
+        "single_thread": {"us_per_step": round(one_s * 1e6, 1),
+                          "sample": f"{len(few)} sequences x 128 heads x {nsteps} tokens on 1 thread, "
+                                    f"scaled to {batch} sequences"},
+        "host_cpu": _cpu_model(),
     }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def _device():

@@ -264,7 +264,7 @@ __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& 
 }
 
 template <int HD, int DS, int NT, typename InT, int RM>
-__global__ __launch_bounds__(NT, 2048 / NT) void replay_kernel(const ReplayArgs a) {
+__global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
     extern __shared__ float lds[];
     using G32 = TileGeo<HD, DS, NT, 4>;
     constexpr int EBC = RM == READ_BF16 ? 2 : 1;     // element size of the read copy
