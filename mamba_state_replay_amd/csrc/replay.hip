@@ -38,28 +38,42 @@ namespace rssm {
 
 namespace {
 
-// LDS plan in floats.  x rows are padded to XS = HD + 4 floats so that the
-// lanes of a row group, each reading a different record's x rows in step 5,
-// fall on different banks.
+// LDS plan in floats for a workgroup serving HPW heads of one group.  x rows
+// are padded to XS = HD + 4 floats so that the lanes of a row group, each
+// reading a different record's x rows in step 5, fall on different banks.
+// Per-head arrays are indexed [head][...]; B and C rows are the group's and
+// are shared by the heads.
 struct Lds {
     int X, XS, K, Cq, DT, AA, CO, DQ, WF, RED, total;
 };
 
-__host__ __device__ inline Lds lds_plan(int HD, int DS, int cap, int T) {
+constexpr int kRedSlots = 64;   // cross-wave reduction slots: [head][wave]
+
+__host__ __device__ inline Lds lds_plan(int HD, int DS, int cap, int T, int HPW) {
     Lds l;
     int o = 0;
     l.XS = HD + 4;
-    l.X = o;  o += cap * l.XS; // x of records then queries, window order
-    l.K = o;  o += cap * DS;   // B of records then queries
-    l.Cq = o; o += T * DS;     // C of the queries
-    l.DT = o; o += cap;        // dt, window order
-    l.AA = o; o += cap;        // a = dt * A
-    l.CO = o; o += T * cap;    // co[q][c] = dt_c exp(sum_{c<i<=m_q} a_i) (B_c . C_q) [+ D at c = m_q]
-    l.DQ = o; o += T + 1;      // d_q = exp(sum_{first<=i<=m_q} a_i); [T] = flush decay
-    l.WF = o; o += cap;        // flush weights dt_c exp(sum_{c<i<n} a_i)
-    l.RED = o; o += 16;        // cross-wave reductions
+    l.X = o;  o += HPW * cap * l.XS; // x of records then queries, window order, per head
+    l.K = o;  o += cap * DS;         // B of records then queries
+    l.Cq = o; o += T * DS;           // C of the queries
+    l.DT = o; o += HPW * cap;        // dt, window order, per head
+    l.AA = o; o += HPW * cap;        // a = dt * A, per head
+    l.CO = o; o += HPW * T * cap;    // co[h][q][c] = dt_c exp(sum_{c<i<=m_q} a_i) (B_c . C_q) [+ D at c = m_q]
+    l.DQ = o; o += HPW * (T + 1);    // d[h][q] = exp(sum_{first<=i<=m_q} a_i); [h][T] = flush decay
+    l.WF = o; o += HPW * cap;        // flush weights dt_c exp(sum_{c<i<n} a_i), per head
+    l.RED = o; o += kRedSlots;       // cross-wave reductions
     l.total = (o + 3) & ~3;
     return l;
+}
+
+// One head's view of the per-head LDS arrays.
+struct HeadView {
+    int X, DT, AA, CO, DQ, WF;
+};
+
+__device__ __forceinline__ HeadView head_view(const Lds& L, int hh, int cap, int T) {
+    return HeadView{L.X + hh * cap * L.XS, L.DT + hh * cap, L.AA + hh * cap, L.CO + hh * T * cap,
+                    L.DQ + hh * (T + 1), L.WF + hh * cap};
 }
 
 // This thread's share of a tile held as raw 16-byte vectors (issued in step
@@ -69,69 +83,62 @@ __host__ __device__ inline Lds lds_plan(int HD, int DS, int cap, int T) {
 template <int HD, int DS, int NT>
 struct TileRegs {
     static constexpr int NMAX = TileGeo<HD, DS, NT, 4>::NV;
-    v4u raw[NMAX];
+    v4f raw[NMAX];   // fp32 values, or the bits of bf16 / e4m3 codes
 
-    template <int EB>
+    // Load one tile of element size EB into vectors off .. off + NV - 1.
+    template <int EB, int OFF = 0>
     __device__ __forceinline__ void load(const void* tile, int tid) {
         using G = TileGeo<HD, DS, NT, EB>;
-        static_assert(G::NV <= NMAX, "copy tile needs more vectors than the FP32 tile");
-        if (tid >= G::ACTIVE) return;
+        static_assert(OFF + G::NV <= NMAX, "tiles need more vectors than the FP32 tile");
+        if (G::ACTIVE < NT && tid >= G::ACTIVE) return;
         const v4u* base = reinterpret_cast<const v4u*>(tile);
 #pragma unroll
-        for (int s = 0; s < G::NV; ++s) raw[s] = __builtin_nontemporal_load(base + G::vec(tid, s));
+        for (int s = 0; s < G::NV; ++s)
+            raw[OFF + s] = __builtin_bit_cast(v4f, __builtin_nontemporal_load(base + G::vec(tid, s)));
     }
 
-    // v[r] += (vector k of row r) . ck for each of the thread's NI rows; ck
-    // holds the EPV columns of C under that vector.  Low-precision words are
-    // widened one at a time, next to their use, so such a row never occupies
-    // a full set of fp32 registers.
-    template <int EB>
-    __device__ __forceinline__ void dot_vec(int k, const float* ck, float* v) const {
+    // v[r] += (row r of this thread's share) . C for each of its NI rows.  cq
+    // points at C in LDS; the thread's columns are (j + W k) * EPV + e.  The
+    // product runs over chunks of 4 columns: one float4 of C, then for every row
+    // the 4 tile values under it (an fp32 quarter-vector, two bf16 words or
+    // one e4m3 word, widened next to its use), so few values are live at once.
+    template <int EB, int OFF = 0>
+    __device__ __forceinline__ void dot(const float* cq, int j, float* v) const {
         using G = TileGeo<HD, DS, NT, EB>;
 #pragma unroll
-        for (int r = 0; r < G::NI; ++r) {
-            const v4u rv = raw[r * G::VPL + k];
-            const uint32_t w[4] = {rv.x, rv.y, rv.z, rv.w};
-            float acc = v[r];
-            if constexpr (EB == 4) {
+        for (int k = 0; k < G::VPL; ++k) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc = fmaf(__uint_as_float(w[e]), ck[e], acc);
-            } else if constexpr (EB == 2) {
+            for (int ch = 0; ch < G::EPV / 4; ++ch) {
+                const float4 c = *reinterpret_cast<const float4*>(cq + (j + G::W * k) * G::EPV + 4 * ch);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t we = w[e];
-                    asm volatile("" : "+v"(we));   // keep the widening inside the query loop
-                    acc = fmaf(__uint_as_float(we << 16), ck[2 * e], acc);
-                    acc = fmaf(__uint_as_float(we & 0xFFFF0000u), ck[2 * e + 1], acc);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t we = w[e];
-                    asm volatile("" : "+v"(we));   // decode next to its use, per query
+                for (int r = 0; r < G::NI; ++r) {
+                    const v4f rf = raw[OFF + r * G::VPL + k];
+                    const v4u rv = __builtin_bit_cast(v4u, rf);
                     float f[4];
-                    e4m3x4_to_f32(we, f);
+                    if constexpr (EB == 4) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc = fmaf(f[i], ck[4 * e + i], acc);
+                        for (int e = 0; e < 4; ++e) f[e] = rf[e];
+                    } else if constexpr (EB == 2) {
+                        uint32_t w0 = rv[2 * ch], w1 = rv[2 * ch + 1];
+                        asm volatile("" : "+v"(w0), "+v"(w1));   // widen inside the query loop
+                        f[0] = __uint_as_float(w0 << 16);
+                        f[1] = __uint_as_float(w0 & 0xFFFF0000u);
+                        f[2] = __uint_as_float(w1 << 16);
+                        f[3] = __uint_as_float(w1 & 0xFFFF0000u);
+                    } else {
+                        uint32_t w = rv[ch];
+                        asm volatile("" : "+v"(w));              // decode inside the query loop
+                        e4m3x4_to_f32(w, f);
+                    }
+                    float acc = v[r];
+                    acc = fmaf(f[0], c.x, acc);
+                    acc = fmaf(f[1], c.y, acc);
+                    acc = fmaf(f[2], c.z, acc);
+                    acc = fmaf(f[3], c.w, acc);
+                    v[r] = acc;
                 }
             }
-            v[r] = acc;
         }
-    }
-
-    // All NMAX vectors as fp32 (FP32 tile only).
-    __device__ __forceinline__ void widen(float (&f)[NMAX][4]) const {
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) f[s][e] = __uint_as_float(raw[s][e]);
-    }
-
-    __device__ __forceinline__ void set(const float (&f)[NMAX][4]) {
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            raw[s] = v4u{__float_as_uint(f[s][0]), __float_as_uint(f[s][1]), __float_as_uint(f[s][2]),
-                         __float_as_uint(f[s][3])};
     }
 };
 
@@ -139,17 +146,17 @@ struct Window {
     int n, first, T, cap;
 };
 
-// Where staged vector v comes from and goes: the x rows of the window, then
-// its B rows, then the queries' C rows.  Rows c < n are committed records read
-// from the ring; rows c >= n are query tokens, whose x and B are also appended
-// to the ring at slot (start + c) % cap.
+// Where staged vector v comes from and goes: the x rows of the window of
+// each head, then the group's B rows, then the queries' C rows.  Rows c < n
+// are committed records read from the ring; rows c >= n are query tokens,
+// whose x and B are also appended to the ring at slot (start + c) % cap.
 struct StageMap {
-    const void* bx;   // this head's x ring
+    const void* bx;   // the first head's x ring (heads follow at cap * HD elements)
     const void* bB;   // this group's B ring
     const void* xt;   // query tokens
     const void* Bt;
     const void* Ct;
-    int start, n, cap, T, b, h, g, nheads, ngroups, nx, nb;
+    int start, n, cap, T, b, h, g, nheads, ngroups, nx, nb, rows;
     int ldsX, ldsXS, ldsK, ldsC;
     bool append_x, append_B;
 };
@@ -170,16 +177,18 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
     StageJob j;
     j.app = nullptr;
     if (v < m.nx) {
-        const int c = v / VR, cv = v - c * VR;
-        const uint4* ring = bx + (size_t)((m.start + c) % m.cap) * VR + cv;
+        const int hh = v / (m.rows * VR);
+        const int u = v - hh * m.rows * VR;
+        const int c = u / VR, cv = u - c * VR;
+        const uint4* ring = bx + ((size_t)hh * m.cap + (m.start + c) % m.cap) * VR + cv;
         if (c < m.n) {
             j.src = ring;
         } else {
             j.src = reinterpret_cast<const uint4*>(m.xt) +
-                    ((size_t)(m.b * m.T + c - m.n) * m.nheads + m.h) * VR + cv;
+                    ((size_t)(m.b * m.T + c - m.n) * m.nheads + m.h + hh) * VR + cv;
             if (m.append_x) j.app = const_cast<uint4*>(ring);
         }
-        j.dst = m.ldsX + c * m.ldsXS + cv * EPVIN;
+        j.dst = m.ldsX + (hh * m.cap + c) * m.ldsXS + cv * EPVIN;
     } else if (v < m.nx + m.nb) {
         const int u = v - m.nx;
         const int c = u / VS, cv = u - c * VS;
@@ -201,16 +210,17 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
     return j;
 }
 
-// Step 5 for one tile held in registers with element size EB.  For query q
-// the thread forms, for each of its NI rows, d_q * (its columns' share of
-// H C_q) plus its share of the record terms: lane j of a row group takes the
-// records c = first + j, first + j + W, ... and adds co[q][c] x_c[row] (the
-// D x_q term rides on co[q][m_q]).  One transposed reduction over the row's
-// W lanes then leaves y_q[row] on one lane, which stores it.
-template <int HD, int DS, int NT, int EB>
+// Step 5 for one head's tile held in registers (vectors OFF ..) with element
+// size EB.  For query q the thread forms, for each of its NI rows, d_q * (its
+// columns' share of H C_q) plus its share of the record terms: lane j of a
+// row group takes the records c = first + j, first + j + W, ... and adds
+// co[q][c] x_c[row] (the D x_q term rides on co[q][m_q]).  One transposed
+// reduction over the row's W lanes then leaves y_q[row] on one lane, which
+// stores it.
+template <int HD, int DS, int NT, int EB, int OFF = 0>
 __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& t, const float* lds,
-                                                    const Lds& L, const Window& w, float scale,
-                                                    float* y_head, size_t y_qstride, int tid) {
+                                                    const Lds& L, const HeadView& hv, const Window& w,
+                                                    float scale, float* y_head, size_t y_qstride, int tid) {
     using G = TileGeo<HD, DS, NT, EB>;
     const int j = tid % G::W;
     const int row0 = G::row0(tid);
@@ -219,27 +229,14 @@ __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& 
         float v[16];
 #pragma unroll
         for (int r = 0; r < G::NI; ++r) v[r] = 0.f;
-#pragma unroll
-        for (int k = 0; k < G::VPL; ++k) {
-            float c[G::EPV];
-#pragma unroll
-            for (int e = 0; e < G::EPV; e += 4) {
-                const float4 cv =
-                    *reinterpret_cast<const float4*>(lds + L.Cq + q * DS + (j + G::W * k) * G::EPV + e);
-                c[e] = cv.x;
-                c[e + 1] = cv.y;
-                c[e + 2] = cv.z;
-                c[e + 3] = cv.w;
-            }
-            t.template dot_vec<EB>(k, c, v);
-        }
-        const float dq = lds[L.DQ + q] * scale;
+        t.template dot<EB, OFF>(lds + L.Cq + q * DS, j, v);
+        const float dq = lds[hv.DQ + q] * scale;
 #pragma unroll
         for (int r = 0; r < G::NI; ++r) v[r] *= dq;
         const int m = w.n + q;
         for (int cc = w.first + j; cc <= m; cc += G::W) {
-            const float co = lds[L.CO + q * w.cap + cc];
-            const float* xr = lds + L.X + cc * L.XS + row0;
+            const float co = lds[hv.CO + q * w.cap + cc];
+            const float* xr = lds + hv.X + cc * L.XS + row0;
             if constexpr (G::NI % 4 == 0) {
 #pragma unroll
                 for (int r = 0; r < G::NI; r += 4) {
@@ -263,32 +260,59 @@ __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& 
     }
 }
 
-template <int HD, int DS, int NT, typename InT, int RM>
+// The read-copy tiles of HPW heads, each over the whole workgroup in its own
+// vectors of the register array: step 5 for every head.
+template <int HD, int DS, int NT, int EBC, int HPW, int HH = 0>
+__device__ __forceinline__ void copy_queries(const TileRegs<HD, DS, NT>& t, const float* lds, const Lds& L,
+                                             const Window& w, const float* scales, float* y0,
+                                             size_t y_qstride, int tid) {
+    if constexpr (HH < HPW) {
+        using GC = TileGeo<HD, DS, NT, EBC>;
+        const HeadView hv = head_view(L, HH, w.cap, w.T);
+        if (tid < GC::ACTIVE)
+            queries_and_outputs<HD, DS, NT, EBC, HH * GC::NV>(t, lds, L, hv, w, scales ? scales[HH] : 1.0f,
+                                                             y0 ? y0 + HH * HD : nullptr, y_qstride, tid);
+        copy_queries<HD, DS, NT, EBC, HPW, HH + 1>(t, lds, L, w, scales, y0, y_qstride, tid);
+    }
+}
+
+template <int HD, int DS, int NT, typename InT, int RM, int HPW>
 __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
     extern __shared__ float lds[];
     using G32 = TileGeo<HD, DS, NT, 4>;
     constexpr int EBC = RM == READ_BF16 ? 2 : 1;     // element size of the read copy
+    using GC = TileGeo<HD, DS, NT, EBC>;
     constexpr int EPVIN = InTraits<InT>::EPV;
     constexpr int VR = HD / EPVIN;                   // 16-byte vectors per x row
     constexpr int VS = DS / EPVIN;                   // 16-byte vectors per B/C row
     constexpr int NW = NT / 64;
     constexpr int JOBS = 2;                          // staged vectors per thread issued up front
+    static_assert(HPW == 1 || (RM != READ_F32 && HPW * GC::NV <= G32::NV && GC::ACTIVE == NT),
+                  "several heads per workgroup only for read copies that fill the register array");
+    static_assert(HPW * NW <= kRedSlots, "reduction slots");
 
-    const int nwg = a.batch * a.nheads;
+    const int chunks = a.nheads / HPW;
+    const int nwg = a.batch * chunks;
     const int wg = xcd_remap(blockIdx.x, nwg);
-    const int b = wg / a.nheads;
-    const int h = wg - b * a.nheads;
+    const int b = wg / chunks;
+    const int h0 = (wg - b * chunks) * HPW;          // first head of this workgroup
     const int hpg = a.nheads / a.ngroups;
-    const int g = h / hpg;
+    const int g = h0 / hpg;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int cap = a.cap;
     const int T = a.T;
-    const size_t tile = (size_t)b * a.nheads + h;
+    const size_t tile0 = (size_t)b * a.nheads + h0;
 
-    const int start = a.meta[2 * tile];
-    const int n_stored = a.meta[2 * tile + 1];
+    // Every head keeps its own copy of the ring pointer; those of a workgroup's
+    // heads must agree.
+    const int start = a.meta[2 * tile0];
+    const int n_stored = a.meta[2 * tile0 + 1];
+    bool same = true;
+#pragma unroll
+    for (int hh = 1; hh < HPW; ++hh)
+        same = same && a.meta[2 * (tile0 + hh)] == start && a.meta[2 * (tile0 + hh) + 1] == n_stored;
     // Fused commit of the previous verification: len += accepted_prev[b].
     int acc_prev = 0;
     bool acc_ok = true;
@@ -298,11 +322,12 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
     }
     const int n = n_stored + acc_prev;
 
-    if (!(acc_ok && start >= 0 && start < cap && n >= 0 && n + T <= cap)) {
-        if (tid == 0 && h == 0 && a.status) atomicOr(a.status, (int)(acc_ok ? kStatusMeta : kStatusAccept));
-        for (int o = tid; o < T * HD; o += NT) {
-            const int q = o / HD, i = o - q * HD;
-            a.y[((size_t)(b * T + q) * a.nheads + h) * HD + i] = __builtin_nanf("");
+    if (!(same && acc_ok && start >= 0 && start < cap && n >= 0 && n + T <= cap)) {
+        if (tid == 0 && h0 == 0 && a.status) atomicOr(a.status, (int)(acc_ok ? kStatusMeta : kStatusAccept));
+        for (int o = tid; o < HPW * T * HD; o += NT) {
+            const int hh = o / (T * HD), r = o - hh * T * HD;
+            const int q = r / HD, i = r - q * HD;
+            a.y[((size_t)(b * T + q) * a.nheads + h0 + hh) * HD + i] = __builtin_nanf("");
         }
         return;
     }
@@ -314,42 +339,55 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
     const int first = fold ? n : 0;  // first window index of the outputs
     const bool append = !flush_call;
     const int rows = n + T;          // window rows staged in LDS
-    const float Ah = a.A[h];
-    const float Dh = a.D[h];
 
-    const Lds L = lds_plan(HD, DS, cap, T);
+    const Lds L = lds_plan(HD, DS, cap, T, HPW);
+    float Ah[HPW], Dh[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+        Ah[hh] = a.A[h0 + hh];
+        Dh[hh] = a.D[h0 + hh];
+    }
 
     // ---- 1/2. record loads, then the tile stream, then LDS staging --------------
-    const InT* bx = reinterpret_cast<const InT*>(a.buf_x) + tile * cap * HD;
+    const InT* bx = reinterpret_cast<const InT*>(a.buf_x) + tile0 * cap * HD;
     const InT* bB = reinterpret_cast<const InT*>(a.buf_B) + ((size_t)b * a.ngroups + g) * cap * DS;
     const InT* xt = reinterpret_cast<const InT*>(a.x);
     const InT* Bt = reinterpret_cast<const InT*>(a.B);
     const InT* Ct = reinterpret_cast<const InT*>(a.C);
-    const bool writer = (h % hpg) == 0;
-    const int nx = rows * VR, nb = rows * VS, nc = T * VS;
+    const bool writer = (h0 % hpg) == 0;
+    const int nx = HPW * rows * VR, nb = rows * VS, nc = T * VS;
     const int nv = nx + nb + nc;
 
-    const StageMap sm{bx, bB, xt, Bt, Ct, start, n, cap, T, b, h, g, a.nheads, a.ngroups,
-                      nx, nb, L.X, L.XS, L.K, L.Cq, append, append && writer};
+    const StageMap sm{bx, bB, xt, Bt, Ct, start, n, cap, T, b, h0, g, a.nheads, a.ngroups,
+                      nx, nb, rows, L.X, L.XS, L.K, L.Cq, append, append && writer};
     uint4 jv[JOBS];
 #pragma unroll
     for (int j = 0; j < JOBS; ++j) {
         const int v = tid + j * NT;
         if (v < nv) jv[j] = *stage_job<HD, DS, InT>(sm, v).src;
     }
+    // dt of (head hh, window row c) for t = hh * rows + c: from the ring for
+    // committed records, from the tokens (and appended to the ring) for queries.
+    float* const bdt0 = a.buf_dt + tile0 * cap;
     float dtv = 0.f;
-    float* bdt = a.buf_dt + tile * cap;
-    if (tid < rows) {
-        const int slot = (start + tid) % cap;
-        dtv = tid < n ? bdt[slot] : a.dt[(size_t)(b * T + (tid - n)) * a.nheads + h];
+    if (tid < HPW * rows) {
+        const int hh = HPW == 1 ? 0 : tid / rows, c = tid - hh * rows;
+        dtv = c < n ? bdt0[hh * cap + (start + c) % cap] : a.dt[(size_t)(b * T + (c - n)) * a.nheads + h0 + hh];
     }
 
-    // The tile this call streams: FP32 when it flushes or has no read copy.
+    // The tile this call streams: FP32 when it flushes or has no read copy,
+    // else the read copies of the workgroup's heads.  A flushing call with
+    // several heads starts the first head's FP32 tile here and streams the
+    // others in step 4.
     TileRegs<HD, DS, NT> treg;
-    if (fold || RM == READ_F32) {
-        treg.template load<4>(a.ckpt + tile * HD * DS, tid);
+    if (RM == READ_F32 || fold) {
+        treg.template load<4>(a.ckpt + tile0 * HD * DS, tid);
     } else {
-        treg.template load<EBC>(reinterpret_cast<const uint8_t*>(a.ckpt_read) + tile * HD * DS * EBC, tid);
+        const uint8_t* cp = reinterpret_cast<const uint8_t*>(a.ckpt_read) + tile0 * HD * DS * EBC;
+        treg.template load<EBC, 0>(cp, tid);
+        if constexpr (HPW > 1) treg.template load<EBC, GC::NV>(cp + 1 * HD * DS * EBC, tid);
+        if constexpr (HPW > 2) treg.template load<EBC, 2 * GC::NV>(cp + 2 * HD * DS * EBC, tid);
+        if constexpr (HPW > 3) treg.template load<EBC, 3 * GC::NV>(cp + 3 * HD * DS * EBC, tid);
     }
 
 #pragma unroll
@@ -367,29 +405,26 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
         if (jb.app) *jb.app = val;
         widen16<InT>(val, lds + jb.dst);
     }
-    if (tid < rows) {
-        if (append && tid >= n) bdt[(start + tid) % cap] = dtv;
-        lds[L.DT + tid] = dtv;
-        lds[L.AA + tid] = dtv * Ah;
-    }
-    for (int c = tid + NT; c < rows; c += NT) {   // windows longer than the workgroup
-        const int slot = (start + c) % cap;
-        float d;
-        if (c < n) {
-            d = bdt[slot];
-        } else {
-            d = a.dt[(size_t)(b * T + (c - n)) * a.nheads + h];
-            if (append) bdt[slot] = d;
-        }
-        lds[L.DT + c] = d;
-        lds[L.AA + c] = d * Ah;
+    for (int t = tid; t < HPW * rows; t += NT) {
+        const int hh = HPW == 1 ? 0 : t / rows, c = t - hh * rows;
+        float d = dtv;
+        if (t >= NT)                                        // windows longer than the workgroup
+            d = c < n ? bdt0[hh * cap + (start + c) % cap] : a.dt[(size_t)(b * T + (c - n)) * a.nheads + h0 + hh];
+        if (append && c >= n) bdt0[hh * cap + (start + c) % cap] = d;
+        float ah = Ah[0];
+#pragma unroll
+        for (int k = 1; k < HPW; ++k) ah = hh == k ? Ah[k] : ah;
+        lds[L.DT + hh * cap + c] = d;
+        lds[L.AA + hh * cap + c] = d * ah;
     }
     __syncthreads();
 
     // ---- 3. coefficients: one 8-lane group per (query, record) pair ---------------
-    // Pairs (q, c), c = first .. m_q, give co[q][c]; when the call folds, the n
-    // pairs (T, c), c < n, give the flush weights.  The group's lanes split the
-    // segment sum of a over (c, m] and the score B_c . C_q, and reduce both.
+    // Pairs (q, c), c = first .. m_q, give co[h][q][c] for every head h of the
+    // workgroup (the score B_c . C_q is the group's, formed once); when the
+    // call folds, the n pairs (T, c), c < n, give the flush weights.  The
+    // group's lanes split the score and each head's segment sum of a over
+    // (c, m], and reduce them.
     {
         constexpr int NG = NT / 8;
         const int sub = tid & 7;
@@ -408,8 +443,6 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
                 c = first + r;
             }
             const int m = q < T ? n + q : n - 1;             // last record the weight spans
-            float seg = 0.f;
-            for (int i = c + 1 + sub; i <= m; i += 8) seg += lds[L.AA + i];
             float sc = 0.f;
             if (q < T) {
                 for (int j4 = sub; j4 < DS / 4; j4 += 8) {
@@ -422,15 +455,21 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
                 }
                 sc = group_sum<8>(sc);
             }
-            seg = group_sum<8>(seg);
-            if (sub == 0) {
-                const float wgt = lds[L.DT + c] * expf(seg);
-                if (q < T) {
-                    lds[L.CO + q * cap + c] = fmaf(wgt, sc, c == m ? Dh : 0.f);
-                    if (c == first) lds[L.DQ + q] = expf(seg + lds[L.AA + c]);
-                } else {
-                    lds[L.WF + c] = wgt;
-                    if (c == 0) lds[L.DQ + T] = expf(seg + lds[L.AA + 0]);
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) {
+                const HeadView hv = head_view(L, hh, cap, T);
+                float seg = 0.f;
+                for (int i = c + 1 + sub; i <= m; i += 8) seg += lds[hv.AA + i];
+                seg = group_sum<8>(seg);
+                if (sub == 0) {
+                    const float wgt = lds[hv.DT + c] * expf(seg);
+                    if (q < T) {
+                        lds[hv.CO + q * cap + c] = fmaf(wgt, sc, c == m ? Dh[hh] : 0.f);
+                        if (c == first) lds[hv.DQ + q] = expf(seg + lds[hv.AA + c]);
+                    } else {
+                        lds[hv.WF + c] = wgt;
+                        if (c == 0) lds[hv.DQ + T] = expf(seg + lds[hv.AA + 0]);
+                    }
                 }
             }
         }
@@ -439,133 +478,178 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
 
     // ---- 4/5. flush in registers, then queries and outputs --------------------------
     const Window win{n, first, T, cap};
-    float* y_head = a.y ? a.y + ((size_t)b * T * a.nheads + h) * HD : nullptr;
+    float* y0 = a.y ? a.y + ((size_t)b * T * a.nheads + h0) * HD : nullptr;
     const size_t y_qstride = (size_t)a.nheads * HD;
     if (fold) {
-        float f[G32::NV][4];
         const bool active = tid < G32::ACTIVE;
         const int j = tid % G32::W;
         const int row0 = G32::row0(tid);
-        float* ck = a.ckpt + tile * HD * DS;
-        float amax = 0.f;
-        if (active) {
-            treg.widen(f);
-            if (n > 0) {
-                const float df = lds[L.DQ + T];
+#pragma unroll 1
+        for (int hh = 0; hh < HPW; ++hh) {                   // one head's FP32 tile at a time
+            const HeadView hv = head_view(L, hh, cap, T);
+            const size_t tile = tile0 + hh;
+            if (HPW > 1 && hh > 0) treg.template load<4>(a.ckpt + tile * HD * DS, tid);
+            v4f* f = treg.raw;                                // the tile, updated in place
+            float* ck = a.ckpt + tile * HD * DS;
+            float amax = 0.f;
+            if (active) {
+                if (n > 0) {
+                    const float df = lds[hv.DQ + T];
 #pragma unroll
-                for (int s = 0; s < G32::NV; ++s)
+                    for (int s = 0; s < G32::NV; ++s) f[s] *= df;
+                    for (int c = 0; c < n; ++c) {
+                        const float wf = lds[hv.WF + c];
+                        float xs[G32::NI];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) f[s][e] *= df;
-                for (int c = 0; c < n; ++c) {
-                    const float wf = lds[L.WF + c];
-                    float xs[G32::NI];
+                        for (int r = 0; r < G32::NI; ++r) xs[r] = lds[hv.X + c * L.XS + row0 + r] * wf;
 #pragma unroll
-                    for (int r = 0; r < G32::NI; ++r) xs[r] = lds[L.X + c * L.XS + row0 + r] * wf;
+                        for (int k = 0; k < G32::VPL; ++k) {
+                            const float4 kb =
+                                *reinterpret_cast<const float4*>(lds + L.K + c * DS + (j + G32::W * k) * 4);
 #pragma unroll
-                    for (int k = 0; k < G32::VPL; ++k) {
-                        const float4 kb = *reinterpret_cast<const float4*>(lds + L.K + c * DS + (j + G32::W * k) * 4);
-#pragma unroll
-                        for (int r = 0; r < G32::NI; ++r) {
-                            float* fv = f[r * G32::VPL + k];
-                            fv[0] = fmaf(xs[r], kb.x, fv[0]);
-                            fv[1] = fmaf(xs[r], kb.y, fv[1]);
-                            fv[2] = fmaf(xs[r], kb.z, fv[2]);
-                            fv[3] = fmaf(xs[r], kb.w, fv[3]);
+                            for (int r = 0; r < G32::NI; ++r) {
+                                v4f& fv = f[r * G32::VPL + k];
+                                fv.x = fmaf(xs[r], kb.x, fv.x);
+                                fv.y = fmaf(xs[r], kb.y, fv.y);
+                                fv.z = fmaf(xs[r], kb.z, fv.z);
+                                fv.w = fmaf(xs[r], kb.w, fv.w);
+                            }
                         }
                     }
-                }
-                v4f* out = reinterpret_cast<v4f*>(ck);
+                    v4f* out = reinterpret_cast<v4f*>(ck);
 #pragma unroll
-                for (int s = 0; s < G32::NV; ++s) {
-                    const v4f val = {f[s][0], f[s][1], f[s][2], f[s][3]};
-                    __builtin_nontemporal_store(val, out + G32::vec(tid, s));
+                    for (int s = 0; s < G32::NV; ++s) __builtin_nontemporal_store(f[s], out + G32::vec(tid, s));
                 }
-            }
-            if constexpr (RM == READ_BF16) {
-                uint2* out = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.ckpt_read) + tile * HD * DS);
+                if constexpr (RM == READ_BF16) {
+                    uint2* out =
+                        reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.ckpt_read) + tile * HD * DS);
 #pragma unroll
-                for (int s = 0; s < G32::NV; ++s)
-                    out[G32::vec(tid, s)] =
-                        make_uint2(f32x2_to_bf16x2(f[s][0], f[s][1]), f32x2_to_bf16x2(f[s][2], f[s][3]));
+                    for (int s = 0; s < G32::NV; ++s)
+                        out[G32::vec(tid, s)] =
+                            make_uint2(f32x2_to_bf16x2(f[s].x, f[s].y), f32x2_to_bf16x2(f[s].z, f[s].w));
+                }
+                if constexpr (RM == READ_E4M3) {
+#pragma unroll
+                    for (int s = 0; s < G32::NV; ++s)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(f[s][e]));
+                }
             }
             if constexpr (RM == READ_E4M3) {
+                amax = group_max<64>(amax);
+                if (lane == 0) lds[L.RED + hh * NW + wave] = amax;
+                __syncthreads();
+                amax = 0.f;
 #pragma unroll
-                for (int s = 0; s < G32::NV; ++s)
+                for (int w = 0; w < NW; ++w) amax = fmaxf(amax, lds[L.RED + hh * NW + w]);
+                const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+                const float inv = 1.0f / sc;
+                if (active) {
+                    uint32_t* out =
+                        reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.ckpt_read) + tile * HD * DS);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(f[s][e]));
+                    for (int s = 0; s < G32::NV; ++s)
+                        out[G32::vec(tid, s)] = f32x4_to_e4m3(f[s].x * inv, f[s].y * inv, f[s].z * inv, f[s].w * inv);
+                }
+                if (tid == 0) a.ckpt_scale[tile] = sc;
             }
-        }
-        if constexpr (RM == READ_E4M3) {
-            amax = group_max<64>(amax);
-            if (lane == 0) lds[L.RED + wave] = amax;
-            __syncthreads();
-            amax = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) amax = fmaxf(amax, lds[L.RED + w]);
-            const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-            const float inv = 1.0f / sc;
-            if (active) {
-                uint32_t* out = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.ckpt_read) + tile * HD * DS);
-#pragma unroll
-                for (int s = 0; s < G32::NV; ++s)
-                    out[G32::vec(tid, s)] = f32x4_to_e4m3(f[s][0] * inv, f[s][1] * inv, f[s][2] * inv, f[s][3] * inv);
-            }
-            if (tid == 0) a.ckpt_scale[tile] = sc;
-        }
-        if (active && T > 0) {
-            treg.set(f);
-            queries_and_outputs<HD, DS, NT, 4>(treg, lds, L, win, 1.0f, y_head, y_qstride, tid);
+            if (active && T > 0)
+                queries_and_outputs<HD, DS, NT, 4>(treg, lds, L, hv, win, 1.0f, y0 ? y0 + hh * HD : nullptr,
+                                                   y_qstride, tid);
         }
     } else if constexpr (RM == READ_F32) {
         if (tid < G32::ACTIVE)
-            queries_and_outputs<HD, DS, NT, 4>(treg, lds, L, win, 1.0f, y_head, y_qstride, tid);
+            queries_and_outputs<HD, DS, NT, 4>(treg, lds, L, head_view(L, 0, cap, T), win, 1.0f, y0, y_qstride,
+                                               tid);
     } else {
-        if (tid < TileGeo<HD, DS, NT, EBC>::ACTIVE) {
-            const float sc = RM == READ_E4M3 ? a.ckpt_scale[tile] : 1.0f;
-            queries_and_outputs<HD, DS, NT, EBC>(treg, lds, L, win, sc, y_head, y_qstride, tid);
-        }
+        float scales[HPW];
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) scales[hh] = RM == READ_E4M3 ? a.ckpt_scale[tile0 + hh] : 1.0f;
+        copy_queries<HD, DS, NT, EBC, HPW>(treg, lds, L, win, scales, y0, y_qstride, tid);
     }
 
-    // ---- 6. advance this head's ring pointer -----------------------------------------
+    // ---- 6. advance the heads' ring pointers -----------------------------------------
     const int new_start = fold && n > 0 ? (start + n) % cap : start;
     const int new_n = (fold ? 0 : n) + (a.mode == MODE_DECODE ? 1 : 0);
-    if ((new_start != start || new_n != n_stored) && tid == 0) {
-        a.meta[2 * tile] = new_start;
-        a.meta[2 * tile + 1] = new_n;
+    if ((new_start != start || new_n != n_stored) && tid < HPW) {
+        a.meta[2 * (tile0 + tid)] = new_start;
+        a.meta[2 * (tile0 + tid) + 1] = new_n;
     }
 }
 
-template <int HD, int DS, typename InT, int RM>
+int threads_for(int hd, int ds) {
+    if (hd == 16 && ds == 16) return ShapeNT<16, 16>::NT;
+    if (hd == 64 && ds == 64) return ShapeNT<64, 64>::NT;
+    if (hd == 64 && ds == 128) return ShapeNT<64, 128>::NT;
+    return ShapeNT<128, 128>::NT;
+}
+
+// Heads per workgroup: the read-copy modes serve several heads of one group
+// per workgroup (so each streams as many bytes as one FP32 tile and the heads
+// share the group's B/C staging and scores) when the heads of a group split
+// evenly and the workgroup's LDS stays within 64 KiB; flush-only calls and
+// the FP32 mode use one head.
+int heads_per_wg(int hd, int ds, int nheads, int ngroups, int cap, int T, int read_mode, int mode) {
+    // (the launchers fall back to fewer heads where a shape's copy tile does not
+    // leave room in the register array for this many)
+    if (read_mode == READ_F32 || mode == MODE_FLUSH || hd == 16) return 1;
+    const int want = read_mode == READ_E4M3 ? 4 : 2;
+    const int hpg = nheads / ngroups;
+    for (int hpw = want; hpw > 1; hpw /= 2)
+        if (hpg % hpw == 0 && (size_t)lds_plan(hd, ds, cap, T, hpw).total * sizeof(float) <= 65536 &&
+            hpw * (threads_for(hd, ds) / 64) <= kRedSlots)
+            return hpw;
+    return 1;
+}
+
+template <int HD, int DS, typename InT, int RM, int HPW>
 hipError_t launch_one(const ReplayArgs& a, hipStream_t stream) {
     constexpr int NT = ShapeNT<HD, DS>::NT;
-    const int nwg = a.batch * a.nheads;
-    const size_t lds = (size_t)lds_plan(HD, DS, a.cap, a.T).total * sizeof(float);
-    hipLaunchKernelGGL((replay_kernel<HD, DS, NT, InT, RM>), dim3(nwg), dim3(NT), lds, stream, a);
+    const int nwg = a.batch * (a.nheads / HPW);
+    const size_t lds = (size_t)lds_plan(HD, DS, a.cap, a.T, HPW).total * sizeof(float);
+    hipLaunchKernelGGL((replay_kernel<HD, DS, NT, InT, RM, HPW>), dim3(nwg), dim3(NT), lds, stream, a);
     return hipGetLastError();
+}
+
+// Read-copy launch with hpw heads per workgroup; the multi-head kernels are
+// compiled only where a copy tile leaves room for them (not 16 x 16).
+template <int HD, int DS, int RM, int HPW>
+constexpr bool multi_head_fits() {
+    using GC = TileGeo<HD, DS, ShapeNT<HD, DS>::NT, RM == READ_BF16 ? 2 : 1>;
+    return HD != 16 && HPW * GC::NV <= TileGeo<HD, DS, ShapeNT<HD, DS>::NT, 4>::NV &&
+           GC::ACTIVE == ShapeNT<HD, DS>::NT;
+}
+
+template <int HD, int DS, typename InT, int RM>
+hipError_t launch_copy(const ReplayArgs& a, int hpw, hipStream_t stream) {
+    if constexpr (RM == READ_E4M3 && multi_head_fits<HD, DS, RM, 4>())
+        if (hpw == 4) return launch_one<HD, DS, InT, RM, 4>(a, stream);
+    if constexpr (multi_head_fits<HD, DS, RM, 2>())
+        if (hpw >= 2) return launch_one<HD, DS, InT, RM, 2>(a, stream);
+    return launch_one<HD, DS, InT, RM, 1>(a, stream);
+}
+
+template <int HD, int DS, typename InT>
+hipError_t launch_type(const ReplayArgs& a, int read_mode, int hpw, hipStream_t stream) {
+    switch (read_mode) {
+        case READ_F32: return launch_one<HD, DS, InT, READ_F32, 1>(a, stream);
+        case READ_BF16: return launch_copy<HD, DS, InT, READ_BF16>(a, hpw, stream);
+        case READ_E4M3: return launch_copy<HD, DS, InT, READ_E4M3>(a, hpw, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int HD, int DS>
 hipError_t launch_shape(const ReplayArgs& a, int in_type, int read_mode, hipStream_t stream) {
-    if (in_type == IN_F32) {
-        switch (read_mode) {
-            case READ_F32: return launch_one<HD, DS, float, READ_F32>(a, stream);
-            case READ_BF16: return launch_one<HD, DS, float, READ_BF16>(a, stream);
-            case READ_E4M3: return launch_one<HD, DS, float, READ_E4M3>(a, stream);
-        }
-    } else {
-        switch (read_mode) {
-            case READ_F32: return launch_one<HD, DS, uint16_t, READ_F32>(a, stream);
-            case READ_BF16: return launch_one<HD, DS, uint16_t, READ_BF16>(a, stream);
-            case READ_E4M3: return launch_one<HD, DS, uint16_t, READ_E4M3>(a, stream);
-        }
-    }
-    return hipErrorInvalidValue;
+    const int hpw = heads_per_wg(HD, DS, a.nheads, a.ngroups, a.cap, a.T, read_mode, a.mode);
+    if (in_type == IN_F32) return launch_type<HD, DS, float>(a, read_mode, hpw, stream);
+    return launch_type<HD, DS, uint16_t>(a, read_mode, hpw, stream);
 }
 
 }  // namespace
 
 size_t replay_lds_bytes(int hd, int ds, int cap, int T, int /*in_bytes: records are widened to fp32*/) {
-    return (size_t)lds_plan(hd, ds, cap, T).total * sizeof(float);
+    return (size_t)lds_plan(hd, ds, cap, T, 1).total * sizeof(float);   // one head per workgroup
 }
 
 bool shape_supported(int hd, int ds) {
