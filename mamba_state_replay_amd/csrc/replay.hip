@@ -38,22 +38,24 @@ namespace rssm {
 
 namespace {
 
-// LDS plan in floats for a workgroup serving HPW heads of one group.  x rows
-// are padded to XS = HD + 4 floats so that the lanes of a row group, each
-// reading a different record's x rows in step 5, fall on different banks.
-// Per-head arrays are indexed [head][...]; B and C rows are the group's and
-// are shared by the heads.
+// LDS plan in floats for a workgroup serving HPW heads of one group.  The x
+// rows keep the input element type (xbytes = 4 for fp32, 2 for bf16; they
+// are widened where they are read) and are padded to XS elements, a row
+// stride of 4 banks mod 32, so that the lanes of a row group, each reading a
+// different record's x in step 5, fall on different banks.  Per-head arrays
+// are indexed [head][...]; B and C rows are the group's, widened to fp32 and
+// shared by the heads.
 struct Lds {
     int X, XS, K, Cq, DT, AA, CO, DQ, WF, RED, total;
 };
 
 constexpr int kRedSlots = 64;   // cross-wave reduction slots: [head][wave]
 
-__host__ __device__ inline Lds lds_plan(int HD, int DS, int cap, int T, int HPW) {
+__host__ __device__ inline Lds lds_plan(int HD, int DS, int cap, int T, int HPW, int xbytes) {
     Lds l;
     int o = 0;
-    l.XS = HD + 4;
-    l.X = o;  o += HPW * cap * l.XS; // x of records then queries, window order, per head
+    l.XS = xbytes == 4 ? HD + 4 : HD + 8;           // elements; 16-byte aligned rows
+    l.X = o;  o += HPW * cap * l.XS * xbytes / 4;    // x of records then queries, window order, per head
     l.K = o;  o += cap * DS;         // B of records then queries
     l.Cq = o; o += T * DS;           // C of the queries
     l.DT = o; o += HPW * cap;        // dt, window order, per head
@@ -71,9 +73,49 @@ struct HeadView {
     int X, DT, AA, CO, DQ, WF;
 };
 
+// X is the head's x block in floats; its rows hold elements of type InT.
+template <typename InT>
 __device__ __forceinline__ HeadView head_view(const Lds& L, int hh, int cap, int T) {
-    return HeadView{L.X + hh * cap * L.XS, L.DT + hh * cap, L.AA + hh * cap, L.CO + hh * T * cap,
-                    L.DQ + hh * (T + 1), L.WF + hh * cap};
+    return HeadView{L.X + hh * cap * L.XS * (int)sizeof(InT) / 4, L.DT + hh * cap, L.AA + hh * cap,
+                    L.CO + hh * T * cap, L.DQ + hh * (T + 1), L.WF + hh * cap};
+}
+
+// x_c[row0 .. row0 + N - 1] of one head as fp32, from a row of InT elements.
+template <typename InT, int N>
+__device__ __forceinline__ void load_x(const float* lds, int xblock, int elem, float (&out)[N]) {
+    if constexpr (sizeof(InT) == 4) {
+        const float* p = lds + xblock + elem;
+        if constexpr (N % 4 == 0) {
+#pragma unroll
+            for (int r = 0; r < N; r += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(p + r);
+                out[r] = v.x;
+                out[r + 1] = v.y;
+                out[r + 2] = v.z;
+                out[r + 3] = v.w;
+            }
+        } else if constexpr (N == 2) {
+            const float2 v = *reinterpret_cast<const float2*>(p);
+            out[0] = v.x;
+            out[1] = v.y;
+        } else {
+#pragma unroll
+            for (int r = 0; r < N; ++r) out[r] = p[r];
+        }
+    } else {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(lds + xblock) + elem;
+        if constexpr (N % 2 == 0) {
+#pragma unroll
+            for (int r = 0; r < N; r += 2) {
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(p + r);
+                out[r] = __uint_as_float(w << 16);
+                out[r + 1] = __uint_as_float(w & 0xFFFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < N; ++r) out[r] = bf16_to_f32(p[r]);
+        }
+    }
 }
 
 // This thread's share of a tile held as raw 16-byte vectors (issued in step
@@ -164,7 +206,8 @@ struct StageMap {
 struct StageJob {
     const uint4* src;
     uint4* app;   // ring destination of a query's record, or null
-    int dst;      // LDS offset (floats)
+    int dst;      // LDS offset in bytes
+    bool wide;    // widen to fp32 (B and C rows) or keep the input type (x rows)
 };
 
 template <int HD, int DS, typename InT>
@@ -188,7 +231,8 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
                     ((size_t)(m.b * m.T + c - m.n) * m.nheads + m.h + hh) * VR + cv;
             if (m.append_x) j.app = const_cast<uint4*>(ring);
         }
-        j.dst = m.ldsX + (hh * m.cap + c) * m.ldsXS + cv * EPVIN;
+        j.dst = m.ldsX * 4 + ((hh * m.cap + c) * m.ldsXS + cv * EPVIN) * (int)sizeof(InT);
+        j.wide = false;
     } else if (v < m.nx + m.nb) {
         const int u = v - m.nx;
         const int c = u / VS, cv = u - c * VS;
@@ -200,14 +244,25 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
                     ((size_t)(m.b * m.T + c - m.n) * m.ngroups + m.g) * VS + cv;
             if (m.append_B) j.app = const_cast<uint4*>(ring);
         }
-        j.dst = m.ldsK + c * DS + cv * EPVIN;
+        j.dst = (m.ldsK + c * DS + cv * EPVIN) * 4;
+        j.wide = true;
     } else {
         const int u = v - m.nx - m.nb;
         const int q = u / VS, cv = u - q * VS;
         j.src = reinterpret_cast<const uint4*>(m.Ct) + ((size_t)(m.b * m.T + q) * m.ngroups + m.g) * VS + cv;
-        j.dst = m.ldsC + q * DS + cv * EPVIN;
+        j.dst = (m.ldsC + q * DS + cv * EPVIN) * 4;
+        j.wide = true;
     }
     return j;
+}
+
+template <typename InT>
+__device__ __forceinline__ void stage_store(float* lds, const StageJob& jb, const uint4 v) {
+    char* d = reinterpret_cast<char*>(lds) + jb.dst;
+    if (sizeof(InT) == 4 || !jb.wide)
+        *reinterpret_cast<uint4*>(d) = v;
+    else
+        widen16<InT>(v, reinterpret_cast<float*>(d));
 }
 
 // Step 5 for one head's tile held in registers (vectors OFF ..) with element
@@ -217,7 +272,7 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
 // co[q][c] x_c[row] (the D x_q term rides on co[q][m_q]).  One transposed
 // reduction over the row's W lanes then leaves y_q[row] on one lane, which
 // stores it.
-template <int HD, int DS, int NT, int EB, int OFF = 0>
+template <int HD, int DS, int NT, typename InT, int EB, int OFF = 0>
 __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& t, const float* lds,
                                                     const Lds& L, const HeadView& hv, const Window& w,
                                                     float scale, float* y_head, size_t y_qstride, int tid) {
@@ -236,23 +291,10 @@ __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& 
         const int m = w.n + q;
         for (int cc = w.first + j; cc <= m; cc += G::W) {
             const float co = lds[hv.CO + q * w.cap + cc];
-            const float* xr = lds + hv.X + cc * L.XS + row0;
-            if constexpr (G::NI % 4 == 0) {
+            float xv[G::NI];
+            load_x<InT, G::NI>(lds, hv.X, cc * L.XS + row0, xv);
 #pragma unroll
-                for (int r = 0; r < G::NI; r += 4) {
-                    const float4 xv = *reinterpret_cast<const float4*>(xr + r);
-                    v[r] = fmaf(co, xv.x, v[r]);
-                    v[r + 1] = fmaf(co, xv.y, v[r + 1]);
-                    v[r + 2] = fmaf(co, xv.z, v[r + 2]);
-                    v[r + 3] = fmaf(co, xv.w, v[r + 3]);
-                }
-            } else if constexpr (G::NI == 2) {
-                const float2 xv = *reinterpret_cast<const float2*>(xr);
-                v[0] = fmaf(co, xv.x, v[0]);
-                v[1] = fmaf(co, xv.y, v[1]);
-            } else {
-                v[0] = fmaf(co, xr[0], v[0]);
-            }
+            for (int r = 0; r < G::NI; ++r) v[r] = fmaf(co, xv[r], v[r]);
         }
         int idx;
         const float u = transpose_reduce<G::NI, G::W>(v, lane, idx);
@@ -262,17 +304,17 @@ __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& 
 
 // The read-copy tiles of HPW heads, each over the whole workgroup in its own
 // vectors of the register array: step 5 for every head.
-template <int HD, int DS, int NT, int EBC, int HPW, int HH = 0>
+template <int HD, int DS, int NT, typename InT, int EBC, int HPW, int HH = 0>
 __device__ __forceinline__ void copy_queries(const TileRegs<HD, DS, NT>& t, const float* lds, const Lds& L,
                                              const Window& w, const float* scales, float* y0,
                                              size_t y_qstride, int tid) {
     if constexpr (HH < HPW) {
         using GC = TileGeo<HD, DS, NT, EBC>;
-        const HeadView hv = head_view(L, HH, w.cap, w.T);
+        const HeadView hv = head_view<InT>(L, HH, w.cap, w.T);
         if (tid < GC::ACTIVE)
-            queries_and_outputs<HD, DS, NT, EBC, HH * GC::NV>(t, lds, L, hv, w, scales ? scales[HH] : 1.0f,
-                                                             y0 ? y0 + HH * HD : nullptr, y_qstride, tid);
-        copy_queries<HD, DS, NT, EBC, HPW, HH + 1>(t, lds, L, w, scales, y0, y_qstride, tid);
+            queries_and_outputs<HD, DS, NT, InT, EBC, HH * GC::NV>(t, lds, L, hv, w, scales ? scales[HH] : 1.0f,
+                                                                  y0 ? y0 + HH * HD : nullptr, y_qstride, tid);
+        copy_queries<HD, DS, NT, InT, EBC, HPW, HH + 1>(t, lds, L, w, scales, y0, y_qstride, tid);
     }
 }
 
@@ -340,7 +382,7 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
     const bool append = !flush_call;
     const int rows = n + T;          // window rows staged in LDS
 
-    const Lds L = lds_plan(HD, DS, cap, T, HPW);
+    const Lds L = lds_plan(HD, DS, cap, T, HPW, sizeof(InT));
     float Ah[HPW], Dh[HPW];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -396,14 +438,14 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
         if (v < nv) {
             const StageJob jb = stage_job<HD, DS, InT>(sm, v);
             if (jb.app) *jb.app = jv[j];
-            widen16<InT>(jv[j], lds + jb.dst);
+            stage_store<InT>(lds, jb, jv[j]);
         }
     }
     for (int v = tid + JOBS * NT; v < nv; v += NT) {   // windows too long for JOBS vectors a thread
         const StageJob jb = stage_job<HD, DS, InT>(sm, v);
         const uint4 val = *jb.src;
         if (jb.app) *jb.app = val;
-        widen16<InT>(val, lds + jb.dst);
+        stage_store<InT>(lds, jb, val);
     }
     for (int t = tid; t < HPW * rows; t += NT) {
         const int hh = HPW == 1 ? 0 : t / rows, c = t - hh * rows;
@@ -457,7 +499,7 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
             }
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
-                const HeadView hv = head_view(L, hh, cap, T);
+                const HeadView hv = head_view<InT>(L, hh, cap, T);
                 float seg = 0.f;
                 for (int i = c + 1 + sub; i <= m; i += 8) seg += lds[hv.AA + i];
                 seg = group_sum<8>(seg);
@@ -486,7 +528,7 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
         const int row0 = G32::row0(tid);
 #pragma unroll 1
         for (int hh = 0; hh < HPW; ++hh) {                   // one head's FP32 tile at a time
-            const HeadView hv = head_view(L, hh, cap, T);
+            const HeadView hv = head_view<InT>(L, hh, cap, T);
             const size_t tile = tile0 + hh;
             if (HPW > 1 && hh > 0) treg.template load<4>(a.ckpt + tile * HD * DS, tid);
             v4f* f = treg.raw;                                // the tile, updated in place
@@ -500,8 +542,9 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
                     for (int c = 0; c < n; ++c) {
                         const float wf = lds[hv.WF + c];
                         float xs[G32::NI];
+                        load_x<InT, G32::NI>(lds, hv.X, c * L.XS + row0, xs);
 #pragma unroll
-                        for (int r = 0; r < G32::NI; ++r) xs[r] = lds[hv.X + c * L.XS + row0 + r] * wf;
+                        for (int r = 0; r < G32::NI; ++r) xs[r] *= wf;
 #pragma unroll
                         for (int k = 0; k < G32::VPL; ++k) {
                             const float4 kb =
@@ -554,18 +597,18 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
                 if (tid == 0) a.ckpt_scale[tile] = sc;
             }
             if (active && T > 0)
-                queries_and_outputs<HD, DS, NT, 4>(treg, lds, L, hv, win, 1.0f, y0 ? y0 + hh * HD : nullptr,
-                                                   y_qstride, tid);
+                queries_and_outputs<HD, DS, NT, InT, 4>(treg, lds, L, hv, win, 1.0f, y0 ? y0 + hh * HD : nullptr,
+                                                        y_qstride, tid);
         }
     } else if constexpr (RM == READ_F32) {
         if (tid < G32::ACTIVE)
-            queries_and_outputs<HD, DS, NT, 4>(treg, lds, L, head_view(L, 0, cap, T), win, 1.0f, y0, y_qstride,
-                                               tid);
+            queries_and_outputs<HD, DS, NT, InT, 4>(treg, lds, L, head_view<InT>(L, 0, cap, T), win, 1.0f, y0,
+                                                    y_qstride, tid);
     } else {
         float scales[HPW];
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) scales[hh] = RM == READ_E4M3 ? a.ckpt_scale[tile0 + hh] : 1.0f;
-        copy_queries<HD, DS, NT, EBC, HPW>(treg, lds, L, win, scales, y0, y_qstride, tid);
+        copy_queries<HD, DS, NT, InT, EBC, HPW>(treg, lds, L, win, scales, y0, y_qstride, tid);
     }
 
     // ---- 6. advance the heads' ring pointers -----------------------------------------
@@ -589,14 +632,14 @@ int threads_for(int hd, int ds) {
 // share the group's B/C staging and scores) when the heads of a group split
 // evenly and the workgroup's LDS stays within 64 KiB; flush-only calls and
 // the FP32 mode use one head.
-int heads_per_wg(int hd, int ds, int nheads, int ngroups, int cap, int T, int read_mode, int mode) {
+int heads_per_wg(int hd, int ds, int nheads, int ngroups, int cap, int T, int read_mode, int mode, int xbytes) {
     // (the launchers fall back to fewer heads where a shape's copy tile does not
     // leave room in the register array for this many)
     if (read_mode == READ_F32 || mode == MODE_FLUSH || hd == 16) return 1;
     const int want = read_mode == READ_E4M3 ? 4 : 2;
     const int hpg = nheads / ngroups;
     for (int hpw = want; hpw > 1; hpw /= 2)
-        if (hpg % hpw == 0 && (size_t)lds_plan(hd, ds, cap, T, hpw).total * sizeof(float) <= 65536 &&
+        if (hpg % hpw == 0 && (size_t)lds_plan(hd, ds, cap, T, hpw, xbytes).total * sizeof(float) <= 65536 &&
             hpw * (threads_for(hd, ds) / 64) <= kRedSlots)
             return hpw;
     return 1;
@@ -606,7 +649,7 @@ template <int HD, int DS, typename InT, int RM, int HPW>
 hipError_t launch_one(const ReplayArgs& a, hipStream_t stream) {
     constexpr int NT = ShapeNT<HD, DS>::NT;
     const int nwg = a.batch * (a.nheads / HPW);
-    const size_t lds = (size_t)lds_plan(HD, DS, a.cap, a.T, HPW).total * sizeof(float);
+    const size_t lds = (size_t)lds_plan(HD, DS, a.cap, a.T, HPW, sizeof(InT)).total * sizeof(float);
     hipLaunchKernelGGL((replay_kernel<HD, DS, NT, InT, RM, HPW>), dim3(nwg), dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
@@ -641,15 +684,16 @@ hipError_t launch_type(const ReplayArgs& a, int read_mode, int hpw, hipStream_t 
 
 template <int HD, int DS>
 hipError_t launch_shape(const ReplayArgs& a, int in_type, int read_mode, hipStream_t stream) {
-    const int hpw = heads_per_wg(HD, DS, a.nheads, a.ngroups, a.cap, a.T, read_mode, a.mode);
+    const int hpw = heads_per_wg(HD, DS, a.nheads, a.ngroups, a.cap, a.T, read_mode, a.mode,
+                                 in_type == IN_F32 ? 4 : 2);
     if (in_type == IN_F32) return launch_type<HD, DS, float>(a, read_mode, hpw, stream);
     return launch_type<HD, DS, uint16_t>(a, read_mode, hpw, stream);
 }
 
 }  // namespace
 
-size_t replay_lds_bytes(int hd, int ds, int cap, int T, int /*in_bytes: records are widened to fp32*/) {
-    return (size_t)lds_plan(hd, ds, cap, T, 1).total * sizeof(float);   // one head per workgroup
+size_t replay_lds_bytes(int hd, int ds, int cap, int T, int in_bytes) {
+    return (size_t)lds_plan(hd, ds, cap, T, 1, in_bytes).total * sizeof(float);   // one head per workgroup
 }
 
 bool shape_supported(int hd, int ds) {
