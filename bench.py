@@ -145,25 +145,43 @@ def main():
         rb.replayssm_decode_step(cfg, st, p, toks.call(i % ntok), y)
     torch.cuda.synchronize()
 
-    sched, n_end = traffic.decode_schedule(work.n0, L, W + K)
+    # Three passes of K steps after the warm-up: eager launches with an event
+    # pair around each (the kernel's own duration), then the same K launches
+    # captured in one HIP graph, replayed once to warm up and once timed (the
+    # step time without the host's per-launch cost, as a decode loop runs them).
+    sched, n_end = traffic.decode_schedule(work.n0, L, W + 3 * K)
     sz = traffic.sizes(128, 64, 128, 8, 2, read_copy)
-    timed_sched = sched[W:]
-    bytes_per_launch = [traffic.decode_step_bytes(sz, n, f) for n, f in timed_sched]
-    folds = sum(int(f.any()) for _, f in timed_sched)
+    eager_sched = sched[W:W + K]
+    graph_sched = sched[W + 2 * K:W + 3 * K]
+    bytes_per_launch = [traffic.decode_step_bytes(sz, n, f) for n, f in eager_sched]
+    folds = sum(int(f.any()) for _, f in graph_sched)
 
-    total_ms, per_ms = timed_launches(
-        lambda i: rb.replayssm_decode_step(cfg, st, p, toks.call((W + i) % ntok), y), K, torch)
+    step = lambda i: rb.replayssm_decode_step(cfg, st, p, toks.call((W + i) % ntok), y)
+    eager_ms, per_ms = timed_launches(step, K, torch)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            rb.replayssm_decode_step(cfg, st, p, toks.call((W + K + i) % ntok), y)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    del g
     meta = st.meta.cpu().numpy()
     assert np.all(meta[:, :, 1] == n_end[:, None]), "ring pointers disagree with the flush schedule"
     assert int(st.status.cpu()[0]) == 0 and bool(torch.isfinite(y).all())
 
-    total_bytes = sum(bytes_per_launch)
+    total_bytes = sum(traffic.decode_step_bytes(sz, n, f) for n, f in graph_sched)
     us_step = total_ms * 1e3 / K
     gbs = total_bytes / (total_ms * 1e-3) / 1e9
     kernel_ms = float(np.mean(per_ms))
-    achieved = (total_bytes / K) / (kernel_ms * 1e-3) / 1e9
-    fold_ms = [t for t, (_, f) in zip(per_ms, timed_sched) if f.any()]
-    nonfold_ms = [t for t, (_, f) in zip(per_ms, timed_sched) if not f.any()]
+    achieved = (sum(bytes_per_launch) / K) / (kernel_ms * 1e-3) / 1e9
+    fold_ms = [t for t, (_, f) in zip(per_ms, eager_sched) if f.any()]
+    nonfold_ms = [t for t, (_, f) in zip(per_ms, eager_sched) if not f.any()]
 
     traffic_bytes = None
     if COUNTERS.exists():
@@ -180,6 +198,8 @@ def main():
         "warmup": W,
         "ms_per_step": round(total_ms / K, 6),
         "us_per_step": round(us_step, 2),
+        "timing": "K steps captured in one HIP graph, one replay timed with HIP events after a warm replay",
+        "eager_us_per_step": round(eager_ms * 1e3 / K, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -202,7 +222,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
             "traffic": traffic_bytes,
-            "algorithmic_bytes_per_launch": int(total_bytes / K),
+            "algorithmic_bytes_per_launch": int(sum(bytes_per_launch) / K),
             "avg_launch_us": round(kernel_ms * 1e3, 2),
             "nonflush_launch_us": round(float(np.mean(nonfold_ms)) * 1e3, 2) if nonfold_ms else None,
             "flush_launch_us": round(float(np.mean(fold_ms)) * 1e3, 2) if fold_ms else None,
@@ -213,12 +233,14 @@ def main():
         states = staging.conventional_states(cfg, work.h0, 1, dev)
         for i in range(W):
             rb.conventional_state_update(cfg, states, p, toks.call(i % ntok), y)
-        ctot, cper = timed_launches(
-            lambda i: rb.conventional_state_update(cfg, states, p, toks.call((W + i) % ntok), y), K, torch)
+        cstep = lambda i: rb.conventional_state_update(cfg, states, p, toks.call((W + i) % ntok), y)
+        ceager, cper = timed_launches(cstep, K, torch)
+        ctot = graph_time(cstep, K, torch)
         cbytes = traffic.conventional_step_bytes(sz, shape.batch)
         c_us = ctot * 1e3 / K
         result["conventional"] = {
             "us_per_step": round(c_us, 2),
+            "eager_us_per_step": round(ceager * 1e3 / K, 2),
             "gbs": round(cbytes / (c_us * 1e-6) / 1e9, 1),
             "avg_launch_us": round(float(np.mean(cper)) * 1e3, 2),
             "frac": round(cbytes / (float(np.mean(cper)) * 1e-3) / 1e9 / PEAK_GBS, 4),
@@ -324,12 +346,17 @@ def _verify_point(T, batch=512, L=16, rounds=64, seed=1003, snapshots=True):
     acc = torch.from_numpy(work.extra["accepted"]).to(dev)
     y = torch.empty((batch, T, 128, 64), device=dev)
     sz = traffic.sizes(128, 64, 128, 8, 2, None)
-    n = work.n0.astype(np.int64).copy()
-    rbytes = []
-    for r in range(rounds):
-        fold = n >= L
-        rbytes.append(traffic.verify_bytes(sz, n, fold, T))
-        n = np.where(fold, 0, n) + work.extra["accepted"][r]
+    acc_np = work.extra["accepted"]
+
+    def schedule(n, passes):
+        """Bytes per round of `passes` consecutive passes over the rounds, from fill n."""
+        out = []
+        for _ in range(passes):
+            for r in range(rounds):
+                fold = n >= L
+                out.append(traffic.verify_bytes(sz, n, fold, T))
+                n = np.where(fold, 0, n) + acc_np[r]
+        return out, n
 
     def replay_round(r):
         rb.replayssm_verify_drafts(cfg, st, p, toks.call(r), y)
@@ -337,34 +364,47 @@ def _verify_point(T, batch=512, L=16, rounds=64, seed=1003, snapshots=True):
     for r in range(8):                       # warm-up on a throw-away copy of the state
         replay_round(r)
     st = staging.replay_state(cfg, work, dev)
+    # pass 1: eager launches (per-round events); passes 2 and 3: the same rounds
+    # captured in one HIP graph, a warm replay and a timed one
+    rbytes, n_end = schedule(work.n0.astype(np.int64).copy(), 3)
     ms, per = timed_launches(replay_round, rounds, torch)
+    gms = graph_time(replay_round, rounds, torch)
     meta = st.meta.cpu().numpy()
-    assert np.all(meta[:, :, 1] == n[:, None]) and int(st.status.cpu()[0]) == 0
+    assert np.all(meta[:, :, 1] == n_end[:, None]) and int(st.status.cpu()[0]) == 0
     replay_us = ms * 1e3 / rounds
+    replay_graph_us = gms * 1e3 / rounds
+    eager_bytes = float(np.mean(rbytes[:rounds]))
+    graph_bytes = float(np.mean(rbytes[2 * rounds:]))
 
     # the same rounds with the commit fused into the next verification
     st = staging.replay_state(cfg, work, dev)
 
-    def fused_round(r):
-        if r == 0:
+    def fused_round(r, first_pass=True):
+        if r == 0 and first_pass:
             rb.replayssm_verify_drafts(cfg, st, p, toks.call(r), y)
         else:
-            rb.replayssm_commit_verify(cfg, st, p, acc[r - 1], T, toks.call(r), y)
+            rb.replayssm_commit_verify(cfg, st, p, acc[(r - 1) % rounds], T, toks.call(r), y)
     fms, fper = timed_launches(fused_round, rounds, torch)
+    fgms = graph_time(lambda r: fused_round(r, first_pass=False), rounds, torch)
     rb.replayssm_commit(cfg, st, acc[rounds - 1], T)
     meta = st.meta.cpu().numpy()
-    assert np.all(meta[:, :, 1] == n[:, None]) and int(st.status.cpu()[0]) == 0
+    assert np.all(meta[:, :, 1] == n_end[:, None]) and int(st.status.cpu()[0]) == 0
     fused_us = fms * 1e3 / rounds
+    fused_graph_us = fgms * 1e3 / rounds
     ring = batch * 128 * cfg.cap * (64 * 2 + 4) + batch * 8 * cfg.cap * 128 * 2
     del st
     torch.cuda.empty_cache()
     out = {
         "T": T,
-        "replay": {"us_per_round": round(replay_us, 2), "gbs": round(np.mean(rbytes) / (replay_us * 1e-6) / 1e9, 1),
-                   "algorithmic_bytes_per_round": int(np.mean(rbytes)),
+        "replay": {"us_per_round": round(replay_graph_us, 2),
+                   "gbs": round(graph_bytes / (replay_graph_us * 1e-6) / 1e9, 1),
+                   "eager_us_per_round": round(replay_us, 2),
+                   "eager_gbs": round(eager_bytes / (replay_us * 1e-6) / 1e9, 1),
+                   "algorithmic_bytes_per_round": int(graph_bytes),
                    "state_bytes": batch * sz.S + ring},
-        "replay_fused_commit": {"us_per_round": round(fused_us, 2),
-                                "gbs": round(np.mean(rbytes) / (fused_us * 1e-6) / 1e9, 1),
+        "replay_fused_commit": {"us_per_round": round(fused_graph_us, 2),
+                                "gbs": round(graph_bytes / (fused_graph_us * 1e-6) / 1e9, 1),
+                                "eager_us_per_round": round(fused_us, 2),
                                 "launches_per_round": 1},
         "mean_accepted": float(work.extra["accepted"].mean()),
     }
@@ -379,16 +419,21 @@ def _verify_point(T, batch=512, L=16, rounds=64, seed=1003, snapshots=True):
             snapshot_round(r)
         slot.zero_()
         cms, cper = timed_launches(snapshot_round, rounds, torch)
-        snap_us = cms * 1e3 / rounds
+        cgms = graph_time(snapshot_round, rounds, torch)
+        snap_eager_us = cms * 1e3 / rounds
+        snap_us = cgms * 1e3 / rounds
         sbytes = traffic.snapshot_verify_bytes(sz, batch, T)
         del states
         torch.cuda.empty_cache()
         out["snapshot_baseline"] = {"us_per_round": round(snap_us, 2),
                                     "gbs": round(sbytes / (snap_us * 1e-6) / 1e9, 1),
+                                    "eager_us_per_round": round(snap_eager_us, 2),
                                     "algorithmic_bytes_per_round": sbytes,
                                     "state_bytes": (T + 1) * batch * sz.S}
-        out["speedup"] = round(snap_us / replay_us, 3)
-        out["speedup_fused"] = round(snap_us / fused_us, 3)
+        out["speedup"] = round(snap_us / replay_graph_us, 3)
+        out["speedup_fused"] = round(snap_us / fused_graph_us, 3)
+        out["timing"] = ("us_per_round: the rounds captured in one HIP graph, one replay timed after a warm "
+                         "replay; eager_*: one Python call per launch")
     return out
 
 
@@ -511,12 +556,14 @@ def bench_dual(args):
         sched, _ = traffic.decode_schedule(n0, L, steps)
         sz = traffic.sizes(128, 64, 128, 8, 2, mode)
         tot = sum(traffic.decode_step_bytes(sz, n, f) for n, f in sched)
-        ms, per = timed_launches(lambda i: rb.replayssm_decode_step(cfg, st, p, toks.call(i % 64), y),
-                                 steps, torch)
+        dstep = lambda i: rb.replayssm_decode_step(cfg, st, p, toks.call(i % 64), y)
+        ms, per = timed_launches(dstep, steps, torch)
+        gms = graph_time(dstep, steps, torch)          # 4096 steps = whole windows: same phase
         per = np.array(per)
         folds = np.array([f.any() for _, f in sched])
-        res[mode or "fp32"] = {"us_per_step": round(ms * 1e3 / steps, 2),
-                               "gbs": round(tot / (ms * 1e-3) / 1e9, 1),
+        res[mode or "fp32"] = {"us_per_step": round(gms * 1e3 / steps, 2),
+                               "gbs": round(tot / (gms * 1e-3) / 1e9, 1),
+                               "eager_us_per_step": round(ms * 1e3 / steps, 2),
                                "nonflush_launch_us": round(float(per[~folds].mean()) * 1e3, 2),
                                "flush_launch_us": round(float(per[folds].mean()) * 1e3, 2)}
         del st
@@ -555,19 +602,24 @@ def summarize_configs(logs):
     md = ["# Bench configurations beyond the headline decode step (one MI355X)", "",
           "Commands (from the repository root):", "", "```"]
     md += [f"python -u bench.py --config {k}" for k in ("verify", "verify_sweep", "sweep", "dual") if k in lines]
-    md += ["```", "", "Times are HIP events around the launches on the launch stream; GB/s are algorithmic "
-           "bytes (mamba_state_replay_amd/traffic.py) over that time.", ""]
+    md += ["```", "", "Per-step and per-round times are one replay of the steps captured in a HIP graph (after a "
+           "warm replay), timed with HIP events on the launch stream; \"eager\" times have one Python call "
+           "per launch and an event pair around each; launch times are those event pairs. GB/s are "
+           "algorithmic bytes (mamba_state_replay_amd/traffic.py) over the time.", ""]
     if "verify" in lines:
         v = lines["verify"]
         md += ["## Speculative verification: batch 512, T = 3, accepted U{0..3}, 64 rounds, L = 16", "",
-               "| | us per round | algorithmic GB/s | bytes per round | state + buffer bytes |",
-               "|---|---|---|---|---|",
-               f"| replay: verify_drafts + commit | {v['replay']['us_per_round']} | {v['replay']['gbs']} | "
+               "| | us per round | eager us per round | algorithmic GB/s | bytes per round | state + buffer bytes |",
+               "|---|---|---|---|---|---|",
+               f"| replay: verify_drafts + commit | {v['replay']['us_per_round']} | "
+               f"{v['replay'].get('eager_us_per_round')} | {v['replay']['gbs']} | "
                f"{v['replay']['algorithmic_bytes_per_round']:,} | {v['replay']['state_bytes']:,} |",
                f"| replay: commit fused into the next verification | {v['replay_fused_commit']['us_per_round']} | "
+               f"{v['replay_fused_commit'].get('eager_us_per_round')} | "
                f"{v['replay_fused_commit']['gbs']} | same | same |",
                f"| conventional with one FP32 snapshot per draft + slot commit | "
-               f"{v['snapshot_baseline']['us_per_round']} | {v['snapshot_baseline']['gbs']} | "
+               f"{v['snapshot_baseline']['us_per_round']} | {v['snapshot_baseline'].get('eager_us_per_round')} | "
+               f"{v['snapshot_baseline']['gbs']} | "
                f"{v['snapshot_baseline']['algorithmic_bytes_per_round']:,} | "
                f"{v['snapshot_baseline']['state_bytes']:,} |", "",
                f"Speed-up of a verification round: {v['speedup']}x (fused commit: {v['speedup_fused']}x).", ""]
@@ -599,11 +651,12 @@ def summarize_configs(logs):
                "streams its state from HBM.", ""]
     if "dual" in lines:
         md += ["## Dual precision: batch 256, L = 16, 4096 decode steps", "",
-               "| checkpoint / read copy | us per step | algorithmic GB/s | non-flush launch us | flush launch us |",
-               "|---|---|---|---|---|"]
+               "| checkpoint / read copy | us per step | eager us per step | algorithmic GB/s | non-flush launch us | "
+               "flush launch us |",
+               "|---|---|---|---|---|---|"]
         for k, m in lines["dual"]["modes"].items():
-            md.append(f"| {k} | {m['us_per_step']} | {m['gbs']} | {m['nonflush_launch_us']} | "
-                      f"{m['flush_launch_us']} |")
+            md.append(f"| {k} | {m['us_per_step']} | {m.get('eager_us_per_step')} | {m['gbs']} | "
+                      f"{m['nonflush_launch_us']} | {m['flush_launch_us']} |")
         md.append("")
     CONFIG_SUMMARY.write_text("\n".join(md) + "\n")
     print(f"wrote {CONFIG_SUMMARY}")
@@ -674,7 +727,7 @@ def ingest_counters(fetch_dir, write_dir, trace_dir):
         md.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
     md += ["", "Template arguments: `<headdim, dstate, threads, input type (unsigned short = bf16 bits), "
-           "read mode (0 = FP32 checkpoint)>`. The replay average mixes non-flush and flush launches "
+           "read mode (0 = FP32 checkpoint), heads per workgroup>`. The replay average mixes non-flush and flush launches "
            "(one in 16 flushes); min is a non-flush launch, max a flush launch.", "",
            "HBM counters (separate runs, one counter each):", "", "```", PROFILE_CMDS["fetch"],
            PROFILE_CMDS["write"], "```", "",
