@@ -300,3 +300,90 @@ def test_dual_4096_steps_bound_and_no_drift():
               + (f", worst error/bound {worst_ratio[m]:.3f}" if m else ""), flush=True)
         if m:
             assert pw[-q:].max() <= 2 * pw[:q].max(), f"{m}: read error grows over the run"
+
+
+COPY_VERIFY_SHAPES = {
+    "64x128": NEMO,                                                    # 4 (e4m3) / 2 (bf16) heads per workgroup
+    "64x64": SHAPES["64x64"],
+    "hpg2": dict(nheads=6, headdim=64, dstate=128, ngroups=3),         # 2 heads per group
+    "hpg1": dict(nheads=5, headdim=64, dstate=128, ngroups=5),         # one head per group
+}
+
+
+@pytest.mark.parametrize("T", [3, 8])
+@pytest.mark.parametrize("tile", list(COPY_VERIFY_SHAPES))
+@pytest.mark.parametrize("copy", ["bf16", "e4m3"])
+def test_copy_verify_rounds(copy, tile, T):
+    """Speculative rounds (verify + commit) with a read copy against the same
+    rounds in FP32-only mode, on the same GPU: the FP32 checkpoint and ring
+    pointers stay bit-identical; outputs of rounds that flush (computed from
+    fresh FP32 registers) match to 1e-6; in the other rounds the difference is
+    the copy's read error alone, d_q (H_copy - H_s) C_q, and must lie within
+    d_q sum_j |C_q[j]| (u |H_s[i,j]| + delta) per element (u and delta as in
+    the dual-precision bound), with H_s the FP32 checkpoint of that round and
+    d_q the decay since the last flush, both taken from the run itself."""
+    dev = device()
+    L, rounds = 8, 14
+    shape = synth.LayerShape(batch=2, window=L, max_drafts=T, **COPY_VERIFY_SHAPES[tile])
+    work = synth.verify_workload(shape, rounds, T, seed=1015)
+    acc = torch.from_numpy(work.extra["accepted"]).to(dev)
+    p = staging.params(work, dev)
+    stream = staging.TokenStream(work.steps, dev, T=T)
+    say(f"copy verify {copy} {tile} T={T}")
+    runs = {}
+    for mode in (None, copy):
+        cfg = staging.config(shape, read_copy=mode)
+        st = staging.replay_state(cfg, work, dev)
+        rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST if mode else 0)
+        ys, hs, scs, metas = [], [], [], []
+        y = torch.empty((shape.batch, T, shape.nheads, shape.headdim), device=dev)
+        for r in range(rounds):
+            rb.replayssm_verify_drafts(cfg, st, p, stream.call(r), y)
+            rb.replayssm_commit(cfg, st, acc[r], T)
+            ys.append(host(y).copy())
+            hs.append(host(st.ckpt).astype(np.float64))
+            metas.append(host(st.meta).copy())
+            if mode == "e4m3":
+                scs.append(host(st.ckpt_scale).astype(np.float64))
+        torch.cuda.synchronize()
+        assert int(host(st.status)[0]) == 0
+        runs[mode] = (ys, hs, scs, metas)
+    y32, h32, _, m32 = runs[None]
+    yc, hc, scc, mc = runs[copy]
+    A = work.A.astype(np.float64)
+    hpg = shape.nheads // shape.ngroups
+    dt = work.steps.dt.astype(np.float64)                  # [rounds * T][batch][nheads]
+    C = work.steps.C.astype(np.float64)                    # [rounds * T][batch][ngroups][dstate]
+    n = np.zeros(shape.batch, np.int64)                    # committed records since the last flush
+    seg = np.zeros((shape.batch, shape.nheads))            # sum of their dt
+    worst = 0.0
+    for r in range(rounds):
+        assert np.array_equal(hc[r], h32[r]), f"round {r}: read copy changed the FP32 checkpoint"
+        assert np.array_equal(mc[r], m32[r])
+        flushed = n >= L
+        n = np.where(flushed, 0, n)
+        seg = np.where(flushed[:, None], 0.0, seg)
+        scale = np.abs(y32[r]).max(axis=(1, 3))            # per (seq, head)
+        for b in range(shape.batch):
+            d_run = seg[b].copy()
+            for q in range(T):
+                t = r * T + q
+                d_run = d_run + dt[t, b]
+                diff = np.abs(yc[r][b, q].astype(np.float64) - y32[r][b, q].astype(np.float64))   # [h][hd]
+                if flushed[b]:
+                    assert float((diff.max(axis=-1) / scale[b]).max()) <= 1e-6, f"round {r} seq {b}: flush outputs"
+                    continue
+                Cq = np.repeat(np.abs(C[t, b]), hpg, axis=0)                                       # [h][ds]
+                Hs = np.abs(hc[r][b])                                                              # [h][hd][ds]
+                read = UNIT[copy] * np.einsum("hij,hj->hi", Hs, Cq)
+                if copy == "e4m3":
+                    read = read + (scc[r][b] * 2.0 ** -10 * 1.001)[:, None] * Cq.sum(-1)[:, None]
+                bound = np.exp(A * d_run)[:, None] * read * 1.001 + 1e-6 * scale[b][:, None]
+                ratio = float((diff / bound).max())
+                worst = max(worst, ratio)
+                assert ratio <= 1.0, f"round {r} seq {b} draft {q}: error / bound {ratio:.3f}"
+        a_r = work.extra["accepted"][r]
+        for b in range(shape.batch):
+            seg[b] += dt[r * T:r * T + a_r[b], b].sum(axis=0)
+        n = n + a_r
+    print(f"[gpu] {copy} {tile} T={T}: worst error/bound {worst:.3f}", flush=True)
