@@ -64,16 +64,17 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
 }
 
 // Four fp32 -> four OCP e4m3fn codes (low byte = a), round to nearest even,
-// saturating: inputs are clamped to +-448 (the largest finite e4m3fn value)
-// and converted by gfx950's fp8 converter; NaN stays NaN.
+// saturating: magnitudes above 448 (the largest finite e4m3fn value) are
+// clamped to +-448 by a compare and select, which leaves a NaN a NaN (a med3
+// clamp would return a bound for it), then converted by gfx950's fp8
+// converter.
+__device__ __forceinline__ float sat448(float v) {
+    return fabsf(v) > 448.0f ? copysignf(448.0f, v) : v;
+}
+
 __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
-    const float lim = 448.0f;
-    a = __builtin_amdgcn_fmed3f(a, -lim, lim);
-    b = __builtin_amdgcn_fmed3f(b, -lim, lim);
-    c = __builtin_amdgcn_fmed3f(c, -lim, lim);
-    d = __builtin_amdgcn_fmed3f(d, -lim, lim);
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
     return (uint32_t)w;
 }
 

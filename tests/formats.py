@@ -52,3 +52,49 @@ def same_code(a, b) -> np.ndarray:
     a = np.asarray(a, np.int64)
     b = np.asarray(b, np.int64)
     return (a == b) | (((a & 0x7F) == 0) & ((b & 0x7F) == 0))
+
+
+def encode_bf16_bits(bits) -> np.ndarray:
+    """bf16 bit patterns of fp32 bit patterns (uint32 array): round to nearest,
+    ties to even, on the 16 dropped bits; values past the largest finite bf16
+    round to infinity; a NaN stays a NaN (quieted, sign and top payload kept)."""
+    b = np.asarray(bits, np.uint32)
+    r = b + np.uint32(0x7FFF)
+    r += (b >> np.uint32(16)) & np.uint32(1)       # wraps only for NaN patterns, replaced below
+    r >>= np.uint32(16)
+    nan = ((b & np.uint32(0x7F800000)) == np.uint32(0x7F800000)) & ((b & np.uint32(0x7FFFFF)) != 0)
+    r[nan] = (b[nan] >> np.uint32(16)) | np.uint32(0x40)
+    return r.astype(np.uint16)
+
+
+def bf16_is_nan(h) -> np.ndarray:
+    h = np.asarray(h, np.uint16).astype(np.uint32)
+    return (((h >> 7) & 0xFF) == 0xFF) & ((h & 0x7F) != 0)
+
+
+def encode_e4m3fn_fast(x) -> np.ndarray:
+    """Same result as encode_e4m3fn for fp32 input, computed on the bits (for
+    large arrays): in the normal range (|x| >= 2^-6) the 23 mantissa bits are
+    rounded to 3 (nearest, ties to even), carrying into the exponent; below it
+    the code is the subnormal count m = |x| 2^9 rounded to nearest even (m = 8
+    is the smallest normal code), i.e. the 24-bit significand shifted right by
+    14 - e; codes saturate at 0x7E (448); NaN gives 0x7F."""
+    x = np.asarray(x, np.float32)
+    b = x.view(np.uint32)
+    mag = b & np.uint32(0x7FFFFFFF)
+    e = (mag >> np.uint32(23)).astype(np.int32) - 127
+    m = mag & np.uint32(0x7FFFFF)
+    m3 = (m + np.uint32(0x7FFFF) + ((m >> np.uint32(20)) & np.uint32(1))) >> np.uint32(20)   # 0..8
+    code = ((e + 7) << 3) + m3.astype(np.int32)                       # m3 = 8 carries into the exponent
+    # subnormal range: significand (with the implicit bit) shifted right by 14 - e, to nearest even
+    sh = np.clip(14 - e, 1, 25).astype(np.uint32)
+    sig = (m | np.uint32(0x800000)) * (e > -127)                     # fp32 subnormals: below 2^-10, code 0
+    q = sig >> sh
+    rem = sig - (q << sh)
+    half = np.uint32(1) << (sh - np.uint32(1))
+    q = q + ((rem > half) | ((rem == half) & ((q & np.uint32(1)) == 1)))
+    code = np.where(e < -6, q.astype(np.int32), code)
+    code = np.minimum(code, 0x7E)
+    code |= ((b >> np.uint32(31)) << np.uint32(7)).astype(np.int32)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
