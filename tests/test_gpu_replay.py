@@ -360,3 +360,58 @@ def test_commit_verify_rejects_bad_accepted_count():
     assert torch.isnan(y[1]).all() and torch.isfinite(y[0]).all() and torch.isfinite(y[2]).all()
     meta = host(st.meta)
     assert np.all(meta[0, :, 1] == 2) and np.all(meta[1, :, 1] == 1) and np.all(meta[2, :, 1] == 1)
+
+
+@pytest.mark.parametrize("read_copy", [None, "e4m3"])
+def test_rollback_equals_decoding_the_accepted_prefix(read_copy):
+    """verify(T drafts) + commit(a) + K decode steps on one state; on a second
+    state, only the accepted drafts are stepped (one draft per launch, the
+    rejected ones rolled back by committing 0 of them), then the same K steps.
+    The K steps' outputs and the final checkpoints agree within 1e-6 of their
+    scale (the two paths fold at different moments, so only rounding differs);
+    accepted counts differ per sequence, 0 .. T."""
+    dev = device()
+    T, L, K = 4, 6, 13
+    batch = T + 1
+    shape = synth.LayerShape(batch=batch, window=L, max_drafts=T, **NEMO)
+    work = synth.decode_workload(shape, T + K, seed=1016, n0=synth.staggered_fill(batch, L))
+    cfg = staging.config(shape, read_copy=read_copy)
+    p = staging.params(work, dev)
+    accepted = np.arange(batch, dtype=np.int32) % (T + 1)                 # 0, 1, .., T
+    drafts = staging.tokens_block(work.steps, 0, T, dev)
+    later = staging.TokenStream(work.steps.slice(T, T + K), dev)
+    say(f"rollback vs accepted-prefix decode, copy={read_copy}")
+
+    def finish(st):
+        y = torch.empty((K, batch, 1, shape.nheads, shape.headdim), device=dev)
+        for t in range(K):
+            rb.replayssm_decode_step(cfg, st, p, later.call(t), y[t])
+        rb.replayssm_flush(cfg, st, p)
+        torch.cuda.synchronize()
+        assert int(host(st.status)[0]) == 0
+        return host(y)[:, :, 0], host(st.ckpt)
+
+    st_a = staging.replay_state(cfg, work, dev)
+    if read_copy:
+        rb.replayssm_flush(cfg, st_a, p, rb.RSSM_FLUSH_FORCE_CAST)
+    ya = torch.empty((batch, T, shape.nheads, shape.headdim), device=dev)
+    rb.replayssm_verify_drafts(cfg, st_a, p, drafts, ya)
+    rb.replayssm_commit(cfg, st_a, torch.from_numpy(accepted).to(dev), T)
+    y_a, h_a = finish(st_a)
+
+    st_b = staging.replay_state(cfg, work, dev)
+    if read_copy:
+        rb.replayssm_flush(cfg, st_b, p, rb.RSSM_FLUSH_FORCE_CAST)
+    one = staging.TokenStream(work.steps.slice(0, T), dev)
+    yb = torch.empty((batch, 1, shape.nheads, shape.headdim), device=dev)
+    for j in range(T):
+        rb.replayssm_verify_drafts(cfg, st_b, p, one.call(j), yb)
+        rb.replayssm_commit(cfg, st_b, torch.from_numpy((j < accepted).astype(np.int32)).to(dev), 1)
+    y_b, h_b = finish(st_b)
+
+    assert np.all(host(st_a.meta)[:, :, 1] == 0) and np.all(host(st_b.meta)[:, :, 1] == 0)
+    scale = np.abs(y_b).max(axis=(0, 3))
+    err = np.abs(y_a - y_b).max(axis=(0, 3)) / scale
+    print(f"[gpu] rollback: max output difference {err.max():.2e} of scale", flush=True)
+    assert err.max() <= 1e-6
+    assert tile_err(h_a, h_b).max() <= 1e-6
