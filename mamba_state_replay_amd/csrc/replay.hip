@@ -39,12 +39,13 @@ namespace rssm {
 namespace {
 
 // LDS plan in floats for a workgroup serving HPW heads of one group.  The x
-// rows keep the input element type (xbytes = 4 for fp32, 2 for bf16; they
-// are widened where they are read) and are padded to XS elements, a row
-// stride of 4 banks mod 32, so that the lanes of a row group, each reading a
-// different record's x in step 5, fall on different banks.  Per-head arrays
-// are indexed [head][...]; B and C rows are the group's, widened to fp32 and
-// shared by the heads.
+// and B rows keep the input element type (xbytes = 4 for fp32, 2 for bf16;
+// they are widened where they are read), which keeps a workgroup's LDS small
+// enough for 8 workgroups per CU at up to 8 drafts; x rows are padded to XS
+// elements, a row stride of 4 banks mod 32, so that the lanes of a row group,
+// each reading a different record's x in step 5, fall on different banks.
+// Per-head arrays are indexed [head][...]; B rows are the group's and shared
+// by the heads; the queries' C rows are widened to fp32.
 struct Lds {
     int X, XS, K, Cq, DT, AA, CO, DQ, WF, RED, total;
 };
@@ -56,7 +57,7 @@ __host__ __device__ inline Lds lds_plan(int HD, int DS, int cap, int T, int HPW,
     int o = 0;
     l.XS = xbytes == 4 ? HD + 4 : HD + 8;           // elements; 16-byte aligned rows
     l.X = o;  o += HPW * cap * l.XS * xbytes / 4;    // x of records then queries, window order, per head
-    l.K = o;  o += cap * DS;         // B of records then queries
+    l.K = o;  o += cap * DS * xbytes / 4;   // B of records then queries (input type)
     l.Cq = o; o += T * DS;           // C of the queries
     l.DT = o; o += HPW * cap;        // dt, window order, per head
     l.AA = o; o += HPW * cap;        // a = dt * A, per head
@@ -244,8 +245,8 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
                     ((size_t)(m.b * m.T + c - m.n) * m.ngroups + m.g) * VS + cv;
             if (m.append_B) j.app = const_cast<uint4*>(ring);
         }
-        j.dst = (m.ldsK + c * DS + cv * EPVIN) * 4;
-        j.wide = true;
+        j.dst = m.ldsK * 4 + (c * DS + cv * EPVIN) * (int)sizeof(InT);
+        j.wide = false;
     } else {
         const int u = v - m.nx - m.nb;
         const int q = u / VS, cv = u - q * VS;
@@ -263,6 +264,18 @@ __device__ __forceinline__ void stage_store(float* lds, const StageJob& jb, cons
         *reinterpret_cast<uint4*>(d) = v;
     else
         widen16<InT>(v, reinterpret_cast<float*>(d));
+}
+
+// B_c[col .. col + 3] as fp32 from the B rows in LDS (input type).
+template <typename InT, int DS>
+__device__ __forceinline__ float4 load_b4(const float* lds, int K, int c, int col) {
+    if constexpr (sizeof(InT) == 4) {
+        return *reinterpret_cast<const float4*>(lds + K + c * DS + col);
+    } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(lds + K) + c * DS + col);
+        return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                           __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+    }
 }
 
 // Step 5 for one head's tile held in registers (vectors OFF ..) with element
@@ -488,7 +501,7 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
             float sc = 0.f;
             if (q < T) {
                 for (int j4 = sub; j4 < DS / 4; j4 += 8) {
-                    const float4 kb = *reinterpret_cast<const float4*>(lds + L.K + c * DS + 4 * j4);
+                    const float4 kb = load_b4<InT, DS>(lds, L.K, c, 4 * j4);
                     const float4 cq = *reinterpret_cast<const float4*>(lds + L.Cq + q * DS + 4 * j4);
                     sc = fmaf(kb.x, cq.x, sc);
                     sc = fmaf(kb.y, cq.y, sc);
@@ -548,7 +561,7 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
 #pragma unroll
                         for (int k = 0; k < G32::VPL; ++k) {
                             const float4 kb =
-                                *reinterpret_cast<const float4*>(lds + L.K + c * DS + (j + G32::W * k) * 4);
+                                load_b4<InT, DS>(lds, L.K, c, (j + G32::W * k) * 4);
 #pragma unroll
                             for (int r = 0; r < G32::NI; ++r) {
                                 v4f& fv = f[r * G32::VPL + k];
