@@ -51,6 +51,7 @@ extern "C" {
 #define RSSM_BF16 1
 #define RSSM_FP8_E4M3 2 /* OCP e4m3fn: max 448, no infinities */
 #define RSSM_NONE 3
+#define RSSM_MXFP4 4    /* OCP MX FP4: E2M1 codes, one E8M0 scale per 32 consecutive dstate elements */
 
 /* Return codes. */
 #define RSSM_OK 0
@@ -76,7 +77,7 @@ typedef struct {
     int32_t window;     /* L: a call that starts with >= L committed records flushes first */
     int32_t max_drafts; /* T_max: largest T passed to replayssm_verify_drafts */
     int32_t in_dtype;   /* RSSM_F32 or RSSM_BF16: tokens x, B, C and the x/B records */
-    int32_t read_copy;  /* RSSM_NONE, RSSM_BF16 or RSSM_FP8_E4M3 */
+    int32_t read_copy;  /* RSSM_NONE, RSSM_BF16, RSSM_FP8_E4M3 or RSSM_MXFP4 (needs dstate % 32 == 0) */
 } rssm_config;
 
 /*
@@ -89,8 +90,13 @@ typedef struct {
  */
 typedef struct {
     float *ckpt;        /* [batch][nheads][headdim][dstate] fp32 checkpoint H_s */
-    void *ckpt_read;    /* same layout in read_copy's type; NULL iff read_copy == RSSM_NONE */
-    float *ckpt_scale;  /* [batch][nheads] fp32 scale of the e4m3 copy; NULL unless e4m3 */
+    void *ckpt_read;    /* same layout in read_copy's type; NULL iff read_copy == RSSM_NONE.
+                           MXFP4: [batch][nheads][headdim][dstate/2] bytes, two E2M1 codes per
+                           byte, the lower column in the low nibble */
+    void *ckpt_scale;   /* e4m3: [batch][nheads] fp32, one scale per tile; MXFP4:
+                           [batch][nheads][headdim][dstate/32] E8M0 bytes, one per block of 32
+                           columns (scale 2^(e-127); e = 255 marks a block holding a NaN);
+                           NULL for the other modes */
     void *buf_x;        /* [batch][nheads][cap][headdim] in_dtype */
     void *buf_B;        /* [batch][ngroups][cap][dstate] in_dtype */
     float *buf_dt;      /* [batch][nheads][cap] fp32 (after softplus) */

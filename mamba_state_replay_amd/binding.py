@@ -17,7 +17,7 @@ import torch
 PKG = Path(__file__).resolve().parent
 LIBRARY = PKG / "libreplayssm.so"
 
-RSSM_F32, RSSM_BF16, RSSM_FP8_E4M3, RSSM_NONE = 0, 1, 2, 3
+RSSM_F32, RSSM_BF16, RSSM_FP8_E4M3, RSSM_NONE, RSSM_MXFP4 = 0, 1, 2, 3, 4
 RSSM_FLUSH_FORCE_CAST = 1
 RSSM_STATUS_META, RSSM_STATUS_ACCEPT, RSSM_STATUS_SLOT = 1, 2, 4
 RSSM_MAX_DRAFTS, RSSM_MAX_WINDOW = 8, 64
@@ -25,8 +25,18 @@ RSSM_MAX_DRAFTS, RSSM_MAX_WINDOW = 8, 64
 NUM_BUFS = 7
 
 _DTYPES = {"f32": RSSM_F32, "bf16": RSSM_BF16, "e4m3": RSSM_FP8_E4M3, None: RSSM_NONE,
-           "none": RSSM_NONE}
-_TORCH = {RSSM_F32: torch.float32, RSSM_BF16: torch.bfloat16, RSSM_FP8_E4M3: torch.uint8}
+           "none": RSSM_NONE, "mxfp4": RSSM_MXFP4}
+_TORCH = {RSSM_F32: torch.float32, RSSM_BF16: torch.bfloat16, RSSM_FP8_E4M3: torch.uint8,
+          RSSM_MXFP4: torch.uint8}
+
+
+def _copy_shapes(rc, b, nh, hd, ds):
+    """(ckpt_read shape, ckpt_scale shape and dtype) of a read-copy mode."""
+    if rc == RSSM_MXFP4:
+        return (b, nh, hd, ds // 2), ((b, nh, hd, ds // 32), torch.uint8)
+    if rc == RSSM_FP8_E4M3:
+        return (b, nh, hd, ds), ((b, nh), torch.float32)
+    return (b, nh, hd, ds), None
 
 
 class rssm_config(ctypes.Structure):
@@ -124,7 +134,7 @@ class Config:
     window: int = 16
     max_drafts: int = 1
     in_dtype: str = "bf16"       # "f32" or "bf16"
-    read_copy: str | None = None  # None, "bf16" or "e4m3"
+    read_copy: str | None = None  # None, "bf16", "e4m3" or "mxfp4"
 
     @property
     def cap(self) -> int:
@@ -178,10 +188,11 @@ class State:
         b, nh, hd, ds, ng, cap = cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.cap
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
         rc = _DTYPES[cfg.read_copy]
+        read_shape, scale = _copy_shapes(rc, b, nh, hd, ds)
         st = cls(
             ckpt=z((b, nh, hd, ds), torch.float32),
-            ckpt_read=None if rc == RSSM_NONE else z((b, nh, hd, ds), _TORCH[rc]),
-            ckpt_scale=z((b, nh), torch.float32) if rc == RSSM_FP8_E4M3 else None,
+            ckpt_read=None if rc == RSSM_NONE else z(read_shape, _TORCH[rc]),
+            ckpt_scale=z(*scale) if scale else None,
             buf_x=z((b, nh, cap, hd), cfg.in_torch),
             buf_B=z((b, ng, cap, ds), cfg.in_torch),
             buf_dt=z((b, nh, cap), torch.float32),
@@ -203,11 +214,12 @@ class State:
             if self.ckpt_read is not None or self.ckpt_scale is not None:
                 raise ValueError("read_copy is None but ckpt_read/ckpt_scale are set")
         else:
-            _expect("ckpt_read", self.ckpt_read, (b, nh, hd, ds), _TORCH[rc], dev)
-            if rc == RSSM_FP8_E4M3:
-                _expect("ckpt_scale", self.ckpt_scale, (b, nh), torch.float32, dev)
+            read_shape, scale = _copy_shapes(rc, b, nh, hd, ds)
+            _expect("ckpt_read", self.ckpt_read, read_shape, _TORCH[rc], dev)
+            if scale:
+                _expect("ckpt_scale", self.ckpt_scale, scale[0], scale[1], dev)
             elif self.ckpt_scale is not None:
-                raise ValueError("ckpt_scale is only used by the e4m3 read copy")
+                raise ValueError("ckpt_scale is only used by the e4m3 and mxfp4 read copies")
         _expect("buf_x", self.buf_x, (b, nh, cap, hd), cfg.in_torch, dev)
         _expect("buf_B", self.buf_B, (b, ng, cap, ds), cfg.in_torch, dev)
         _expect("buf_dt", self.buf_dt, (b, nh, cap), torch.float32, dev)

@@ -46,8 +46,12 @@ int check_config(const rssm_config* c, bool need_window) {
             return fail(RSSM_ERR_SHAPE, "window %d outside 1..%d", c->window, RSSM_MAX_WINDOW);
         if (c->max_drafts < 1 || c->max_drafts > RSSM_MAX_DRAFTS)
             return fail(RSSM_ERR_SHAPE, "max_drafts %d outside 1..%d", c->max_drafts, RSSM_MAX_DRAFTS);
-        if (c->read_copy != RSSM_NONE && c->read_copy != RSSM_BF16 && c->read_copy != RSSM_FP8_E4M3)
-            return fail(RSSM_ERR_DTYPE, "read_copy must be RSSM_NONE, RSSM_BF16 or RSSM_FP8_E4M3");
+        if (c->read_copy != RSSM_NONE && c->read_copy != RSSM_BF16 && c->read_copy != RSSM_FP8_E4M3 &&
+            c->read_copy != RSSM_MXFP4)
+            return fail(RSSM_ERR_DTYPE, "read_copy must be RSSM_NONE, RSSM_BF16, RSSM_FP8_E4M3 or RSSM_MXFP4");
+        if (c->read_copy == RSSM_MXFP4 && c->dstate % 32 != 0)
+            return fail(RSSM_ERR_SHAPE, "RSSM_MXFP4 needs dstate %% 32 == 0 (blocks of 32 columns), got %d",
+                        c->dstate);
         const int cap = c->window + 2 * c->max_drafts - 1;
         if (rssm::replay_lds_bytes(c->headdim, c->dstate, cap, c->max_drafts, c->in_dtype == RSSM_BF16 ? 2 : 4) >
             kMaxLds)
@@ -57,8 +61,9 @@ int check_config(const rssm_config* c, bool need_window) {
 }
 
 int read_mode(const rssm_config* c) {
-    return c->read_copy == RSSM_BF16 ? rssm::READ_BF16
+    return c->read_copy == RSSM_BF16       ? rssm::READ_BF16
            : c->read_copy == RSSM_FP8_E4M3 ? rssm::READ_E4M3
+           : c->read_copy == RSSM_MXFP4    ? rssm::READ_MXFP4
                                             : rssm::READ_F32;
 }
 
@@ -68,8 +73,8 @@ int check_state(const rssm_config* c, const rssm_state* s) {
         return fail(RSSM_ERR_NULL, "state: ckpt, buf_x, buf_B, buf_dt and meta are required");
     if ((c->read_copy == RSSM_NONE) != (s->ckpt_read == nullptr))
         return fail(RSSM_ERR_NULL, "state: ckpt_read must be set iff read_copy != RSSM_NONE");
-    if ((c->read_copy == RSSM_FP8_E4M3) != (s->ckpt_scale != nullptr))
-        return fail(RSSM_ERR_NULL, "state: ckpt_scale must be set iff read_copy == RSSM_FP8_E4M3");
+    if ((c->read_copy == RSSM_FP8_E4M3 || c->read_copy == RSSM_MXFP4) != (s->ckpt_scale != nullptr))
+        return fail(RSSM_ERR_NULL, "state: ckpt_scale must be set iff read_copy is RSSM_FP8_E4M3 or RSSM_MXFP4");
     if (!aligned(s->ckpt, 16) || !aligned(s->buf_x, 16) || !aligned(s->buf_B, 16) ||
         (s->ckpt_read && !aligned(s->ckpt_read, 16)))
         return fail(RSSM_ERR_SHAPE, "state: ckpt, ckpt_read, buf_x and buf_B must be 16-byte aligned");
@@ -96,7 +101,7 @@ rssm::ReplayArgs replay_args(const rssm_config* c, const rssm_state* s, const rs
     std::memset(&a, 0, sizeof a);
     a.ckpt = s->ckpt;
     a.ckpt_read = s->ckpt_read;
-    a.ckpt_scale = s->ckpt_scale;
+    a.ckpt_scale = static_cast<float*>(s->ckpt_scale);
     a.buf_x = s->buf_x;
     a.buf_B = s->buf_B;
     a.buf_dt = s->buf_dt;
@@ -160,10 +165,13 @@ int replayssm_sizes(const rssm_config* c, size_t bytes[RSSM_NUM_BUFS]) {
     const size_t cap = (size_t)(c->window + 2 * c->max_drafts - 1);
     const size_t in_bytes = c->in_dtype == RSSM_BF16 ? 2 : 4;
     bytes[RSSM_BUF_CKPT] = tiles * tile * 4;
-    bytes[RSSM_BUF_CKPT_READ] = c->read_copy == RSSM_BF16 ? tiles * tile * 2
+    bytes[RSSM_BUF_CKPT_READ] = c->read_copy == RSSM_BF16       ? tiles * tile * 2
                                 : c->read_copy == RSSM_FP8_E4M3 ? tiles * tile
+                                : c->read_copy == RSSM_MXFP4    ? tiles * tile / 2
                                                                 : 0;
-    bytes[RSSM_BUF_CKPT_SCALE] = c->read_copy == RSSM_FP8_E4M3 ? tiles * 4 : 0;
+    bytes[RSSM_BUF_CKPT_SCALE] = c->read_copy == RSSM_FP8_E4M3 ? tiles * 4
+                                 : c->read_copy == RSSM_MXFP4  ? tiles * tile / 32
+                                                               : 0;
     bytes[RSSM_BUF_X] = tiles * cap * c->headdim * in_bytes;
     bytes[RSSM_BUF_B] = (size_t)c->batch * c->ngroups * cap * c->dstate * in_bytes;
     bytes[RSSM_BUF_DT] = tiles * cap * 4;

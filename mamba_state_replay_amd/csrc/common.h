@@ -22,11 +22,12 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 //     row (t / W) * NI + s / VPL,  vector column t % W + W * (s % VPL),
 // so each load instruction (fixed s) of a wave reads whole 128-byte lines,
 // and a row's dot product needs a reduction over only W lanes.  EB is the
-// element size of the tile's storage type (4 fp32, 2 bf16, 1 e4m3).
+// element size of the tile's storage type (4 fp32, 2 bf16, 1 e4m3, 0 for
+// 4-bit codes, 32 to a vector).
 // ---------------------------------------------------------------------------
 template <int HD, int DS, int NT, int EB>
 struct TileGeo {
-    static constexpr int EPV = 16 / EB;                  // elements per 16-byte vector
+    static constexpr int EPV = EB == 0 ? 32 : 16 / EB;   // elements per 16-byte vector (EB 0: fp4)
     static constexpr int VPR = DS / EPV;                 // vectors per row
     static constexpr int W = VPR < 8 ? VPR : 8;          // lanes per row
     static constexpr int VPL = VPR / W;                  // vectors per lane per row
@@ -89,6 +90,21 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float out[4]) {
     out[3] = hi[1];
 }
 
+// MX block scale (E8M0 byte e: 2^(e - 127), e = 255 NaN) as fp32.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+    return e == 255u ? __builtin_nanf("") : e == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);
+}
+
+// E8M0 scale of an MXFP4 block with largest magnitude amax (fp32 bits): the
+// block's largest exponent minus 2 (the largest E2M1 exponent), clamped to
+// 1 .. 254 so that the scale is a normal fp32 number; 255 if the block holds
+// a NaN.
+__device__ __forceinline__ uint32_t mx_block_scale(float amax, bool has_nan) {
+    const int biased = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+    const int e = biased - 2 < 1 ? 1 : biased - 2 > 254 ? 254 : biased - 2;
+    return has_nan ? 255u : (uint32_t)e;
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane exchange within 32-lane halves: DPP quad permutes for xor 1 and
 // xor 2, ds_swizzle (bit-mask mode) for xor 4, 8 and 16.
@@ -125,6 +141,17 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (W >= 16) v += xor_shfl<8>(v);
     if constexpr (W >= 32) v += xor_shfl<16>(v);
     if constexpr (W >= 64) v += xor_shfl<32>(v);
+    return v;
+}
+
+// Unsigned maximum over groups of W consecutive lanes (W <= 32).
+template <int W>
+__device__ __forceinline__ uint32_t group_umax(uint32_t v) {
+    if constexpr (W >= 2) v = max(v, __float_as_uint(xor_shfl<1>(__uint_as_float(v))));
+    if constexpr (W >= 4) v = max(v, __float_as_uint(xor_shfl<2>(__uint_as_float(v))));
+    if constexpr (W >= 8) v = max(v, __float_as_uint(xor_shfl<4>(__uint_as_float(v))));
+    if constexpr (W >= 16) v = max(v, __float_as_uint(xor_shfl<8>(__uint_as_float(v))));
+    if constexpr (W >= 32) v = max(v, __float_as_uint(xor_shfl<16>(__uint_as_float(v))));
     return v;
 }
 

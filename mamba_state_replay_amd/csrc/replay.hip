@@ -331,12 +331,84 @@ __device__ __forceinline__ void copy_queries(const TileRegs<HD, DS, NT>& t, cons
     }
 }
 
+// The read-copy tiles of HPW heads (consecutive, tile_bytes apart) into the
+// register array, head hh in vectors hh * NV ..
+template <int HD, int DS, int NT, int EB, int HPW, int HH = 0>
+__device__ __forceinline__ void load_heads(TileRegs<HD, DS, NT>& t, const uint8_t* cp, size_t tile_bytes, int tid) {
+    if constexpr (HH < HPW) {
+        t.template load<EB, HH * TileGeo<HD, DS, NT, EB>::NV>(cp + HH * tile_bytes, tid);
+        load_heads<HD, DS, NT, EB, HPW, HH + 1>(t, cp, tile_bytes, tid);
+    }
+}
+
+// Step 5 for HPW heads' MXFP4 tiles (one 32-column block per thread and
+// head, in vector hh of the register array).  The heads share the group's C,
+// so each chunk of 4 columns of C_q is read once and multiplied into every
+// head's block (codes decoded by gfx950's fp4 converter, two per
+// instruction); each head's sum is scaled by its block's E8M0 scale and d_q,
+// gets its record terms, and is reduced over the W lanes of its row.
+template <int HD, int DS, int NT, typename InT, int HPW>
+__device__ __forceinline__ void mx_queries(const TileRegs<HD, DS, NT>& t, const uint32_t* mxs, const float* lds,
+                                           const Lds& L, const Window& w, float* y0, size_t y_qstride, int tid) {
+    using G = TileGeo<HD, DS, NT, 0>;
+    static_assert(G::NV == 1 && G::NI == 1, "one block per thread and head");
+    const int j = tid % G::W;
+    const int row = G::row0(tid);
+    for (int q = 0; q < w.T; ++q) {
+        float v[HPW];
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) v[hh] = 0.f;
+        const float* cq = lds + L.Cq + q * DS + j * 32;
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) {
+            asm volatile("" ::: "memory");   // one chunk of C live at a time
+            const float4 c = *reinterpret_cast<const float4*>(cq + 4 * ch);
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) {
+                uint32_t word = __builtin_bit_cast(v4u, t.raw[hh])[ch / 2];
+                asm volatile("" : "+v"(word));                 // decode inside the query loop
+                typedef float f2 __attribute__((ext_vector_type(2)));
+                f2 lo, hi;
+                if (ch % 2 == 0) {
+                    lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
+                    hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
+                } else {
+                    lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
+                    hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+                }
+                float acc = v[hh];
+                acc = fmaf(lo[0], c.x, acc);
+                acc = fmaf(lo[1], c.y, acc);
+                acc = fmaf(hi[0], c.z, acc);
+                acc = fmaf(hi[1], c.w, acc);
+                v[hh] = acc;
+            }
+        }
+        const int m = w.n + q;
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+            const HeadView hv = head_view<InT>(L, hh, w.cap, w.T);
+            float u = v[hh] * (e8m0_to_f32((mxs[hh / 4] >> (8 * (hh % 4))) & 0xFFu) * lds[hv.DQ + q]);
+            for (int cc = w.first + j; cc <= m; cc += G::W) {
+                float xv[1];
+                load_x<InT, 1>(lds, hv.X, cc * L.XS + row, xv);
+                u = fmaf(lds[hv.CO + q * w.cap + cc], xv[0], u);
+            }
+            u = group_sum<G::W>(u);
+            if (j == 0 && y0) y0[hh * HD + q * y_qstride + row] = u;
+        }
+    }
+}
+
+// 8 waves per SIMD (64 VGPRs); the MXFP4 kernels, which hold up to 8 heads
+// per workgroup, keep enough bytes in flight with 4 and get 128 VGPRs.
 template <int HD, int DS, int NT, typename InT, int RM, int HPW>
-__global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
+__global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 4 : 8) void replay_kernel(const ReplayArgs a) {
     extern __shared__ float lds[];
     using G32 = TileGeo<HD, DS, NT, 4>;
-    constexpr int EBC = RM == READ_BF16 ? 2 : 1;     // element size of the read copy
+    constexpr int EBC = RM == READ_MXFP4 ? 0 : RM == READ_BF16 ? 2 : 1;  // read-copy element bytes (0: fp4)
     using GC = TileGeo<HD, DS, NT, EBC>;
+    constexpr size_t CB = EBC ? (size_t)HD * DS * EBC : (size_t)HD * DS / 2;   // read-copy tile bytes
     constexpr int EPVIN = InTraits<InT>::EPV;
     constexpr int VR = HD / EPVIN;                   // 16-byte vectors per x row
     constexpr int VS = DS / EPVIN;                   // 16-byte vectors per B/C row
@@ -437,12 +509,20 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
     TileRegs<HD, DS, NT> treg;
     if (RM == READ_F32 || fold) {
         treg.template load<4>(a.ckpt + tile0 * HD * DS, tid);
-    } else {
-        const uint8_t* cp = reinterpret_cast<const uint8_t*>(a.ckpt_read) + tile0 * HD * DS * EBC;
-        treg.template load<EBC, 0>(cp, tid);
-        if constexpr (HPW > 1) treg.template load<EBC, GC::NV>(cp + 1 * HD * DS * EBC, tid);
-        if constexpr (HPW > 2) treg.template load<EBC, 2 * GC::NV>(cp + 2 * HD * DS * EBC, tid);
-        if constexpr (HPW > 3) treg.template load<EBC, 3 * GC::NV>(cp + 3 * HD * DS * EBC, tid);
+    } else if constexpr (RM != READ_F32) {
+        const uint8_t* cp = reinterpret_cast<const uint8_t*>(a.ckpt_read) + tile0 * CB;
+        load_heads<HD, DS, NT, EBC, HPW>(treg, cp, CB, tid);
+    }
+    // MXFP4: the E8M0 scale of each head's block this thread holds (one byte
+    // per head, packed four to a word).
+    uint32_t mxs[(HPW + 3) / 4] = {};
+    if constexpr (RM == READ_MXFP4) {
+        if (!fold) {
+            const uint8_t* sp = reinterpret_cast<const uint8_t*>(a.ckpt_scale) + tile0 * (HD * DS / 32);
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh)
+                mxs[hh / 4] |= (uint32_t)sp[hh * (HD * DS / 32) + GC::vec(tid, 0)] << (8 * (hh % 4));
+        }
     }
 
 #pragma unroll
@@ -590,6 +670,36 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(f[s][e]));
                 }
+                if constexpr (RM == READ_MXFP4) {
+                    // Block k of row r (32 columns) is vector k of that row on the 8
+                    // lanes of the row group: its largest magnitude and NaN flag are
+                    // reduced over those lanes, then each lane encodes its 4 values
+                    // (v / X, nearest even, saturating) into 16 bits of the block.
+                    uint16_t* out = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(a.ckpt_read) + tile * CB);
+                    uint8_t* sc_out = reinterpret_cast<uint8_t*>(a.ckpt_scale) + tile * (HD * DS / 32);
+                    const int jr = tid % G32::W;
+                    // largest |v| of each block as fp32 bits: a NaN (bits above those of
+                    // infinity) wins the unsigned maximum, so one reduction also finds NaNs
+                    uint32_t mb[G32::NV];
+#pragma unroll
+                    for (int s = 0; s < G32::NV; ++s) {
+                        const v4u u = __builtin_bit_cast(v4u, f[s]) & 0x7FFFFFFFu;
+                        mb[s] = max(max(u.x, u.y), max(u.z, u.w));
+                    }
+#pragma unroll
+                    for (int s = 0; s < G32::NV; ++s) mb[s] = group_umax<G32::W>(mb[s]);
+#pragma unroll
+                    for (int s = 0; s < G32::NV; ++s) {
+                        const uint32_t e = mx_block_scale(__uint_as_float(mb[s]), mb[s] > 0x7F800000u);
+                        const float X = e == 255u ? 1.0f : e8m0_to_f32(e);
+                        const v4f fv = f[s];
+                        uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, fv.x, fv.y, X, 0);
+                        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fv.z, fv.w, X, 1);
+                        const int vi = G32::vec(tid, s);           // fp32 vector = 4 columns = 2 bytes
+                        out[vi] = (uint16_t)w;
+                        if (jr == 0) sc_out[vi / 8] = (uint8_t)e;  // 8 fp32 vectors per block
+                    }
+                }
             }
             if constexpr (RM == READ_E4M3) {
                 amax = group_max<64>(amax);
@@ -617,6 +727,8 @@ __global__ __launch_bounds__(NT, 8) void replay_kernel(const ReplayArgs a) {
         if (tid < G32::ACTIVE)
             queries_and_outputs<HD, DS, NT, InT, 4>(treg, lds, L, head_view<InT>(L, 0, cap, T), win, 1.0f, y0,
                                                     y_qstride, tid);
+    } else if constexpr (RM == READ_MXFP4) {
+        mx_queries<HD, DS, NT, InT, HPW>(treg, mxs, lds, L, win, y0, y_qstride, tid);
     } else {
         float scales[HPW];
 #pragma unroll
@@ -649,7 +761,7 @@ int heads_per_wg(int hd, int ds, int nheads, int ngroups, int cap, int T, int re
     // (the launchers fall back to fewer heads where a shape's copy tile does not
     // leave room in the register array for this many)
     if (read_mode == READ_F32 || mode == MODE_FLUSH || hd == 16) return 1;
-    const int want = read_mode == READ_E4M3 ? 4 : 2;
+    const int want = read_mode == READ_MXFP4 ? 8 : read_mode == READ_E4M3 ? 4 : 2;
     const int hpg = nheads / ngroups;
     for (int hpw = want; hpw > 1; hpw /= 2)
         if (hpg % hpw == 0 && (size_t)lds_plan(hd, ds, cap, T, hpw, xbytes).total * sizeof(float) <= 65536 &&
@@ -671,15 +783,17 @@ hipError_t launch_one(const ReplayArgs& a, hipStream_t stream) {
 // compiled only where a copy tile leaves room for them (not 16 x 16).
 template <int HD, int DS, int RM, int HPW>
 constexpr bool multi_head_fits() {
-    using GC = TileGeo<HD, DS, ShapeNT<HD, DS>::NT, RM == READ_BF16 ? 2 : 1>;
+    using GC = TileGeo<HD, DS, ShapeNT<HD, DS>::NT, RM == READ_BF16 ? 2 : RM == READ_E4M3 ? 1 : 0>;
     return HD != 16 && HPW * GC::NV <= TileGeo<HD, DS, ShapeNT<HD, DS>::NT, 4>::NV &&
            GC::ACTIVE == ShapeNT<HD, DS>::NT;
 }
 
 template <int HD, int DS, typename InT, int RM>
 hipError_t launch_copy(const ReplayArgs& a, int hpw, hipStream_t stream) {
-    if constexpr (RM == READ_E4M3 && multi_head_fits<HD, DS, RM, 4>())
-        if (hpw == 4) return launch_one<HD, DS, InT, RM, 4>(a, stream);
+    if constexpr (RM == READ_MXFP4 && multi_head_fits<HD, DS, RM, 8>())
+        if (hpw == 8) return launch_one<HD, DS, InT, RM, 8>(a, stream);
+    if constexpr (RM != READ_BF16 && multi_head_fits<HD, DS, RM, 4>())
+        if (hpw >= 4) return launch_one<HD, DS, InT, RM, 4>(a, stream);
     if constexpr (multi_head_fits<HD, DS, RM, 2>())
         if (hpw >= 2) return launch_one<HD, DS, InT, RM, 2>(a, stream);
     return launch_one<HD, DS, InT, RM, 1>(a, stream);
@@ -691,6 +805,9 @@ hipError_t launch_type(const ReplayArgs& a, int read_mode, int hpw, hipStream_t 
         case READ_F32: return launch_one<HD, DS, InT, READ_F32, 1>(a, stream);
         case READ_BF16: return launch_copy<HD, DS, InT, READ_BF16>(a, hpw, stream);
         case READ_E4M3: return launch_copy<HD, DS, InT, READ_E4M3>(a, hpw, stream);
+        case READ_MXFP4:
+            if constexpr (DS % 32 == 0) return launch_copy<HD, DS, InT, READ_MXFP4>(a, hpw, stream);
+            return hipErrorInvalidValue;
     }
     return hipErrorInvalidValue;
 }

@@ -3,8 +3,9 @@
 Counts what each call must move at minimum, per sequence:
 
   S    = nheads*headdim*dstate*4          FP32 checkpoint (or state) bytes
-  S_r  = bytes of the tile a non-flush call reads: S, S/2 (bf16 copy) or
-         S/4 + nheads*4 (e4m3 copy + per-tile scales)
+  S_r  = bytes of the tile a non-flush call reads: S, S/2 (bf16 copy),
+         S/4 + nheads*4 (e4m3 copy + per-tile scales) or S/8 + S/128
+         (MXFP4 codes + one E8M0 byte per 32 elements)
   S_c  = read-copy bytes a flush writes (0 without a copy)
   R    = nheads*headdim*e + ngroups*dstate*e + nheads*4   one record (x, B, dt)
   TOK  = R + ngroups*dstate*e                             one token's inputs (+ C)
@@ -46,6 +47,8 @@ def sizes(nheads, headdim, dstate, ngroups, in_bytes=2, read_copy=None) -> Sizes
         S_r = S_c = S // 2
     elif read_copy == "e4m3":
         S_r = S_c = S // 4 + nheads * 4
+    elif read_copy == "mxfp4":
+        S_r = S_c = S // 8 + S // 128
     else:
         raise ValueError(read_copy)
     R = nheads * headdim * in_bytes + ngroups * dstate * in_bytes + nheads * 4

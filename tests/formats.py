@@ -98,3 +98,71 @@ def encode_e4m3fn_fast(x) -> np.ndarray:
     code |= ((b >> np.uint32(31)) << np.uint32(7)).astype(np.int32)
     code = np.where(np.isnan(x), 0x7F, code)
     return code.astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (OCP Microscaling formats, version 1.0): blocks of 32 elements share
+# one E8M0 scale X = 2^(e - 127) (e = 255 is NaN); the elements are FP4 E2M1
+# (1 sign, 2 exponent bits with bias 1, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3,
+# 4, 6; no infinity, no NaN).  The scale of a block is X = 2^(floor(log2 amax)
+# - 2), 2 being the largest exponent of E2M1, so amax / X lies in [4, 8); the
+# elements are v / X rounded to the nearest E2M1 value (ties to even code),
+# saturating at +-6.  Here: X is clamped to 2^-126 .. 2^127 (e = 1 .. 254, so
+# the scale is always a normal fp32 number; a block of zeros or of values below
+# 2^-124 gets e = 1), and a block holding a NaN gets e = 255.
+# ---------------------------------------------------------------------------
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, np.int64)
+    v = E2M1[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def e2m1_encode(a) -> np.ndarray:
+    """Nearest E2M1 code of a (float64, already divided by the scale), ties to
+    the even code, saturating at +-6."""
+    a = np.asarray(a, np.float64)
+    m = np.minimum(np.abs(a), 6.0)
+    hi = np.clip(np.searchsorted(E2M1, m), 0, 7)
+    lo = np.clip(hi - 1, 0, 7)
+    dlo, dhi = m - E2M1[lo], E2M1[hi] - m
+    code = np.where((dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0)), hi, lo)
+    return (code | np.where(np.signbit(a), 8, 0)).astype(np.uint8)
+
+
+def e8m0_value(e) -> np.ndarray:
+    e = np.asarray(e, np.int64)
+    return np.where(e == 255, np.nan, np.exp2(e.astype(np.float64) - 127.0))
+
+
+def mxfp4_encode(x) -> tuple[np.ndarray, np.ndarray]:
+    """fp32 array [..., 32 k] -> (E8M0 scales [..., k] uint8, E2M1 codes
+    [..., 32 k] uint8, one code per byte)."""
+    x = np.asarray(x, np.float32)
+    blk = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.abs(blk).max(axis=-1).astype(np.float32)          # NaN if the block holds one
+    biased = ((amax.view(np.uint32) >> 23) & 0xFF).astype(np.int64)
+    e = np.clip(biased - 2, 1, 254)
+    e = np.where(np.isnan(amax), 255, e)
+    X = e8m0_value(e)
+    codes = e2m1_encode(blk.astype(np.float64) / np.where(np.isnan(X), 1.0, X)[..., None])
+    return e.astype(np.uint8), codes.reshape(x.shape)
+
+
+def mxfp4_decode(scales, codes) -> np.ndarray:
+    c = np.asarray(codes)
+    v = e2m1_decode(c).reshape(c.shape[:-1] + (c.shape[-1] // 32, 32))
+    return (v * e8m0_value(scales)[..., None]).reshape(c.shape)
+
+
+def e2m1_encode_fast(x) -> np.ndarray:
+    """Same as e2m1_encode for fp32 input (no NaN), by counting the midpoints
+    passed: a tie at a midpoint goes to the even code (the thresholds at
+    0.75, 1.75 and 3.5 are inclusive, those at 0.25, 1.25, 2.5 and 5 are not)."""
+    x = np.asarray(x, np.float32)
+    a = np.abs(x)
+    code = ((a > 0.25).astype(np.uint8) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5)
+            + (a > 5.0)).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << 3)

@@ -77,3 +77,63 @@ def test_fast_e4m3_encoder_matches_table_encoder():
                           g.choice([-1.0, 1.0], 500_000)]).astype(np.float32)
     x = np.concatenate([near, rnd, np.array([np.nan, -np.nan, 0.0, -0.0, 448.0, 464.0, 1e30], np.float32)])
     assert np.array_equal(formats.encode_e4m3fn_fast(x), formats.encode_e4m3fn(x))
+
+
+def test_e2m1_codes_and_rounding():
+    """Every E2M1 code decodes to its value and encodes back to itself; the
+    midpoints between neighbours go to the even code; magnitudes above 6
+    saturate; the sign is kept on zero."""
+    codes = np.arange(16)
+    vals = formats.e2m1_decode(codes)
+    assert np.array_equal(np.abs(vals[:8]), [0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    back = formats.e2m1_encode(vals)
+    assert np.array_equal(back, codes.astype(np.uint8))
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    assert np.array_equal(formats.e2m1_encode(mids), [0, 2, 2, 4, 4, 6, 6])
+    assert np.array_equal(formats.e2m1_encode(-mids), np.array([0, 2, 2, 4, 4, 6, 6]) | 8)
+    assert np.array_equal(formats.e2m1_encode([6.5, 8.0, 1e30, -7.0]), [7, 7, 7, 15])
+    near = np.nextafter(mids, 0.0), np.nextafter(mids, 10.0)
+    assert np.array_equal(formats.e2m1_encode(near[0]), [0, 1, 2, 3, 4, 5, 6])
+    assert np.array_equal(formats.e2m1_encode(near[1]), [1, 2, 3, 4, 5, 6, 7])
+
+
+def test_mxfp4_block_scale_and_error():
+    """The block scale puts amax / X in [4, 8); every element's decode error is
+    at most |v| / 4 + X / 4 (the bound the read-copy tests use); a block of
+    zeros gets the smallest normal scale 2^-126 and zero codes; a NaN makes
+    the scale NaN."""
+    g = np.random.default_rng(11)
+    x = (np.exp(g.uniform(-20, 20, (500, 1))) * g.standard_normal((500, 128))).astype(np.float32)
+    e, c = formats.mxfp4_encode(x)
+    X = formats.e8m0_value(e)
+    amax = np.abs(x.reshape(500, 4, 32)).max(axis=-1)
+    big = amax >= 2.0 ** -124                 # below it the scale is clamped at 2^-126
+    assert np.all((amax / X >= 4) & (amax / X < 8) | ~big)
+    dec = formats.mxfp4_decode(e, c)
+    err = np.abs(dec - x.astype(np.float64))
+    Xe = np.repeat(X, 32, axis=-1)
+    assert np.all(err <= np.abs(x) / 4 + Xe / 4)
+    z = np.zeros((1, 32), np.float32)
+    ez, cz = formats.mxfp4_encode(z)
+    assert ez[0, 0] == 1 and np.all(cz == 0)
+    n = np.ones((1, 32), np.float32)
+    n[0, 7] = np.nan
+    en, _ = formats.mxfp4_encode(n)
+    assert en[0, 0] == 255 and np.all(np.isnan(formats.mxfp4_decode(en, _)))
+    # a worked block: amax 5 -> floor(log2 5) = 2 -> X = 2^0; codes are the E2M1 encodings of v
+    w = np.array([[5.0, -0.3, 0.25, 0.75, 2.6, 3.4, 1.0, -6.0] + [0.0] * 24], np.float32)
+    ew, cw = formats.mxfp4_encode(w)
+    assert ew[0, 0] == 127
+    assert list(cw[0, :8]) == [6, 9, 0, 2, 5, 5, 2, 15]
+
+
+def test_fast_e2m1_encoder_matches_definition():
+    """The midpoint-counting E2M1 encoder used for exhaustive checks equals the
+    nearest-value encoder on every fp32 within 2 ulp of each value, midpoint
+    and the saturation point, and on random values."""
+    g = np.random.default_rng(12)
+    pts = np.concatenate([formats.E2M1, (formats.E2M1[1:] + formats.E2M1[:-1]) / 2, [7.0, 8.0]]).astype(np.float32)
+    near = (pts.view(np.int32)[:, None] + np.arange(-2, 3, dtype=np.int32)[None, :]).ravel().view(np.float32)
+    x = np.concatenate([near, -near, g.uniform(-9, 9, 1_000_000).astype(np.float32)])
+    x = x[np.isfinite(x)]                     # steps below +0 land on NaN patterns
+    assert np.array_equal(formats.e2m1_encode_fast(x), formats.e2m1_encode(x))

@@ -28,7 +28,21 @@ SHAPES = {
     "64x128": NEMO,
     "128x128": dict(nheads=8, headdim=128, dstate=128, ngroups=1),
 }
-UNIT = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -4}   # relative rounding bound of one read
+UNIT = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -4, "mxfp4": 2.0 ** -2}   # relative rounding bound of one read
+
+
+def read_delta(copy, scale, hd, ds):
+    """Absolute part of the per-element read bound, broadcastable to
+    [batch][nheads][hd][ds]: 0 for bf16; half the e4m3 subnormal step, s 2^-10,
+    for e4m3 (one scale s per tile); a quarter of the block scale X, half the
+    E2M1 spacing below 1, for MXFP4 (scales [batch][nheads][hd][ds / 32] E8M0).
+    A margin of 1e-3 covers fp32 rounding."""
+    if copy == "bf16":
+        return 0.0
+    scale = np.asarray(scale)
+    if copy == "e4m3":
+        return (scale.astype(np.float64) * 2.0 ** -10 * 1.001)[..., None, None]
+    return np.repeat(formats.e8m0_value(scale) / 4 * 1.001, 32, axis=-1)
 
 
 def test_e4m3_decode_every_code():
@@ -96,7 +110,53 @@ def test_cast_only_encoding(copy):
         assert np.all(formats.same_code(got, formats.encode_e4m3fn(h)))
 
 
-@pytest.mark.parametrize("copy", ["bf16", "e4m3"])
+def unpack_fp4(packed):
+    """[..., ds / 2] bytes -> [..., ds] E2M1 codes (low nibble = even column)."""
+    b = np.asarray(packed, np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def same_fp4(got_scales, got_codes, want_scales, want_codes):
+    """Equal scales, and equal codes where the block is not NaN (+0 and -0 one value)."""
+    if not np.array_equal(got_scales, want_scales):
+        return False
+    live = np.repeat(want_scales != 255, 32, axis=-1)
+    same = (got_codes == want_codes) | (((got_codes & 7) == 0) & ((want_codes & 7) == 0))
+    return bool(np.all(same | ~live))
+
+
+def test_mxfp4_cast_only_encoding():
+    """flush(FORCE_CAST) with nothing to fold writes the MXFP4 encoding of the
+    checkpoint: blocks over 40 orders of magnitude, every E2M1 value and
+    midpoint times the block scale, zero blocks, a block with a NaN, and fp32
+    subnormals; codes and E8M0 scales against the host encoder."""
+    dev = device()
+    g = np.random.default_rng(22)
+    cfg = rb.Config(2, 8, 64, 128, 8, window=16, max_drafts=1, in_dtype="bf16", read_copy="mxfp4")
+    st = rb.State.allocate(cfg, dev)
+    h = (np.exp(g.uniform(-45, 45, (2, 8, 64, 4, 1))) * g.standard_normal((2, 8, 64, 4, 32))).astype(np.float32)
+    grid = np.concatenate([formats.E2M1, (formats.E2M1[1:] + formats.E2M1[:-1]) / 2])          # 15 values
+    h[0, 0, :, 0, :15] = grid * 2.0 ** g.integers(-20, 20, (64, 1))
+    h[0, 0, :, 0, 15] = 6.0 * 2.0 ** g.integers(-20, 20, 64)
+    h[0, 1, :, 1, :] = 0.0
+    h[0, 2, 5, 2, 7] = np.nan
+    h[1, 3, :, 3, :] = np.float32(1e-41) * g.standard_normal((64, 32)).astype(np.float32)
+    h = h.reshape(2, 8, 64, 128)
+    st.ckpt.copy_(torch.from_numpy(h))
+    p = rb.Params(torch.full((8,), -1.0, device=dev), torch.zeros(8, device=dev))
+    say("cast-only flush mxfp4")
+    rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST)
+    torch.cuda.synchronize()
+    assert torch.equal(st.ckpt.cpu().view(torch.int32), torch.from_numpy(h).view(torch.int32)), \
+        "cast-only flush changed the FP32 checkpoint"
+    ws, wc = formats.mxfp4_encode(h)
+    assert same_fp4(host(st.ckpt_scale), unpack_fp4(host(st.ckpt_read)), ws, wc)
+
+
+@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4"])
 def test_flush_encoding_and_scale(copy):
     """A real flush (5 committed records): the copy is the encoding of the new
     FP32 checkpoint, with scale absmax/448 per tile for e4m3."""
@@ -114,6 +174,9 @@ def test_flush_encoding_and_scale(copy):
     if copy == "bf16":
         ref = torch.from_numpy(H).to(torch.bfloat16)
         assert torch.equal(st.ckpt_read.cpu().view(torch.int16), ref.view(torch.int16))
+    elif copy == "mxfp4":
+        ws, wc = formats.mxfp4_encode(H.astype(np.float32))
+        assert same_fp4(host(st.ckpt_scale), unpack_fp4(host(st.ckpt_read)), ws, wc)
     else:
         amax = np.abs(H).max(axis=(-1, -2)).astype(np.float32)
         sc = (amax / np.float32(448.0)).astype(np.float32)
@@ -135,24 +198,30 @@ def _run_dual(cfg, work, dev, steps, poison_before=()):
         if t in poison_before:
             if cfg.read_copy == "bf16":
                 st.ckpt_read.view(torch.int16).fill_(0x7FC0)
-            else:
+            elif cfg.read_copy == "e4m3":
                 st.ckpt_read.fill_(0x7F)
+            else:
+                st.ckpt_read.fill_(0xFF)          # E2M1 -6 in both nibbles, block scales NaN
+                st.ckpt_scale.fill_(255)
         rb.replayssm_decode_step(cfg, st, p, stream.call(t), y[t])
-        if cfg.read_copy == "e4m3":
+        if cfg.read_copy in ("e4m3", "mxfp4"):
             scales[t] = st.ckpt_scale.clone()
     torch.cuda.synchronize()
     return host(y)[:, :, 0], st, {k: host(v) for k, v in scales.items()}
 
 
 @pytest.mark.parametrize("tile", ["64x128", "16x16", "64x64", "128x128"])
-@pytest.mark.parametrize("copy", ["bf16", "e4m3"])
+@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4"])
 def test_dual_precision_error_bound(copy, tile):
     """Outputs of non-flush steps read the copy; per element
     |y - y_ref| <= d_q sum_j |C_q[j]| (u |H_s[i,j]| + delta) + 1e-4 * (head output scale),
-    u = 2^-8 (bf16) or 2^-4 (e4m3), delta = 0 (bf16) or s 2^-10 (e4m3, half the
-    subnormal step scaled), H_s the oracle state at the last flush, d_q the decay
-    since then.  Flushing steps read FP32 registers and meet the FP32 tolerance.
-    The FP32 checkpoint must be bit-identical to an FP32-only run."""
+    u = 2^-8 (bf16), 2^-4 (e4m3) or 2^-2 (MXFP4), delta = 0 (bf16), s 2^-10
+    (e4m3, half the subnormal step scaled) or X / 4 (MXFP4, X the block's scale),
+    H_s the oracle state at the last flush, d_q the decay since then.  Flushing
+    steps read FP32 registers and meet the FP32 tolerance.  The FP32 checkpoint
+    must be bit-identical to an FP32-only run."""
+    if copy == "mxfp4" and SHAPES[tile]["dstate"] % 32:
+        pytest.skip("MXFP4 blocks are 32 columns of dstate")
     dev = device()
     L, steps = 16, 72
     shape = synth.LayerShape(batch=4, window=L, **SHAPES[tile])
@@ -181,11 +250,8 @@ def test_dual_precision_error_bound(copy, tile):
         for t in win:
             dec = np.exp(work.A[None, :] * work.steps.dt[tf:t + 1].astype(np.float64).sum(0))  # [b][h]
             Cg = np.repeat(work.steps.C[t].astype(np.float64), shape.nheads // shape.ngroups, axis=1)  # [b][h][ds]
-            if copy == "bf16":
-                delta = 0.0
-            else:
-                sc = scales[max(x for x in [0] + sorted(flush_steps) if x <= t)]
-                delta = (sc.astype(np.float64) * 2.0 ** -10)[:, :, None, None] * 1.001
+            sc = scales[max(x for x in [0] + sorted(flush_steps) if x <= t)] if copy != "bf16" else None
+            delta = read_delta(copy, sc, shape.headdim, shape.dstate)
             term = UNIT[copy] * np.abs(Hs) + delta                      # [b][h][hd][ds]
             bound = dec[:, :, None] * np.einsum("bhij,bhj->bhi", term, np.abs(Cg)) + 1e-4 * scale[:, :, None]
             err = np.abs(yc[t] - yref[t])
@@ -200,7 +266,7 @@ def test_dual_precision_error_bound(copy, tile):
     assert_rows_close(yc[fl], yref[fl], what=f"{copy} flushing-step outputs")
 
 
-@pytest.mark.parametrize("copy", ["bf16", "e4m3"])
+@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4"])
 def test_poisoned_copy_never_enters_recurrence(copy):
     """NaN-fill the copy right before a flushing step: that step's outputs (read
     from FP32 registers) and the checkpoint it writes are unchanged, and later
@@ -217,6 +283,8 @@ def test_poisoned_copy_never_enters_recurrence(copy):
     assert np.array_equal(y_clean, y_pois)
     assert torch.equal(st_clean.ckpt, st_pois.ckpt)
     assert torch.equal(st_clean.ckpt_read, st_pois.ckpt_read)
+    if copy != "bf16":
+        assert torch.equal(st_clean.ckpt_scale, st_pois.ckpt_scale)
 
 
 def test_dual_4096_steps_bound_and_no_drift():
@@ -235,12 +303,12 @@ def test_dual_4096_steps_bound_and_no_drift():
     L, steps = 16, 4096
     shape = synth.LayerShape(batch=8, window=L, **NEMO)
     work = synth.decode_workload(shape, steps, seed=1005, n0=L)
-    modes = (None, "bf16", "e4m3")
+    modes = (None, "bf16", "e4m3", "mxfp4")
     cfgs = {m: staging.config(shape, read_copy=m) for m in modes}
     sts = {m: staging.replay_state(cfgs[m], work, dev) for m in modes}
     p = staging.params(work, dev)
     stream = staging.TokenStream(work.steps, dev)
-    say("dual precision, 4096 steps, 8 sequences, three modes")
+    say("dual precision, 4096 steps, 8 sequences, four modes")
     for m in modes[1:]:
         rb.replayssm_flush(cfgs[m], sts[m], p, rb.RSSM_FLUSH_FORCE_CAST)
     rb.replayssm_flush(cfgs[None], sts[None], p)
@@ -257,7 +325,7 @@ def test_dual_4096_steps_bound_and_no_drift():
             for m in modes:
                 rb.replayssm_decode_step(cfgs[m], sts[m], p, stream.call(t), y[m][t - t0])
             if t == t0:
-                scales = host(sts["e4m3"].ckpt_scale).astype(np.float64)
+                scales = {m: host(sts[m].ckpt_scale) for m in ("e4m3", "mxfp4")}
         torch.cuda.synchronize()
         tok = work.steps
         Hs = H
@@ -282,7 +350,10 @@ def test_dual_4096_steps_bound_and_no_drift():
             per_window[m].append(float((err[copy_rows].max(axis=(0, 3)) / scale).max()))
             read = UNIT[m] * HC                                       # u sum_j |H_s[i,j]| |C_q[j]|
             if m == "e4m3":
-                read = read + (scales * 2.0 ** -10 * 1.001)[None, :, :, None] * Csum[..., None]
+                read = read + (scales[m] * 2.0 ** -10 * 1.001)[None, :, :, None] * Csum[..., None]
+            elif m == "mxfp4":                                         # sum_j |C_q[j]| X(i, j) / 4
+                Xq = torch.from_numpy(np.ascontiguousarray(read_delta(m, scales[m], 64, 128)))
+                read = read + torch.einsum("bhij,tbhj->tbhi", Xq, Cabs).numpy()
             bound = dec[..., None] * read + TOL * scale[None, :, :, None]
             ratio = float((err[copy_rows] / bound[copy_rows]).max())
             worst_ratio[m] = max(worst_ratio[m], ratio)
@@ -312,7 +383,7 @@ COPY_VERIFY_SHAPES = {
 
 @pytest.mark.parametrize("T", [3, 8])
 @pytest.mark.parametrize("tile", list(COPY_VERIFY_SHAPES))
-@pytest.mark.parametrize("copy", ["bf16", "e4m3"])
+@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4"])
 def test_copy_verify_rounds(copy, tile, T):
     """Speculative rounds (verify + commit) with a read copy against the same
     rounds in FP32-only mode, on the same GPU: the FP32 checkpoint and ring
@@ -343,8 +414,8 @@ def test_copy_verify_rounds(copy, tile, T):
             ys.append(host(y).copy())
             hs.append(host(st.ckpt).astype(np.float64))
             metas.append(host(st.meta).copy())
-            if mode == "e4m3":
-                scs.append(host(st.ckpt_scale).astype(np.float64))
+            if mode in ("e4m3", "mxfp4"):
+                scs.append(host(st.ckpt_scale).copy())
         torch.cuda.synchronize()
         assert int(host(st.status)[0]) == 0
         runs[mode] = (ys, hs, scs, metas)
@@ -378,6 +449,8 @@ def test_copy_verify_rounds(copy, tile, T):
                 read = UNIT[copy] * np.einsum("hij,hj->hi", Hs, Cq)
                 if copy == "e4m3":
                     read = read + (scc[r][b] * 2.0 ** -10 * 1.001)[:, None] * Cq.sum(-1)[:, None]
+                elif copy == "mxfp4":
+                    read = read + np.einsum("hij,hj->hi", read_delta(copy, scc[r][b], 0, 0), Cq)
                 bound = np.exp(A * d_run)[:, None] * read * 1.001 + 1e-6 * scale[b][:, None]
                 ratio = float((diff / bound).max())
                 worst = max(worst, ratio)
