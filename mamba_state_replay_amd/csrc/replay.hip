@@ -342,69 +342,75 @@ __device__ __forceinline__ void load_heads(TileRegs<HD, DS, NT>& t, const uint8_
 }
 
 // Step 5 for HPW heads' MXFP4 tiles (one 32-column block per thread and
-// head, in vector hh of the register array).  The heads share the group's C,
-// so each chunk of 4 columns of C_q is read once and multiplied into every
-// head's block (codes decoded by gfx950's fp4 converter, two per
-// instruction); each head's sum is scaled by its block's E8M0 scale and d_q,
-// gets its record terms, and is reduced over the W lanes of its row.
+// head, in vector hh of the register array), head after head so that only one
+// head's sums and addresses are live.  gfx950's fp4 converter decodes two
+// codes per instruction and applies the block's E8M0 scale (its operand must
+// be a power of two: the converter takes only the exponent of that operand,
+// so d_q is applied to the sum afterwards).  A block whose scale byte is 255
+// (NaN) gives its row a NaN.  The decode is repeated per query rather than
+// kept decoded in registers across queries.  Each sum then gets its record
+// terms and is reduced over the W lanes of its row.
 template <int HD, int DS, int NT, typename InT, int HPW>
 __device__ __forceinline__ void mx_queries(const TileRegs<HD, DS, NT>& t, const uint32_t* mxs, const float* lds,
                                            const Lds& L, const Window& w, float* y0, size_t y_qstride, int tid) {
     using G = TileGeo<HD, DS, NT, 0>;
     static_assert(G::NV == 1 && G::NI == 1, "one block per thread and head");
+    typedef float f2 __attribute__((ext_vector_type(2)));
     const int j = tid % G::W;
     const int row = G::row0(tid);
-    for (int q = 0; q < w.T; ++q) {
-        float v[HPW];
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) v[hh] = 0.f;
-        const float* cq = lds + L.Cq + q * DS + j * 32;
+    for (int hh = 0; hh < HPW; ++hh) {
+        const HeadView hv = head_view<InT>(L, hh, w.cap, w.T);
+        const uint32_t e = (mxs[hh / 4] >> (8 * (hh % 4))) & 0xFFu;
+        const v4u words = __builtin_bit_cast(v4u, t.raw[hh]);
+        const float bs = e == 255u ? 1.0f : e8m0_to_f32(e);
+        for (int q = 0; q < w.T; ++q) {
+            float sq = bs;
+            asm volatile("" : "+v"(sq));     // decode per query, not hoisted into registers
+            const float* cq = lds + L.Cq + q * DS + j * 32;
+            float acc = 0.f;
 #pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {
-            asm volatile("" ::: "memory");   // one chunk of C live at a time
-            const float4 c = *reinterpret_cast<const float4*>(cq + 4 * ch);
-#pragma unroll
-            for (int hh = 0; hh < HPW; ++hh) {
-                uint32_t word = __builtin_bit_cast(v4u, t.raw[hh])[ch / 2];
-                asm volatile("" : "+v"(word));                 // decode inside the query loop
-                typedef float f2 __attribute__((ext_vector_type(2)));
+            for (int ch = 0; ch < 8; ++ch) {
+                const float4 c = *reinterpret_cast<const float4*>(cq + 4 * ch);
                 f2 lo, hi;
                 if (ch % 2 == 0) {
-                    lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
-                    hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
+                    lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 0);
+                    hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 1);
                 } else {
-                    lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
-                    hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+                    lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 2);
+                    hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 3);
                 }
-                float acc = v[hh];
                 acc = fmaf(lo[0], c.x, acc);
                 acc = fmaf(lo[1], c.y, acc);
                 acc = fmaf(hi[0], c.z, acc);
                 acc = fmaf(hi[1], c.w, acc);
-                v[hh] = acc;
+                if (ch % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // two chunks of C live at a time
             }
-        }
-        const int m = w.n + q;
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-            const HeadView hv = head_view<InT>(L, hh, w.cap, w.T);
-            float u = v[hh] * (e8m0_to_f32((mxs[hh / 4] >> (8 * (hh % 4))) & 0xFFu) * lds[hv.DQ + q]);
+            acc = e == 255u ? __builtin_nanf("") : acc * lds[hv.DQ + q];
+            const int m = w.n + q;
             for (int cc = w.first + j; cc <= m; cc += G::W) {
                 float xv[1];
                 load_x<InT, 1>(lds, hv.X, cc * L.XS + row, xv);
-                u = fmaf(lds[hv.CO + q * w.cap + cc], xv[0], u);
+                acc = fmaf(lds[hv.CO + q * w.cap + cc], xv[0], acc);
             }
-            u = group_sum<G::W>(u);
-            if (j == 0 && y0) y0[hh * HD + q * y_qstride + row] = u;
+            acc = group_sum<G::W>(acc);
+            if (j == 0 && y0) y0[hh * HD + q * y_qstride + row] = acc;
         }
     }
 }
 
-// 8 waves per SIMD (64 VGPRs); the MXFP4 kernels, which hold up to 8 heads
-// per workgroup, keep enough bytes in flight with 4 and get 128 VGPRs.
-template <int HD, int DS, int NT, typename InT, int RM, int HPW>
-__global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 4 : 8) void replay_kernel(const ReplayArgs a) {
-    extern __shared__ float lds[];
+// Where a workgroup's call stands once its ring pointers are checked.
+struct WgCtx {
+    size_t tile0;           // tile of the first head
+    int b, h0, g, hpg;      // sequence, first head, group, heads per group
+    int start, n_stored, n; // ring start, records stored, records counted (with a fused commit)
+    bool flush_call;
+};
+
+// Steps 1-6 of a decode / verify / flush call for one workgroup; FOLD: the call
+// folds its window into the FP32 checkpoint (and rewrites the read copy).
+template <int HD, int DS, int NT, typename InT, int RM, int HPW, bool FOLD>
+__device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ctx, float* lds) {
     using G32 = TileGeo<HD, DS, NT, 4>;
     constexpr int EBC = RM == READ_MXFP4 ? 0 : RM == READ_BF16 ? 2 : 1;  // read-copy element bytes (0: fp4)
     using GC = TileGeo<HD, DS, NT, EBC>;
@@ -417,52 +423,16 @@ __global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 4 : 8) void replay_kernel(co
     static_assert(HPW == 1 || (RM != READ_F32 && HPW * GC::NV <= G32::NV && GC::ACTIVE == NT),
                   "several heads per workgroup only for read copies that fill the register array");
     static_assert(HPW * NW <= kRedSlots, "reduction slots");
-
-    const int chunks = a.nheads / HPW;
-    const int nwg = a.batch * chunks;
-    const int wg = xcd_remap(blockIdx.x, nwg);
-    const int b = wg / chunks;
-    const int h0 = (wg - b * chunks) * HPW;          // first head of this workgroup
-    const int hpg = a.nheads / a.ngroups;
-    const int g = h0 / hpg;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int cap = a.cap;
     const int T = a.T;
-    const size_t tile0 = (size_t)b * a.nheads + h0;
-
-    // Every head keeps its own copy of the ring pointer; those of a workgroup's
-    // heads must agree.
-    const int start = a.meta[2 * tile0];
-    const int n_stored = a.meta[2 * tile0 + 1];
-    bool same = true;
-#pragma unroll
-    for (int hh = 1; hh < HPW; ++hh)
-        same = same && a.meta[2 * (tile0 + hh)] == start && a.meta[2 * (tile0 + hh) + 1] == n_stored;
-    // Fused commit of the previous verification: len += accepted_prev[b].
-    int acc_prev = 0;
-    bool acc_ok = true;
-    if (a.accepted_prev) {
-        acc_prev = a.accepted_prev[b];
-        acc_ok = acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap;
-    }
-    const int n = n_stored + acc_prev;
-
-    if (!(same && acc_ok && start >= 0 && start < cap && n >= 0 && n + T <= cap)) {
-        if (tid == 0 && h0 == 0 && a.status) atomicOr(a.status, (int)(acc_ok ? kStatusMeta : kStatusAccept));
-        for (int o = tid; o < HPW * T * HD; o += NT) {
-            const int hh = o / (T * HD), r = o - hh * T * HD;
-            const int q = r / HD, i = r - q * HD;
-            a.y[((size_t)(b * T + q) * a.nheads + h0 + hh) * HD + i] = __builtin_nanf("");
-        }
-        return;
-    }
-
-    const bool flush_call = a.mode == MODE_FLUSH;
-    const bool cast_only = flush_call && n == 0 && (a.flags & kFlushForceCast) && RM != READ_F32;
-    const bool fold = flush_call ? (n > 0 || cast_only) : (n >= a.L);
-    if (flush_call && !fold) return;
+    const size_t tile0 = ctx.tile0;
+    const int b = ctx.b, h0 = ctx.h0, g = ctx.g, hpg = ctx.hpg;
+    const int start = ctx.start, n_stored = ctx.n_stored, n = ctx.n;
+    const bool flush_call = ctx.flush_call;
+    constexpr bool fold = FOLD;
     const int first = fold ? n : 0;  // first window index of the outputs
     const bool append = !flush_call;
     const int rows = n + T;          // window rows staged in LDS
@@ -688,6 +658,11 @@ __global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 4 : 8) void replay_kernel(co
                     }
 #pragma unroll
                     for (int s = 0; s < G32::NV; ++s) mb[s] = group_umax<G32::W>(mb[s]);
+                    // vector s of a thread is block s % VPL of its row s / VPL; the
+                    // scale bytes of a row's DS / 32 blocks are adjacent, and lane 0 of
+                    // the row group stores them in one write per row
+                    static_assert(G32::VPL * 32 == DS && (G32::VPL == 2 || G32::VPL == 4), "blocks per row");
+                    uint32_t packed[G32::NI] = {};
 #pragma unroll
                     for (int s = 0; s < G32::NV; ++s) {
                         const uint32_t e = mx_block_scale(__uint_as_float(mb[s]), mb[s] > 0x7F800000u);
@@ -695,9 +670,18 @@ __global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 4 : 8) void replay_kernel(co
                         const v4f fv = f[s];
                         uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, fv.x, fv.y, X, 0);
                         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fv.z, fv.w, X, 1);
-                        const int vi = G32::vec(tid, s);           // fp32 vector = 4 columns = 2 bytes
-                        out[vi] = (uint16_t)w;
-                        if (jr == 0) sc_out[vi / 8] = (uint8_t)e;  // 8 fp32 vectors per block
+                        out[G32::vec(tid, s)] = (uint16_t)w;       // fp32 vector = 4 columns = 2 bytes
+                        packed[s / G32::VPL] |= e << (8 * (s % G32::VPL));
+                    }
+                    if (jr == 0) {
+#pragma unroll
+                        for (int r = 0; r < G32::NI; ++r) {
+                            uint8_t* dst = sc_out + G32::vec(tid, r * G32::VPL) / 8;   // 8 fp32 vectors per block
+                            if constexpr (G32::VPL == 4)
+                                *reinterpret_cast<uint32_t*>(dst) = packed[r];
+                            else
+                                *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed[r];
+                        }
                     }
                 }
             }
@@ -745,6 +729,65 @@ __global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 4 : 8) void replay_kernel(co
     }
 }
 
+// 8 waves per SIMD (64 VGPRs).  The MXFP4 kernels get 5 (96 VGPRs): their
+// query loop decodes two fp4 codes per instruction into fp32 registers, and
+// at 64 VGPRs it spills.
+template <int HD, int DS, int NT, typename InT, int RM, int HPW>
+__global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 5 : 8) void replay_kernel(const ReplayArgs a) {
+    extern __shared__ float lds[];
+
+    const int chunks = a.nheads / HPW;
+    const int nwg = a.batch * chunks;
+    const int wg = xcd_remap(blockIdx.x, nwg);
+    const int b = wg / chunks;
+    const int h0 = (wg - b * chunks) * HPW;          // first head of this workgroup
+    const int hpg = a.nheads / a.ngroups;
+    const int g = h0 / hpg;
+    const int tid = threadIdx.x;
+    const int cap = a.cap;
+    const int T = a.T;
+    const size_t tile0 = (size_t)b * a.nheads + h0;
+
+    // Every head keeps its own copy of the ring pointer; those of a workgroup's
+    // heads must agree.
+    const int start = a.meta[2 * tile0];
+    const int n_stored = a.meta[2 * tile0 + 1];
+    bool same = true;
+#pragma unroll
+    for (int hh = 1; hh < HPW; ++hh)
+        same = same && a.meta[2 * (tile0 + hh)] == start && a.meta[2 * (tile0 + hh) + 1] == n_stored;
+    // Fused commit of the previous verification: len += accepted_prev[b].
+    int acc_prev = 0;
+    bool acc_ok = true;
+    if (a.accepted_prev) {
+        acc_prev = a.accepted_prev[b];
+        acc_ok = acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap;
+    }
+    const int n = n_stored + acc_prev;
+
+    if (!(same && acc_ok && start >= 0 && start < cap && n >= 0 && n + T <= cap)) {
+        if (tid == 0 && h0 == 0 && a.status) atomicOr(a.status, (int)(acc_ok ? kStatusMeta : kStatusAccept));
+        for (int o = tid; o < HPW * T * HD; o += NT) {
+            const int hh = o / (T * HD), r = o - hh * T * HD;
+            const int q = r / HD, i = r - q * HD;
+            a.y[((size_t)(b * T + q) * a.nheads + h0 + hh) * HD + i] = __builtin_nanf("");
+        }
+        return;
+    }
+
+    const bool flush_call = a.mode == MODE_FLUSH;
+    const bool cast_only = flush_call && n == 0 && (a.flags & kFlushForceCast) && RM != READ_F32;
+    const bool fold = flush_call ? (n > 0 || cast_only) : (n >= a.L);
+    if (flush_call && !fold) return;
+    // One body per case, so that the registers of the FP32 tile a flush holds
+    // are not kept live across the read-copy path.
+    const WgCtx ctx{tile0, b, h0, g, hpg, start, n_stored, n, flush_call};
+    if (fold)
+        replay_body<HD, DS, NT, InT, RM, HPW, true>(a, ctx, lds);
+    else
+        replay_body<HD, DS, NT, InT, RM, HPW, false>(a, ctx, lds);
+}
+
 int threads_for(int hd, int ds) {
     if (hd == 16 && ds == 16) return ShapeNT<16, 16>::NT;
     if (hd == 64 && ds == 64) return ShapeNT<64, 64>::NT;
@@ -761,7 +804,7 @@ int heads_per_wg(int hd, int ds, int nheads, int ngroups, int cap, int T, int re
     // (the launchers fall back to fewer heads where a shape's copy tile does not
     // leave room in the register array for this many)
     if (read_mode == READ_F32 || mode == MODE_FLUSH || hd == 16) return 1;
-    const int want = read_mode == READ_MXFP4 ? 8 : read_mode == READ_E4M3 ? 4 : 2;
+    const int want = read_mode == READ_BF16 ? 2 : 4;
     const int hpg = nheads / ngroups;
     for (int hpw = want; hpw > 1; hpw /= 2)
         if (hpg % hpw == 0 && (size_t)lds_plan(hd, ds, cap, T, hpw, xbytes).total * sizeof(float) <= 65536 &&
@@ -790,8 +833,6 @@ constexpr bool multi_head_fits() {
 
 template <int HD, int DS, typename InT, int RM>
 hipError_t launch_copy(const ReplayArgs& a, int hpw, hipStream_t stream) {
-    if constexpr (RM == READ_MXFP4 && multi_head_fits<HD, DS, RM, 8>())
-        if (hpw == 8) return launch_one<HD, DS, InT, RM, 8>(a, stream);
     if constexpr (RM != READ_BF16 && multi_head_fits<HD, DS, RM, 4>())
         if (hpw >= 4) return launch_one<HD, DS, InT, RM, 4>(a, stream);
     if constexpr (multi_head_fits<HD, DS, RM, 2>())
