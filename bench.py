@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--window", type=int, default=16)
-    ap.add_argument("--read-copy", choices=["none", "bf16", "e4m3", "mxfp4"], default="none")
+    ap.add_argument("--read-copy", choices=["none", "bf16", "e4m3", "mxfp4", "mxfp8"], default="none")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-conventional", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
@@ -535,8 +535,8 @@ def bench_sweep(args):
 
 def bench_dual(args):
     """Dual precision: FP32 checkpoint with no copy, a bf16 copy, an e4m3 copy
-    (one scale per head) or an MXFP4 copy (E2M1 codes, one E8M0 scale per 32
-    columns).  Throughput: batch 256, L = 16, 4096 decode steps (token inputs cycle
+    (one scale per head), an MXFP4 copy (E2M1 codes) or an MXFP8 copy (e4m3
+    codes), the MX copies with one E8M0 scale per 32 columns.  Throughput: batch 256, L = 16, 4096 decode steps (token inputs cycle
     through 64 seeded steps).  The accuracy of the same modes over 4096 steps is
     a GPU test (tests/test_gpu_dual.py), not part of this timing."""
     torch, dev = _device()
@@ -546,7 +546,7 @@ def bench_dual(args):
     res = {}
     shape = synth.LayerShape(batch=256, nheads=128, headdim=64, dstate=128, ngroups=8, window=L)
     work = synth.decode_workload(shape, 64, seed=1004, n0=L)
-    for mode in (None, "bf16", "e4m3", "mxfp4"):
+    for mode in (None, "bf16", "e4m3", "mxfp4", "mxfp8"):
         cfg = staging.config(shape, read_copy=mode)
         st = staging.replay_state(cfg, work, dev)
         p = staging.params(work, dev)

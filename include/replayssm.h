@@ -52,6 +52,8 @@ extern "C" {
 #define RSSM_FP8_E4M3 2 /* OCP e4m3fn: max 448, no infinities */
 #define RSSM_NONE 3
 #define RSSM_MXFP4 4    /* OCP MX FP4: E2M1 codes, one E8M0 scale per 32 consecutive dstate elements */
+#define RSSM_MXFP8 5    /* MX FP8: e4m3fn codes, one E8M0 scale per 32 consecutive dstate elements,
+                           chosen so that no element saturates (smallest X with max |v| / X <= 448) */
 
 /* Return codes. */
 #define RSSM_OK 0
@@ -77,7 +79,8 @@ typedef struct {
     int32_t window;     /* L: a call that starts with >= L committed records flushes first */
     int32_t max_drafts; /* T_max: largest T passed to replayssm_verify_drafts */
     int32_t in_dtype;   /* RSSM_F32 or RSSM_BF16: tokens x, B, C and the x/B records */
-    int32_t read_copy;  /* RSSM_NONE, RSSM_BF16, RSSM_FP8_E4M3 or RSSM_MXFP4 (needs dstate % 32 == 0) */
+    int32_t read_copy;  /* RSSM_NONE, RSSM_BF16, RSSM_FP8_E4M3, RSSM_MXFP4 or RSSM_MXFP8 (the MX modes
+                           need dstate % 32 == 0) */
 } rssm_config;
 
 /*
@@ -92,8 +95,9 @@ typedef struct {
     float *ckpt;        /* [batch][nheads][headdim][dstate] fp32 checkpoint H_s */
     void *ckpt_read;    /* same layout in read_copy's type; NULL iff read_copy == RSSM_NONE.
                            MXFP4: [batch][nheads][headdim][dstate/2] bytes, two E2M1 codes per
-                           byte, the lower column in the low nibble */
-    void *ckpt_scale;   /* e4m3: [batch][nheads] fp32, one scale per tile; MXFP4:
+                           byte, the lower column in the low nibble; MXFP8: one e4m3 byte per
+                           element */
+    void *ckpt_scale;   /* e4m3: [batch][nheads] fp32, one scale per tile; MXFP4 and MXFP8:
                            [batch][nheads][headdim][dstate/32] E8M0 bytes, one per block of 32
                            columns (scale 2^(e-127); e = 255 marks a block holding a NaN);
                            NULL for the other modes */

@@ -17,7 +17,7 @@ import torch
 PKG = Path(__file__).resolve().parent
 LIBRARY = PKG / "libreplayssm.so"
 
-RSSM_F32, RSSM_BF16, RSSM_FP8_E4M3, RSSM_NONE, RSSM_MXFP4 = 0, 1, 2, 3, 4
+RSSM_F32, RSSM_BF16, RSSM_FP8_E4M3, RSSM_NONE, RSSM_MXFP4, RSSM_MXFP8 = 0, 1, 2, 3, 4, 5
 RSSM_FLUSH_FORCE_CAST = 1
 RSSM_STATUS_META, RSSM_STATUS_ACCEPT, RSSM_STATUS_SLOT = 1, 2, 4
 RSSM_MAX_DRAFTS, RSSM_MAX_WINDOW = 8, 64
@@ -25,15 +25,17 @@ RSSM_MAX_DRAFTS, RSSM_MAX_WINDOW = 8, 64
 NUM_BUFS = 7
 
 _DTYPES = {"f32": RSSM_F32, "bf16": RSSM_BF16, "e4m3": RSSM_FP8_E4M3, None: RSSM_NONE,
-           "none": RSSM_NONE, "mxfp4": RSSM_MXFP4}
+           "none": RSSM_NONE, "mxfp4": RSSM_MXFP4, "mxfp8": RSSM_MXFP8}
 _TORCH = {RSSM_F32: torch.float32, RSSM_BF16: torch.bfloat16, RSSM_FP8_E4M3: torch.uint8,
-          RSSM_MXFP4: torch.uint8}
+          RSSM_MXFP4: torch.uint8, RSSM_MXFP8: torch.uint8}
 
 
 def _copy_shapes(rc, b, nh, hd, ds):
     """(ckpt_read shape, ckpt_scale shape and dtype) of a read-copy mode."""
     if rc == RSSM_MXFP4:
         return (b, nh, hd, ds // 2), ((b, nh, hd, ds // 32), torch.uint8)
+    if rc == RSSM_MXFP8:
+        return (b, nh, hd, ds), ((b, nh, hd, ds // 32), torch.uint8)
     if rc == RSSM_FP8_E4M3:
         return (b, nh, hd, ds), ((b, nh), torch.float32)
     return (b, nh, hd, ds), None
@@ -134,7 +136,7 @@ class Config:
     window: int = 16
     max_drafts: int = 1
     in_dtype: str = "bf16"       # "f32" or "bf16"
-    read_copy: str | None = None  # None, "bf16", "e4m3" or "mxfp4"
+    read_copy: str | None = None  # None, "bf16", "e4m3", "mxfp4" or "mxfp8"
 
     @property
     def cap(self) -> int:
@@ -219,7 +221,7 @@ class State:
             if scale:
                 _expect("ckpt_scale", self.ckpt_scale, scale[0], scale[1], dev)
             elif self.ckpt_scale is not None:
-                raise ValueError("ckpt_scale is only used by the e4m3 and mxfp4 read copies")
+                raise ValueError("ckpt_scale is only used by the e4m3, mxfp4 and mxfp8 read copies")
         _expect("buf_x", self.buf_x, (b, nh, cap, hd), cfg.in_torch, dev)
         _expect("buf_B", self.buf_B, (b, ng, cap, ds), cfg.in_torch, dev)
         _expect("buf_dt", self.buf_dt, (b, nh, cap), torch.float32, dev)

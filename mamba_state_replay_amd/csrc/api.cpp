@@ -47,10 +47,11 @@ int check_config(const rssm_config* c, bool need_window) {
         if (c->max_drafts < 1 || c->max_drafts > RSSM_MAX_DRAFTS)
             return fail(RSSM_ERR_SHAPE, "max_drafts %d outside 1..%d", c->max_drafts, RSSM_MAX_DRAFTS);
         if (c->read_copy != RSSM_NONE && c->read_copy != RSSM_BF16 && c->read_copy != RSSM_FP8_E4M3 &&
-            c->read_copy != RSSM_MXFP4)
-            return fail(RSSM_ERR_DTYPE, "read_copy must be RSSM_NONE, RSSM_BF16, RSSM_FP8_E4M3 or RSSM_MXFP4");
-        if (c->read_copy == RSSM_MXFP4 && c->dstate % 32 != 0)
-            return fail(RSSM_ERR_SHAPE, "RSSM_MXFP4 needs dstate %% 32 == 0 (blocks of 32 columns), got %d",
+            c->read_copy != RSSM_MXFP4 && c->read_copy != RSSM_MXFP8)
+            return fail(RSSM_ERR_DTYPE,
+                        "read_copy must be RSSM_NONE, RSSM_BF16, RSSM_FP8_E4M3, RSSM_MXFP4 or RSSM_MXFP8");
+        if ((c->read_copy == RSSM_MXFP4 || c->read_copy == RSSM_MXFP8) && c->dstate % 32 != 0)
+            return fail(RSSM_ERR_SHAPE, "the MX read copies need dstate %% 32 == 0 (blocks of 32 columns), got %d",
                         c->dstate);
         const int cap = c->window + 2 * c->max_drafts - 1;
         if (rssm::replay_lds_bytes(c->headdim, c->dstate, cap, c->max_drafts, c->in_dtype == RSSM_BF16 ? 2 : 4) >
@@ -64,6 +65,7 @@ int read_mode(const rssm_config* c) {
     return c->read_copy == RSSM_BF16       ? rssm::READ_BF16
            : c->read_copy == RSSM_FP8_E4M3 ? rssm::READ_E4M3
            : c->read_copy == RSSM_MXFP4    ? rssm::READ_MXFP4
+           : c->read_copy == RSSM_MXFP8    ? rssm::READ_MXFP8
                                             : rssm::READ_F32;
 }
 
@@ -73,8 +75,10 @@ int check_state(const rssm_config* c, const rssm_state* s) {
         return fail(RSSM_ERR_NULL, "state: ckpt, buf_x, buf_B, buf_dt and meta are required");
     if ((c->read_copy == RSSM_NONE) != (s->ckpt_read == nullptr))
         return fail(RSSM_ERR_NULL, "state: ckpt_read must be set iff read_copy != RSSM_NONE");
-    if ((c->read_copy == RSSM_FP8_E4M3 || c->read_copy == RSSM_MXFP4) != (s->ckpt_scale != nullptr))
-        return fail(RSSM_ERR_NULL, "state: ckpt_scale must be set iff read_copy is RSSM_FP8_E4M3 or RSSM_MXFP4");
+    if ((c->read_copy == RSSM_FP8_E4M3 || c->read_copy == RSSM_MXFP4 || c->read_copy == RSSM_MXFP8) !=
+        (s->ckpt_scale != nullptr))
+        return fail(RSSM_ERR_NULL,
+                    "state: ckpt_scale must be set iff read_copy is RSSM_FP8_E4M3, RSSM_MXFP4 or RSSM_MXFP8");
     if (!aligned(s->ckpt, 16) || !aligned(s->buf_x, 16) || !aligned(s->buf_B, 16) ||
         (s->ckpt_read && !aligned(s->ckpt_read, 16)))
         return fail(RSSM_ERR_SHAPE, "state: ckpt, ckpt_read, buf_x and buf_B must be 16-byte aligned");
@@ -167,10 +171,12 @@ int replayssm_sizes(const rssm_config* c, size_t bytes[RSSM_NUM_BUFS]) {
     bytes[RSSM_BUF_CKPT] = tiles * tile * 4;
     bytes[RSSM_BUF_CKPT_READ] = c->read_copy == RSSM_BF16       ? tiles * tile * 2
                                 : c->read_copy == RSSM_FP8_E4M3 ? tiles * tile
+                                : c->read_copy == RSSM_MXFP8    ? tiles * tile
                                 : c->read_copy == RSSM_MXFP4    ? tiles * tile / 2
                                                                 : 0;
     bytes[RSSM_BUF_CKPT_SCALE] = c->read_copy == RSSM_FP8_E4M3 ? tiles * 4
                                  : c->read_copy == RSSM_MXFP4  ? tiles * tile / 32
+                                 : c->read_copy == RSSM_MXFP8  ? tiles * tile / 32
                                                                : 0;
     bytes[RSSM_BUF_X] = tiles * cap * c->headdim * in_bytes;
     bytes[RSSM_BUF_B] = (size_t)c->batch * c->ngroups * cap * c->dstate * in_bytes;

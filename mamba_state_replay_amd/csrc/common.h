@@ -105,6 +105,18 @@ __device__ __forceinline__ uint32_t mx_block_scale(float amax, bool has_nan) {
     return has_nan ? 255u : (uint32_t)e;
 }
 
+// E8M0 scale of an MXFP8 (e4m3) block with largest magnitude amax: the
+// smallest power of two X with amax / X <= 448, so that no element saturates
+// (amax = m 2^E needs X = 2^(E - 8), or 2^(E - 7) when m > 1.75), clamped to
+// 1 .. 254; 255 if the block holds a NaN.  An infinite amax gets the scale of
+// the largest finite fp32 value.
+__device__ __forceinline__ uint32_t mx8_block_scale(float amax, bool has_nan) {
+    const uint32_t bits = __float_as_uint(amax);
+    const int e0 = (int)((bits >> 23) & 0xFF) - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    const int e = e0 < 1 ? 1 : e0 > 254 ? 254 : e0;
+    return has_nan ? 255u : (uint32_t)e;
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane exchange within 32-lane halves: DPP quad permutes for xor 1 and
 // xor 2, ds_swizzle (bit-mask mode) for xor 4, 8 and 16.

@@ -9,7 +9,7 @@ namespace rssm {
 
 enum Mode : int32_t { MODE_DECODE = 0, MODE_VERIFY = 1, MODE_FLUSH = 2 };
 enum InType : int32_t { IN_F32 = 0, IN_BF16 = 1 };
-enum ReadMode : int32_t { READ_F32 = 0, READ_BF16 = 1, READ_E4M3 = 2, READ_MXFP4 = 3 };
+enum ReadMode : int32_t { READ_F32 = 0, READ_BF16 = 1, READ_E4M3 = 2, READ_MXFP4 = 3, READ_MXFP8 = 4 };
 
 constexpr uint32_t kStatusMeta = 1u;
 constexpr uint32_t kStatusAccept = 2u;

@@ -47,17 +47,20 @@ namespace {
 // Per-head arrays are indexed [head][...]; B rows are the group's and shared
 // by the heads; the queries' C rows are widened to fp32.
 struct Lds {
-    int X, XS, K, Cq, DT, AA, CO, DQ, WF, RED, total;
+    int X, XS, K, SC, Cq, DT, AA, CO, DQ, WF, RED, total;
 };
 
 constexpr int kRedSlots = 64;   // cross-wave reduction slots: [head][wave]
 
-__host__ __device__ inline Lds lds_plan(int HD, int DS, int cap, int T, int HPW, int xbytes) {
+// mxbytes: the MX scale bytes of one head's tile (HD * DS / 32), staged for
+// the copy-reading calls of the MX modes; 0 otherwise.
+__host__ __device__ inline Lds lds_plan(int HD, int DS, int cap, int T, int HPW, int xbytes, int mxbytes = 0) {
     Lds l;
     int o = 0;
     l.XS = xbytes == 4 ? HD + 4 : HD + 8;           // elements; 16-byte aligned rows
     l.X = o;  o += HPW * cap * l.XS * xbytes / 4;    // x of records then queries, window order, per head
     l.K = o;  o += cap * DS * xbytes / 4;   // B of records then queries (input type)
+    l.SC = o; o += HPW * mxbytes / 4;       // MX scale bytes of the heads' tiles
     l.Cq = o; o += T * DS;           // C of the queries
     l.DT = o; o += HPW * cap;        // dt, window order, per head
     l.AA = o; o += HPW * cap;        // a = dt * A, per head
@@ -190,7 +193,8 @@ struct Window {
 };
 
 // Where staged vector v comes from and goes: the x rows of the window of
-// each head, then the group's B rows, then the queries' C rows.  Rows c < n
+// each head, then the group's B rows, then the queries' C rows, then (MX
+// copies, calls that read the copy) the heads' scale bytes.  Rows c < n
 // are committed records read from the ring; rows c >= n are query tokens,
 // whose x and B are also appended to the ring at slot (start + c) % cap.
 struct StageMap {
@@ -202,6 +206,8 @@ struct StageMap {
     int start, n, cap, T, b, h, g, nheads, ngroups, nx, nb, rows;
     int ldsX, ldsXS, ldsK, ldsC;
     bool append_x, append_B;
+    const void* sc;   // MX scale bytes of the workgroup's heads (contiguous), staged after the C rows
+    int nc, ldsSC;
 };
 
 struct StageJob {
@@ -247,12 +253,17 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
         }
         j.dst = m.ldsK * 4 + (c * DS + cv * EPVIN) * (int)sizeof(InT);
         j.wide = false;
-    } else {
+    } else if (v < m.nx + m.nb + m.nc) {
         const int u = v - m.nx - m.nb;
         const int q = u / VS, cv = u - q * VS;
         j.src = reinterpret_cast<const uint4*>(m.Ct) + ((size_t)(m.b * m.T + q) * m.ngroups + m.g) * VS + cv;
         j.dst = (m.ldsC + q * DS + cv * EPVIN) * 4;
         j.wide = true;
+    } else {
+        const int u = v - m.nx - m.nb - m.nc;
+        j.src = reinterpret_cast<const uint4*>(m.sc) + u;
+        j.dst = m.ldsSC * 4 + u * 16;
+        j.wide = false;
     }
     return j;
 }
@@ -284,11 +295,12 @@ __device__ __forceinline__ float4 load_b4(const float* lds, int K, int c, int co
 // row group takes the records c = first + j, first + j + W, ... and adds
 // co[q][c] x_c[row] (the D x_q term rides on co[q][m_q]).  One transposed
 // reduction over the row's W lanes then leaves y_q[row] on one lane, which
-// stores it.
+// stores it.  rs[r] scales the tile's share of row r (the read copy's scale:
+// one per tile, or per block of 32 columns for the MX copies).
 template <int HD, int DS, int NT, typename InT, int EB, int OFF = 0>
 __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& t, const float* lds,
                                                     const Lds& L, const HeadView& hv, const Window& w,
-                                                    float scale, float* y_head, size_t y_qstride, int tid) {
+                                                    const float* rs, float* y_head, size_t y_qstride, int tid) {
     using G = TileGeo<HD, DS, NT, EB>;
     const int j = tid % G::W;
     const int row0 = G::row0(tid);
@@ -298,9 +310,9 @@ __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& 
 #pragma unroll
         for (int r = 0; r < G::NI; ++r) v[r] = 0.f;
         t.template dot<EB, OFF>(lds + L.Cq + q * DS, j, v);
-        const float dq = lds[hv.DQ + q] * scale;
+        const float dq = lds[hv.DQ + q];
 #pragma unroll
-        for (int r = 0; r < G::NI; ++r) v[r] *= dq;
+        for (int r = 0; r < G::NI; ++r) v[r] *= dq * rs[r];
         const int m = w.n + q;
         for (int cc = w.first + j; cc <= m; cc += G::W) {
             const float co = lds[hv.CO + q * w.cap + cc];
@@ -315,19 +327,34 @@ __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& 
     }
 }
 
+// The E8M0 scale byte of the block that row r of the thread's share of head
+// hh's copy tile lies in (from the scale bytes staged in LDS).
+template <int HD, int DS, int NT, int EBC>
+__device__ __forceinline__ uint32_t mx_scale_byte(const float* lds, const Lds& L, int hh, int r, int tid) {
+    using GC = TileGeo<HD, DS, NT, EBC>;
+    const int blk = GC::vec(tid, r * GC::VPL) * GC::EPV / 32;
+    return reinterpret_cast<const uint8_t*>(lds + L.SC)[hh * (HD * DS / 32) + blk];
+}
+
 // The read-copy tiles of HPW heads, each over the whole workgroup in its own
-// vectors of the register array: step 5 for every head.
-template <int HD, int DS, int NT, typename InT, int EBC, int HPW, int HH = 0>
+// vectors of the register array: step 5 for every head.  Row scales: the
+// head's tile scale (scales[HH], or 1 without one), or with MX the E8M0 scale
+// of the block each of the thread's rows holds.
+template <int HD, int DS, int NT, typename InT, int EBC, int HPW, bool MX, int HH = 0>
 __device__ __forceinline__ void copy_queries(const TileRegs<HD, DS, NT>& t, const float* lds, const Lds& L,
                                              const Window& w, const float* scales, float* y0,
                                              size_t y_qstride, int tid) {
     if constexpr (HH < HPW) {
         using GC = TileGeo<HD, DS, NT, EBC>;
         const HeadView hv = head_view<InT>(L, HH, w.cap, w.T);
+        float rs[GC::NI];
+#pragma unroll
+        for (int r = 0; r < GC::NI; ++r)
+            rs[r] = MX ? e8m0_to_f32(mx_scale_byte<HD, DS, NT, EBC>(lds, L, HH, r, tid)) : scales ? scales[HH] : 1.0f;
         if (tid < GC::ACTIVE)
-            queries_and_outputs<HD, DS, NT, InT, EBC, HH * GC::NV>(t, lds, L, hv, w, scales ? scales[HH] : 1.0f,
+            queries_and_outputs<HD, DS, NT, InT, EBC, HH * GC::NV>(t, lds, L, hv, w, rs,
                                                                   y0 ? y0 + HH * HD : nullptr, y_qstride, tid);
-        copy_queries<HD, DS, NT, InT, EBC, HPW, HH + 1>(t, lds, L, w, scales, y0, y_qstride, tid);
+        copy_queries<HD, DS, NT, InT, EBC, HPW, MX, HH + 1>(t, lds, L, w, scales, y0, y_qstride, tid);
     }
 }
 
@@ -351,8 +378,8 @@ __device__ __forceinline__ void load_heads(TileRegs<HD, DS, NT>& t, const uint8_
 // kept decoded in registers across queries.  Each sum then gets its record
 // terms and is reduced over the W lanes of its row.
 template <int HD, int DS, int NT, typename InT, int HPW>
-__device__ __forceinline__ void mx_queries(const TileRegs<HD, DS, NT>& t, const uint32_t* mxs, const float* lds,
-                                           const Lds& L, const Window& w, float* y0, size_t y_qstride, int tid) {
+__device__ __forceinline__ void mx_queries(const TileRegs<HD, DS, NT>& t, const float* lds, const Lds& L,
+                                           const Window& w, float* y0, size_t y_qstride, int tid) {
     using G = TileGeo<HD, DS, NT, 0>;
     static_assert(G::NV == 1 && G::NI == 1, "one block per thread and head");
     typedef float f2 __attribute__((ext_vector_type(2)));
@@ -361,7 +388,7 @@ __device__ __forceinline__ void mx_queries(const TileRegs<HD, DS, NT>& t, const 
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
         const HeadView hv = head_view<InT>(L, hh, w.cap, w.T);
-        const uint32_t e = (mxs[hh / 4] >> (8 * (hh % 4))) & 0xFFu;
+        const uint32_t e = mx_scale_byte<HD, DS, NT, 0>(lds, L, hh, 0, tid);
         const v4u words = __builtin_bit_cast(v4u, t.raw[hh]);
         const float bs = e == 255u ? 1.0f : e8m0_to_f32(e);
         for (int q = 0; q < w.T; ++q) {
@@ -437,7 +464,9 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
     const bool append = !flush_call;
     const int rows = n + T;          // window rows staged in LDS
 
-    const Lds L = lds_plan(HD, DS, cap, T, HPW, sizeof(InT));
+    constexpr bool MX = RM == READ_MXFP4 || RM == READ_MXFP8;
+    constexpr int MXB = MX ? HD * DS / 32 : 0;       // MX scale bytes per head tile
+    const Lds L = lds_plan(HD, DS, cap, T, HPW, sizeof(InT), MXB);
     float Ah[HPW], Dh[HPW];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -453,10 +482,12 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
     const InT* Ct = reinterpret_cast<const InT*>(a.C);
     const bool writer = (h0 % hpg) == 0;
     const int nx = HPW * rows * VR, nb = rows * VS, nc = T * VS;
-    const int nv = nx + nb + nc;
+    const int ns = fold ? 0 : HPW * MXB / 16;        // the copy's scale bytes, 16 per vector
+    const int nv = nx + nb + nc + ns;
 
     const StageMap sm{bx, bB, xt, Bt, Ct, start, n, cap, T, b, h0, g, a.nheads, a.ngroups,
-                      nx, nb, rows, L.X, L.XS, L.K, L.Cq, append, append && writer};
+                      nx, nb, rows, L.X, L.XS, L.K, L.Cq, append, append && writer,
+                      reinterpret_cast<const uint8_t*>(a.ckpt_scale) + tile0 * MXB, nc, L.SC};
     uint4 jv[JOBS];
 #pragma unroll
     for (int j = 0; j < JOBS; ++j) {
@@ -482,17 +513,6 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
     } else if constexpr (RM != READ_F32) {
         const uint8_t* cp = reinterpret_cast<const uint8_t*>(a.ckpt_read) + tile0 * CB;
         load_heads<HD, DS, NT, EBC, HPW>(treg, cp, CB, tid);
-    }
-    // MXFP4: the E8M0 scale of each head's block this thread holds (one byte
-    // per head, packed four to a word).
-    uint32_t mxs[(HPW + 3) / 4] = {};
-    if constexpr (RM == READ_MXFP4) {
-        if (!fold) {
-            const uint8_t* sp = reinterpret_cast<const uint8_t*>(a.ckpt_scale) + tile0 * (HD * DS / 32);
-#pragma unroll
-            for (int hh = 0; hh < HPW; ++hh)
-                mxs[hh / 4] |= (uint32_t)sp[hh * (HD * DS / 32) + GC::vec(tid, 0)] << (8 * (hh % 4));
-        }
     }
 
 #pragma unroll
@@ -583,6 +603,7 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
 
     // ---- 4/5. flush in registers, then queries and outputs --------------------------
     const Window win{n, first, T, cap};
+    const float kOnes[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};   // FP32 tile: no row scales
     float* y0 = a.y ? a.y + ((size_t)b * T * a.nheads + h0) * HD : nullptr;
     const size_t y_qstride = (size_t)a.nheads * HD;
     if (fold) {
@@ -640,12 +661,13 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
 #pragma unroll
                         for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(f[s][e]));
                 }
-                if constexpr (RM == READ_MXFP4) {
+                if constexpr (MX) {
                     // Block k of row r (32 columns) is vector k of that row on the 8
                     // lanes of the row group: its largest magnitude and NaN flag are
                     // reduced over those lanes, then each lane encodes its 4 values
-                    // (v / X, nearest even, saturating) into 16 bits of the block.
-                    uint16_t* out = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(a.ckpt_read) + tile * CB);
+                    // (v / X, nearest even) into 16 bits (E2M1, saturating at 6) or
+                    // 32 bits (e4m3; the MXFP8 scale leaves nothing to saturate).
+                    uint8_t* out = reinterpret_cast<uint8_t*>(a.ckpt_read) + tile * CB;
                     uint8_t* sc_out = reinterpret_cast<uint8_t*>(a.ckpt_scale) + tile * (HD * DS / 32);
                     const int jr = tid % G32::W;
                     // largest |v| of each block as fp32 bits: a NaN (bits above those of
@@ -665,12 +687,21 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
                     uint32_t packed[G32::NI] = {};
 #pragma unroll
                     for (int s = 0; s < G32::NV; ++s) {
-                        const uint32_t e = mx_block_scale(__uint_as_float(mb[s]), mb[s] > 0x7F800000u);
-                        const float X = e == 255u ? 1.0f : e8m0_to_f32(e);
+                        const bool nan = mb[s] > 0x7F800000u;
                         const v4f fv = f[s];
-                        uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, fv.x, fv.y, X, 0);
-                        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fv.z, fv.w, X, 1);
-                        out[G32::vec(tid, s)] = (uint16_t)w;       // fp32 vector = 4 columns = 2 bytes
+                        uint32_t e;
+                        if constexpr (RM == READ_MXFP4) {
+                            e = mx_block_scale(__uint_as_float(mb[s]), nan);
+                            const float X = e == 255u ? 1.0f : e8m0_to_f32(e);
+                            uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, fv.x, fv.y, X, 0);
+                            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fv.z, fv.w, X, 1);
+                            reinterpret_cast<uint16_t*>(out)[G32::vec(tid, s)] = (uint16_t)w;   // 4 columns = 2 bytes
+                        } else {
+                            e = mx8_block_scale(__uint_as_float(mb[s]), nan);
+                            const float inv = e == 255u ? 1.0f : e8m0_to_f32(254u - e);        // 1 / X, exact
+                            reinterpret_cast<uint32_t*>(out)[G32::vec(tid, s)] =
+                                f32x4_to_e4m3(fv.x * inv, fv.y * inv, fv.z * inv, fv.w * inv);
+                        }
                         packed[s / G32::VPL] |= e << (8 * (s % G32::VPL));
                     }
                     if (jr == 0) {
@@ -704,20 +735,20 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
                 if (tid == 0) a.ckpt_scale[tile] = sc;
             }
             if (active && T > 0)
-                queries_and_outputs<HD, DS, NT, InT, 4>(treg, lds, L, hv, win, 1.0f, y0 ? y0 + hh * HD : nullptr,
+                queries_and_outputs<HD, DS, NT, InT, 4>(treg, lds, L, hv, win, kOnes, y0 ? y0 + hh * HD : nullptr,
                                                         y_qstride, tid);
         }
     } else if constexpr (RM == READ_F32) {
         if (tid < G32::ACTIVE)
-            queries_and_outputs<HD, DS, NT, InT, 4>(treg, lds, L, head_view<InT>(L, 0, cap, T), win, 1.0f, y0,
+            queries_and_outputs<HD, DS, NT, InT, 4>(treg, lds, L, head_view<InT>(L, 0, cap, T), win, kOnes, y0,
                                                     y_qstride, tid);
     } else if constexpr (RM == READ_MXFP4) {
-        mx_queries<HD, DS, NT, InT, HPW>(treg, mxs, lds, L, win, y0, y_qstride, tid);
+        mx_queries<HD, DS, NT, InT, HPW>(treg, lds, L, win, y0, y_qstride, tid);
     } else {
         float scales[HPW];
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) scales[hh] = RM == READ_E4M3 ? a.ckpt_scale[tile0 + hh] : 1.0f;
-        copy_queries<HD, DS, NT, InT, EBC, HPW>(treg, lds, L, win, scales, y0, y_qstride, tid);
+        copy_queries<HD, DS, NT, InT, EBC, HPW, MX>(treg, lds, L, win, scales, y0, y_qstride, tid);
     }
 
     // ---- 6. advance the heads' ring pointers -----------------------------------------
@@ -788,6 +819,11 @@ __global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 5 : 8) void replay_kernel(co
         replay_body<HD, DS, NT, InT, RM, HPW, false>(a, ctx, lds);
 }
 
+// MX scale bytes per head tile staged in LDS by the MX read modes.
+constexpr int mx_bytes(int hd, int ds, int read_mode) {
+    return read_mode == READ_MXFP4 || read_mode == READ_MXFP8 ? hd * ds / 32 : 0;
+}
+
 int threads_for(int hd, int ds) {
     if (hd == 16 && ds == 16) return ShapeNT<16, 16>::NT;
     if (hd == 64 && ds == 64) return ShapeNT<64, 64>::NT;
@@ -807,7 +843,8 @@ int heads_per_wg(int hd, int ds, int nheads, int ngroups, int cap, int T, int re
     const int want = read_mode == READ_BF16 ? 2 : 4;
     const int hpg = nheads / ngroups;
     for (int hpw = want; hpw > 1; hpw /= 2)
-        if (hpg % hpw == 0 && (size_t)lds_plan(hd, ds, cap, T, hpw, xbytes).total * sizeof(float) <= 65536 &&
+        if (hpg % hpw == 0 && (size_t)lds_plan(hd, ds, cap, T, hpw, xbytes, mx_bytes(hd, ds, read_mode)).total *
+                                      sizeof(float) <= 65536 &&
             hpw * (threads_for(hd, ds) / 64) <= kRedSlots)
             return hpw;
     return 1;
@@ -817,7 +854,8 @@ template <int HD, int DS, typename InT, int RM, int HPW>
 hipError_t launch_one(const ReplayArgs& a, hipStream_t stream) {
     constexpr int NT = ShapeNT<HD, DS>::NT;
     const int nwg = a.batch * (a.nheads / HPW);
-    const size_t lds = (size_t)lds_plan(HD, DS, a.cap, a.T, HPW, sizeof(InT)).total * sizeof(float);
+    const size_t lds =
+        (size_t)lds_plan(HD, DS, a.cap, a.T, HPW, sizeof(InT), mx_bytes(HD, DS, RM)).total * sizeof(float);
     hipLaunchKernelGGL((replay_kernel<HD, DS, NT, InT, RM, HPW>), dim3(nwg), dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
@@ -826,7 +864,7 @@ hipError_t launch_one(const ReplayArgs& a, hipStream_t stream) {
 // compiled only where a copy tile leaves room for them (not 16 x 16).
 template <int HD, int DS, int RM, int HPW>
 constexpr bool multi_head_fits() {
-    using GC = TileGeo<HD, DS, ShapeNT<HD, DS>::NT, RM == READ_BF16 ? 2 : RM == READ_E4M3 ? 1 : 0>;
+    using GC = TileGeo<HD, DS, ShapeNT<HD, DS>::NT, RM == READ_BF16 ? 2 : RM == READ_MXFP4 ? 0 : 1>;
     return HD != 16 && HPW * GC::NV <= TileGeo<HD, DS, ShapeNT<HD, DS>::NT, 4>::NV &&
            GC::ACTIVE == ShapeNT<HD, DS>::NT;
 }
@@ -849,6 +887,9 @@ hipError_t launch_type(const ReplayArgs& a, int read_mode, int hpw, hipStream_t 
         case READ_MXFP4:
             if constexpr (DS % 32 == 0) return launch_copy<HD, DS, InT, READ_MXFP4>(a, hpw, stream);
             return hipErrorInvalidValue;
+        case READ_MXFP8:
+            if constexpr (DS % 32 == 0) return launch_copy<HD, DS, InT, READ_MXFP8>(a, hpw, stream);
+            return hipErrorInvalidValue;
     }
     return hipErrorInvalidValue;
 }
@@ -864,7 +905,8 @@ hipError_t launch_shape(const ReplayArgs& a, int in_type, int read_mode, hipStre
 }  // namespace
 
 size_t replay_lds_bytes(int hd, int ds, int cap, int T, int in_bytes) {
-    return (size_t)lds_plan(hd, ds, cap, T, 1, in_bytes).total * sizeof(float);   // one head per workgroup
+    // one head per workgroup, with room for MX scale bytes (an upper bound for every read mode)
+    return (size_t)lds_plan(hd, ds, cap, T, 1, in_bytes, hd * ds / 32).total * sizeof(float);
 }
 
 bool shape_supported(int hd, int ds) {

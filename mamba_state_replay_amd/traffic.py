@@ -49,6 +49,8 @@ def sizes(nheads, headdim, dstate, ngroups, in_bytes=2, read_copy=None) -> Sizes
         S_r = S_c = S // 4 + nheads * 4
     elif read_copy == "mxfp4":
         S_r = S_c = S // 8 + S // 128
+    elif read_copy == "mxfp8":
+        S_r = S_c = S // 4 + S // 128
     else:
         raise ValueError(read_copy)
     R = nheads * headdim * in_bytes + ngroups * dstate * in_bytes + nheads * 4

@@ -157,6 +157,40 @@ def mxfp4_decode(scales, codes) -> np.ndarray:
     return (v * e8m0_value(scales)[..., None]).reshape(c.shape)
 
 
+def mxfp8_scale(amax) -> np.ndarray:
+    """E8M0 byte of an MXFP8 block scale, from its definition: the smallest
+    power of two X = 2^(e - 127) with amax / X <= 448 (e clamped to 1..254);
+    255 for a NaN; an infinite amax is taken as the largest finite fp32."""
+    a = np.asarray(amax, np.float64)
+    fin = np.where(np.isnan(a), 0.0, np.minimum(a, float(np.finfo(np.float32).max)))
+    k = np.ceil(np.log2(np.where(fin > 0, fin, 1.0) / 448.0)).astype(np.int64)
+    # guard the floating-point log: X = 2^k must hold amax, 2^(k-1) must not (448 * 2^k is exact)
+    k = np.where(fin > 448.0 * np.exp2(k.astype(np.float64)), k + 1, k)
+    k = np.where(fin <= 448.0 * np.exp2(k.astype(np.float64) - 1.0), k - 1, k)
+    e = np.clip(k + 127, 1, 254)
+    e = np.where(fin == 0, 1, e)
+    return np.where(np.isnan(a), 255, e).astype(np.int64)
+
+
+def mxfp8_encode(x) -> tuple[np.ndarray, np.ndarray]:
+    """fp32 array [..., 32 k] -> (E8M0 scales [..., k] uint8, e4m3fn codes
+    [..., 32 k] uint8): each block's codes encode v / X (exact division by a
+    power of two), nearest even; a NaN block keeps X = 1 for its codes."""
+    x = np.asarray(x, np.float32)
+    blk = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.abs(blk).max(axis=-1).astype(np.float32)
+    e = mxfp8_scale(amax)
+    X = e8m0_value(e)
+    codes = encode_e4m3fn(blk.astype(np.float64) / np.where(np.isnan(X), 1.0, X)[..., None])
+    return e.astype(np.uint8), codes.reshape(x.shape)
+
+
+def mxfp8_decode(scales, codes) -> np.ndarray:
+    c = np.asarray(codes)
+    v = decode_e4m3fn(c).reshape(c.shape[:-1] + (c.shape[-1] // 32, 32))
+    return (v * e8m0_value(scales)[..., None]).reshape(c.shape)
+
+
 def e2m1_encode_fast(x) -> np.ndarray:
     """Same as e2m1_encode for fp32 input (no NaN), by counting the midpoints
     passed: a tie at a midpoint goes to the even code (the thresholds at

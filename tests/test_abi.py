@@ -65,6 +65,18 @@ def test_sizes_and_capacity(rb):
     assert rb.replayssm_capacity(e4) == 21
     sz = rb.replayssm_sizes(e4)
     assert sz[rb.BUF_CKPT_READ] == 1 << 28 and sz[rb.BUF_CKPT_SCALE] == 256 * 128 * 4
+    # MX copies: one E8M0 byte per 32 columns; E2M1 codes two to a byte, e4m3 one
+    for mode, code_bytes in (("mxfp4", 1 << 27), ("mxfp8", 1 << 28)):
+        sz = rb.replayssm_sizes(rb.Config(256, 128, 64, 128, 8, 16, 1, "bf16", mode))
+        assert sz[rb.BUF_CKPT_READ] == code_bytes and sz[rb.BUF_CKPT_SCALE] == 256 * 128 * 64 * 128 // 32
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp8"])
+def test_mx_copies_need_blocks_of_32_columns(rb, mode):
+    with pytest.raises(rb.ReplaySSMError) as e:
+        rb.replayssm_sizes(rb.Config(4, 4, 16, 16, 1, 4, 1, "f32", mode))
+    assert e.value.code == -2 and "32" in str(e.value)
+    rb.replayssm_sizes(rb.Config(4, 16, 64, 64, 2, 4, 1, "f32", mode))     # dstate 64: accepted
 
 
 @pytest.mark.parametrize("bad,code", [

@@ -127,6 +127,42 @@ def test_mxfp4_block_scale_and_error():
     assert list(cw[0, :8]) == [6, 9, 0, 2, 5, 5, 2, 15]
 
 
+def test_mxfp8_block_scale_and_error():
+    """The MXFP8 block scale is the smallest power of two X with amax / X <=
+    448, so amax / X lies in (224, 448] and nothing saturates; every element's
+    decode error is at most |v| / 16 + X / 1024 (half the e4m3 spacing,
+    relative in the normal range, absolute below it); worked scales at the
+    edges of the rule; zeros, NaN and infinity."""
+    g = np.random.default_rng(13)
+    x = (np.exp(g.uniform(-20, 20, (500, 1))) * g.standard_normal((500, 128))).astype(np.float32)
+    e, c = formats.mxfp8_encode(x)
+    X = formats.e8m0_value(e)
+    amax = np.abs(x.reshape(500, 4, 32)).max(axis=-1).astype(np.float64)
+    big = amax >= 2.0 ** -117                 # below it the scale is clamped at 2^-126
+    r = amax / X
+    assert np.all((r > 224) & (r <= 448) | ~big)
+    dec = formats.mxfp8_decode(e, c)
+    err = np.abs(dec - x.astype(np.float64))
+    Xe = np.repeat(X, 32, axis=-1)
+    assert np.all(err <= np.abs(x) / 16 + Xe / 1024)
+    # worked scales: 448 fits X = 1; the next fp32 above needs X = 2; 1.0 and 1.75 fit 2^-8
+    # (256 and 448), the fp32 just above 1.75 needs 2^-7; 0 -> the smallest normal scale
+    f32 = np.float32
+    cases = {448.0: 127, float(np.nextafter(f32(448), f32(1e9))): 128, 1.0: 119, 1.75: 119,
+             float(np.nextafter(f32(1.75), f32(2))): 120, 0.0: 1, float("inf"): 247, 2.0 ** -130: 1}
+    for a, want in cases.items():
+        assert formats.mxfp8_scale(np.float32(a)) == want, (a, want)
+    n = np.ones((1, 32), np.float32)
+    n[0, 3] = np.nan
+    en, cn = formats.mxfp8_encode(n)
+    assert en[0, 0] == 255 and np.all(np.isnan(formats.mxfp8_decode(en, cn)))
+    # a worked block: amax 3.0 -> X = 2^-7 (3 * 128 = 384 <= 448, 3 * 256 > 448); codes encode v * 128
+    w = np.array([[3.0, -1.0, 0.5, 2.0 ** -9] + [0.0] * 28], np.float32)
+    ew, cw = formats.mxfp8_encode(w)
+    assert ew[0, 0] == 120
+    assert np.array_equal(formats.decode_e4m3fn(cw[0, :4]), [384.0, -128.0, 64.0, 0.25])
+
+
 def test_fast_e2m1_encoder_matches_definition():
     """The midpoint-counting E2M1 encoder used for exhaustive checks equals the
     nearest-value encoder on every fp32 within 2 ulp of each value, midpoint

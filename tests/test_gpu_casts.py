@@ -128,46 +128,67 @@ def test_e4m3_cast_of_nan_is_nan():
     assert np.all(host(st.ckpt_scale) == 1.0)
 
 
-def test_mxfp4_cast_every_pattern_below_8():
-    """Every fp32 value with |v| < 8, in MXFP4 blocks whose largest magnitude
-    lies in [4, 8) (one lane of each block holds 4.0), so the block scale is
-    2^0 and each code is the E2M1 encoding of v itself (nearest, ties to even,
-    saturating at 6)."""
+def _mx_cast_every_pattern(copy, top, anchor, scale_byte, want_fn):
+    """Every fp32 pattern with magnitude up to the pattern top, 31 to a block
+    of 32 whose first lane holds anchor (the block's largest magnitude, which
+    fixes its scale byte): the codes against want_fn(values)."""
     dev = device()
-    top = int(np.nextafter(np.float32(8.0), np.float32(0)).view(np.uint32))
     mags = np.arange(0, top + 1, dtype=np.uint32)
     pats = np.concatenate([mags, mags | np.uint32(0x80000000)])
     per_blk = 31
     nblk = -(-pats.size // per_blk)
     batch = 256
     blocks_per_launch = batch * 128 * TILE // 32
-    cfg = rb.Config(batch, 128, 64, 128, 8, window=16, max_drafts=1, in_dtype="bf16", read_copy="mxfp4")
+    cfg = rb.Config(batch, 128, 64, 128, 8, window=16, max_drafts=1, in_dtype="bf16", read_copy=copy)
     st = rb.State.allocate(cfg, dev)
     p = rb.Params(torch.full((128,), -1.0, device=dev), torch.zeros(128, device=dev))
-    anchor = np.float32(4.0).view(np.uint32)
     bad = 0
     for b0 in range(0, nblk, blocks_per_launch):
-        say(f"mxfp4 cast, blocks {b0} .. of {nblk}")
+        say(f"{copy} cast, blocks {b0} .. of {nblk}")
         nb = min(blocks_per_launch, nblk - b0)
         chunk = pats[b0 * per_blk:(b0 + nb) * per_blk]
         blk = np.zeros((blocks_per_launch, 32), np.uint32)
         flat = blk[:nb, 1:].reshape(-1)
         flat[:chunk.size] = chunk
         blk[:nb, 1:] = flat.reshape(nb, per_blk)
-        blk[:, 0] = anchor
+        blk[:, 0] = np.float32(anchor).view(np.uint32)
         st.ckpt.view(torch.int32).view(-1).copy_(torch.from_numpy(blk.view(np.int32).reshape(-1)))
         rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST)
         torch.cuda.synchronize()
-        assert np.all(host(st.ckpt_scale) == 127), "a block with largest magnitude in [4, 8) has scale 2^0"
-        packed = host(st.ckpt_read).reshape(blocks_per_launch, 16)
-        codes = np.empty((blocks_per_launch, 32), np.uint8)
-        codes[:, 0::2] = packed & 0xF
-        codes[:, 1::2] = packed >> 4
+        assert np.all(host(st.ckpt_scale) == scale_byte), f"every block's scale byte is {scale_byte}"
+        if copy == "mxfp4":
+            packed = host(st.ckpt_read).reshape(blocks_per_launch, 16)
+            codes = np.empty((blocks_per_launch, 32), np.uint8)
+            codes[:, 0::2] = packed & 0xF
+            codes[:, 1::2] = packed >> 4
+            zero_mask = 7
+        else:
+            codes = host(st.ckpt_read).reshape(blocks_per_launch, 32)
+            zero_mask = 0x7F
         got = codes[:nb, 1:].reshape(-1)[:chunk.size]
-        want = _encode(formats.e2m1_encode_fast, chunk.view(np.float32), np.uint8)
-        mism = (got != want) & ~(((got & 7) == 0) & ((want & 7) == 0))
+        want = want_fn(chunk.view(np.float32))
+        mism = (got != want) & ~(((got & zero_mask) == 0) & ((want & zero_mask) == 0))
         if mism.any():
             i = np.flatnonzero(mism)[:5]
             print(f"[gpu] mismatches at fp32 patterns {chunk[i]} -> got {got[i]} want {want[i]}", flush=True)
         bad += int(mism.sum())
-    assert bad == 0, f"{bad} fp32 values cast to the wrong E2M1 code"
+    assert bad == 0, f"{bad} fp32 values cast to the wrong {copy} code"
+
+
+def test_mxfp4_cast_every_pattern_below_8():
+    """Every fp32 value with |v| < 8, in MXFP4 blocks whose largest magnitude
+    lies in [4, 8) (one lane of each block holds 4.0), so the block scale is
+    2^0 and each code is the E2M1 encoding of v itself (nearest, ties to even,
+    saturating at 6)."""
+    top = int(np.nextafter(np.float32(8.0), np.float32(0)).view(np.uint32))
+    _mx_cast_every_pattern("mxfp4", top, 4.0, 127,
+                           lambda v: _encode(formats.e2m1_encode_fast, v, np.uint8))
+
+
+def test_mxfp8_cast_every_pattern_up_to_448():
+    """Every fp32 value with |v| <= 448, in MXFP8 blocks whose largest magnitude
+    is 448 (one lane of each block holds it), so the block scale is 2^0 and
+    each code is the e4m3 encoding of v itself (nearest, ties to even)."""
+    top = int(np.float32(448.0).view(np.uint32))
+    _mx_cast_every_pattern("mxfp8", top, 448.0, 127,
+                           lambda v: _encode(formats.encode_e4m3fn_fast, v, np.uint8))

@@ -1,8 +1,9 @@
-"""GPU tests of the dual-precision mode: FP32 checkpoint + bf16 / e4m3 read copy.
+"""GPU tests of the dual-precision mode: FP32 checkpoint + a bf16, e4m3 (one
+scale per tile), MXFP4 or MXFP8 (an E8M0 scale per 32 columns) read copy.
 
-* the kernels' e4m3 decoding of every finite code, and their bf16 / e4m3
-  encoding on the cast-only and the flush paths, against host encoders written
-  from the format definitions (tests/formats.py);
+* the kernels' e4m3 decoding of every finite code, and their encodings on the
+  cast-only and the flush paths, against host encoders written from the format
+  definitions (tests/formats.py);
 * outputs read from the copy stay within the stated bound of the fp64 oracle;
 * the copy never enters the recurrence: the FP32 checkpoint is bit-identical
   to an FP32-only run, and a NaN-poisoned copy leaves every flush unchanged
@@ -28,20 +29,24 @@ SHAPES = {
     "64x128": NEMO,
     "128x128": dict(nheads=8, headdim=128, dstate=128, ngroups=1),
 }
-UNIT = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -4, "mxfp4": 2.0 ** -2}   # relative rounding bound of one read
+UNIT = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -4, "mxfp4": 2.0 ** -2, "mxfp8": 2.0 ** -4}   # relative bound of one read
+MX = ("mxfp4", "mxfp8")
 
 
 def read_delta(copy, scale, hd, ds):
     """Absolute part of the per-element read bound, broadcastable to
     [batch][nheads][hd][ds]: 0 for bf16; half the e4m3 subnormal step, s 2^-10,
     for e4m3 (one scale s per tile); a quarter of the block scale X, half the
-    E2M1 spacing below 1, for MXFP4 (scales [batch][nheads][hd][ds / 32] E8M0).
+    E2M1 spacing below 1, for MXFP4, and X 2^-10, half the e4m3 subnormal step,
+    for MXFP8 (scales [batch][nheads][hd][ds / 32] E8M0).
     A margin of 1e-3 covers fp32 rounding."""
     if copy == "bf16":
         return 0.0
     scale = np.asarray(scale)
     if copy == "e4m3":
         return (scale.astype(np.float64) * 2.0 ** -10 * 1.001)[..., None, None]
+    if copy == "mxfp8":
+        return np.repeat(formats.e8m0_value(scale) * 2.0 ** -10 * 1.001, 32, axis=-1)
     return np.repeat(formats.e8m0_value(scale) / 4 * 1.001, 32, axis=-1)
 
 
@@ -128,35 +133,101 @@ def same_fp4(got_scales, got_codes, want_scales, want_codes):
     return bool(np.all(same | ~live))
 
 
-def test_mxfp4_cast_only_encoding():
-    """flush(FORCE_CAST) with nothing to fold writes the MXFP4 encoding of the
-    checkpoint: blocks over 40 orders of magnitude, every E2M1 value and
-    midpoint times the block scale, zero blocks, a block with a NaN, and fp32
-    subnormals; codes and E8M0 scales against the host encoder."""
+def same_fp8(got_scales, got_codes, want_scales, want_codes):
+    """Equal scales, and equal e4m3 codes (+0 and -0 one value, any NaN code
+    equal to any other)."""
+    if not np.array_equal(got_scales, want_scales):
+        return False
+    both_nan = ((np.asarray(got_codes) & 0x7F) == 0x7F) & ((np.asarray(want_codes) & 0x7F) == 0x7F)
+    return bool(np.all(formats.same_code(got_codes, want_codes) | both_nan))
+
+
+def same_mx(copy, st, want):
+    """The state's MX copy equals the host encoding want = (scales, codes)."""
+    if copy == "mxfp4":
+        return same_fp4(host(st.ckpt_scale), unpack_fp4(host(st.ckpt_read)), *want)
+    return same_fp8(host(st.ckpt_scale), host(st.ckpt_read), *want)
+
+
+def mx_encode(copy, h):
+    return formats.mxfp4_encode(h) if copy == "mxfp4" else formats.mxfp8_encode(h)
+
+
+@pytest.mark.parametrize("copy", MX)
+def test_mx_cast_only_encoding(copy):
+    """flush(FORCE_CAST) with nothing to fold writes the MX encoding of the
+    checkpoint: blocks over 40 orders of magnitude, a grid of code values and
+    midpoints (every E2M1 value and midpoint; the top binades of e4m3) times
+    the block scale, blocks whose largest magnitude sits at the edge of the
+    scale rule, zero blocks, a block with a NaN, and fp32 subnormals; codes and
+    E8M0 scales against the host encoder."""
     dev = device()
     g = np.random.default_rng(22)
-    cfg = rb.Config(2, 8, 64, 128, 8, window=16, max_drafts=1, in_dtype="bf16", read_copy="mxfp4")
+    cfg = rb.Config(2, 8, 64, 128, 8, window=16, max_drafts=1, in_dtype="bf16", read_copy=copy)
     st = rb.State.allocate(cfg, dev)
     h = (np.exp(g.uniform(-45, 45, (2, 8, 64, 4, 1))) * g.standard_normal((2, 8, 64, 4, 32))).astype(np.float32)
-    grid = np.concatenate([formats.E2M1, (formats.E2M1[1:] + formats.E2M1[:-1]) / 2])          # 15 values
+    if copy == "mxfp4":
+        grid = np.concatenate([formats.E2M1, (formats.E2M1[1:] + formats.E2M1[:-1]) / 2])      # 15 values
+        top = 6.0
+    else:   # e4m3 values and midpoints from 240 to 448, and a subnormal midpoint
+        grid = np.concatenate([np.arange(240.0, 449.0, 16.0), [1.5 * 2.0 ** -9]])       # 15 values
+        top = 448.0
     h[0, 0, :, 0, :15] = grid * 2.0 ** g.integers(-20, 20, (64, 1))
-    h[0, 0, :, 0, 15] = 6.0 * 2.0 ** g.integers(-20, 20, 64)
+    h[0, 0, :, 0, 15] = top * 2.0 ** g.integers(-20, 20, 64)
+    # largest magnitude just above / at / below a power-of-two multiple of the top code
+    edge = (top * 2.0 ** g.integers(-20, 20, (64, 1))).astype(np.float32)
+    h[0, 4, :, 1:, :] = (edge[:, :, None] * g.uniform(-0.9, 0.9, (64, 3, 32))).astype(np.float32)
+    h[0, 4, :, 1, 0] = np.nextafter(edge[:, 0], np.float32(np.inf))
+    h[0, 4, :, 2, 0] = edge[:, 0]
+    h[0, 4, :, 3, 0] = np.nextafter(edge[:, 0], np.float32(0))
     h[0, 1, :, 1, :] = 0.0
     h[0, 2, 5, 2, 7] = np.nan
     h[1, 3, :, 3, :] = np.float32(1e-41) * g.standard_normal((64, 32)).astype(np.float32)
     h = h.reshape(2, 8, 64, 128)
     st.ckpt.copy_(torch.from_numpy(h))
     p = rb.Params(torch.full((8,), -1.0, device=dev), torch.zeros(8, device=dev))
-    say("cast-only flush mxfp4")
+    say(f"cast-only flush {copy}")
     rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST)
     torch.cuda.synchronize()
     assert torch.equal(st.ckpt.cpu().view(torch.int32), torch.from_numpy(h).view(torch.int32)), \
         "cast-only flush changed the FP32 checkpoint"
-    ws, wc = formats.mxfp4_encode(h)
-    assert same_fp4(host(st.ckpt_scale), unpack_fp4(host(st.ckpt_read)), ws, wc)
+    assert same_mx(copy, st, mx_encode(copy, h))
 
 
-@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4"])
+def test_block_scales_keep_small_rows():
+    """Rows of one tile whose magnitudes span 2^-24 .. 1 (outlier channels):
+    with one e4m3 scale per tile the smallest rows fall below the e4m3 range
+    and read back as zero, while the MXFP8 copy (a scale per 32 columns) keeps
+    every row's largest read error within 2^-4 of the row's largest magnitude
+    (its per-element bound |v| 2^-4 + X 2^-10, X <= that magnitude / 224)."""
+    dev = device()
+    g = np.random.default_rng(23)
+    h = g.standard_normal((2, 8, 64, 128)).astype(np.float32)
+    h *= (2.0 ** -g.uniform(0, 24, (2, 8, 64, 1))).astype(np.float32)
+    h[:, :, 0, 0] = 4.0                                   # every tile keeps a large row
+    p = rb.Params(torch.full((8,), -1.0, device=dev), torch.zeros(8, device=dev))
+    row_err = {}
+    for copy in ("e4m3", "mxfp8"):
+        cfg = rb.Config(2, 8, 64, 128, 8, window=16, max_drafts=1, in_dtype="bf16", read_copy=copy)
+        st = rb.State.allocate(cfg, dev)
+        st.ckpt.copy_(torch.from_numpy(h))
+        say(f"row magnitudes, cast-only flush {copy}")
+        rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST)
+        torch.cuda.synchronize()
+        codes = host(st.ckpt_read)
+        if copy == "e4m3":
+            dec = formats.decode_e4m3fn(codes) * host(st.ckpt_scale)[:, :, None, None]
+        else:
+            dec = formats.mxfp8_decode(host(st.ckpt_scale), codes)
+        row_err[copy] = np.abs(dec - h).max(axis=-1) / np.abs(h).max(axis=-1)
+    small = np.abs(h).max(axis=-1) < 2.0 ** -17         # under half e4m3's smallest step at scale 4/448
+    print(f"[gpu] row magnitudes: worst row read error e4m3 {row_err['e4m3'].max():.3g} "
+          f"({int(small.sum())} rows read as zero), mxfp8 {row_err['mxfp8'].max():.3g}", flush=True)
+    assert small.sum() > 100 and np.all(row_err["e4m3"][small] == 1.0)
+    assert row_err["mxfp8"].max() <= 2.0 ** -4 * 1.001
+
+
+@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4", "mxfp8"])
 def test_flush_encoding_and_scale(copy):
     """A real flush (5 committed records): the copy is the encoding of the new
     FP32 checkpoint, with scale absmax/448 per tile for e4m3."""
@@ -174,9 +245,8 @@ def test_flush_encoding_and_scale(copy):
     if copy == "bf16":
         ref = torch.from_numpy(H).to(torch.bfloat16)
         assert torch.equal(st.ckpt_read.cpu().view(torch.int16), ref.view(torch.int16))
-    elif copy == "mxfp4":
-        ws, wc = formats.mxfp4_encode(H.astype(np.float32))
-        assert same_fp4(host(st.ckpt_scale), unpack_fp4(host(st.ckpt_read)), ws, wc)
+    elif copy in MX:
+        assert same_mx(copy, st, mx_encode(copy, H.astype(np.float32)))
     else:
         amax = np.abs(H).max(axis=(-1, -2)).astype(np.float32)
         sc = (amax / np.float32(448.0)).astype(np.float32)
@@ -200,28 +270,32 @@ def _run_dual(cfg, work, dev, steps, poison_before=()):
                 st.ckpt_read.view(torch.int16).fill_(0x7FC0)
             elif cfg.read_copy == "e4m3":
                 st.ckpt_read.fill_(0x7F)
-            else:
+            elif cfg.read_copy == "mxfp4":
                 st.ckpt_read.fill_(0xFF)          # E2M1 -6 in both nibbles, block scales NaN
                 st.ckpt_scale.fill_(255)
+            else:
+                st.ckpt_read.fill_(0x7F)          # e4m3 NaN, block scales NaN
+                st.ckpt_scale.fill_(255)
         rb.replayssm_decode_step(cfg, st, p, stream.call(t), y[t])
-        if cfg.read_copy in ("e4m3", "mxfp4"):
+        if cfg.read_copy in ("e4m3",) + MX:
             scales[t] = st.ckpt_scale.clone()
     torch.cuda.synchronize()
     return host(y)[:, :, 0], st, {k: host(v) for k, v in scales.items()}
 
 
 @pytest.mark.parametrize("tile", ["64x128", "16x16", "64x64", "128x128"])
-@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4"])
+@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4", "mxfp8"])
 def test_dual_precision_error_bound(copy, tile):
     """Outputs of non-flush steps read the copy; per element
     |y - y_ref| <= d_q sum_j |C_q[j]| (u |H_s[i,j]| + delta) + 1e-4 * (head output scale),
-    u = 2^-8 (bf16), 2^-4 (e4m3) or 2^-2 (MXFP4), delta = 0 (bf16), s 2^-10
-    (e4m3, half the subnormal step scaled) or X / 4 (MXFP4, X the block's scale),
+    u = 2^-8 (bf16), 2^-4 (e4m3, MXFP8) or 2^-2 (MXFP4), delta = 0 (bf16), s 2^-10
+    (e4m3, half the subnormal step scaled), X / 4 (MXFP4, X the block's scale) or
+    X 2^-10 (MXFP8),
     H_s the oracle state at the last flush, d_q the decay since then.  Flushing
     steps read FP32 registers and meet the FP32 tolerance.  The FP32 checkpoint
     must be bit-identical to an FP32-only run."""
-    if copy == "mxfp4" and SHAPES[tile]["dstate"] % 32:
-        pytest.skip("MXFP4 blocks are 32 columns of dstate")
+    if copy in MX and SHAPES[tile]["dstate"] % 32:
+        pytest.skip("MX blocks are 32 columns of dstate")
     dev = device()
     L, steps = 16, 72
     shape = synth.LayerShape(batch=4, window=L, **SHAPES[tile])
@@ -266,7 +340,7 @@ def test_dual_precision_error_bound(copy, tile):
     assert_rows_close(yc[fl], yref[fl], what=f"{copy} flushing-step outputs")
 
 
-@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4"])
+@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4", "mxfp8"])
 def test_poisoned_copy_never_enters_recurrence(copy):
     """NaN-fill the copy right before a flushing step: that step's outputs (read
     from FP32 registers) and the checkpoint it writes are unchanged, and later
@@ -288,7 +362,7 @@ def test_poisoned_copy_never_enters_recurrence(copy):
 
 
 def test_dual_4096_steps_bound_and_no_drift():
-    """4096 decode steps, 8 sequences x 128 heads, L = 16, all three modes run
+    """4096 decode steps, 8 sequences x 128 heads, L = 16, all five modes run
     side by side, window by window, against the fp64 oracle stepped over the
     same window:
     * FP32-only outputs within the FP32 tolerance in every window;
@@ -296,19 +370,19 @@ def test_dual_4096_steps_bound_and_no_drift():
       test above in every window (flushing steps read FP32 registers and meet
       the FP32 tolerance);
     * the copy never enters the recurrence: after 4096 steps the FP32
-      checkpoints of the three modes are bit-identical;
+      checkpoints of the five modes are bit-identical;
     * the read error does not grow: the largest normalized error of the last
       quarter of windows is no more than twice that of the first quarter."""
     dev = device()
     L, steps = 16, 4096
     shape = synth.LayerShape(batch=8, window=L, **NEMO)
     work = synth.decode_workload(shape, steps, seed=1005, n0=L)
-    modes = (None, "bf16", "e4m3", "mxfp4")
+    modes = (None, "bf16", "e4m3", "mxfp4", "mxfp8")
     cfgs = {m: staging.config(shape, read_copy=m) for m in modes}
     sts = {m: staging.replay_state(cfgs[m], work, dev) for m in modes}
     p = staging.params(work, dev)
     stream = staging.TokenStream(work.steps, dev)
-    say("dual precision, 4096 steps, 8 sequences, four modes")
+    say("dual precision, 4096 steps, 8 sequences, five modes")
     for m in modes[1:]:
         rb.replayssm_flush(cfgs[m], sts[m], p, rb.RSSM_FLUSH_FORCE_CAST)
     rb.replayssm_flush(cfgs[None], sts[None], p)
@@ -325,7 +399,7 @@ def test_dual_4096_steps_bound_and_no_drift():
             for m in modes:
                 rb.replayssm_decode_step(cfgs[m], sts[m], p, stream.call(t), y[m][t - t0])
             if t == t0:
-                scales = {m: host(sts[m].ckpt_scale) for m in ("e4m3", "mxfp4")}
+                scales = {m: host(sts[m].ckpt_scale) for m in ("e4m3",) + MX}
         torch.cuda.synchronize()
         tok = work.steps
         Hs = H
@@ -351,7 +425,7 @@ def test_dual_4096_steps_bound_and_no_drift():
             read = UNIT[m] * HC                                       # u sum_j |H_s[i,j]| |C_q[j]|
             if m == "e4m3":
                 read = read + (scales[m] * 2.0 ** -10 * 1.001)[None, :, :, None] * Csum[..., None]
-            elif m == "mxfp4":                                         # sum_j |C_q[j]| X(i, j) / 4
+            elif m in MX:                                       # sum_j |C_q[j]| delta(i, j)
                 Xq = torch.from_numpy(np.ascontiguousarray(read_delta(m, scales[m], 64, 128)))
                 read = read + torch.einsum("bhij,tbhj->tbhi", Xq, Cabs).numpy()
             bound = dec[..., None] * read + TOL * scale[None, :, :, None]
@@ -383,7 +457,7 @@ COPY_VERIFY_SHAPES = {
 
 @pytest.mark.parametrize("T", [3, 8])
 @pytest.mark.parametrize("tile", list(COPY_VERIFY_SHAPES))
-@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4"])
+@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4", "mxfp8"])
 def test_copy_verify_rounds(copy, tile, T):
     """Speculative rounds (verify + commit) with a read copy against the same
     rounds in FP32-only mode, on the same GPU: the FP32 checkpoint and ring
@@ -414,7 +488,7 @@ def test_copy_verify_rounds(copy, tile, T):
             ys.append(host(y).copy())
             hs.append(host(st.ckpt).astype(np.float64))
             metas.append(host(st.meta).copy())
-            if mode in ("e4m3", "mxfp4"):
+            if mode in ("e4m3",) + MX:
                 scs.append(host(st.ckpt_scale).copy())
         torch.cuda.synchronize()
         assert int(host(st.status)[0]) == 0
@@ -449,7 +523,7 @@ def test_copy_verify_rounds(copy, tile, T):
                 read = UNIT[copy] * np.einsum("hij,hj->hi", Hs, Cq)
                 if copy == "e4m3":
                     read = read + (scc[r][b] * 2.0 ** -10 * 1.001)[:, None] * Cq.sum(-1)[:, None]
-                elif copy == "mxfp4":
+                elif copy in MX:
                     read = read + np.einsum("hij,hj->hi", read_delta(copy, scc[r][b], 0, 0), Cq)
                 bound = np.exp(A * d_run)[:, None] * read * 1.001 + 1e-6 * scale[b][:, None]
                 ratio = float((diff / bound).max())
