@@ -54,6 +54,7 @@ extern "C" {
 #define RSSM_MXFP4 4    /* OCP MX FP4: E2M1 codes, one E8M0 scale per 32 consecutive dstate elements */
 #define RSSM_MXFP8 5    /* MX FP8: e4m3fn codes, one E8M0 scale per 32 consecutive dstate elements,
                            chosen so that no element saturates (smallest X with max |v| / X <= 448) */
+#define RSSM_F16 6      /* IEEE binary16 (the checkpoint, written with stochastic rounding) */
 
 /* Return codes. */
 #define RSSM_OK 0
@@ -81,6 +82,14 @@ typedef struct {
     int32_t in_dtype;   /* RSSM_F32 or RSSM_BF16: tokens x, B, C and the x/B records */
     int32_t read_copy;  /* RSSM_NONE, RSSM_BF16, RSSM_FP8_E4M3, RSSM_MXFP4 or RSSM_MXFP8 (the MX modes
                            need dstate % 32 == 0) */
+    int32_t ckpt_dtype; /* RSSM_F32 (0): FP32 checkpoint.  RSSM_F16: half-precision recurrence
+                           checkpoint (blog section "Benefit 3": an FP16 recurrence with stochastic
+                           rounding tracks FP32): each flush computes the new state in fp32
+                           registers, writes it to fp16 with stochastic rounding (see
+                           rssm_params.sr_seed) and casts the read copy from the same registers;
+                           non-flush calls read the fp16 checkpoint itself when read_copy is
+                           RSSM_NONE.  With RSSM_F16, read_copy must be RSSM_NONE or RSSM_MXFP4
+                           (else RSSM_ERR_DTYPE).  The conventional entry points need RSSM_F32. */
 } rssm_config;
 
 /*
@@ -92,7 +101,8 @@ typedef struct {
  * only the copies of the heads it owns and never waits on another workgroup.
  */
 typedef struct {
-    float *ckpt;        /* [batch][nheads][headdim][dstate] fp32 checkpoint H_s */
+    void *ckpt;         /* [batch][nheads][headdim][dstate] checkpoint H_s: fp32, or fp16 bits with
+                           ckpt_dtype == RSSM_F16 */
     void *ckpt_read;    /* same layout in read_copy's type; NULL iff read_copy == RSSM_NONE.
                            MXFP4: [batch][nheads][headdim][dstate/2] bytes, two E2M1 codes per
                            byte, the lower column in the low nibble; MXFP8: one e4m3 byte per
@@ -118,8 +128,16 @@ typedef struct {
 } rssm_tokens;
 
 typedef struct {
-    const float *A; /* [nheads], negative */
-    const float *D; /* [nheads] skip */
+    const float *A;   /* [nheads], negative */
+    const float *D;   /* [nheads] skip */
+    uint64_t sr_seed; /* RSSM_F16 checkpoint only: key of this call's rounding.  A flush rounds
+                         checkpoint element 4v + e (row-major over the whole array) away from zero
+                         iff its distance above the fp16 value below it, in units of their
+                         spacing and taken to 13 bits, plus the low 13 bits of word e of
+                         Philox4x32-10 (Salmon et al., SC 2011) at counter (v low 32 bits, v high
+                         32 bits, 0, 0) under key (sr_seed low, sr_seed high) reaches 2^13.  Pass a
+                         new value on every call (a step counter will do), or flushes reuse the
+                         same random words; |v| >= 65504 saturates, NaN stays NaN. */
 } rssm_params;
 
 /* Buffers of rssm_state, in the order of replayssm_sizes(). */

@@ -19,7 +19,7 @@ LIBRARY = PKG / "libreplayssm.so"
 OBJDIR = PKG / "_build"
 
 ARCH = "gfx950"
-SOURCES = ["replay.hip", "conventional.hip", "probe.hip", "api.cpp"]
+SOURCES = ["replay.hip", "replay_f16.hip", "conventional.hip", "probe.hip", "api.cpp"]
 
 # Packed fp32 instructions are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -40,7 +40,7 @@ def _compile(src: Path, obj: Path, extra: list[str]) -> None:
         raise RuntimeError(f"hipcc failed for {src.name}:\n{proc.stderr}")
 
 
-def build(extra: list[str] | None = None, jobs: int = 4) -> Path:
+def build(extra: list[str] | None = None, jobs: int = 5) -> Path:
     """Compile every source and link libreplayssm.so; returns its path."""
     extra = list(extra or [])
     OBJDIR.mkdir(exist_ok=True)

@@ -17,7 +17,7 @@ import torch
 PKG = Path(__file__).resolve().parent
 LIBRARY = PKG / "libreplayssm.so"
 
-RSSM_F32, RSSM_BF16, RSSM_FP8_E4M3, RSSM_NONE, RSSM_MXFP4, RSSM_MXFP8 = 0, 1, 2, 3, 4, 5
+RSSM_F32, RSSM_BF16, RSSM_FP8_E4M3, RSSM_NONE, RSSM_MXFP4, RSSM_MXFP8, RSSM_F16 = 0, 1, 2, 3, 4, 5, 6
 RSSM_FLUSH_FORCE_CAST = 1
 RSSM_STATUS_META, RSSM_STATUS_ACCEPT, RSSM_STATUS_SLOT = 1, 2, 4
 RSSM_MAX_DRAFTS, RSSM_MAX_WINDOW = 8, 64
@@ -25,9 +25,9 @@ RSSM_MAX_DRAFTS, RSSM_MAX_WINDOW = 8, 64
 NUM_BUFS = 7
 
 _DTYPES = {"f32": RSSM_F32, "bf16": RSSM_BF16, "e4m3": RSSM_FP8_E4M3, None: RSSM_NONE,
-           "none": RSSM_NONE, "mxfp4": RSSM_MXFP4, "mxfp8": RSSM_MXFP8}
+           "none": RSSM_NONE, "mxfp4": RSSM_MXFP4, "mxfp8": RSSM_MXFP8, "f16": RSSM_F16}
 _TORCH = {RSSM_F32: torch.float32, RSSM_BF16: torch.bfloat16, RSSM_FP8_E4M3: torch.uint8,
-          RSSM_MXFP4: torch.uint8, RSSM_MXFP8: torch.uint8}
+          RSSM_MXFP4: torch.uint8, RSSM_MXFP8: torch.uint8, RSSM_F16: torch.float16}
 
 
 def _copy_shapes(rc, b, nh, hd, ds):
@@ -44,7 +44,7 @@ def _copy_shapes(rc, b, nh, hd, ds):
 class rssm_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "nheads", "headdim", "dstate", "ngroups", "window", "max_drafts",
-        "in_dtype", "read_copy")]
+        "in_dtype", "read_copy", "ckpt_dtype")]
 
 
 class rssm_state(ctypes.Structure):
@@ -60,7 +60,7 @@ class rssm_tokens(ctypes.Structure):
 
 
 class rssm_params(ctypes.Structure):
-    _fields_ = [("A", ctypes.c_void_p), ("D", ctypes.c_void_p)]
+    _fields_ = [("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("sr_seed", ctypes.c_uint64)]
 
 
 _LIB = None
@@ -94,6 +94,8 @@ _SIGS = {
     "rssm_probe_sink_elems": (ctypes.c_size_t, [ctypes.c_size_t]),
     "rssm_probe_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "rssm_probe_copy": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "rssm_probe_sr_f16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint64,
+                                         ctypes.c_uint64, ctypes.c_void_p]),
 }
 
 
@@ -137,6 +139,7 @@ class Config:
     max_drafts: int = 1
     in_dtype: str = "bf16"       # "f32" or "bf16"
     read_copy: str | None = None  # None, "bf16", "e4m3", "mxfp4" or "mxfp8"
+    ckpt_dtype: str = "f32"       # "f32", or "f16": FP16 checkpoint written with stochastic rounding
 
     @property
     def cap(self) -> int:
@@ -149,7 +152,11 @@ class Config:
     def c(self) -> rssm_config:
         return rssm_config(self.batch, self.nheads, self.headdim, self.dstate, self.ngroups,
                            self.window, self.max_drafts, _DTYPES[self.in_dtype],
-                           _DTYPES[self.read_copy])
+                           _DTYPES[self.read_copy], _DTYPES[self.ckpt_dtype])
+
+    @property
+    def ckpt_torch(self) -> torch.dtype:
+        return _TORCH[_DTYPES[self.ckpt_dtype]]
 
 
 def _ptr(t):
@@ -192,7 +199,7 @@ class State:
         rc = _DTYPES[cfg.read_copy]
         read_shape, scale = _copy_shapes(rc, b, nh, hd, ds)
         st = cls(
-            ckpt=z((b, nh, hd, ds), torch.float32),
+            ckpt=z((b, nh, hd, ds), cfg.ckpt_torch),
             ckpt_read=None if rc == RSSM_NONE else z(read_shape, _TORCH[rc]),
             ckpt_scale=z(*scale) if scale else None,
             buf_x=z((b, nh, cap, hd), cfg.in_torch),
@@ -210,7 +217,7 @@ class State:
     def validate(self, cfg: Config):
         b, nh, hd, ds, ng, cap = cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.cap
         dev = self.ckpt.device
-        _expect("ckpt", self.ckpt, (b, nh, hd, ds), torch.float32, dev)
+        _expect("ckpt", self.ckpt, (b, nh, hd, ds), cfg.ckpt_torch, dev)
         rc = _DTYPES[cfg.read_copy]
         if rc == RSSM_NONE:
             if self.ckpt_read is not None or self.ckpt_scale is not None:
@@ -262,13 +269,14 @@ class Tokens:
 class Params:
     A: torch.Tensor
     D: torch.Tensor
+    sr_seed: int = 0    # FP16 checkpoint: key of the call's stochastic rounding (vary it per call)
 
     def validate(self, cfg: Config, device):
         _expect("A", self.A, (cfg.nheads,), torch.float32, device)
         _expect("D", self.D, (cfg.nheads,), torch.float32, device)
 
     def c(self) -> rssm_params:
-        return rssm_params(_ptr(self.A), _ptr(self.D))
+        return rssm_params(_ptr(self.A), _ptr(self.D), int(self.sr_seed) & 0xFFFFFFFFFFFFFFFF)
 
 
 def _stream(stream):
@@ -399,6 +407,17 @@ def rssm_probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
     if dst.numel() * dst.element_size() != nbytes or not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("dst and src must be contiguous and the same size")
     _check("rssm_probe_copy", lib().rssm_probe_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)))
+
+
+def rssm_probe_sr_f16(src: torch.Tensor, dst: torch.Tensor, vec0: int, seed: int, stream=None) -> None:
+    """dst (fp16) = the FP16 checkpoint flush's stochastic rounding of src (fp32),
+    value i with the random word of checkpoint vector vec0 + i // 4."""
+    if src.dtype != torch.float32 or dst.dtype != torch.float16 or src.numel() != dst.numel():
+        raise ValueError("src fp32 and dst fp16 of the same size")
+    if not (src.is_contiguous() and dst.is_contiguous()) or src.device.type != "cuda":
+        raise ValueError("contiguous GPU tensors required")
+    _check("rssm_probe_sr_f16", lib().rssm_probe_sr_f16(_ptr(src), _ptr(dst), src.numel(), int(vec0), int(seed),
+                                                        _stream(stream)))
 
 
 def probe_sink_elems(nbytes: int) -> int:

@@ -50,6 +50,11 @@ int check_config(const rssm_config* c, bool need_window) {
             c->read_copy != RSSM_MXFP4 && c->read_copy != RSSM_MXFP8)
             return fail(RSSM_ERR_DTYPE,
                         "read_copy must be RSSM_NONE, RSSM_BF16, RSSM_FP8_E4M3, RSSM_MXFP4 or RSSM_MXFP8");
+        if (c->ckpt_dtype != RSSM_F32 && c->ckpt_dtype != RSSM_F16)
+            return fail(RSSM_ERR_DTYPE, "ckpt_dtype must be RSSM_F32 or RSSM_F16");
+        if (c->ckpt_dtype == RSSM_F16 && c->read_copy != RSSM_NONE && c->read_copy != RSSM_MXFP4)
+            return fail(RSSM_ERR_DTYPE,
+                        "an RSSM_F16 checkpoint is read directly (RSSM_NONE) or through an RSSM_MXFP4 copy");
         if ((c->read_copy == RSSM_MXFP4 || c->read_copy == RSSM_MXFP8) && c->dstate % 32 != 0)
             return fail(RSSM_ERR_SHAPE, "the MX read copies need dstate %% 32 == 0 (blocks of 32 columns), got %d",
                         c->dstate);
@@ -62,6 +67,7 @@ int check_config(const rssm_config* c, bool need_window) {
 }
 
 int read_mode(const rssm_config* c) {
+    if (c->ckpt_dtype == RSSM_F16 && c->read_copy == RSSM_NONE) return rssm::READ_F16;
     return c->read_copy == RSSM_BF16       ? rssm::READ_BF16
            : c->read_copy == RSSM_FP8_E4M3 ? rssm::READ_E4M3
            : c->read_copy == RSSM_MXFP4    ? rssm::READ_MXFP4
@@ -103,7 +109,8 @@ int check_tokens(const rssm_tokens* t, const rssm_params* p, const float* y, int
 rssm::ReplayArgs replay_args(const rssm_config* c, const rssm_state* s, const rssm_params* p) {
     rssm::ReplayArgs a;
     std::memset(&a, 0, sizeof a);
-    a.ckpt = s->ckpt;
+    a.ckpt = static_cast<float*>(s->ckpt);
+    a.ckpt16 = c->ckpt_dtype == RSSM_F16;
     a.ckpt_read = s->ckpt_read;
     a.ckpt_scale = static_cast<float*>(s->ckpt_scale);
     a.buf_x = s->buf_x;
@@ -113,6 +120,7 @@ rssm::ReplayArgs replay_args(const rssm_config* c, const rssm_state* s, const rs
     a.status = s->status;
     a.A = p ? p->A : nullptr;
     a.D = p ? p->D : nullptr;
+    a.sr_seed = p ? p->sr_seed : 0;
     a.batch = c->batch;
     a.nheads = c->nheads;
     a.ngroups = c->ngroups;
@@ -168,7 +176,7 @@ int replayssm_sizes(const rssm_config* c, size_t bytes[RSSM_NUM_BUFS]) {
     const size_t tile = (size_t)c->headdim * c->dstate;
     const size_t cap = (size_t)(c->window + 2 * c->max_drafts - 1);
     const size_t in_bytes = c->in_dtype == RSSM_BF16 ? 2 : 4;
-    bytes[RSSM_BUF_CKPT] = tiles * tile * 4;
+    bytes[RSSM_BUF_CKPT] = tiles * tile * (c->ckpt_dtype == RSSM_F16 ? 2 : 4);
     bytes[RSSM_BUF_CKPT_READ] = c->read_copy == RSSM_BF16       ? tiles * tile * 2
                                 : c->read_copy == RSSM_FP8_E4M3 ? tiles * tile
                                 : c->read_copy == RSSM_MXFP8    ? tiles * tile
@@ -263,6 +271,7 @@ int conventional_state_update(const rssm_config* cfg, float* states, int32_t nsl
                               void* stream) {
     int rc = check_config(cfg, false);
     if (rc) return rc;
+    if (cfg->ckpt_dtype != RSSM_F32) return fail(RSSM_ERR_DTYPE, "the conventional state is fp32 (ckpt_dtype RSSM_F32)");
     if (cfg->batch == 0) return RSSM_OK;
     if (!states) return fail(RSSM_ERR_NULL, "states is NULL");
     if (!aligned(states, 16)) return fail(RSSM_ERR_SHAPE, "states must be 16-byte aligned");

@@ -10,6 +10,7 @@ namespace rssm {
 // Native 16-byte vector types (usable with the nontemporal builtins).
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Tile geometry.
@@ -273,6 +274,79 @@ __device__ __forceinline__ void widen16(const uint4 v, float* out) {
             out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
     }
+}
+
+
+// ---- FP16 checkpoint with stochastic rounding ---------------------------------------
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of two 32 x 32 -> 64-bit products
+// mixing a 128-bit counter under a 64-bit key that is bumped by the Weyl
+// constants between rounds; 4 x 32 random bits per (counter, key).
+struct U32x4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U32x4 philox4x32_10(U32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        c = U32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    }
+    return c;
+}
+
+// fp32 -> fp16 bits with stochastic rounding: |v| goes to the fp16 value above
+// it with probability equal to its distance from the fp16 value below it, in
+// units of their spacing, decided by 13 random bits r (the low 13 bits used):
+// away from zero iff distance * 2^13 + r >= 2^13.  In the fp16 normal range
+// the distance is exactly a 13-bit number (the fp32 mantissa bits below the
+// fp16 ones), so adding r there and truncating is the whole rounding; below
+// 2^-14 (spacing 2^-24) the distance is first truncated to 13 bits.  |v| >=
+// 65504 and infinities give +-65504; a NaN stays a NaN.
+__device__ __forceinline__ uint32_t f32_to_f16_sr(float v, uint32_t r) {
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t sign = (b >> 16) & 0x8000u;
+    const uint32_t u = b & 0x7FFFFFFFu;
+    const uint32_t r13 = r & 0x1FFFu;
+    uint32_t h;
+    if (u > 0x7F800000u) {
+        h = 0x7E00u;                                        // NaN
+    } else if (u >= 0x38800000u) {                          // |v| >= 2^-14
+        const uint32_t t = (u + r13) & ~0x1FFFu;            // on the fp16 grid, possibly one binade up
+        h = t >= 0x477FE000u ? 0x7BFFu : (t >> 13) - ((127u - 15u) << 10);
+    } else {
+        const float w = __uint_as_float(u) * 16777216.0f;    // |v| / 2^-24, exact
+        const uint32_t a = (uint32_t)w;
+        const uint32_t d = (uint32_t)((w - (float)a) * 8192.0f);
+        h = a + ((d + r13) >> 13);                          // at most 0x400, the smallest normal
+    }
+    return sign | h;
+}
+
+// Four consecutive fp32 values of the checkpoint, vector index vi (4 columns
+// each, row-major over the whole [batch][nheads][headdim][dstate] array), to
+// fp16 with stochastic rounding: the random words are Philox4x32-10 of the
+// counter (vi low, vi high, 0, 0) under the key (seed low, seed high), word e
+// for column e of the vector.
+__device__ __forceinline__ uint2 f32x4_to_f16x4_sr(const v4f f, uint64_t vi, uint64_t seed) {
+    const U32x4 r = philox4x32_10(U32x4{(uint32_t)vi, (uint32_t)(vi >> 32), 0u, 0u}, (uint32_t)seed,
+                                  (uint32_t)(seed >> 32));
+    return make_uint2(f32_to_f16_sr(f.x, r.x) | (f32_to_f16_sr(f.y, r.y) << 16),
+                      f32_to_f16_sr(f.z, r.z) | (f32_to_f16_sr(f.w, r.w) << 16));
+}
+
+// fp16 bits (low / high half of a word) to fp32, exact.
+__device__ __forceinline__ float f16lo_to_f32(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16hi_to_f32(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
 }  // namespace rssm

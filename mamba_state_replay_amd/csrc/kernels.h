@@ -9,7 +9,8 @@ namespace rssm {
 
 enum Mode : int32_t { MODE_DECODE = 0, MODE_VERIFY = 1, MODE_FLUSH = 2 };
 enum InType : int32_t { IN_F32 = 0, IN_BF16 = 1 };
-enum ReadMode : int32_t { READ_F32 = 0, READ_BF16 = 1, READ_E4M3 = 2, READ_MXFP4 = 3, READ_MXFP8 = 4 };
+// READ_F16: the FP16 checkpoint read directly (no copy).
+enum ReadMode : int32_t { READ_F32 = 0, READ_BF16 = 1, READ_E4M3 = 2, READ_MXFP4 = 3, READ_MXFP8 = 4, READ_F16 = 5 };
 
 constexpr uint32_t kStatusMeta = 1u;
 constexpr uint32_t kStatusAccept = 2u;
@@ -17,7 +18,7 @@ constexpr uint32_t kStatusSlot = 4u;
 constexpr int32_t kFlushForceCast = 1;
 
 struct ReplayArgs {
-    float* ckpt;
+    float* ckpt;        // fp32, or fp16 bits when ckpt16
     void* ckpt_read;
     float* ckpt_scale;
     void* buf_x;
@@ -36,6 +37,8 @@ struct ReplayArgs {
     int32_t batch, nheads, ngroups;
     int32_t L, cap, T, T_prev;
     int32_t mode, flags;
+    int32_t ckpt16;     // the checkpoint is FP16, written with stochastic rounding
+    uint64_t sr_seed;   // key of the rounding's random words for this call
 };
 
 struct ConvArgs {
@@ -69,6 +72,7 @@ size_t conventional_lds_bytes(int hd, int ds, int T);
 bool shape_supported(int hd, int ds);
 hipError_t launch_replay(const ReplayArgs& a, int hd, int ds, int in_type, int read_mode,
                          hipStream_t stream);
+hipError_t launch_replay_f16(const ReplayArgs& a, int hd, int ds, int in_type, int read_mode, hipStream_t stream);
 hipError_t launch_conventional(const ConvArgs& a, int hd, int ds, int in_type, hipStream_t stream);
 hipError_t launch_replay_commit(const CommitArgs& a, hipStream_t stream);
 hipError_t launch_conventional_commit(const CommitArgs& a, hipStream_t stream);

@@ -67,20 +67,21 @@ def params(work: synth.Workload, device) -> rb.Params:
 
 
 def config(shape: synth.LayerShape, in_dtype="bf16", read_copy=None, window=None,
-           max_drafts=None) -> rb.Config:
+           max_drafts=None, ckpt_dtype="f32") -> rb.Config:
     return rb.Config(shape.batch, shape.nheads, shape.headdim, shape.dstate, shape.ngroups,
                      window if window is not None else shape.window,
                      max_drafts if max_drafts is not None else shape.max_drafts,
-                     in_dtype, read_copy)
+                     in_dtype, read_copy, ckpt_dtype)
 
 
 def replay_state(cfg: rb.Config, work: synth.Workload, device) -> rb.State:
     """State with ckpt = h0 and the n0[b] pre-committed records in slots 0..n0[b]-1
-    (ring pointer {0, n0[b]} in every head's copy)."""
+    (ring pointer {0, n0[b]} in every head's copy).  An FP16 checkpoint holds h0
+    rounded to the nearest fp16."""
     if int(work.n0.max(initial=0)) > cfg.cap:
         raise ValueError("pre-committed records exceed the ring capacity")
     st = rb.State.allocate(cfg, device)
-    st.ckpt.copy_(torch.from_numpy(work.h0.astype(np.float32)))
+    st.ckpt.copy_(torch.from_numpy(work.h0.astype(np.float32)).to(st.ckpt.dtype))
     npre = work.pre.steps
     if npre:
         b, nh, hd, ds, ng, cap = cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.cap

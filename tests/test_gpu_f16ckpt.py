@@ -1,0 +1,243 @@
+"""GPU tests of the FP16 recurrence checkpoint written with stochastic rounding
+(NVIDIA Developer blog "ReplaySSM: Rethinking State Storage for Faster
+Hybrid-Model Decoding", section "Benefit 3: Limit error accumulation with
+separate precisions": an FP16 recurrence with stochastic rounding tracks FP32).
+
+* the kernel's rounding, through the probe entry point, equals the host
+  definition (oracle/sr.py) bit for bit;
+* a flush writes the stochastic rounding of the exact fold: the same fp16
+  value as the oracle for all but the elements whose fp32 value sits at a
+  rounding threshold, and there a neighbouring one;
+* non-flush outputs read the fp16 checkpoint: they equal the oracle stepped
+  from the kernel's own checkpoint to the FP32 tolerance;
+* with an MXFP4 read copy the fp16 checkpoints are bit-identical to a run
+  without one, and the outputs stay within the copy's read bound;
+* where every flush moves the state by less than half an fp16 spacing,
+  round-to-nearest stagnates while the stochastic checkpoint tracks the
+  exact state (mean error near zero).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from mamba_state_replay_amd import binding as rb
+from mamba_state_replay_amd import staging, synth
+from oracle import oracle as orc_mod
+from oracle import sr
+from tests import formats
+from tests.gpu_util import TOL, assert_rows_close, device, host, say
+
+pytestmark = pytest.mark.gpu
+
+NEMO = dict(nheads=128, headdim=64, dstate=128, ngroups=8)
+
+
+def _bits_equal(gpu_f16: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """fp16 results equal to float64 references on the fp16 grid (NaN == NaN)."""
+    want = ref.astype(np.float16)
+    same = gpu_f16.view(np.uint16) == want.view(np.uint16)
+    return same | (np.isnan(gpu_f16) & np.isnan(ref))
+
+
+def test_sr_probe_matches_host_definition():
+    dev = device()
+    g = np.random.default_rng(41)
+    n = 1 << 22
+    parts = [
+        np.exp(g.uniform(np.log(2.0 ** -14), np.log(65504.0), n // 2)),          # fp16 normal range
+        g.uniform(0, 2.0 ** -14, n // 8),                                          # fp16 subnormal range
+        np.exp(g.uniform(-120, -30, n // 16)),                                     # far below
+        g.uniform(60000, 70000, n // 16),                                          # saturation
+        np.arange(1 << 16, dtype=np.uint16).view(np.float16).astype(np.float64),  # the fp16 grid
+        [0.0, -0.0, np.inf, -np.inf, np.nan, 65504.0, 2.0 ** -14, 2.0 ** -24, 1.5 * 2.0 ** -24],
+    ]
+    v = np.concatenate([np.asarray(p, np.float64) for p in parts])
+    v = (v * g.choice([-1.0, 1.0], v.size)).astype(np.float32)
+    v = np.concatenate([v, g.standard_normal((-v.size) % 4).astype(np.float32)])
+    seed = int(g.integers(0, 2 ** 63))
+    vec0 = (1 << 33) + 12345                                                       # high counter word in use
+    src = torch.from_numpy(v).to(dev)
+    dst = torch.empty(v.size, dtype=torch.float16, device=dev)
+    say(f"sr probe, {v.size} values")
+    rb.rssm_probe_sr_f16(src, dst, vec0, seed)
+    torch.cuda.synchronize()
+    want = sr.f16_sr(v, sr.words(np.arange(v.size, dtype=np.uint64) + np.uint64(4 * vec0), seed))
+    ok = _bits_equal(host(dst), want)
+    if not ok.all():
+        i = np.flatnonzero(~ok)[:5]
+        print(f"[gpu] mismatches at {v[i]} -> got {host(dst)[i]} want {want[i]}", flush=True)
+    assert ok.all(), f"{int((~ok).sum())} values rounded differently"
+
+
+def _f16_work(shape, steps, seed, n0, in_dtype="bf16"):
+    """A workload whose initial checkpoint is on the fp16 grid (the values the
+    FP16 state holds), so the oracle starts from exactly what the GPU holds."""
+    work = synth.decode_workload(shape, steps, seed=seed, in_dtype=in_dtype, n0=n0)
+    return dataclasses.replace(work, h0=work.h0.astype(np.float16).astype(np.float32))
+
+
+def test_flush_writes_the_stochastic_rounding_of_the_fold():
+    dev = device()
+    shape = synth.LayerShape(batch=3, window=16, **NEMO)
+    work = _f16_work(shape, 0, 1020, n0=7)
+    cfg = staging.config(shape, ckpt_dtype="f16")
+    st = staging.replay_state(cfg, work, dev)
+    seed = 0x5EED0000F16
+    p = dataclasses.replace(staging.params(work, dev), sr_seed=seed)
+    say("f16 checkpoint flush, 7 records")
+    rb.replayssm_flush(cfg, st, p)
+    torch.cuda.synchronize()
+    got = host(st.ckpt)
+    exact = orc_mod.committed_state(work)
+    want = sr.sr_checkpoint(exact, seed)
+    same = _bits_equal(got, want)
+    # every element is one of the fp16 neighbours of its fp32 fold: within one spacing (the larger of
+    # the two binades' at a binade edge) of the exact value, plus the fp32 fold's own error (1e-6 of
+    # the tile's largest magnitude covers it; it matters only where the fold cancels to near zero)
+    g64 = got.astype(np.float64)
+    spacing = np.maximum(sr.f16_grid(np.abs(exact))[1], sr.f16_grid(np.abs(g64))[1])
+    slack = 1e-6 * np.abs(exact).max(axis=(-1, -2), keepdims=True)
+    dev_ = np.abs(g64 - exact) - spacing - slack
+    print(f"[gpu] f16 flush: {same.mean():.6f} of elements equal the oracle's rounding; "
+          f"largest excess over one spacing {dev_.max():.3g}", flush=True)
+    if (dev_ > 0).any():
+        i = np.unravel_index(np.argmax(dev_), dev_.shape)
+        print(f"[gpu] worst element {i}: got {g64[i]!r} exact {exact[i]!r} oracle {want[i]!r}", flush=True)
+    assert (dev_ <= 0).all(), "an element left the fp16 neighbours of its fold"
+    assert same.mean() >= 0.999
+    assert np.all(host(st.meta)[:, :, 1] == 0)
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+def test_decode_reads_the_f16_checkpoint(in_dtype):
+    """Non-flush outputs from the kernel's own fp16 checkpoint (snapshotted
+    after every flush) stepped by the oracle, to the FP32 tolerance."""
+    dev = device()
+    L, steps = 8, 40
+    shape = synth.LayerShape(batch=4, window=L, **NEMO)
+    work = _f16_work(shape, steps, 1021, n0=L, in_dtype=in_dtype)
+    cfg = staging.config(shape, in_dtype=in_dtype, ckpt_dtype="f16")
+    st = staging.replay_state(cfg, work, dev)
+    p = staging.params(work, dev)
+    toks = staging.TokenStream(work.steps, dev)
+    y = torch.empty((steps, 4, 1, 128, 64), device=dev)
+    snaps = {}
+    say(f"f16 checkpoint decode, {in_dtype} inputs, {steps} steps")
+    for t in range(steps):
+        p.sr_seed = 1000 + t
+        rb.replayssm_decode_step(cfg, st, p, toks.call(t), y[t])
+        if t % L == 0:                                    # steps 0, L, 2L ... flush first
+            snaps[t] = host(st.ckpt).astype(np.float64)
+    torch.cuda.synchronize()
+    yg = host(y)[:, :, 0]
+    tok = work.steps
+    got, ref = [], []
+    for tf, Hs in snaps.items():
+        t1 = min(tf + L, steps)
+        _, yr = orc_mod.conventional(Hs, tok.x[tf:t1], tok.B[tf:t1], tok.C[tf:t1], tok.dt[tf:t1], work.A, work.D)
+        got.append(yg[tf + 1:t1])                         # the non-flush steps of the window
+        ref.append(yr[1:])
+    assert_rows_close(np.concatenate(got), np.concatenate(ref), what="f16-checkpoint non-flush outputs")
+
+
+def test_mxfp4_copy_over_an_f16_checkpoint():
+    """FP16 recurrence + MXFP4 read copy: the checkpoints are bit-identical to
+    an FP16 run without a copy (same seeds); non-flush outputs differ from that
+    run by the copy's read error alone, within d_q sum_j |C_q[j]| (|H_s| / 4 +
+    X / 4 + one fp16 spacing of H_s) per element (the copy is cast from the
+    fp32 registers, H_s is their stochastic rounding)."""
+    dev = device()
+    L, steps = 8, 40
+    shape = synth.LayerShape(batch=3, window=L, **NEMO)
+    work = _f16_work(shape, steps, 1022, n0=L)
+    p = staging.params(work, dev)
+    toks = staging.TokenStream(work.steps, dev)
+    runs = {}
+    for copy in (None, "mxfp4"):
+        cfg = staging.config(shape, read_copy=copy, ckpt_dtype="f16")
+        st = staging.replay_state(cfg, work, dev)       # step 0 flushes the L records and casts the copy
+        y = torch.empty((steps, 3, 1, 128, 64), device=dev)
+        hs, scs = {}, {}
+        say(f"f16 checkpoint + {copy} copy, {steps} steps")
+        for t in range(steps):
+            p.sr_seed = 7000 + t
+            rb.replayssm_decode_step(cfg, st, p, toks.call(t), y[t])
+            if t % L == 0:
+                hs[t] = host(st.ckpt).astype(np.float64)
+                if copy:
+                    scs[t] = host(st.ckpt_scale)
+        torch.cuda.synchronize()
+        runs[copy] = (host(y)[:, :, 0].astype(np.float64), hs, scs)
+    y16, h16, _ = runs[None]
+    yc, hc, scc = runs["mxfp4"]
+    for t in h16:
+        assert np.array_equal(h16[t], hc[t]), f"step {t}: the copy changed the fp16 recurrence"
+    A = work.A.astype(np.float64)
+    hpg = shape.nheads // shape.ngroups
+    worst = 0.0
+    for tf in h16:
+        Hs = np.abs(h16[tf])
+        _, sp = sr.f16_grid(Hs)
+        X = np.repeat(formats.e8m0_value(scc[tf]), 32, axis=-1)
+        term = Hs / 4 + X / 4 * 1.001 + sp
+        for t in range(tf + 1, min(tf + L, steps)):
+            dec = np.exp(A[None, :] * work.steps.dt[tf:t + 1].astype(np.float64).sum(0))
+            Cg = np.repeat(np.abs(work.steps.C[t].astype(np.float64)), hpg, axis=1)
+            bound = dec[:, :, None] * np.einsum("bhij,bhj->bhi", term, Cg) + 1e-5
+            worst = max(worst, float((np.abs(yc[t] - y16[t]) / bound).max()))
+    print(f"[gpu] f16 + mxfp4: worst error/bound {worst:.3f}", flush=True)
+    assert worst <= 1.0
+
+
+def test_stochastic_rounding_tracks_where_nearest_stagnates():
+    """Slow decay (A = -1e-4) and small inputs: every flush moves the state by
+    less than half an fp16 spacing.  Round-to-nearest (emulated on the host,
+    window by window from the exact fold) keeps the initial values; the GPU's
+    stochastic checkpoint follows the exact fp64 state with a mean error (over
+    all elements) near zero."""
+    dev = device()
+    L, windows = 16, 64
+    steps = L * windows
+    b, nh, hd, ds, ng = 1, 8, 64, 128, 8
+    g = np.random.default_rng(43)
+    h0 = g.uniform(1.0, 1.9, (b, nh, hd, ds)).astype(np.float16).astype(np.float32)
+    x = (0.01 * g.standard_normal((steps, b, nh, hd))).astype(np.float32)
+    B = (0.01 * g.standard_normal((steps, b, ng, ds))).astype(np.float32)
+    C = g.standard_normal((steps, b, ng, ds)).astype(np.float32)
+    dt = np.full((steps, b, nh), 0.13, np.float32)
+    A = np.full(nh, -1e-4, np.float32)
+    D = np.zeros(nh, np.float32)
+    cfg = rb.Config(b, nh, hd, ds, ng, window=L, max_drafts=1, in_dtype="f32", ckpt_dtype="f16")
+    st = rb.State.allocate(cfg, dev)
+    st.ckpt.copy_(torch.from_numpy(h0).half())
+    p = rb.Params(torch.from_numpy(A).to(dev), torch.from_numpy(D).to(dev))
+    xs, Bs, Cs, dts = (torch.from_numpy(a).to(dev) for a in (x, B, C, dt))
+    y = torch.empty((b, 1, nh, hd), device=dev)
+    say(f"f16 stagnation case, {steps} steps")
+    for t in range(steps):
+        p.sr_seed = 90000 + t
+        rb.replayssm_decode_step(cfg, st, p, rb.Tokens(xs[t:t + 1].transpose(0, 1).contiguous(),
+                                                       Bs[t:t + 1].transpose(0, 1).contiguous(),
+                                                       Cs[t:t + 1].transpose(0, 1).contiguous(),
+                                                       dts[t:t + 1].transpose(0, 1).contiguous()), y)
+    p.sr_seed = 99999
+    rb.replayssm_flush(cfg, st, p)                        # fold the last window
+    torch.cuda.synchronize()
+    got = host(st.ckpt).astype(np.float64)
+    orc = orc_mod.default()
+    exact, _ = orc.conventional(h0, x, B, C, dt, A, D, outputs=False)
+    rn = h0.astype(np.float64)
+    for w in range(windows):
+        s = slice(w * L, (w + 1) * L)
+        rn, _ = orc.conventional(rn, x[s], B[s], C[s], dt[s], A, D, outputs=False)
+        rn = rn.astype(np.float16).astype(np.float64)     # round to nearest
+    _, sp = sr.f16_grid(np.abs(exact))
+    e_sr = (got - exact) / sp
+    e_rn = (rn - exact) / sp
+    print(f"[gpu] stagnation: mean error in fp16 spacings: stochastic {e_sr.mean():+.3f} (rms {np.sqrt((e_sr ** 2).mean()):.2f}), "
+          f"nearest {e_rn.mean():+.2f}", flush=True)
+    assert abs(e_rn.mean()) > 10                          # the case does stagnate under nearest rounding
+    assert abs(e_sr.mean()) < 0.25
+    assert np.sqrt((e_sr ** 2).mean()) < 6
