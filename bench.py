@@ -31,7 +31,8 @@ sys.path.insert(0, str(ROOT))
 METRIC = "Mamba-2 layer decode-step µs + achieved HBM GB/s at batch 256, L=16"
 PEAK_GBS = 8000.0
 COUNTERS = ROOT / "profiles" / "replay_decode_batch256_L16_counters.json"
-KERNEL_SOURCES = ["mamba_state_replay_amd/csrc/replay.hip", "mamba_state_replay_amd/csrc/common.h"]
+KERNEL_SOURCES = ["mamba_state_replay_amd/csrc/replay.hip", "mamba_state_replay_amd/csrc/replay_impl.h",
+                  "mamba_state_replay_amd/csrc/common.h"]
 
 
 def source_hash(paths) -> str:
@@ -536,9 +537,12 @@ def bench_sweep(args):
 def bench_dual(args):
     """Dual precision: FP32 checkpoint with no copy, a bf16 copy, an e4m3 copy
     (one scale per head), an MXFP4 copy (E2M1 codes) or an MXFP8 copy (e4m3
-    codes), the MX copies with one E8M0 scale per 32 columns.  Throughput: batch 256, L = 16, 4096 decode steps (token inputs cycle
-    through 64 seeded steps).  The accuracy of the same modes over 4096 steps is
-    a GPU test (tests/test_gpu_dual.py), not part of this timing."""
+    codes), the MX copies with one E8M0 scale per 32 columns; and an FP16
+    checkpoint written with stochastic rounding (a new seed every call), read
+    directly or through an MXFP4 copy.  Throughput: batch 256, L = 16, 4096
+    decode steps (token inputs cycle through 64 seeded steps).  The accuracy of
+    the modes is tested on the GPU (tests/test_gpu_dual.py,
+    tests/test_gpu_f16ckpt.py), not part of this timing."""
     torch, dev = _device()
     from mamba_state_replay_amd import binding as rb
     from mamba_state_replay_amd import staging, synth, traffic
@@ -546,8 +550,9 @@ def bench_dual(args):
     res = {}
     shape = synth.LayerShape(batch=256, nheads=128, headdim=64, dstate=128, ngroups=8, window=L)
     work = synth.decode_workload(shape, 64, seed=1004, n0=L)
-    for mode in (None, "bf16", "e4m3", "mxfp4", "mxfp8"):
-        cfg = staging.config(shape, read_copy=mode)
+    modes = [("f32", m) for m in (None, "bf16", "e4m3", "mxfp4", "mxfp8")] + [("f16", None), ("f16", "mxfp4")]
+    for ck, mode in modes:
+        cfg = staging.config(shape, read_copy=mode, ckpt_dtype=ck)
         st = staging.replay_state(cfg, work, dev)
         p = staging.params(work, dev)
         toks = staging.TokenStream(work.steps, dev)
@@ -555,14 +560,18 @@ def bench_dual(args):
         rb.replayssm_flush(cfg, st, p, rb.RSSM_FLUSH_FORCE_CAST)
         n0 = np.zeros(256, np.int64)
         sched, _ = traffic.decode_schedule(n0, L, steps)
-        sz = traffic.sizes(128, 64, 128, 8, 2, mode)
+        sz = traffic.sizes(128, 64, 128, 8, 2, mode, ckpt_bytes=4 if ck == "f32" else 2)
         tot = sum(traffic.decode_step_bytes(sz, n, f) for n, f in sched)
-        dstep = lambda i: rb.replayssm_decode_step(cfg, st, p, toks.call(i % 64), y)
+
+        def dstep(i):
+            p.sr_seed = i + 1                   # the FP16 checkpoint's rounding seed (unused for FP32)
+            rb.replayssm_decode_step(cfg, st, p, toks.call(i % 64), y)
         ms, per = timed_launches(dstep, steps, torch)
         gms = graph_time(dstep, steps, torch)          # 4096 steps = whole windows: same phase
         per = np.array(per)
         folds = np.array([f.any() for _, f in sched])
-        res[mode or "fp32"] = {"us_per_step": round(gms * 1e3 / steps, 2),
+        key = (mode or "fp32") if ck == "f32" else "f16 checkpoint" + (f" + {mode}" if mode else "")
+        res[key] = {"us_per_step": round(gms * 1e3 / steps, 2),
                                "gbs": round(tot / (gms * 1e-3) / 1e9, 1),
                                "eager_us_per_step": round(ms * 1e3 / steps, 2),
                                "nonflush_launch_us": round(float(per[~folds].mean()) * 1e3, 2),

@@ -2,10 +2,11 @@
 
 Counts what each call must move at minimum, per sequence:
 
-  S    = nheads*headdim*dstate*4          FP32 checkpoint (or state) bytes
-  S_r  = bytes of the tile a non-flush call reads: S, S/2 (bf16 copy),
-         S/4 + nheads*4 (e4m3 copy + per-tile scales) or S/8 + S/128
-         (MXFP4 codes + one E8M0 byte per 32 elements)
+  E    = nheads*headdim*dstate            state elements
+  S    = 4E (FP32) or 2E (FP16)           checkpoint (or conventional state) bytes
+  S_r  = bytes of the tile a non-flush call reads: S, 2E (bf16 copy),
+         E + nheads*4 (e4m3 copy + per-tile scales), E/2 + E/32 (MXFP4
+         codes + one E8M0 byte per 32 elements) or E + E/32 (MXFP8)
   S_c  = read-copy bytes a flush writes (0 without a copy)
   R    = nheads*headdim*e + ngroups*dstate*e + nheads*4   one record (x, B, dt)
   TOK  = R + ngroups*dstate*e                             one token's inputs (+ C)
@@ -39,18 +40,20 @@ class Sizes:
     Y: int
 
 
-def sizes(nheads, headdim, dstate, ngroups, in_bytes=2, read_copy=None) -> Sizes:
-    S = nheads * headdim * dstate * 4
+def sizes(nheads, headdim, dstate, ngroups, in_bytes=2, read_copy=None, ckpt_bytes=4) -> Sizes:
+    """Per-sequence sizes; ckpt_bytes = 4 for the FP32 checkpoint, 2 for FP16."""
+    E = nheads * headdim * dstate                  # state elements per sequence
+    S = E * ckpt_bytes
     if read_copy is None:
         S_r, S_c = S, 0
     elif read_copy == "bf16":
-        S_r = S_c = S // 2
+        S_r = S_c = 2 * E
     elif read_copy == "e4m3":
-        S_r = S_c = S // 4 + nheads * 4
+        S_r = S_c = E + nheads * 4
     elif read_copy == "mxfp4":
-        S_r = S_c = S // 8 + S // 128
+        S_r = S_c = E // 2 + E // 32
     elif read_copy == "mxfp8":
-        S_r = S_c = S // 4 + S // 128
+        S_r = S_c = E + E // 32
     else:
         raise ValueError(read_copy)
     R = nheads * headdim * in_bytes + ngroups * dstate * in_bytes + nheads * 4

@@ -71,6 +71,28 @@ def test_sizes_and_capacity(rb):
         assert sz[rb.BUF_CKPT_READ] == code_bytes and sz[rb.BUF_CKPT_SCALE] == 256 * 128 * 64 * 128 // 32
 
 
+def test_f16_checkpoint_sizes_and_combinations(rb):
+    """An FP16 checkpoint takes 2 bytes per element; it is read directly or
+    through an MXFP4 copy, and the conventional state stays fp32."""
+    sz = rb.replayssm_sizes(rb.Config(256, 128, 64, 128, 8, 16, 1, "bf16", None, "f16"))
+    assert sz[rb.BUF_CKPT] == 256 * 128 * 64 * 128 * 2 and sz[rb.BUF_CKPT_READ] == 0
+    sz = rb.replayssm_sizes(rb.Config(256, 128, 64, 128, 8, 16, 1, "bf16", "mxfp4", "f16"))
+    assert sz[rb.BUF_CKPT] == 256 * 128 * 64 * 128 * 2 and sz[rb.BUF_CKPT_SCALE] == 256 * 128 * 64 * 128 // 32
+    for copy in ("bf16", "e4m3", "mxfp8"):
+        with pytest.raises(rb.ReplaySSMError) as e:
+            rb.replayssm_sizes(rb.Config(4, 128, 64, 128, 8, 16, 1, "bf16", copy, "f16"))
+        assert e.value.code == -3
+    L = rb.lib()
+    c = rb.Config(4, 128, 64, 128, 8, ckpt_dtype="f16").c()
+    p = rb.rssm_params()
+    t = rb.rssm_tokens(None, None, None, None, 1)
+    assert L.conventional_state_update(ctypes.byref(c), None, 1, None, None, ctypes.byref(p),
+                                       ctypes.byref(t), None, None) == -3
+    bad = rb.Config(4, 128, 64, 128, 8).c()
+    bad.ckpt_dtype = 1                                   # bf16 is no checkpoint type
+    assert L.replayssm_sizes(ctypes.byref(bad), (ctypes.c_size_t * 8)()) == -3
+
+
 @pytest.mark.parametrize("mode", ["mxfp4", "mxfp8"])
 def test_mx_copies_need_blocks_of_32_columns(rb, mode):
     with pytest.raises(rb.ReplaySSMError) as e:
