@@ -197,7 +197,23 @@ struct StageJob {
     bool wide;    // widen to fp32 (B and C rows) or keep the input type (x rows)
 };
 
-template <int HD, int DS, typename InT>
+// (start + c) mod cap for 0 <= start < cap and 0 <= c < cap (a window never
+// exceeds the ring), without a division.
+__device__ __forceinline__ int ring_slot(int start, int c, int cap) {
+    const int s = start + c;
+    return s >= cap ? s - cap : s;
+}
+
+// v / span for 0 <= v < HPW * span, without a division (HPW <= 4).
+template <int HPW>
+__device__ __forceinline__ int block_of(int v, int span) {
+    int k = 0;
+#pragma unroll
+    for (int i = 1; i < HPW; ++i) k += v >= i * span ? 1 : 0;
+    return k;
+}
+
+template <int HD, int DS, typename InT, int HPW>
 __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
     constexpr int EPVIN = InTraits<InT>::EPV;
     constexpr int VR = HD / EPVIN;
@@ -207,10 +223,10 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
     StageJob j;
     j.app = nullptr;
     if (v < m.nx) {
-        const int hh = v / (m.rows * VR);
+        const int hh = block_of<HPW>(v, m.rows * VR);
         const int u = v - hh * m.rows * VR;
         const int c = u / VR, cv = u - c * VR;
-        const uint4* ring = bx + ((size_t)hh * m.cap + (m.start + c) % m.cap) * VR + cv;
+        const uint4* ring = bx + ((size_t)hh * m.cap + ring_slot(m.start, c, m.cap)) * VR + cv;
         if (c < m.n) {
             j.src = ring;
         } else {
@@ -223,7 +239,7 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
     } else if (v < m.nx + m.nb) {
         const int u = v - m.nx;
         const int c = u / VS, cv = u - c * VS;
-        const uint4* ring = bB + (size_t)((m.start + c) % m.cap) * VS + cv;
+        const uint4* ring = bB + (size_t)ring_slot(m.start, c, m.cap) * VS + cv;
         if (c < m.n) {
             j.src = ring;
         } else {
@@ -524,15 +540,15 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
 #pragma unroll
     for (int j = 0; j < JOBS; ++j) {
         const int v = tid + j * NT;
-        if (v < nv) jv[j] = *stage_job<HD, DS, InT>(sm, v).src;
+        if (v < nv) jv[j] = *stage_job<HD, DS, InT, HPW>(sm, v).src;
     }
     // dt of (head hh, window row c) for t = hh * rows + c: from the ring for
     // committed records, from the tokens (and appended to the ring) for queries.
     float* const bdt0 = a.buf_dt + tile0 * cap;
     float dtv = 0.f;
     if (tid < HPW * rows) {
-        const int hh = HPW == 1 ? 0 : tid / rows, c = tid - hh * rows;
-        dtv = c < n ? bdt0[hh * cap + (start + c) % cap] : a.dt[(size_t)(b * T + (c - n)) * a.nheads + h0 + hh];
+        const int hh = block_of<HPW>(tid, rows), c = tid - hh * rows;
+        dtv = c < n ? bdt0[hh * cap + ring_slot(start, c, cap)] : a.dt[(size_t)(b * T + (c - n)) * a.nheads + h0 + hh];
     }
 
     // The tile this call streams: FP32 when it flushes or has no read copy,
@@ -553,23 +569,23 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
     for (int j = 0; j < JOBS; ++j) {
         const int v = tid + j * NT;
         if (v < nv) {
-            const StageJob jb = stage_job<HD, DS, InT>(sm, v);
+            const StageJob jb = stage_job<HD, DS, InT, HPW>(sm, v);
             if (jb.app) *jb.app = jv[j];
             stage_store<InT>(lds, jb, jv[j]);
         }
     }
     for (int v = tid + JOBS * NT; v < nv; v += NT) {   // windows too long for JOBS vectors a thread
-        const StageJob jb = stage_job<HD, DS, InT>(sm, v);
+        const StageJob jb = stage_job<HD, DS, InT, HPW>(sm, v);
         const uint4 val = *jb.src;
         if (jb.app) *jb.app = val;
         stage_store<InT>(lds, jb, val);
     }
     for (int t = tid; t < HPW * rows; t += NT) {
-        const int hh = HPW == 1 ? 0 : t / rows, c = t - hh * rows;
+        const int hh = block_of<HPW>(t, rows), c = t - hh * rows;
         float d = dtv;
         if (t >= NT)                                        // windows longer than the workgroup
-            d = c < n ? bdt0[hh * cap + (start + c) % cap] : a.dt[(size_t)(b * T + (c - n)) * a.nheads + h0 + hh];
-        if (append && c >= n) bdt0[hh * cap + (start + c) % cap] = d;
+            d = c < n ? bdt0[hh * cap + ring_slot(start, c, cap)] : a.dt[(size_t)(b * T + (c - n)) * a.nheads + h0 + hh];
+        if (append && c >= n) bdt0[hh * cap + ring_slot(start, c, cap)] = d;
         float ah = Ah[0];
 #pragma unroll
         for (int k = 1; k < HPW; ++k) ah = hh == k ? Ah[k] : ah;
