@@ -51,3 +51,24 @@ def test_verify_workload_acceptance():
     assert set(np.unique(acc)) == {0, 1, 2, 3}
     assert w.steps.steps == 30
     assert np.all(w.n0 >= 0) and np.all(w.n0 < 16)
+
+
+def test_gdn_tokens_shapes_and_laws():
+    from mamba_state_replay_amd import synth_gdn as sg
+    shape = sg.GdnShape(batch=3, nv=4, nk=2, dk=16, dv=32, window=4, max_drafts=2)
+    w = sg.gdn_workload(shape, 5, seed=3)
+    t = w.steps
+    assert t.q.shape == (5, 3, 2, 16) and t.k.shape == (5, 3, 2, 16) and t.v.shape == (5, 3, 4, 32)
+    assert t.g.shape == (5, 3, 4) and t.beta.shape == (5, 3, 4)
+    # bf16 storage: values are the bf16 patterns widened
+    assert np.array_equal((t.k_bits.astype(np.uint32) << 16).view(np.float32), t.k)
+    # unit keys and queries of norm 1/sqrt(dk), up to bf16 rounding
+    assert np.allclose(np.linalg.norm(t.k, axis=-1), 1.0, atol=1e-2)
+    assert np.allclose(np.linalg.norm(t.q, axis=-1), 0.25, atol=1e-2)
+    assert np.all(t.g < 0) and np.all((t.beta > 0) & (t.beta < 1))
+    assert w.S0.shape == (3, 4, 32, 16)
+    w2 = sg.gdn_workload(shape, 5, seed=3)
+    assert np.array_equal(w2.steps.v, t.v) and np.array_equal(w2.S0, w.S0)
+    v = sg.gdn_workload(shape, 4, seed=4, T=2)
+    assert v.steps.steps == 8 and v.extra["accepted"].shape == (4, 3)
+    assert v.extra["accepted"].min() >= 0 and v.extra["accepted"].max() <= 2
