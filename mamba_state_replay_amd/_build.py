@@ -19,7 +19,7 @@ LIBRARY = PKG / "libreplayssm.so"
 OBJDIR = PKG / "_build"
 
 ARCH = "gfx950"
-SOURCES = ["replay.hip", "replay_f16.hip", "conventional.hip", "probe.hip", "api.cpp"]
+SOURCES = ["replay.hip", "replay_f16.hip", "conventional.hip", "gdn.hip", "probe.hip", "api.cpp"]
 
 # Packed fp32 instructions are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

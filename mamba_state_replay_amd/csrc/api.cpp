@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "../../include/replayssm.h"
+#include "../../include/replayssm_gdn.h"
 #include "kernels.h"
 
 namespace {
@@ -155,6 +156,92 @@ int run_replay(const rssm_config* c, const rssm_state* s, const rssm_params* p, 
     const int in_type = c->in_dtype == RSSM_BF16 ? rssm::IN_BF16 : rssm::IN_F32;
     return launched(rssm::launch_replay(a, c->headdim, c->dstate, in_type, read_mode(c),
                                         static_cast<hipStream_t>(stream)),
+                    what);
+}
+
+
+// ---- Gated DeltaNet layer --------------------------------------------------
+
+int gdn_check_config(const gdn_config* c) {
+    if (!c) return fail(RSSM_ERR_NULL, "config is NULL");
+    if (c->batch < 0) return fail(RSSM_ERR_SHAPE, "batch %d < 0", c->batch);
+    if (c->nv <= 0 || c->nk <= 0 || c->nv % c->nk != 0)
+        return fail(RSSM_ERR_SHAPE, "nv %d must be a positive multiple of nk %d", c->nv, c->nk);
+    if (!rssm::gdn_shape_supported(c->dk, c->dv))
+        return fail(RSSM_ERR_SHAPE, "(dk, dv) = (%d, %d) not compiled; supported: dk 16 with dv %% 16 == 0, "
+                    "dk 128 with dv %% 64 == 0", c->dk, c->dv);
+    if ((long long)c->batch * c->nv * (c->dv / rssm::gdn_rows(c->dk)) > INT_MAX)
+        return fail(RSSM_ERR_SHAPE, "batch * nv * row blocks too large");
+    if (c->in_dtype != RSSM_F32 && c->in_dtype != RSSM_BF16)
+        return fail(RSSM_ERR_DTYPE, "in_dtype must be RSSM_F32 or RSSM_BF16");
+    if (c->window < 1 || c->window > RSSM_MAX_WINDOW)
+        return fail(RSSM_ERR_SHAPE, "window %d outside 1..%d", c->window, RSSM_MAX_WINDOW);
+    if (c->max_drafts < 1 || c->max_drafts > RSSM_MAX_DRAFTS)
+        return fail(RSSM_ERR_SHAPE, "max_drafts %d outside 1..%d", c->max_drafts, RSSM_MAX_DRAFTS);
+    if (rssm::gdn_lds_bytes(c->dk, c->window + 2 * c->max_drafts - 1, c->max_drafts) > kMaxLds)
+        return fail(RSSM_ERR_SHAPE, "window/max_drafts need more than 64 KiB of LDS");
+    return RSSM_OK;
+}
+
+int gdn_check_state(const gdn_state* s) {
+    if (!s) return fail(RSSM_ERR_NULL, "state is NULL");
+    if (!s->ckpt || !s->buf_k || !s->buf_u || !s->buf_g || !s->meta)
+        return fail(RSSM_ERR_NULL, "state: ckpt, buf_k, buf_u, buf_g and meta are required");
+    if (!aligned(s->ckpt, 16) || !aligned(s->buf_k, 16) || !aligned(s->buf_u, 16))
+        return fail(RSSM_ERR_SHAPE, "state: ckpt, buf_k and buf_u must be 16-byte aligned");
+    if (!aligned(s->buf_g, 4) || !aligned(s->meta, 8) || (s->status && !aligned(s->status, 4)))
+        return fail(RSSM_ERR_SHAPE, "state: misaligned scalar buffer");
+    return RSSM_OK;
+}
+
+int gdn_check_tokens(const gdn_tokens* t, const float* o, int tmin, int tmax) {
+    if (!t) return fail(RSSM_ERR_NULL, "tokens is NULL");
+    if (!t->q || !t->k || !t->v || !t->g || !t->beta || !o)
+        return fail(RSSM_ERR_NULL, "tokens q, k, v, g, beta and o are required");
+    if (t->T < tmin || t->T > tmax) return fail(RSSM_ERR_DRAFTS, "T = %d outside %d..%d", t->T, tmin, tmax);
+    if (!aligned(t->q, 16) || !aligned(t->k, 16) || !aligned(t->v, 16))
+        return fail(RSSM_ERR_SHAPE, "tokens q, k, v must be 16-byte aligned");
+    if (!aligned(t->g, 4) || !aligned(t->beta, 4) || !aligned(o, 4))
+        return fail(RSSM_ERR_SHAPE, "misaligned g, beta or o");
+    return RSSM_OK;
+}
+
+rssm::GdnArgs gdn_args(const gdn_config* c, const gdn_state* s, const gdn_tokens* t, float* o, int mode) {
+    rssm::GdnArgs a;
+    std::memset(&a, 0, sizeof a);
+    if (s) {
+        a.ckpt = s->ckpt;
+        a.buf_k = s->buf_k;
+        a.buf_u = s->buf_u;
+        a.buf_g = s->buf_g;
+        a.meta = s->meta;
+        a.status = s->status;
+    }
+    if (t) {
+        a.q = t->q;
+        a.k = t->k;
+        a.v = t->v;
+        a.g = t->g;
+        a.beta = t->beta;
+        a.T = t->T;
+    }
+    a.o = o;
+    a.batch = c->batch;
+    a.nv = c->nv;
+    a.nk = c->nk;
+    a.dv = c->dv;
+    a.parts = c->dv / rssm::gdn_rows(c->dk);
+    a.L = c->window;
+    a.cap = c->window + 2 * c->max_drafts - 1;
+    a.mode = mode;
+    return a;
+}
+
+int run_gdn(const gdn_config* c, const gdn_state* s, const gdn_tokens* t, float* o, int mode, void* stream,
+            const char* what) {
+    const rssm::GdnArgs a = gdn_args(c, s, t, o, mode);
+    return launched(rssm::launch_gdn_replay(a, c->dk, c->in_dtype == RSSM_BF16 ? rssm::IN_BF16 : rssm::IN_F32,
+                                            static_cast<hipStream_t>(stream)),
                     what);
 }
 
@@ -326,6 +413,94 @@ int conventional_commit(const rssm_config* cfg, int32_t* slot, int32_t nslots, c
     a.nslots = nslots;
     return launched(rssm::launch_conventional_commit(a, static_cast<hipStream_t>(stream)),
                     "conventional_commit");
+}
+
+int gdn_row_blocks(const gdn_config* cfg) {
+    const int rc = gdn_check_config(cfg);
+    if (rc) return rc;
+    return cfg->dv / rssm::gdn_rows(cfg->dk);
+}
+
+int gdn_sizes(const gdn_config* c, size_t bytes[GDN_NUM_BUFS]) {
+    const int rc = gdn_check_config(c);
+    if (rc) return rc;
+    if (!bytes) return fail(RSSM_ERR_NULL, "bytes is NULL");
+    const size_t cap = (size_t)(c->window + 2 * c->max_drafts - 1);
+    const size_t in_bytes = c->in_dtype == RSSM_BF16 ? 2 : 4;
+    const size_t heads = (size_t)c->batch * c->nv;
+    bytes[0] = heads * c->dv * c->dk * 4;
+    bytes[1] = (size_t)c->batch * c->nk * cap * c->dk * in_bytes;
+    bytes[2] = heads * cap * c->dv * 4;
+    bytes[3] = heads * cap * 4;
+    bytes[4] = heads * (c->dv / rssm::gdn_rows(c->dk)) * 2 * 4;
+    g_err[0] = '\0';
+    return RSSM_OK;
+}
+
+int gdn_decode_step(const gdn_config* cfg, const gdn_state* st, const gdn_tokens* tok, float* o, void* stream) {
+    int rc = gdn_check_config(cfg);
+    if (rc) return rc;
+    if (cfg->batch == 0) return RSSM_OK;
+    rc = gdn_check_state(st);
+    if (!rc) rc = gdn_check_tokens(tok, o, 1, 1);
+    if (rc) return rc;
+    return run_gdn(cfg, st, tok, o, rssm::MODE_DECODE, stream, "gdn_decode_step");
+}
+
+int gdn_verify_drafts(const gdn_config* cfg, const gdn_state* st, const gdn_tokens* tok, float* o, void* stream) {
+    int rc = gdn_check_config(cfg);
+    if (rc) return rc;
+    if (cfg->batch == 0) return RSSM_OK;
+    rc = gdn_check_state(st);
+    if (!rc) rc = gdn_check_tokens(tok, o, 1, cfg->max_drafts);
+    if (rc) return rc;
+    return run_gdn(cfg, st, tok, o, rssm::MODE_VERIFY, stream, "gdn_verify_drafts");
+}
+
+int gdn_flush(const gdn_config* cfg, const gdn_state* st, void* stream) {
+    int rc = gdn_check_config(cfg);
+    if (rc) return rc;
+    if (cfg->batch == 0) return RSSM_OK;
+    rc = gdn_check_state(st);
+    if (rc) return rc;
+    return run_gdn(cfg, st, nullptr, nullptr, rssm::MODE_FLUSH, stream, "gdn_flush");
+}
+
+int gdn_commit(const gdn_config* cfg, const gdn_state* st, const int32_t* accepted, int32_t T, void* stream) {
+    int rc = gdn_check_config(cfg);
+    if (rc) return rc;
+    if (T < 1 || T > cfg->max_drafts) return fail(RSSM_ERR_DRAFTS, "T = %d outside 1..%d", T, cfg->max_drafts);
+    if (cfg->batch == 0) return RSSM_OK;
+    if (!st || !st->meta || !accepted) return fail(RSSM_ERR_NULL, "state meta and accepted are required");
+    if (!aligned(st->meta, 8) || !aligned(accepted, 4) || (st->status && !aligned(st->status, 4)))
+        return fail(RSSM_ERR_SHAPE, "misaligned meta, accepted or status");
+    rssm::CommitArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.meta = st->meta;
+    a.accepted = accepted;
+    a.status = st->status;
+    a.batch = cfg->batch;
+    a.nheads = cfg->nv * (cfg->dv / rssm::gdn_rows(cfg->dk));   // one pointer copy per workgroup
+    a.T = T;
+    a.cap = cfg->window + 2 * cfg->max_drafts - 1;
+    return launched(rssm::launch_replay_commit(a, static_cast<hipStream_t>(stream)), "gdn_commit");
+}
+
+int gdn_conventional_update(const gdn_config* cfg, float* state, const gdn_tokens* tok, float* o, void* stream) {
+    int rc = gdn_check_config(cfg);
+    if (rc) return rc;
+    if (cfg->batch == 0) return RSSM_OK;
+    if (!state) return fail(RSSM_ERR_NULL, "state is NULL");
+    if (!aligned(state, 16)) return fail(RSSM_ERR_SHAPE, "state must be 16-byte aligned");
+    rc = gdn_check_tokens(tok, o, 1, 1);
+    if (rc) return rc;
+    gdn_state s;
+    std::memset(&s, 0, sizeof s);
+    s.ckpt = state;
+    const rssm::GdnArgs a = gdn_args(cfg, &s, tok, o, rssm::MODE_DECODE);
+    return launched(rssm::launch_gdn_conventional(a, cfg->dk, cfg->in_dtype == RSSM_BF16 ? rssm::IN_BF16 : rssm::IN_F32,
+                                                  static_cast<hipStream_t>(stream)),
+                    "gdn_conventional_update");
 }
 
 const char* replayssm_last_error(void) { return g_err; }

@@ -1,0 +1,498 @@
+// Gated DeltaNet (GDN) layer in ReplaySSM form on gfx950: the decode / verify /
+// flush kernel over an FP32 checkpoint plus corrected-value records, and the
+// conventional GDN step (the in-library baseline).
+//
+// Method: NVIDIA Developer blog "ReplaySSM: Rethinking State Storage for Faster
+// Hybrid-Model Decoding".  Its section "Why SSM layers can become a decoding
+// bottleneck" says GDN's delta-rule update can be written in Mamba-2's
+// outer-product form, so the checkpoint-plus-buffer state (section "How
+// ReplaySSM represents the state") and output-only evaluation (section
+// "Benefit 2") carry over.  The gated delta rule (Yang, Kautz and Hatamizadeh,
+// "Gated Delta Networks", ICLR 2025), S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T)
+// + beta_t v_t k_t^T, o_t = S_t q_t, expands to S_t = alpha_t S_{t-1} + u_t k_t^T
+// with u_t = beta_t (v_t - alpha_t S_{t-1} k_t).  A record is (k, u, g = log
+// alpha); u is formed when its token arrives, from the checkpoint (one more
+// product with the streamed tile) and the records before it.
+//
+// Row i of u_t needs only row i of S_{t-1}, so the rows of a value head's state
+// are independent: a head's dv x dk state is split into blocks of ROWS rows,
+// one workgroup each, streaming one ROWS x DK fp32 tile (64 x 128 = 32 KiB)
+// with the thread layout of TileGeo (8 lanes per row, 16-byte loads).
+//
+// One call of gdn_replay_kernel, workgroup = (sequence b, value head h, row block p):
+//  1. read the workgroup's ring pointer {start, n}; decide the flush (n >= L,
+//     or n > 0 in flush mode); issue the tile's loads;
+//  2. stage the committed records (keys widened to fp32, this block's u rows,
+//     g) and the call's tokens (q, k, this block's v rows, g, beta) in LDS; the
+//     first block of the key head's first value head appends the tokens' keys
+//     to the key ring;
+//  3. flush: fold the records into the tile registers (rank-n update), store
+//     the tile once, move the pointer past the folded records;
+//  4. one 8-lane group per (query, window position) pair forms the segment
+//     decay and the key-key and key-query scores;
+//  5. per query, each thread forms its rows' share of S_s k_q and S_s q_q from
+//     the registers, scaled by the query's checkpoint decay, adds the committed
+//     records' terms (records split over the row's lanes) and the row's lanes
+//     reduce;
+//  6. one thread per row walks the queries in order, adding the draft records'
+//     terms: u_q, then o_q; it writes o and appends u;
+//  7. write the ring pointer (decode commits its token).
+#include "common.h"
+#include "kernels.h"
+
+namespace rssm {
+
+namespace {
+
+template <int DK>
+struct GdnGeo;
+template <>
+struct GdnGeo<16> { static constexpr int ROWS = 16, NT = 64; };
+template <>
+struct GdnGeo<128> { static constexpr int ROWS = 64, NT = 256; };
+
+// LDS plan in floats.  Committed records use window positions 0 .. n-1; the
+// call's tokens (queries) sit at n .. n+T-1 after any flush.
+struct GdnLds {
+    int K, KQ, QQ, U, US, V, G, GQ, BE, CK, CQ, DD, WF, PK, PQ, UD, total;
+};
+
+__host__ __device__ inline GdnLds gdn_plan(int DK, int ROWS, int cap, int T) {
+    GdnLds l;
+    int o = 0;
+    l.US = ROWS + 4;                // u row stride: lanes reading different records hit different banks
+    l.K = o;  o += cap * DK;        // committed records' keys
+    l.KQ = o; o += T * DK;          // tokens' keys
+    l.QQ = o; o += T * DK;          // tokens' queries
+    l.U = o;  o += cap * l.US;      // committed records' u, this block's rows
+    l.V = o;  o += T * ROWS;        // tokens' v, this block's rows
+    l.G = o;  o += cap;             // committed records' g
+    l.GQ = o; o += T;               // tokens' g
+    l.BE = o; o += T;               // tokens' beta
+    l.CK = o; o += T * cap;         // ck[q][c] = exp(sum_{c<i<=m_q} g_i) (key_c . k_q), c < m_q
+    l.CQ = o; o += T * cap;         // cq[q][c] = exp(sum_{c<i<=m_q} g_i) (key_c . q_q), c <= m_q
+    l.DD = o; o += T + 1;           // dd[q] = exp(sum_{i<=m_q} g_i); [T]: the flush's checkpoint decay
+    l.WF = o; o += cap;             // flush weights exp(sum_{c<i<n} g_i)
+    l.PK = o; o += T * ROWS;        // reduced checkpoint + committed-record part of alpha_q S k_q
+    l.PQ = o; o += T * ROWS;        // same for S q_q
+    l.UD = o; o += T * ROWS;        // the tokens' u
+    l.total = (o + 3) & ~3;
+    return l;
+}
+
+constexpr int kGdnIntSlots = 4;     // LDS ints after the float plan: start, n, fold, ok
+
+__device__ __forceinline__ float dot4(const v4f a, const float4 b) {
+    float s = a[0] * b.x;
+    s = fmaf(a[1], b.y, s);
+    s = fmaf(a[2], b.z, s);
+    return fmaf(a[3], b.w, s);
+}
+
+template <int DK, typename InT>
+__global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_replay_kernel(const GdnArgs a) {
+    constexpr int ROWS = GdnGeo<DK>::ROWS;
+    constexpr int NT = GdnGeo<DK>::NT;
+    using Geo = TileGeo<ROWS, DK, NT, 4>;
+    constexpr int W = Geo::W;
+    constexpr int EPV = InTraits<InT>::EPV;       // input elements per 16-byte vector
+    constexpr int KV = DK / EPV;                  // vectors per key / query
+    constexpr int RV = ROWS / EPV;                // vectors per block of v rows
+    constexpr int UV = ROWS / 4;                  // fp32 vectors per block of u rows
+    extern __shared__ float smem[];
+
+    const int tid = threadIdx.x;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);   // = (b * nv + h) * parts + p
+    const int p = wg % a.parts;
+    const int bh = wg / a.parts;
+    const int b = bh / a.nv;
+    const int h = bh % a.nv;
+    const int kh = h / (a.nv / a.nk);
+    const int cap = a.cap;
+    const int T = a.mode == MODE_FLUSH ? 0 : a.T;
+    const GdnLds Ls = gdn_plan(DK, ROWS, cap, T);
+    int* si = reinterpret_cast<int*>(smem + Ls.total);
+
+    // 1. ring pointer and flush decision
+    if (tid == 0) {
+        const int start = a.meta[2 * wg];
+        const int n = a.meta[2 * wg + 1];
+        bool ok = start >= 0 && start < cap && n >= 0 && n <= cap;
+        const int fold = ok && (a.mode == MODE_FLUSH ? n > 0 : n >= a.L);
+        const int np = fold ? 0 : n;
+        ok = ok && np + T <= cap;
+        si[0] = start;
+        si[1] = n;
+        si[2] = fold;
+        si[3] = ok;
+        if (!ok && a.status) atomicOr(a.status, (int)kStatusMeta);
+    }
+    __syncthreads();
+    const int start = si[0], n = si[1];
+    const bool fold = si[2] != 0;
+    if (!si[3]) {
+        for (int i = tid; i < T * ROWS; i += NT)
+            a.o[((size_t)(b * T + i / ROWS) * a.nv + h) * a.dv + p * ROWS + i % ROWS] = __builtin_nanf("");
+        return;
+    }
+    if (!fold && T == 0) return;                          // flush call with nothing to fold
+    const int np = fold ? 0 : n;                          // committed records seen by the queries
+    const int qstart = fold ? (start + n) % cap : start;  // ring start after the flush
+
+    float* const tile_p = a.ckpt + ((size_t)bh * a.dv + p * ROWS) * DK;
+    v4f raw[Geo::NV];
+#pragma unroll
+    for (int s = 0; s < Geo::NV; ++s)
+        raw[s] = __builtin_bit_cast(v4f, __builtin_nontemporal_load(reinterpret_cast<const v4u*>(tile_p) +
+                                                                    Geo::vec(tid, s)));
+
+    // 2. stage records and tokens
+    {
+        const InT* kring = static_cast<const InT*>(a.buf_k) + (size_t)(b * a.nk + kh) * cap * DK;
+        const float* uring = a.buf_u + (size_t)bh * cap * a.dv + p * ROWS;
+        const float* gring = a.buf_g + (size_t)bh * cap;
+        const bool append_k = (h % (a.nv / a.nk)) == 0 && p == 0;
+        const int nk = n * KV, nu = n * UV, ntk = T * KV, ntv = T * RV;
+        const int total = nk + nu + 2 * ntk + ntv;
+        for (int i = tid; i < total; i += NT) {
+            int r = i;
+            if (r < nk) {
+                const int c = r / KV, e = r % KV;
+                int slot = start + c;
+                slot -= slot >= cap ? cap : 0;
+                const uint4 v = reinterpret_cast<const uint4*>(kring + (size_t)slot * DK)[e];
+                widen16<InT>(v, smem + Ls.K + c * DK + e * EPV);
+                continue;
+            }
+            r -= nk;
+            if (r < nu) {
+                const int c = r / UV, e = r % UV;
+                int slot = start + c;
+                slot -= slot >= cap ? cap : 0;
+                const float4 v = reinterpret_cast<const float4*>(uring + (size_t)slot * a.dv)[e];
+                *reinterpret_cast<float4*>(smem + Ls.U + c * Ls.US + 4 * e) = v;
+                continue;
+            }
+            r -= nu;
+            if (r < 2 * ntk) {
+                const bool isq = r >= ntk;
+                const int rr = isq ? r - ntk : r;
+                const int q = rr / KV, e = rr % KV;
+                const InT* src = static_cast<const InT*>(isq ? a.q : a.k) + ((size_t)(b * T + q) * a.nk + kh) * DK;
+                const uint4 v = reinterpret_cast<const uint4*>(src)[e];
+                widen16<InT>(v, smem + (isq ? Ls.QQ : Ls.KQ) + q * DK + e * EPV);
+                if (!isq && append_k) {
+                    int slot = qstart + np + q;
+                    slot -= slot >= cap ? cap : 0;
+                    reinterpret_cast<uint4*>(static_cast<InT*>(a.buf_k) +
+                                             ((size_t)(b * a.nk + kh) * cap + slot) * DK)[e] = v;
+                }
+                continue;
+            }
+            r -= 2 * ntk;
+            {
+                const int q = r / RV, e = r % RV;
+                const InT* src = static_cast<const InT*>(a.v) + ((size_t)(b * T + q) * a.nv + h) * a.dv + p * ROWS;
+                const uint4 v = reinterpret_cast<const uint4*>(src)[e];
+                widen16<InT>(v, smem + Ls.V + q * ROWS + e * EPV);
+            }
+        }
+        for (int i = tid; i < n; i += NT) {
+            int slot = start + i;
+            slot -= slot >= cap ? cap : 0;
+            smem[Ls.G + i] = gring[slot];
+        }
+        for (int i = tid; i < T; i += NT) {
+            const size_t ti = (size_t)(b * T + i) * a.nv + h;
+            smem[Ls.GQ + i] = a.g[ti];
+            smem[Ls.BE + i] = a.beta[ti];
+        }
+    }
+    __syncthreads();
+
+    const int row0 = Geo::row0(tid);
+    const int lane = tid % W;
+
+    // 3. flush: S <- exp(sum g) S + sum_c exp(sum_{c<i<n} g_i) u_c k_c^T, stored once
+    if (fold) {
+        for (int c = tid; c < n; c += NT) {
+            float s = 0.0f;
+            for (int i = c + 1; i < n; ++i) s += smem[Ls.G + i];
+            smem[Ls.WF + c] = __expf(s);
+        }
+        if (tid == NT - 1) {
+            float s = 0.0f;
+            for (int i = 0; i < n; ++i) s += smem[Ls.G + i];
+            smem[Ls.DD + T] = __expf(s);
+        }
+        __syncthreads();
+        const float gf = smem[Ls.DD + T];
+#pragma unroll
+        for (int s = 0; s < Geo::NV; ++s) {
+            const int row = row0 + s / Geo::VPL;
+            const int vc = lane + W * (s % Geo::VPL);
+            v4f acc = raw[s] * gf;
+            for (int c = 0; c < n; ++c) {
+                const float coef = smem[Ls.WF + c] * smem[Ls.U + c * Ls.US + row];
+                const float4 kc = *reinterpret_cast<const float4*>(smem + Ls.K + c * DK + 4 * vc);
+                acc[0] = fmaf(coef, kc.x, acc[0]);
+                acc[1] = fmaf(coef, kc.y, acc[1]);
+                acc[2] = fmaf(coef, kc.z, acc[2]);
+                acc[3] = fmaf(coef, kc.w, acc[3]);
+            }
+            raw[s] = acc;
+        }
+#pragma unroll
+        for (int s = 0; s < Geo::NV; ++s)
+            __builtin_nontemporal_store(__builtin_bit_cast(v4u, raw[s]),
+                                        reinterpret_cast<v4u*>(tile_p) + Geo::vec(tid, s));
+        if (T == 0) {
+            if (tid == 0) {
+                a.meta[2 * wg] = qstart;
+                a.meta[2 * wg + 1] = 0;
+            }
+            return;
+        }
+    }
+
+    // 4. coefficients: one 8-lane group per (query q, window position c <= np + q)
+    {
+        const int m = np + T;                             // window positions of the call
+        const int grp = tid / 8, gl = tid % 8;
+        for (int idx = grp; idx < T * m; idx += NT / 8) {
+            const int q = idx / m, c = idx % m;
+            const int mq = np + q;
+            if (c > mq) continue;                         // the whole group skips together
+            const float* key = c < np ? smem + Ls.K + c * DK : smem + Ls.KQ + (c - np) * DK;
+            const float* kq = smem + Ls.KQ + q * DK;
+            const float* qq = smem + Ls.QQ + q * DK;
+            float sk = 0.0f, sq = 0.0f, seg = 0.0f;
+            for (int e = gl; e < DK; e += 8) {
+                sk = fmaf(key[e], kq[e], sk);
+                sq = fmaf(key[e], qq[e], sq);
+            }
+            for (int i = c + 1 + gl; i <= mq; i += 8) seg += i < np ? smem[Ls.G + i] : smem[Ls.GQ + i - np];
+            sk = group_sum<8>(sk);
+            sq = group_sum<8>(sq);
+            seg = group_sum<8>(seg);
+            if (gl == 0) {
+                const float w = __expf(seg);
+                smem[Ls.CK + q * cap + c] = c < mq ? w * sk : 0.0f;
+                smem[Ls.CQ + q * cap + c] = w * sq;
+            }
+        }
+        for (int q = tid; q < T; q += NT) {
+            float s = 0.0f;
+            for (int i = 0; i <= np + q; ++i) s += i < np ? smem[Ls.G + i] : smem[Ls.GQ + i - np];
+            smem[Ls.DD + q] = __expf(s);
+        }
+    }
+    __syncthreads();
+
+    // 5. checkpoint products and committed-record terms, reduced over each row's lanes
+    for (int q = 0; q < T; ++q) {
+        float pk[Geo::NI], pq[Geo::NI];
+#pragma unroll
+        for (int r = 0; r < Geo::NI; ++r) {
+            pk[r] = 0.0f;
+            pq[r] = 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < Geo::NV; ++s) {
+            const int r = s / Geo::VPL;
+            const int vc = lane + W * (s % Geo::VPL);
+            const float4 k4 = *reinterpret_cast<const float4*>(smem + Ls.KQ + q * DK + 4 * vc);
+            const float4 q4 = *reinterpret_cast<const float4*>(smem + Ls.QQ + q * DK + 4 * vc);
+            pk[r] += dot4(raw[s], k4);
+            pq[r] += dot4(raw[s], q4);
+        }
+        const float d = smem[Ls.DD + q];
+#pragma unroll
+        for (int r = 0; r < Geo::NI; ++r) {
+            pk[r] *= d;
+            pq[r] *= d;
+        }
+        for (int c = lane; c < np; c += W) {
+            const float ck = smem[Ls.CK + q * cap + c];
+            const float cq = smem[Ls.CQ + q * cap + c];
+#pragma unroll
+            for (int r = 0; r < Geo::NI; ++r) {
+                const float u = smem[Ls.U + c * Ls.US + row0 + r];
+                pk[r] = fmaf(ck, u, pk[r]);
+                pq[r] = fmaf(cq, u, pq[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < Geo::NI; ++r) {
+            pk[r] = group_sum<W>(pk[r]);
+            pq[r] = group_sum<W>(pq[r]);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < Geo::NI; ++r) {
+                smem[Ls.PK + q * ROWS + row0 + r] = pk[r];
+                smem[Ls.PQ + q * ROWS + row0 + r] = pq[r];
+            }
+        }
+    }
+    __syncthreads();
+
+    // 6. drafts in order, one thread per row: u_q, then o_q; append u (and g)
+    if (tid < ROWS) {
+        const int row = tid;
+        float* const uring = a.buf_u + (size_t)bh * cap * a.dv + p * ROWS + row;
+        for (int q = 0; q < T; ++q) {
+            const int mq = np + q;
+            float sk = smem[Ls.PK + q * ROWS + row];
+            for (int d = 0; d < q; ++d) sk = fmaf(smem[Ls.CK + q * cap + np + d], smem[Ls.UD + d * ROWS + row], sk);
+            const float u = smem[Ls.BE + q] * (smem[Ls.V + q * ROWS + row] - sk);
+            smem[Ls.UD + q * ROWS + row] = u;
+            float o = smem[Ls.PQ + q * ROWS + row];
+            for (int d = 0; d <= q; ++d) o = fmaf(smem[Ls.CQ + q * cap + np + d], smem[Ls.UD + d * ROWS + row], o);
+            a.o[((size_t)(b * T + q) * a.nv + h) * a.dv + p * ROWS + row] = o;
+            int slot = qstart + mq;
+            slot -= slot >= cap ? cap : 0;
+            uring[(size_t)slot * a.dv] = u;
+        }
+    }
+    if (p == 0 && tid < T) {
+        int slot = qstart + np + tid;
+        slot -= slot >= cap ? cap : 0;
+        a.buf_g[(size_t)bh * cap + slot] = smem[Ls.GQ + tid];
+    }
+
+    // 7. ring pointer: verify leaves the length, decode commits its token
+    if (tid == 0) {
+        a.meta[2 * wg] = qstart;
+        a.meta[2 * wg + 1] = np + (a.mode == MODE_DECODE ? T : 0);
+    }
+}
+
+// Conventional GDN step: read the tile, S k, u = beta (v - alpha S k),
+// S <- alpha S + u k^T, o = S q, store the tile.
+template <int DK, typename InT>
+__global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_conventional_kernel(const GdnArgs a) {
+    constexpr int ROWS = GdnGeo<DK>::ROWS;
+    constexpr int NT = GdnGeo<DK>::NT;
+    using Geo = TileGeo<ROWS, DK, NT, 4>;
+    constexpr int W = Geo::W;
+    constexpr int EPV = InTraits<InT>::EPV;
+    constexpr int KV = DK / EPV;
+    constexpr int RV = ROWS / EPV;
+    extern __shared__ float smem[];
+    float* const kk = smem;             // [DK]
+    float* const qq = smem + DK;        // [DK]
+    float* const vv = smem + 2 * DK;    // [ROWS]
+
+    const int tid = threadIdx.x;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int p = wg % a.parts;
+    const int bh = wg / a.parts;
+    const int b = bh / a.nv;
+    const int h = bh % a.nv;
+    const int kh = h / (a.nv / a.nk);
+
+    float* const tile_p = a.ckpt + ((size_t)bh * a.dv + p * ROWS) * DK;
+    v4f raw[Geo::NV];
+#pragma unroll
+    for (int s = 0; s < Geo::NV; ++s)
+        raw[s] = __builtin_bit_cast(v4f, __builtin_nontemporal_load(reinterpret_cast<const v4u*>(tile_p) +
+                                                                    Geo::vec(tid, s)));
+    for (int i = tid; i < 2 * KV + RV; i += NT) {
+        if (i < 2 * KV) {
+            const bool isq = i >= KV;
+            const int e = isq ? i - KV : i;
+            const InT* src = static_cast<const InT*>(isq ? a.q : a.k) + ((size_t)b * a.nk + kh) * DK;
+            widen16<InT>(reinterpret_cast<const uint4*>(src)[e], (isq ? qq : kk) + e * EPV);
+        } else {
+            const int e = i - 2 * KV;
+            const InT* src = static_cast<const InT*>(a.v) + ((size_t)b * a.nv + h) * a.dv + p * ROWS;
+            widen16<InT>(reinterpret_cast<const uint4*>(src)[e], vv + e * EPV);
+        }
+    }
+    __syncthreads();
+    const float alpha = __expf(a.g[(size_t)b * a.nv + h]);
+    const float beta = a.beta[(size_t)b * a.nv + h];
+    const int row0 = Geo::row0(tid);
+    const int lane = tid % W;
+
+    float sk[Geo::NI];
+#pragma unroll
+    for (int r = 0; r < Geo::NI; ++r) sk[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < Geo::NV; ++s) {
+        const int vc = lane + W * (s % Geo::VPL);
+        sk[s / Geo::VPL] += dot4(raw[s], *reinterpret_cast<const float4*>(kk + 4 * vc));
+    }
+    float u[Geo::NI];
+#pragma unroll
+    for (int r = 0; r < Geo::NI; ++r) u[r] = beta * (vv[row0 + r] - alpha * group_sum<W>(sk[r]));
+    float o[Geo::NI];
+#pragma unroll
+    for (int r = 0; r < Geo::NI; ++r) o[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < Geo::NV; ++s) {
+        const int r = s / Geo::VPL;
+        const int vc = lane + W * (s % Geo::VPL);
+        const float4 k4 = *reinterpret_cast<const float4*>(kk + 4 * vc);
+        v4f x = raw[s];
+        x[0] = fmaf(alpha, x[0], u[r] * k4.x);
+        x[1] = fmaf(alpha, x[1], u[r] * k4.y);
+        x[2] = fmaf(alpha, x[2], u[r] * k4.z);
+        x[3] = fmaf(alpha, x[3], u[r] * k4.w);
+        raw[s] = x;
+        o[r] += dot4(x, *reinterpret_cast<const float4*>(qq + 4 * vc));
+    }
+#pragma unroll
+    for (int s = 0; s < Geo::NV; ++s)
+        __builtin_nontemporal_store(__builtin_bit_cast(v4u, raw[s]), reinterpret_cast<v4u*>(tile_p) + Geo::vec(tid, s));
+#pragma unroll
+    for (int r = 0; r < Geo::NI; ++r) o[r] = group_sum<W>(o[r]);
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < Geo::NI; ++r) a.o[((size_t)b * a.nv + h) * a.dv + p * ROWS + row0 + r] = o[r];
+    }
+}
+
+template <int DK, typename InT>
+hipError_t launch_replay_t(const GdnArgs& a, hipStream_t stream) {
+    constexpr int ROWS = GdnGeo<DK>::ROWS, NT = GdnGeo<DK>::NT;
+    const int T = a.mode == MODE_FLUSH ? 0 : a.T;
+    const size_t lds = (size_t)gdn_plan(DK, ROWS, a.cap, T).total * 4 + kGdnIntSlots * 4;
+    const int nwg = a.batch * a.nv * a.parts;
+    hipLaunchKernelGGL((gdn_replay_kernel<DK, InT>), dim3(nwg), dim3(NT), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int DK, typename InT>
+hipError_t launch_conv_t(const GdnArgs& a, hipStream_t stream) {
+    constexpr int ROWS = GdnGeo<DK>::ROWS, NT = GdnGeo<DK>::NT;
+    const size_t lds = (size_t)(2 * DK + ROWS) * 4;
+    const int nwg = a.batch * a.nv * a.parts;
+    hipLaunchKernelGGL((gdn_conventional_kernel<DK, InT>), dim3(nwg), dim3(NT), lds, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool gdn_shape_supported(int dk, int dv) {
+    return (dk == 16 && dv > 0 && dv % 16 == 0) || (dk == 128 && dv > 0 && dv % 64 == 0);
+}
+
+int gdn_rows(int dk) { return dk == 16 ? GdnGeo<16>::ROWS : GdnGeo<128>::ROWS; }
+
+size_t gdn_lds_bytes(int dk, int cap, int T) {
+    return (size_t)gdn_plan(dk, gdn_rows(dk), cap, T).total * 4 + kGdnIntSlots * 4;
+}
+
+hipError_t launch_gdn_replay(const GdnArgs& a, int dk, int in_type, hipStream_t stream) {
+    if (dk == 16) return in_type == IN_BF16 ? launch_replay_t<16, uint16_t>(a, stream) : launch_replay_t<16, float>(a, stream);
+    return in_type == IN_BF16 ? launch_replay_t<128, uint16_t>(a, stream) : launch_replay_t<128, float>(a, stream);
+}
+
+hipError_t launch_gdn_conventional(const GdnArgs& a, int dk, int in_type, hipStream_t stream) {
+    if (dk == 16) return in_type == IN_BF16 ? launch_conv_t<16, uint16_t>(a, stream) : launch_conv_t<16, float>(a, stream);
+    return in_type == IN_BF16 ? launch_conv_t<128, uint16_t>(a, stream) : launch_conv_t<128, float>(a, stream);
+}
+
+}  // namespace rssm

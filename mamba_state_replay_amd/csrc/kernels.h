@@ -77,4 +77,29 @@ hipError_t launch_conventional(const ConvArgs& a, int hd, int ds, int in_type, h
 hipError_t launch_replay_commit(const CommitArgs& a, hipStream_t stream);
 hipError_t launch_conventional_commit(const CommitArgs& a, hipStream_t stream);
 
+// Gated DeltaNet layer (gdn.hip): one workgroup per (sequence, value head,
+// row block of ROWS value rows).
+struct GdnArgs {
+    float* ckpt;        // [batch][nv][dv][dk] fp32 (replay checkpoint, or the conventional state)
+    void* buf_k;        // [batch][nk][cap][dk] input type
+    float* buf_u;       // [batch][nv][cap][dv]
+    float* buf_g;       // [batch][nv][cap]
+    int32_t* meta;      // [batch][nv][parts][2]
+    int32_t* status;
+    const void* q;      // [batch][T][nk][dk]
+    const void* k;
+    const void* v;      // [batch][T][nv][dv]
+    const float* g;     // [batch][T][nv]
+    const float* beta;
+    float* o;           // [batch][T][nv][dv]
+    int32_t batch, nv, nk, dv, parts;
+    int32_t L, cap, T, mode;
+};
+
+bool gdn_shape_supported(int dk, int dv);
+int gdn_rows(int dk);   // value rows per workgroup
+size_t gdn_lds_bytes(int dk, int cap, int T);
+hipError_t launch_gdn_replay(const GdnArgs& a, int dk, int in_type, hipStream_t stream);
+hipError_t launch_gdn_conventional(const GdnArgs& a, int dk, int in_type, hipStream_t stream);
+
 }  // namespace rssm

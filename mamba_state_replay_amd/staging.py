@@ -108,3 +108,32 @@ def conventional_states(cfg: rb.Config, h: np.ndarray, nslots: int, device) -> t
                      device=device)
     st[:, 0].copy_(torch.from_numpy(np.asarray(h, np.float32)))
     return st
+
+
+class GdnTokenStream:
+    """Every GDN token of a run resident on the device, as [calls][batch][T][...];
+    call(i) is the i-th call's gdn_tokens (pure data movement)."""
+
+    def __init__(self, tokens, device, T: int = 1):
+        from . import binding_gdn as bg
+        self._bg = bg
+        if tokens.steps % T:
+            raise ValueError("steps must be a multiple of T")
+        self.T = T
+        self.calls = tokens.steps // T
+        self._t = {}
+        for name in ("q", "k", "v", "g", "beta"):
+            arr = tokens.storage(name)
+            dt = None
+            if arr.dtype == np.uint16:
+                arr, dt = arr.view(np.int16), torch.bfloat16
+            else:
+                arr = arr.astype(np.float32)
+            shp = (self.calls, T) + arr.shape[1:]
+            self._t[name] = _dev(np.swapaxes(arr.reshape(shp), 1, 2), device, dt)
+
+    def call(self, i: int):
+        return self._bg.GdnTokens(*(self._t[n][i] for n in ("q", "k", "v", "g", "beta")))
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self._t.values())

@@ -1,0 +1,235 @@
+"""GPU parity of the Gated DeltaNet entry points against the fp64 oracle
+(oracle/gdn.py): decode with flushes, verify + commit rounds, the standalone
+flush, the conventional kernel, pointer semantics and data-error handling."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gdn as ogdn
+from mamba_state_replay_amd import synth_gdn as sg
+from tests.gpu_util import TOL, assert_rows_close, say
+
+pytestmark = pytest.mark.gpu
+
+TINY = sg.GdnShape(batch=3, nv=4, nk=2, dk=16, dv=32, window=4)
+LAYER_SMALL = sg.GdnShape(batch=3, nv=32, nk=16, dk=128, dv=128, window=16)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _bg():
+    from mamba_state_replay_amd import binding_gdn as bg
+    return bg
+
+
+def _cfg(shape, T, in_dtype):
+    bg = _bg()
+    return bg.GdnConfig(shape.batch, shape.nv, shape.nk, shape.dk, shape.dv, shape.window, T, in_dtype)
+
+
+def _state(cfg, S0, dev):
+    st = _bg().GdnState.allocate(cfg, dev)
+    st.ckpt.copy_(torch.from_numpy(np.ascontiguousarray(S0)).to(dev))
+    return st
+
+
+def state_err(got, ref):
+    """Per (sequence, head) state error normalized by the head's largest |ref|."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return np.abs(got - ref).max(axis=(-1, -2)) / np.maximum(np.abs(ref).max(axis=(-1, -2)), 1e-30)
+
+
+def _decode(shape, steps, seed, in_dtype, dev):
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    w = sg.gdn_workload(shape, steps, seed, in_dtype)
+    cfg = _cfg(shape, 1, in_dtype)
+    st = _state(cfg, w.S0, dev)
+    ts = GdnTokenStream(w.steps, dev)
+    o = torch.empty((steps, shape.batch, 1, shape.nv, shape.dv), device=dev)
+    say(f"gdn decode {shape} steps={steps} {in_dtype}")
+    for t in range(steps):
+        bg.gdn_decode_step(cfg, st, ts.call(t), o[t])
+    torch.cuda.synchronize()
+    return w, cfg, st, o.cpu().numpy()[:, :, 0]
+
+
+@pytest.mark.parametrize("shape,steps,in_dtype", [(TINY, 23, "f32"), (TINY, 23, "bf16"),
+                                                  (LAYER_SMALL, 37, "bf16")],
+                         ids=["tiny-f32", "tiny-bf16", "layer-bf16"])
+def test_gdn_decode_and_flush(shape, steps, in_dtype, dev):
+    """Decode from an empty buffer through several flushes; outputs and, after
+    a final flush, the checkpoint match stepping the gated delta rule."""
+    bg = _bg()
+    w, cfg, st, og = _decode(shape, steps, 31, in_dtype, dev)
+    t = w.steps
+    Sref, oref = ogdn.conventional(w.S0, t.q, t.k, t.v, t.g, t.beta)
+    assert_rows_close(og, oref, what="gdn decode outputs")
+    say("gdn flush")
+    bg.gdn_flush(cfg, st)
+    torch.cuda.synchronize()
+    err = state_err(st.ckpt.cpu().numpy(), Sref)
+    print(f"[gpu] gdn flushed state: max error per head {err.max():.2e}", flush=True)
+    assert err.max() <= TOL
+    meta = st.meta.cpu().numpy()
+    assert np.all(meta[..., 1] == 0) and np.all(meta == meta[:1, :1, :1])
+    assert int(st.status.cpu()[0]) == 0
+
+
+@pytest.mark.parametrize("shape,T,rounds,in_dtype", [(TINY, 3, 9, "f32"), (TINY, 2, 9, "bf16"),
+                                                     (LAYER_SMALL, 3, 12, "bf16"),
+                                                     (LAYER_SMALL, 1, 20, "bf16")],
+                         ids=["tiny-T3-f32", "tiny-T2-bf16", "layer-T3", "layer-T1"])
+def test_gdn_verify_commit(shape, T, rounds, in_dtype, dev):
+    """Speculative rounds: every draft's output equals stepping the accepted
+    tokens so far and then the drafts; rollback is a pointer move, so the
+    final checkpoint equals stepping only the accepted drafts."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    w = sg.gdn_workload(shape, rounds, 41 + T, in_dtype, T=T)
+    acc = w.extra["accepted"]
+    cfg = _cfg(shape, T, in_dtype)
+    st = _state(cfg, w.S0, dev)
+    ts = GdnTokenStream(w.steps, dev, T)
+    acc_d = torch.from_numpy(acc).to(dev)
+    o = torch.empty((rounds, shape.batch, T, shape.nv, shape.dv), device=dev)
+    say(f"gdn verify {shape} T={T} rounds={rounds} {in_dtype}")
+    for r in range(rounds):
+        bg.gdn_verify_drafts(cfg, st, ts.call(r), o[r])
+        bg.gdn_commit(cfg, st, acc_d[r], T)
+    bg.gdn_flush(cfg, st)
+    torch.cuda.synchronize()
+    tk = w.steps
+    S = w.S0.astype(np.float64)
+    oref = np.zeros((rounds, T, shape.batch, shape.nv, shape.dv))
+    for r in range(rounds):
+        sl = slice(r * T, (r + 1) * T)
+        args = (tk.q[sl], tk.k[sl], tk.v[sl], tk.g[sl], tk.beta[sl])
+        _, oref[r] = ogdn.conventional(S, *args)
+        S, _ = ogdn.conventional(S, *args, nsteps=acc[r])
+    og = np.swapaxes(o.cpu().numpy(), 1, 2)      # [rounds][T][batch][nv][dv]
+    assert_rows_close(og, oref, what="gdn draft outputs")
+    err = state_err(st.ckpt.cpu().numpy(), S)
+    print(f"[gpu] gdn state after rounds: max error per head {err.max():.2e}", flush=True)
+    assert err.max() <= TOL
+    assert int(st.status.cpu()[0]) == 0
+
+
+@pytest.mark.parametrize("shape,in_dtype", [(TINY, "f32"), (LAYER_SMALL, "bf16")], ids=["tiny", "layer"])
+def test_gdn_conventional_kernel(shape, in_dtype, dev):
+    """The conventional GDN step (baseline) matches the oracle step by step."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    steps = 9
+    w = sg.gdn_workload(shape, steps, 51, in_dtype)
+    cfg = _cfg(shape, 1, in_dtype)
+    S = torch.from_numpy(w.S0.copy()).to(dev)
+    ts = GdnTokenStream(w.steps, dev)
+    o = torch.empty((steps, shape.batch, 1, shape.nv, shape.dv), device=dev)
+    say(f"gdn conventional {shape} {in_dtype}")
+    for t in range(steps):
+        bg.gdn_conventional_update(cfg, S, ts.call(t), o[t])
+    torch.cuda.synchronize()
+    tk = w.steps
+    Sref, oref = ogdn.conventional(w.S0, tk.q, tk.k, tk.v, tk.g, tk.beta)
+    assert_rows_close(o.cpu().numpy()[:, :, 0], oref, what="gdn conventional outputs")
+    assert state_err(S.cpu().numpy(), Sref).max() <= TOL
+
+
+def test_gdn_decode_equals_verify_one_and_commit(dev):
+    """decode_step is verify(T=1) + commit(1), bit for bit, flushes included."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    shape = LAYER_SMALL
+    steps = 20
+    w = sg.gdn_workload(shape, steps, 61)
+    cfg = _cfg(shape, 1, "bf16")
+    a, b = _state(cfg, w.S0, dev), _state(cfg, w.S0, dev)
+    ts = GdnTokenStream(w.steps, dev)
+    one = torch.ones(shape.batch, dtype=torch.int32, device=dev)
+    oa = torch.empty((steps, shape.batch, 1, shape.nv, shape.dv), device=dev)
+    ob = torch.empty_like(oa)
+    say("gdn decode vs verify(1)+commit(1)")
+    for t in range(steps):
+        bg.gdn_decode_step(cfg, a, ts.call(t), oa[t])
+        bg.gdn_verify_drafts(cfg, b, ts.call(t), ob[t])
+        bg.gdn_commit(cfg, b, one, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
+    assert torch.equal(a.ckpt, b.ckpt) and torch.equal(a.meta, b.meta)
+
+
+def test_gdn_records_beyond_pointer_are_never_read(dev):
+    """Poison every ring slot outside the committed window with NaN before each
+    call: outputs are unchanged (records past the pointer are ignored)."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    shape = TINY
+    T, rounds = 2, 10
+    w = sg.gdn_workload(shape, rounds, 71, "f32", T=T)
+    acc = torch.from_numpy(w.extra["accepted"]).to(dev)
+    cfg = _cfg(shape, T, "f32")
+    clean, dirty = _state(cfg, w.S0, dev), _state(cfg, w.S0, dev)
+    ts = GdnTokenStream(w.steps, dev, T)
+    oc = torch.empty((rounds, shape.batch, T, shape.nv, shape.dv), device=dev)
+    od = torch.empty_like(oc)
+    cap = cfg.cap
+    say("gdn poisoned ring slots")
+    for r in range(rounds):
+        meta = dirty.meta.cpu().numpy()
+        for bb in range(shape.batch):
+            start, n = int(meta[bb, 0, 0, 0]), int(meta[bb, 0, 0, 1])
+            live = {(start + c) % cap for c in range(n)}
+            for s in range(cap):
+                if s not in live:
+                    dirty.buf_u[bb, :, s] = float("nan")
+                    dirty.buf_g[bb, :, s] = float("nan")
+                    dirty.buf_k[bb, :, s] = float("nan")
+        bg.gdn_verify_drafts(cfg, clean, ts.call(r), oc[r])
+        bg.gdn_verify_drafts(cfg, dirty, ts.call(r), od[r])
+        bg.gdn_commit(cfg, clean, acc[r], T)
+        bg.gdn_commit(cfg, dirty, acc[r], T)
+        torch.cuda.synchronize()
+    assert torch.isfinite(od).all()
+    assert torch.equal(oc, od)
+
+
+def test_gdn_bad_pointer_sets_status(dev):
+    """A ring pointer out of range: status bit, NaN outputs for that sequence,
+    its state untouched; the other sequences proceed."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    shape = TINY
+    w = sg.gdn_workload(shape, 1, 81, "f32")
+    cfg = _cfg(shape, 1, "f32")
+    st = _state(cfg, w.S0, dev)
+    st.meta[1, :, :, 0] = cfg.cap + 3
+    ts = GdnTokenStream(w.steps, dev)
+    o = torch.zeros((shape.batch, 1, shape.nv, shape.dv), device=dev)
+    say("gdn corrupt ring pointer (rejected by the kernel's own check)")
+    bg.gdn_decode_step(cfg, st, ts.call(0), o)
+    torch.cuda.synchronize()
+    assert int(st.status.cpu()[0]) & 1
+    on = o.cpu().numpy()
+    assert np.all(np.isnan(on[1])) and np.all(np.isfinite(on[[0, 2]]))
+    assert torch.equal(st.ckpt[1].cpu(), torch.from_numpy(w.S0[1]))
+    assert np.all(st.meta[1].cpu().numpy()[..., 0] == cfg.cap + 3)
+
+
+def test_gdn_commit_rejects_bad_counts(dev):
+    bg = _bg()
+    cfg = _cfg(TINY, 2, "f32")
+    st = bg.GdnState.allocate(cfg, dev)
+    acc = torch.tensor([0, 3, 1], dtype=torch.int32, device=dev)
+    say("gdn commit with an accepted count above T")
+    bg.gdn_commit(cfg, st, acc, 2)
+    torch.cuda.synchronize()
+    assert int(st.status.cpu()[0]) & 2
+    m = st.meta.cpu().numpy()
+    assert np.all(m[0, ..., 1] == 0) and np.all(m[1, ..., 1] == 0) and np.all(m[2, ..., 1] == 1)
