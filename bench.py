@@ -54,12 +54,16 @@ def parse():
     ap.add_argument("--no-conventional", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU sample")
-    ap.add_argument("--config", choices=["decode", "verify", "verify_sweep", "sweep", "dual"], default="decode",
+    ap.add_argument("--config", choices=["decode", "verify", "verify_sweep", "sweep", "dual", "gdn"], default="decode",
                     help="decode: the headline line (default); verify: speculative rounds at batch 512, "
                          "T=3; verify_sweep: the same for T in 1, 2, 3, 4, 8; sweep: batch x window grid; "
-                         "dual: FP32 / bf16 / e4m3 read copies over 4096 steps")
+                         "dual: FP32 / bf16 / e4m3 read copies over 4096 steps; gdn: Gated DeltaNet layer "
+                         "decode and verify (batch --gdn-batch)")
+    ap.add_argument("--gdn-batch", type=int, default=512)
     ap.add_argument("--summarize-configs", nargs="+", metavar="LOG",
                     help="write the tables of bench logs of the non-default configs into profiles/ and exit")
+    ap.add_argument("--ingest-gdn-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
+                    help="summarise rocprofv3 output of the GDN runs into profiles/ and exit")
     ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                     help="summarise rocprofv3 output of the counter runs into profiles/ and exit")
     return ap.parse_args()
@@ -111,6 +115,9 @@ def main():
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters)
         return
+    if args.ingest_gdn_counters:
+        ingest_gdn_counters(*args.ingest_gdn_counters)
+        return
     if args.summarize_configs:
         summarize_configs(args.summarize_configs)
         return
@@ -120,7 +127,7 @@ def main():
         sys.exit(2)
     if args.config != "decode":
         {"verify": bench_verify, "verify_sweep": bench_verify_sweep, "sweep": bench_sweep,
-         "dual": bench_dual}[args.config](args)
+         "dual": bench_dual, "gdn": bench_gdn}[args.config](args)
         return
 
     import torch
@@ -271,6 +278,157 @@ def main():
         result["cpu_baseline"] = cpu_baseline(work, total_bytes / K, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+GDN_LAYER = dict(nv=32, nk=16, dk=128, dv=128)
+
+
+def bench_gdn(args):
+    """Gated DeltaNet layer (32 value heads over 16 key heads, dk = dv = 128,
+    FP32 state 2 MiB per sequence), batch --gdn-batch, L = --window: replay
+    decode steps (steady state reached from an empty buffer during the
+    warm-up) against the in-library conventional GDN step, then speculative
+    rounds of T = 3 drafts with U{0..3} acceptance; one JSON line."""
+    torch, dev = _device()
+    from mamba_state_replay_amd import binding_gdn as bg
+    from mamba_state_replay_amd import staging, synth_gdn, traffic
+
+    L, batch = args.window, args.gdn_batch
+    shape = synth_gdn.GdnShape(batch=batch, window=L, **GDN_LAYER)
+    ntok = 32
+    w = synth_gdn.gdn_workload(shape, ntok, seed=2001)
+    cfg = bg.GdnConfig(batch, shape.nv, shape.nk, shape.dk, shape.dv, L, 1, "bf16")
+    st = bg.GdnState.allocate(cfg, dev)
+    st.ckpt.copy_(torch.from_numpy(w.S0).to(dev))
+    toks = staging.GdnTokenStream(w.steps, dev)
+    o = torch.empty((batch, 1, shape.nv, shape.dv), device=dev)
+    sz = traffic.gdn_sizes(shape.nv, shape.nk, shape.dk, shape.dv)
+    W, K = max(args.warmup, L + 1), args.steps
+    for i in range(W):
+        bg.gdn_decode_step(cfg, st, toks.call(i % ntok), o)
+    sched, n_end = traffic.decode_schedule(np.zeros(batch, np.int64), L, W + 3 * K)
+    eager_sched, graph_sched = sched[W:W + K], sched[W + 2 * K:W + 3 * K]
+    step = lambda i: bg.gdn_decode_step(cfg, st, toks.call((W + i) % ntok), o)
+    eager_ms, per_ms = timed_launches(step, K, torch)
+    total_ms = graph_time(lambda i: bg.gdn_decode_step(cfg, st, toks.call((W + K + i) % ntok), o), K, torch)
+    meta = st.meta.cpu().numpy()
+    assert np.all(meta[..., 1] == n_end[:, None, None]), "ring pointers disagree with the flush schedule"
+    assert int(st.status.cpu()[0]) == 0 and bool(torch.isfinite(o).all())
+    launch_bytes = [traffic.decode_step_bytes(sz, n, f) for n, f in eager_sched]
+    step_bytes = sum(traffic.decode_step_bytes(sz, n, f) for n, f in graph_sched) / K
+    kernel_ms = float(np.mean(per_ms))
+    achieved = float(np.mean(launch_bytes)) / (kernel_ms * 1e-3) / 1e9
+    fold_ms = [t for t, (_, f) in zip(per_ms, eager_sched) if f.any()]
+    nonfold_ms = [t for t, (_, f) in zip(per_ms, eager_sched) if not f.any()]
+    us_step = total_ms * 1e3 / K
+    gdn_hash = source_hash(["mamba_state_replay_amd/csrc/gdn.hip", "mamba_state_replay_amd/csrc/common.h"])
+    gdn_counters = ROOT / "profiles" / "gdn_decode_batch512_L16_counters.json"
+    traffic_bytes = None
+    if gdn_counters.exists():
+        c = json.loads(gdn_counters.read_text())
+        if c.get("source_hash") == gdn_hash and c.get("batch") == batch and c.get("window") == L:
+            traffic_bytes = c.get("bytes_per_launch")
+
+    S = torch.from_numpy(w.S0).to(dev)
+    cstep = lambda i: bg.gdn_conventional_update(cfg, S, toks.call(i % ntok), o)
+    for i in range(4):
+        cstep(i)
+    ceager, cper = timed_launches(cstep, K, torch)
+    ctot = graph_time(cstep, K, torch)
+    cbytes = traffic.conventional_step_bytes(sz, batch)
+    c_us = ctot * 1e3 / K
+    del S
+
+    # speculative rounds: T = 3 drafts, U{0..3} accepted, verify + commit
+    T, rounds = 3, 32
+    vw = synth_gdn.gdn_workload(shape, rounds, seed=2003, T=T, ckpt_std=0.0)
+    vcfg = bg.GdnConfig(batch, shape.nv, shape.nk, shape.dk, shape.dv, L, T, "bf16")
+    del st, toks
+    vst = bg.GdnState.allocate(vcfg, dev)
+    vst.ckpt.copy_(torch.from_numpy(w.S0).to(dev))
+    vtoks = staging.GdnTokenStream(vw.steps, dev, T)
+    acc = torch.from_numpy(vw.extra["accepted"]).to(dev)
+    vo = torch.empty((batch, T, shape.nv, shape.dv), device=dev)
+    vround = lambda r: (bg.gdn_verify_drafts(vcfg, vst, vtoks.call(r % rounds), vo),
+                        bg.gdn_commit(vcfg, vst, acc[r % rounds], T))
+    for r in range(8):
+        vround(r)
+    v_ms = graph_time(lambda r: vround(8 + r), rounds, torch)
+    assert int(vst.status.cpu()[0]) == 0 and bool(torch.isfinite(vo).all())
+
+    result = {
+        "metric": "GDN layer decode-step us + achieved HBM GB/s",
+        "value": round(step_bytes / (us_step * 1e-6) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(total_ms / K, 6),
+        "us_per_step": round(us_step, 2),
+        "timing": "K steps captured in one HIP graph, one replay timed with HIP events after a warm replay",
+        "eager_us_per_step": round(eager_ms * 1e3 / K, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"Gated DeltaNet layer decode (ReplaySSM), batch {batch}, 32 value heads over 16 "
+                               f"key heads, dk = dv = 128, L={L}, bf16 q/k/v, fp32 g/beta, FP32 checkpoint "
+                               f"(2 MiB per sequence), steady state",
+                   "batch": batch, "window": L, "flush_launches_timed": len(fold_ms)},
+        "kernel_source_hash": gdn_hash,
+        "roofline": {"bound": "hbm", "kernel": "gdn_replay_kernel", "achieved": round(achieved, 1),
+                     "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic_bytes, "algorithmic_bytes_per_launch": int(np.mean(launch_bytes)),
+                     "avg_launch_us": round(kernel_ms * 1e3, 2),
+                     "nonflush_launch_us": round(float(np.mean(nonfold_ms)) * 1e3, 2) if nonfold_ms else None,
+                     "flush_launch_us": round(float(np.mean(fold_ms)) * 1e3, 2) if fold_ms else None},
+        "conventional": {"us_per_step": round(c_us, 2), "eager_us_per_step": round(ceager * 1e3 / K, 2),
+                         "gbs": round(cbytes / (c_us * 1e-6) / 1e9, 1),
+                         "avg_launch_us": round(float(np.mean(cper)) * 1e3, 2),
+                         "frac": round(cbytes / (float(np.mean(cper)) * 1e-3) / 1e9 / PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": cbytes},
+        "speedup_vs_conventional": round(c_us / us_step, 3),
+        "verify_T3": {"us_per_round": round(v_ms * 1e3 / rounds, 2), "rounds": rounds,
+                      "conventional_3_steps_us": round(3 * c_us, 2),
+                      "note": "verify + commit per round, graph-timed; 3 conventional steps for scale"},
+    }
+    if not args.no_probe:
+        from mamba_state_replay_amd import binding as rb
+        del vst, vtoks
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            rb.rssm_probe_copy(dst, src)
+        _, cper = timed_launches(lambda i: rb.rssm_probe_copy(dst, src), 10, torch)
+        copy_gbs = 2 * nbytes / (float(np.median(cper)) * 1e-3) / 1e9
+        result["probe"] = {"copy_gbs": round(copy_gbs, 1), "bytes": nbytes}
+        del src, dst
+    if not args.no_cpu:
+        result["cpu_baseline"] = gdn_cpu_baseline(w, step_bytes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def gdn_cpu_baseline(w, gpu_bytes_per_step, target_s):
+    """The fp64 GDN oracle (numpy, BLAS threads) stepping a bounded sample of
+    the same workload: 4 sequences x 32 heads through the tokens, repeated up
+    to about target_s seconds, scaled to the batch."""
+    from oracle import gdn as ogdn
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    nseq, tk = 4, w.steps
+    sl = slice(0, nseq)
+    t0 = time.perf_counter()
+    passes, nsteps = 0, tk.steps
+    while passes == 0 or (time.perf_counter() - t0 < target_s and passes < 20):
+        ogdn.conventional(w.S0[sl], tk.q[:, sl], tk.k[:, sl], tk.v[:, sl], tk.g[:, sl], tk.beta[:, sl])
+        passes += 1
+    el = time.perf_counter() - t0
+    step_s = el / (passes * nsteps) * w.shape.batch / nseq
+    return {"value": round(gpu_bytes_per_step / step_s / 1e9, 4), "unit": "GB/s",
+            "us_per_step": round(step_s * 1e6, 1), "cores": threads, "kind": "oracle",
+            "sample": f"{nseq} sequences x 32 heads x {nsteps} tokens, {passes} pass(es), {el:.1f} s "
+                      f"(fp64 gated delta rule, numpy), scaled to {w.shape.batch} sequences",
+            "host_cpu": _cpu_model()}
 
 
 def cpu_baseline(work, gpu_bytes_per_step, target_s):
@@ -670,6 +828,103 @@ def summarize_configs(logs):
         md.append("")
     CONFIG_SUMMARY.write_text("\n".join(md) + "\n")
     print(f"wrote {CONFIG_SUMMARY}")
+
+
+GDN_PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/gprof -o trace -- "
+             "python -u bench.py --config gdn --no-cpu --steps 32 --warmup 17",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/gpmc_fetch -o fetch -- "
+             "python -u bench.py --config gdn --no-cpu --steps 16 --warmup 17",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/gpmc_write -o write -- "
+             "python -u bench.py --config gdn --no-cpu --steps 16 --warmup 17",
+}
+
+
+def ingest_gdn_counters(fetch_dir, write_dir, trace_dir):
+    """Summarise the GDN runs of GDN_PROFILE_CMDS into profiles/.
+
+    The bench's eager decode launches are the replay-kernel dispatches warmup ..
+    warmup + steps - 1 (in dispatch order); counters are scaled by what they
+    read for the 1 GiB copy probe of the same run."""
+    import csv
+    from mamba_state_replay_amd import traffic
+
+    def bench_line(d):
+        log = Path(d).parent / (Path(d).name + ".log")
+        for line in reversed(log.read_text().splitlines()):
+            if line.startswith("{"):
+                return json.loads(line)
+        raise ValueError(f"no bench JSON line in {log}")
+
+    def eager(rows, key, line):
+        rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+        W, K = line["warmup"], line["steps"]
+        return rows[W:W + K]
+
+    def counters(d, name):
+        rows = list(csv.DictReader(open(next(Path(d).glob("*counter_collection.csv")))))
+        line = bench_line(d)
+        rep = eager([r for r in rows if "gdn_replay_kernel" in r["Kernel_Name"] and r["Counter_Name"] == name],
+                    name, line)
+        cp = [float(r["Counter_Value"]) for r in rows
+              if "probe_copy_kernel" in r["Kernel_Name"] and r["Counter_Name"] == name]
+        return [float(r["Counter_Value"]) for r in rep], cp, line
+
+    f_rep, f_cp, fl = counters(fetch_dir, "FETCH_SIZE")
+    w_rep, w_cp, wl = counters(write_dir, "WRITE_SIZE")
+    assert fl["kernel_source_hash"] == wl["kernel_source_hash"]
+    gib_kib = (1 << 30) / 1024
+    ff, wf = gib_kib / float(np.mean(f_cp)), gib_kib / float(np.mean(w_cp))
+    fetch_b, write_b = float(np.mean(f_rep)) * ff * 1024, float(np.mean(w_rep)) * wf * 1024
+    L, batch, W, K = fl["config"]["window"], fl["config"]["batch"], fl["warmup"], fl["steps"]
+    sched, _ = traffic.decode_schedule(np.zeros(batch, np.int64), L, W + K)
+    sz = traffic.gdn_sizes(GDN_LAYER["nv"], GDN_LAYER["nk"], GDN_LAYER["dk"], GDN_LAYER["dv"])
+    alg = float(np.mean([traffic.decode_step_bytes(sz, n, f) for n, f in sched[W:W + K]]))
+    out = {"kernel": "gdn_replay_kernel<128, bf16 inputs>", "batch": batch, "window": L, "dispatches": len(f_rep),
+           "source_hash": fl["kernel_source_hash"],
+           "fetch_kib_per_dispatch": round(float(np.mean(f_rep)), 1),
+           "write_kib_per_dispatch": round(float(np.mean(w_rep)), 1),
+           "fetch_scale": round(ff, 4), "write_scale": round(wf, 4),
+           "bytes_per_launch": int(fetch_b + write_b), "algorithmic_bytes_per_launch": int(alg),
+           "traffic_over_algorithmic": round((fetch_b + write_b) / alg, 4),
+           "commands": [GDN_PROFILE_CMDS["fetch"], GDN_PROFILE_CMDS["write"]]}
+    (ROOT / "profiles" / "gdn_decode_batch512_L16_counters.json").write_text(json.dumps(out, indent=1) + "\n")
+
+    trows = list(csv.DictReader(open(next(Path(trace_dir).glob("*kernel_trace.csv")))))
+    tl = bench_line(trace_dir)
+    dec = eager([r for r in trows if "gdn_replay_kernel" in r["Kernel_Name"]], None, tl)
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in dec]
+    tsched, _ = traffic.decode_schedule(np.zeros(batch, np.int64), L, tl["warmup"] + tl["steps"])
+    tsched = tsched[tl["warmup"]:tl["warmup"] + tl["steps"]]
+    fl_d = [d for d, (_, f) in zip(dur, tsched) if f.any()]
+    nf_d = [d for d, (_, f) in zip(dur, tsched) if not f.any()]
+    stats = list(csv.DictReader(open(next(Path(trace_dir).glob("*kernel_stats.csv")))))
+    md = ["# GDN layer decode, batch 512, L = 16 (32 value heads over 16 key heads, dk = dv = 128): "
+          "kernel trace and HBM counters", "", "Kernel trace (one MI355X):", "", "```", GDN_PROFILE_CMDS["trace"],
+          "```", "", "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        if "gdn_" not in r["Name"] and "probe_copy" not in r["Name"] and "commit" not in r["Name"]:
+            continue
+        name = r["Name"].replace("void ", "").replace("rssm::(anonymous namespace)::", "").split("(")[0]
+        md.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    md += ["", "The replay kernel's calls mix decode (T = 1) and verify (T = 3) launches. Its "
+           f"{len(dur)} eager decode launches of the timed region (dispatches {tl['warmup']} .. "
+           f"{tl['warmup'] + tl['steps'] - 1}): average {np.mean(dur):.2f} us, non-flush {np.mean(nf_d):.2f} us, "
+           f"flush {np.mean(fl_d) if fl_d else float('nan'):.2f} us (bench line of the same run: "
+           f"{tl['roofline']['avg_launch_us']} us average).", "",
+           "HBM counters (separate runs, one counter each; the eager decode launches):", "", "```",
+           GDN_PROFILE_CMDS["fetch"], GDN_PROFILE_CMDS["write"], "```", "",
+           "| | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch |", "|---|---|---|",
+           f"| gdn_replay_kernel (average of {len(f_rep)} decode dispatches) | {np.mean(f_rep):.1f} | "
+           f"{np.mean(w_rep):.1f} |",
+           f"| probe_copy_kernel, 1 GiB read + 1 GiB written | {np.mean(f_cp):.1f} | {np.mean(w_cp):.1f} |", "",
+           f"Scale factors from the copy probe: FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {wf:.4f}.",
+           f"GDN replay kernel: {fetch_b / 1e9:.4f} GB fetched + {write_b / 1e9:.4f} GB written = "
+           f"{(fetch_b + write_b) / 1e9:.4f} GB per launch, against {alg / 1e9:.4f} GB algorithmic "
+           f"(ratio {(fetch_b + write_b) / alg:.4f}).", f"Kernel source hash {fl['kernel_source_hash']}."]
+    (ROOT / "profiles" / "gdn_decode_batch512_L16.md").write_text("\n".join(md) + "\n")
+    print(json.dumps(out))
 
 
 def ingest_counters(fetch_dir, write_dir, trace_dir):

@@ -233,3 +233,59 @@ def test_gdn_commit_rejects_bad_counts(dev):
     assert int(st.status.cpu()[0]) & 2
     m = st.meta.cpu().numpy()
     assert np.all(m[0, ..., 1] == 0) and np.all(m[1, ..., 1] == 0) and np.all(m[2, ..., 1] == 1)
+
+
+FULL = sg.GdnShape(batch=512, nv=32, nk=16, dk=128, dv=128, window=16)
+SAMPLE = [0, 137, 300, 511]
+
+
+def test_gdn_fullsize_decode_sampled(dev):
+    """The benchmarked GDN launch (batch 512, 32 value heads, dk = dv = 128,
+    L = 16, bf16 inputs, seed of the bench): 20 decode steps (one flush) over
+    the whole batch, then a flush; sampled sequences against the oracle."""
+    bg = _bg()
+    steps = 20
+    w, cfg, st, og = _decode(FULL, steps, 2001, "bf16", dev)
+    bg.gdn_flush(cfg, st)
+    torch.cuda.synchronize()
+    t = w.steps
+    sl = np.array(SAMPLE)
+    Sref, oref = ogdn.conventional(w.S0[sl], t.q[:, sl], t.k[:, sl], t.v[:, sl], t.g[:, sl], t.beta[:, sl])
+    assert_rows_close(og[:, sl], oref, what="gdn full-size decode outputs (sampled)")
+    err = state_err(st.ckpt[torch.from_numpy(sl).to(dev)].cpu().numpy(), Sref)
+    assert err.max() <= TOL
+    assert int(st.status.cpu()[0]) == 0
+
+
+def test_gdn_fullsize_verify_sampled(dev):
+    """Speculative rounds at the benchmarked size (batch 512, T = 3, U{0..3}
+    acceptance): sampled sequences' draft outputs and final state."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    T, rounds = 3, 8
+    w = sg.gdn_workload(FULL, rounds, 2003, "bf16", T=T)
+    acc = w.extra["accepted"]
+    cfg = _cfg(FULL, T, "bf16")
+    st = _state(cfg, w.S0, dev)
+    ts = GdnTokenStream(w.steps, dev, T)
+    acc_d = torch.from_numpy(acc).to(dev)
+    o = torch.empty((rounds, FULL.batch, T, FULL.nv, FULL.dv), device=dev)
+    say(f"gdn full-size verify T={T} rounds={rounds}")
+    for r in range(rounds):
+        bg.gdn_verify_drafts(cfg, st, ts.call(r), o[r])
+        bg.gdn_commit(cfg, st, acc_d[r], T)
+    bg.gdn_flush(cfg, st)
+    torch.cuda.synchronize()
+    sl = np.array(SAMPLE)
+    tk = w.steps
+    S = w.S0[sl].astype(np.float64)
+    oref = np.zeros((rounds, T, len(sl), FULL.nv, FULL.dv))
+    for r in range(rounds):
+        rs = slice(r * T, (r + 1) * T)
+        args = (tk.q[rs][:, sl], tk.k[rs][:, sl], tk.v[rs][:, sl], tk.g[rs][:, sl], tk.beta[rs][:, sl])
+        _, oref[r] = ogdn.conventional(S, *args)
+        S, _ = ogdn.conventional(S, *args, nsteps=acc[r][sl])
+    og = np.swapaxes(o.cpu().numpy()[:, sl], 1, 2)
+    assert_rows_close(og, oref, what="gdn full-size draft outputs (sampled)")
+    assert state_err(st.ckpt[torch.from_numpy(sl).to(dev)].cpu().numpy(), S).max() <= TOL
+    assert int(st.status.cpu()[0]) == 0
