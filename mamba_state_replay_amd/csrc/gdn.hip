@@ -21,22 +21,22 @@
 //
 // One call of gdn_replay_kernel, workgroup = (sequence b, value head h, row block p):
 //  1. read the workgroup's ring pointer {start, n}; decide the flush (n >= L,
-//     or n > 0 in flush mode); issue the tile's loads;
-//  2. stage the committed records (keys widened to fp32, this block's u rows,
-//     g) and the call's tokens (q, k, this block's v rows, g, beta) in LDS; the
+//     or n > 0 in flush mode);
+//  2. load the committed records (keys, this block's u rows, g) and the call's
+//     tokens (q, k, this block's v rows, g, beta), issue the tile's loads behind
+//     them, and stage the records and tokens in LDS (keys widened to fp32); the
 //     first block of the key head's first value head appends the tokens' keys
 //     to the key ring;
 //  3. flush: fold the records into the tile registers (rank-n update), store
 //     the tile once, move the pointer past the folded records;
 //  4. one 8-lane group per (query, window position) pair forms the segment
 //     decay and the key-key and key-query scores;
-//  5. per query, each thread forms its rows' share of S_s k_q and S_s q_q from
-//     the registers, scaled by the query's checkpoint decay, adds the committed
-//     records' terms (records split over the row's lanes) and the row's lanes
-//     reduce;
-//  6. one thread per row walks the queries in order, adding the draft records'
-//     terms: u_q, then o_q; it writes o and appends u;
-//  7. write the ring pointer (decode commits its token).
+//  5. per query, in order, each thread forms its rows' share of S_s k_q and
+//     S_s q_q from the registers, scaled by the query's checkpoint decay, adds
+//     the committed records' terms (records split over the row's lanes); the
+//     row's lanes reduce and each adds the earlier drafts' terms and forms
+//     u_q, then o_q; one lane per row writes o and appends u;
+//  6. write the ring pointer (decode commits its token).
 #include "common.h"
 #include "kernels.h"
 
@@ -54,7 +54,7 @@ struct GdnGeo<128> { static constexpr int ROWS = 64, NT = 256; };
 // LDS plan in floats.  Committed records use window positions 0 .. n-1; the
 // call's tokens (queries) sit at n .. n+T-1 after any flush.
 struct GdnLds {
-    int K, KQ, QQ, U, US, V, G, GQ, BE, CK, CQ, DD, WF, PK, PQ, UD, total;
+    int K, KQ, QQ, U, US, V, G, GQ, BE, CK, CQ, DD, WF, UD, total;
 };
 
 __host__ __device__ inline GdnLds gdn_plan(int DK, int ROWS, int cap, int T) {
@@ -73,14 +73,10 @@ __host__ __device__ inline GdnLds gdn_plan(int DK, int ROWS, int cap, int T) {
     l.CQ = o; o += T * cap;         // cq[q][c] = exp(sum_{c<i<=m_q} g_i) (key_c . q_q), c <= m_q
     l.DD = o; o += T + 1;           // dd[q] = exp(sum_{i<=m_q} g_i); [T]: the flush's checkpoint decay
     l.WF = o; o += cap;             // flush weights exp(sum_{c<i<n} g_i)
-    l.PK = o; o += T * ROWS;        // reduced checkpoint + committed-record part of alpha_q S k_q
-    l.PQ = o; o += T * ROWS;        // same for S q_q
     l.UD = o; o += T * ROWS;        // the tokens' u
     l.total = (o + 3) & ~3;
     return l;
 }
-
-constexpr int kGdnIntSlots = 4;     // LDS ints after the float plan: start, n, fold, ok
 
 __device__ __forceinline__ float dot4(const v4f a, const float4 b) {
     float s = a[0] * b.x;
@@ -90,7 +86,7 @@ __device__ __forceinline__ float dot4(const v4f a, const float4 b) {
 }
 
 template <int DK, typename InT>
-__global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_replay_kernel(const GdnArgs a) {
+__global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const GdnArgs a) {
     constexpr int ROWS = GdnGeo<DK>::ROWS;
     constexpr int NT = GdnGeo<DK>::NT;
     using Geo = TileGeo<ROWS, DK, NT, 4>;
@@ -111,33 +107,112 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_replay_kernel(const Gdn
     const int cap = a.cap;
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
     const GdnLds Ls = gdn_plan(DK, ROWS, cap, T);
-    int* si = reinterpret_cast<int*>(smem + Ls.total);
 
-    // 1. ring pointer and flush decision
-    if (tid == 0) {
-        const int start = a.meta[2 * wg];
-        const int n = a.meta[2 * wg + 1];
-        bool ok = start >= 0 && start < cap && n >= 0 && n <= cap;
-        const int fold = ok && (a.mode == MODE_FLUSH ? n > 0 : n >= a.L);
-        const int np = fold ? 0 : n;
-        ok = ok && np + T <= cap;
-        si[0] = start;
-        si[1] = n;
-        si[2] = fold;
-        si[3] = ok;
-        if (!ok && a.status) atomicOr(a.status, (int)kStatusMeta);
-    }
-    __syncthreads();
-    const int start = si[0], n = si[1];
-    const bool fold = si[2] != 0;
-    if (!si[3]) {
+    // 1. ring pointer and flush decision (every thread reads the workgroup's copy)
+    const int start = a.meta[2 * wg];
+    const int n = a.meta[2 * wg + 1];
+    const bool valid = start >= 0 && start < cap && n >= 0 && n <= cap;
+    const bool fold = valid && (a.mode == MODE_FLUSH ? n > 0 : n >= a.L);
+    const int np = fold ? 0 : n;                          // committed records seen by the queries
+    if (!valid || np + T > cap) {
+        if (tid == 0 && a.status) atomicOr(a.status, (int)kStatusMeta);
         for (int i = tid; i < T * ROWS; i += NT)
             a.o[((size_t)(b * T + i / ROWS) * a.nv + h) * a.dv + p * ROWS + i % ROWS] = __builtin_nanf("");
         return;
     }
     if (!fold && T == 0) return;                          // flush call with nothing to fold
-    const int np = fold ? 0 : n;                          // committed records seen by the queries
-    const int qstart = fold ? (start + n) % cap : start;  // ring start after the flush
+    int qstart = start + n;                               // ring start after the flush
+    qstart -= qstart >= cap ? cap : 0;
+    if (!fold) qstart = start;
+
+    // 2. staging: the records' and tokens' 16-byte vectors are loaded into
+    // registers first, the tile's loads are issued behind them, and the staged
+    // vectors are stored to LDS while the tile is still in flight (loads
+    // complete in order, so waiting for a staged vector never waits for the tile).
+    const InT* kring = static_cast<const InT*>(a.buf_k) + (size_t)(b * a.nk + kh) * cap * DK;
+    const float* uring = a.buf_u + (size_t)bh * cap * a.dv + p * ROWS;
+    const bool append_k = (h % (a.nv / a.nk)) == 0 && p == 0;
+    const int nkv = n * KV, nuv = n * UV, ntk = T * KV;
+    const int total = nkv + nuv + 2 * ntk + T * RV;
+    // Vector i of the staging list: its source, its LDS destination, whether it
+    // is widened from InT (else copied as fp32), and where a token key is
+    // appended to the key ring (or null).
+    auto job = [&](int i, const uint4*& src, float*& dst, bool& widen, uint4*& app) {
+        app = nullptr;
+        widen = true;
+        if (i < nkv) {
+            const int c = i / KV, e = i - c * KV;
+            int slot = start + c;
+            slot -= slot >= cap ? cap : 0;
+            src = reinterpret_cast<const uint4*>(kring + (size_t)slot * DK) + e;
+            dst = smem + Ls.K + c * DK + e * EPV;
+            return;
+        }
+        i -= nkv;
+        if (i < nuv) {
+            const int c = i / UV, e = i - c * UV;
+            int slot = start + c;
+            slot -= slot >= cap ? cap : 0;
+            src = reinterpret_cast<const uint4*>(uring + (size_t)slot * a.dv) + e;
+            dst = smem + Ls.U + c * Ls.US + 4 * e;
+            widen = false;
+            return;
+        }
+        i -= nuv;
+        if (i < 2 * ntk) {
+            const bool isq = i >= ntk;
+            const int r = isq ? i - ntk : i;
+            const int q = r / KV, e = r - q * KV;
+            src = reinterpret_cast<const uint4*>(static_cast<const InT*>(isq ? a.q : a.k) +
+                                                 ((size_t)(b * T + q) * a.nk + kh) * DK) + e;
+            dst = smem + (isq ? Ls.QQ : Ls.KQ) + q * DK + e * EPV;
+            if (!isq && append_k) {
+                int slot = qstart + np + q;
+                slot -= slot >= cap ? cap : 0;
+                app = reinterpret_cast<uint4*>(static_cast<InT*>(a.buf_k) +
+                                               ((size_t)(b * a.nk + kh) * cap + slot) * DK) + e;
+            }
+            return;
+        }
+        i -= 2 * ntk;
+        const int q = i / RV, e = i - q * RV;
+        src = reinterpret_cast<const uint4*>(static_cast<const InT*>(a.v) +
+                                             ((size_t)(b * T + q) * a.nv + h) * a.dv + p * ROWS) + e;
+        dst = smem + Ls.V + q * ROWS + e * EPV;
+    };
+    auto put = [&](float* dst, bool widen, uint4* app, const uint4 v) {
+        if (app) *app = v;
+        if (widen) {
+            widen16<InT>(v, dst);
+        } else {
+            *reinterpret_cast<uint4*>(dst) = v;
+        }
+    };
+    constexpr int JOBS = 2;
+    uint4 jv[JOBS];
+#pragma unroll
+    for (int j = 0; j < JOBS; ++j) {
+        const int i = tid + j * NT;
+        if (i < total) {
+            const uint4* src;
+            float* dst;
+            bool widen;
+            uint4* app;
+            job(i, src, dst, widen, app);
+            jv[j] = *src;
+        }
+    }
+    float gv = 0.0f, gq = 0.0f, bq = 0.0f;
+    if (tid < n) {
+        int slot = start + tid;
+        slot -= slot >= cap ? cap : 0;
+        gv = a.buf_g[(size_t)bh * cap + slot];
+    }
+    if (tid < T) {
+        const size_t ti = (size_t)(b * T + tid) * a.nv + h;
+        gq = a.g[ti];
+        bq = a.beta[ti];
+    }
 
     float* const tile_p = a.ckpt + ((size_t)bh * a.dv + p * ROWS) * DK;
     v4f raw[Geo::NV];
@@ -146,67 +221,35 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_replay_kernel(const Gdn
         raw[s] = __builtin_bit_cast(v4f, __builtin_nontemporal_load(reinterpret_cast<const v4u*>(tile_p) +
                                                                     Geo::vec(tid, s)));
 
-    // 2. stage records and tokens
-    {
-        const InT* kring = static_cast<const InT*>(a.buf_k) + (size_t)(b * a.nk + kh) * cap * DK;
-        const float* uring = a.buf_u + (size_t)bh * cap * a.dv + p * ROWS;
-        const float* gring = a.buf_g + (size_t)bh * cap;
-        const bool append_k = (h % (a.nv / a.nk)) == 0 && p == 0;
-        const int nk = n * KV, nu = n * UV, ntk = T * KV, ntv = T * RV;
-        const int total = nk + nu + 2 * ntk + ntv;
-        for (int i = tid; i < total; i += NT) {
-            int r = i;
-            if (r < nk) {
-                const int c = r / KV, e = r % KV;
-                int slot = start + c;
-                slot -= slot >= cap ? cap : 0;
-                const uint4 v = reinterpret_cast<const uint4*>(kring + (size_t)slot * DK)[e];
-                widen16<InT>(v, smem + Ls.K + c * DK + e * EPV);
-                continue;
-            }
-            r -= nk;
-            if (r < nu) {
-                const int c = r / UV, e = r % UV;
-                int slot = start + c;
-                slot -= slot >= cap ? cap : 0;
-                const float4 v = reinterpret_cast<const float4*>(uring + (size_t)slot * a.dv)[e];
-                *reinterpret_cast<float4*>(smem + Ls.U + c * Ls.US + 4 * e) = v;
-                continue;
-            }
-            r -= nu;
-            if (r < 2 * ntk) {
-                const bool isq = r >= ntk;
-                const int rr = isq ? r - ntk : r;
-                const int q = rr / KV, e = rr % KV;
-                const InT* src = static_cast<const InT*>(isq ? a.q : a.k) + ((size_t)(b * T + q) * a.nk + kh) * DK;
-                const uint4 v = reinterpret_cast<const uint4*>(src)[e];
-                widen16<InT>(v, smem + (isq ? Ls.QQ : Ls.KQ) + q * DK + e * EPV);
-                if (!isq && append_k) {
-                    int slot = qstart + np + q;
-                    slot -= slot >= cap ? cap : 0;
-                    reinterpret_cast<uint4*>(static_cast<InT*>(a.buf_k) +
-                                             ((size_t)(b * a.nk + kh) * cap + slot) * DK)[e] = v;
-                }
-                continue;
-            }
-            r -= 2 * ntk;
-            {
-                const int q = r / RV, e = r % RV;
-                const InT* src = static_cast<const InT*>(a.v) + ((size_t)(b * T + q) * a.nv + h) * a.dv + p * ROWS;
-                const uint4 v = reinterpret_cast<const uint4*>(src)[e];
-                widen16<InT>(v, smem + Ls.V + q * ROWS + e * EPV);
-            }
+#pragma unroll
+    for (int j = 0; j < JOBS; ++j) {
+        const int i = tid + j * NT;
+        if (i < total) {
+            const uint4* src;
+            float* dst;
+            bool widen;
+            uint4* app;
+            job(i, src, dst, widen, app);
+            put(dst, widen, app, jv[j]);
         }
-        for (int i = tid; i < n; i += NT) {
-            int slot = start + i;
-            slot -= slot >= cap ? cap : 0;
-            smem[Ls.G + i] = gring[slot];
-        }
-        for (int i = tid; i < T; i += NT) {
-            const size_t ti = (size_t)(b * T + i) * a.nv + h;
-            smem[Ls.GQ + i] = a.g[ti];
-            smem[Ls.BE + i] = a.beta[ti];
-        }
+    }
+    for (int i = tid + JOBS * NT; i < total; i += NT) {   // windows longer than JOBS vectors a thread
+        const uint4* src;
+        float* dst;
+        bool widen;
+        uint4* app;
+        job(i, src, dst, widen, app);
+        put(dst, widen, app, *src);
+    }
+    if (tid < n) smem[Ls.G + tid] = gv;
+    for (int i = tid + NT; i < n; i += NT) {
+        int slot = start + i;
+        slot -= slot >= cap ? cap : 0;
+        smem[Ls.G + i] = a.buf_g[(size_t)bh * cap + slot];
+    }
+    if (tid < T) {
+        smem[Ls.GQ + tid] = gq;
+        smem[Ls.BE + tid] = bq;
     }
     __syncthreads();
 
@@ -216,31 +259,36 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_replay_kernel(const Gdn
     // 3. flush: S <- exp(sum g) S + sum_c exp(sum_{c<i<n} g_i) u_c k_c^T, stored once
     if (fold) {
         for (int c = tid; c < n; c += NT) {
-            float s = 0.0f;
-            for (int i = c + 1; i < n; ++i) s += smem[Ls.G + i];
-            smem[Ls.WF + c] = __expf(s);
+            float sg = 0.0f;
+            for (int i = c + 1; i < n; ++i) sg += smem[Ls.G + i];
+            smem[Ls.WF + c] = __expf(sg);
         }
         if (tid == NT - 1) {
-            float s = 0.0f;
-            for (int i = 0; i < n; ++i) s += smem[Ls.G + i];
-            smem[Ls.DD + T] = __expf(s);
+            float sg = 0.0f;
+            for (int i = 0; i < n; ++i) sg += smem[Ls.G + i];
+            smem[Ls.DD + T] = __expf(sg);
         }
         __syncthreads();
         const float gf = smem[Ls.DD + T];
 #pragma unroll
-        for (int s = 0; s < Geo::NV; ++s) {
-            const int row = row0 + s / Geo::VPL;
-            const int vc = lane + W * (s % Geo::VPL);
-            v4f acc = raw[s] * gf;
-            for (int c = 0; c < n; ++c) {
-                const float coef = smem[Ls.WF + c] * smem[Ls.U + c * Ls.US + row];
-                const float4 kc = *reinterpret_cast<const float4*>(smem + Ls.K + c * DK + 4 * vc);
-                acc[0] = fmaf(coef, kc.x, acc[0]);
-                acc[1] = fmaf(coef, kc.y, acc[1]);
-                acc[2] = fmaf(coef, kc.z, acc[2]);
-                acc[3] = fmaf(coef, kc.w, acc[3]);
+        for (int s = 0; s < Geo::NV; ++s) raw[s] *= gf;
+        for (int c = 0; c < n; ++c) {
+            float cf[Geo::NI];
+            const float wc = smem[Ls.WF + c];
+#pragma unroll
+            for (int r = 0; r < Geo::NI; ++r) cf[r] = wc * smem[Ls.U + c * Ls.US + row0 + r];
+#pragma unroll
+            for (int k = 0; k < Geo::VPL; ++k) {
+                const float4 kc = *reinterpret_cast<const float4*>(smem + Ls.K + c * DK + 4 * (lane + W * k));
+#pragma unroll
+                for (int r = 0; r < Geo::NI; ++r) {
+                    v4f& x = raw[r * Geo::VPL + k];
+                    x[0] = fmaf(cf[r], kc.x, x[0]);
+                    x[1] = fmaf(cf[r], kc.y, x[1]);
+                    x[2] = fmaf(cf[r], kc.z, x[2]);
+                    x[3] = fmaf(cf[r], kc.w, x[3]);
+                }
             }
-            raw[s] = acc;
         }
 #pragma unroll
         for (int s = 0; s < Geo::NV; ++s)
@@ -289,7 +337,13 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_replay_kernel(const Gdn
     }
     __syncthreads();
 
-    // 5. checkpoint products and committed-record terms, reduced over each row's lanes
+    // 5. per query, in order: the rows' share of S_s k_q and S_s q_q from the
+    // registers (scaled by the query's checkpoint decay) plus the committed
+    // records' terms (records split over the row's lanes), reduced over the
+    // row's lanes; then, on every lane of the row, the earlier drafts' terms,
+    // u_q and o_q.  The drafts' u rows are kept in LDS (each lane reads back
+    // what it wrote).
+    float* const uring_w = a.buf_u + (size_t)bh * cap * a.dv + p * ROWS;
     for (int q = 0; q < T; ++q) {
         float pk[Geo::NI], pq[Geo::NI];
 #pragma unroll
@@ -298,13 +352,15 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_replay_kernel(const Gdn
             pq[r] = 0.0f;
         }
 #pragma unroll
-        for (int s = 0; s < Geo::NV; ++s) {
-            const int r = s / Geo::VPL;
-            const int vc = lane + W * (s % Geo::VPL);
+        for (int k = 0; k < Geo::VPL; ++k) {
+            const int vc = lane + W * k;
             const float4 k4 = *reinterpret_cast<const float4*>(smem + Ls.KQ + q * DK + 4 * vc);
             const float4 q4 = *reinterpret_cast<const float4*>(smem + Ls.QQ + q * DK + 4 * vc);
-            pk[r] += dot4(raw[s], k4);
-            pq[r] += dot4(raw[s], q4);
+#pragma unroll
+            for (int r = 0; r < Geo::NI; ++r) {
+                pk[r] += dot4(raw[r * Geo::VPL + k], k4);
+                pq[r] += dot4(raw[r * Geo::VPL + k], q4);
+            }
         }
         const float d = smem[Ls.DD + q];
 #pragma unroll
@@ -322,37 +378,27 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_replay_kernel(const Gdn
                 pq[r] = fmaf(cq, u, pq[r]);
             }
         }
+        int slot = qstart + np + q;
+        slot -= slot >= cap ? cap : 0;
+        const float bet = smem[Ls.BE + q];
+        const float cself = smem[Ls.CQ + q * cap + np + q];
 #pragma unroll
         for (int r = 0; r < Geo::NI; ++r) {
-            pk[r] = group_sum<W>(pk[r]);
-            pq[r] = group_sum<W>(pq[r]);
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int r = 0; r < Geo::NI; ++r) {
-                smem[Ls.PK + q * ROWS + row0 + r] = pk[r];
-                smem[Ls.PQ + q * ROWS + row0 + r] = pq[r];
+            const int row = row0 + r;
+            float sk = group_sum<W>(pk[r]);
+            float o = group_sum<W>(pq[r]);
+            for (int dd = 0; dd < q; ++dd) {
+                const float ud = smem[Ls.UD + dd * ROWS + row];
+                sk = fmaf(smem[Ls.CK + q * cap + np + dd], ud, sk);
+                o = fmaf(smem[Ls.CQ + q * cap + np + dd], ud, o);
             }
-        }
-    }
-    __syncthreads();
-
-    // 6. drafts in order, one thread per row: u_q, then o_q; append u (and g)
-    if (tid < ROWS) {
-        const int row = tid;
-        float* const uring = a.buf_u + (size_t)bh * cap * a.dv + p * ROWS + row;
-        for (int q = 0; q < T; ++q) {
-            const int mq = np + q;
-            float sk = smem[Ls.PK + q * ROWS + row];
-            for (int d = 0; d < q; ++d) sk = fmaf(smem[Ls.CK + q * cap + np + d], smem[Ls.UD + d * ROWS + row], sk);
-            const float u = smem[Ls.BE + q] * (smem[Ls.V + q * ROWS + row] - sk);
-            smem[Ls.UD + q * ROWS + row] = u;
-            float o = smem[Ls.PQ + q * ROWS + row];
-            for (int d = 0; d <= q; ++d) o = fmaf(smem[Ls.CQ + q * cap + np + d], smem[Ls.UD + d * ROWS + row], o);
-            a.o[((size_t)(b * T + q) * a.nv + h) * a.dv + p * ROWS + row] = o;
-            int slot = qstart + mq;
-            slot -= slot >= cap ? cap : 0;
-            uring[(size_t)slot * a.dv] = u;
+            const float u = bet * (smem[Ls.V + q * ROWS + row] - sk);
+            o = fmaf(cself, u, o);
+            if (q + 1 < T) smem[Ls.UD + q * ROWS + row] = u;
+            if (lane == r) {
+                a.o[((size_t)(b * T + q) * a.nv + h) * a.dv + p * ROWS + row] = o;
+                uring_w[(size_t)slot * a.dv + row] = u;
+            }
         }
     }
     if (p == 0 && tid < T) {
@@ -361,7 +407,7 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_replay_kernel(const Gdn
         a.buf_g[(size_t)bh * cap + slot] = smem[Ls.GQ + tid];
     }
 
-    // 7. ring pointer: verify leaves the length, decode commits its token
+    // 6. ring pointer: verify leaves the length, decode commits its token
     if (tid == 0) {
         a.meta[2 * wg] = qstart;
         a.meta[2 * wg + 1] = np + (a.mode == MODE_DECODE ? T : 0);
@@ -458,7 +504,7 @@ template <int DK, typename InT>
 hipError_t launch_replay_t(const GdnArgs& a, hipStream_t stream) {
     constexpr int ROWS = GdnGeo<DK>::ROWS, NT = GdnGeo<DK>::NT;
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
-    const size_t lds = (size_t)gdn_plan(DK, ROWS, a.cap, T).total * 4 + kGdnIntSlots * 4;
+    const size_t lds = (size_t)gdn_plan(DK, ROWS, a.cap, T).total * 4;
     const int nwg = a.batch * a.nv * a.parts;
     hipLaunchKernelGGL((gdn_replay_kernel<DK, InT>), dim3(nwg), dim3(NT), lds, stream, a);
     return hipGetLastError();
@@ -482,7 +528,7 @@ bool gdn_shape_supported(int dk, int dv) {
 int gdn_rows(int dk) { return dk == 16 ? GdnGeo<16>::ROWS : GdnGeo<128>::ROWS; }
 
 size_t gdn_lds_bytes(int dk, int cap, int T) {
-    return (size_t)gdn_plan(dk, gdn_rows(dk), cap, T).total * 4 + kGdnIntSlots * 4;
+    return (size_t)gdn_plan(dk, gdn_rows(dk), cap, T).total * 4;
 }
 
 hipError_t launch_gdn_replay(const GdnArgs& a, int dk, int in_type, hipStream_t stream) {

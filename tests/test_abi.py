@@ -148,3 +148,42 @@ def test_binding_checks_tensors_on_host(rb):
                     torch.zeros(2, 1, 8))
     with pytest.raises(ValueError):
         rb.replayssm_decode_step(cfg, st, p, tok, torch.zeros(2, 1, 8, 16))
+
+
+def test_gdn_sizes_and_rejections(rb):
+    from mamba_state_replay_amd import binding_gdn as bg
+    cfg = bg.GdnConfig(batch=512, nv=32, nk=16, dk=128, dv=128, window=16, max_drafts=1)
+    assert bg.gdn_row_blocks(cfg) == 2
+    sz = bg.gdn_sizes(cfg)
+    assert sz[0] == 512 * 32 * 128 * 128 * 4 == 1 << 30          # 2 MiB per sequence
+    assert sz[1] == 512 * 16 * 17 * 128 * 2                      # bf16 keys
+    assert sz[2] == 512 * 32 * 17 * 128 * 4                      # fp32 corrected values
+    assert sz[3] == 512 * 32 * 17 * 4 and sz[4] == 512 * 32 * 2 * 2 * 4
+    assert bg.gdn_row_blocks(bg.GdnConfig(2, 4, 2, 16, 32, 4)) == 2
+    for bad in [dict(dk=64), dict(dv=96), dict(nk=3), dict(nv=0), dict(window=0), dict(window=65),
+                dict(max_drafts=9), dict(batch=-1)]:
+        base = dict(batch=4, nv=32, nk=16, dk=128, dv=128, window=16, max_drafts=1)
+        base.update(bad)
+        with pytest.raises(rb.ReplaySSMError) as e:
+            bg.gdn_sizes(bg.GdnConfig(**base))
+        assert e.value.code == -2, bad
+    c = bg.GdnConfig(4, 32, 16, 128, 128).c()
+    c.in_dtype = 7
+    assert bg.lib().gdn_sizes(ctypes.byref(c), (ctypes.c_size_t * 5)()) == -3
+
+
+def test_gdn_null_pointers_rejected_before_launch(rb):
+    from mamba_state_replay_amd import binding_gdn as bg
+    L = bg.lib()
+    c = bg.GdnConfig(4, 32, 16, 128, 128, window=16, max_drafts=2).c()
+    s = bg.gdn_state()
+    t = bg.gdn_tokens(None, None, None, None, None, 1)
+    assert L.gdn_decode_step(ctypes.byref(c), ctypes.byref(s), ctypes.byref(t), None, None) == -1
+    assert L.gdn_verify_drafts(ctypes.byref(c), ctypes.byref(s), ctypes.byref(t), None, None) == -1
+    assert L.gdn_flush(ctypes.byref(c), ctypes.byref(s), None) == -1
+    assert L.gdn_commit(ctypes.byref(c), ctypes.byref(s), None, 3, None) == -4
+    assert L.gdn_commit(ctypes.byref(c), ctypes.byref(s), None, 1, None) == -1
+    assert L.gdn_conventional_update(ctypes.byref(c), None, ctypes.byref(t), None, None) == -1
+    assert L.gdn_decode_step(None, None, None, None, None) == -1
+    zero = bg.GdnConfig(0, 32, 16, 128, 128).c()
+    assert L.gdn_decode_step(ctypes.byref(zero), None, None, None, None) == 0   # batch 0: nothing to do
