@@ -330,7 +330,7 @@ def bench_gdn(args):
             traffic_bytes = c.get("bytes_per_launch")
 
     S = torch.from_numpy(w.S0).to(dev)
-    cstep = lambda i: bg.gdn_conventional_update(cfg, S, toks.call(i % ntok), o)
+    cstep = lambda i: bg.gdn_conventional_update(cfg, S, toks.call(i % ntok), o)  # nslots 1: in place
     for i in range(4):
         cstep(i)
     ceager, cper = timed_launches(cstep, K, torch)
@@ -339,8 +339,13 @@ def bench_gdn(args):
     c_us = ctot * 1e3 / K
     del S
 
+    # snapshot verification baseline: T = 3 drafts, one FP32 state snapshot per draft
+    T = 3
+    snap = torch.empty((batch, T + 1, shape.nv, shape.dv, shape.dk), device=dev)
+    snap[:, 0] = torch.from_numpy(w.S0).to(dev)
+    slot = torch.zeros(batch, dtype=torch.int32, device=dev)
     # speculative rounds: T = 3 drafts, U{0..3} accepted, verify + commit
-    T, rounds = 3, 32
+    rounds = 32
     vw = synth_gdn.gdn_workload(shape, rounds, seed=2003, T=T, ckpt_std=0.0)
     vcfg = bg.GdnConfig(batch, shape.nv, shape.nk, shape.dk, shape.dv, L, T, "bf16")
     del st, toks
@@ -355,6 +360,13 @@ def bench_gdn(args):
         vround(r)
     v_ms = graph_time(lambda r: vround(8 + r), rounds, torch)
     assert int(vst.status.cpu()[0]) == 0 and bool(torch.isfinite(vo).all())
+    sround = lambda r: (bg.gdn_conventional_update(vcfg, snap, vtoks.call(r % rounds), vo, nslots=T + 1, slot=slot),
+                        bg.gdn_conventional_commit(vcfg, slot, T + 1, acc[r % rounds], T))
+    for r in range(4):
+        sround(r)
+    s_ms = graph_time(lambda r: sround(4 + r), rounds, torch)
+    assert bool(torch.isfinite(vo).all())
+    del snap
 
     result = {
         "metric": "GDN layer decode-step us + achieved HBM GB/s",
@@ -385,8 +397,11 @@ def bench_gdn(args):
                          "algorithmic_bytes_per_launch": cbytes},
         "speedup_vs_conventional": round(c_us / us_step, 3),
         "verify_T3": {"us_per_round": round(v_ms * 1e3 / rounds, 2), "rounds": rounds,
-                      "conventional_3_steps_us": round(3 * c_us, 2),
-                      "note": "verify + commit per round, graph-timed; 3 conventional steps for scale"},
+                      "snapshot_baseline_us_per_round": round(s_ms * 1e3 / rounds, 2),
+                      "speedup_vs_snapshot": round(s_ms / v_ms, 3),
+                      "algorithmic_bytes_snapshot_per_round": traffic.snapshot_verify_bytes(sz, batch, T),
+                      "note": "verify + commit per round vs the conventional kernel writing one FP32 snapshot "
+                              "per draft + slot commit, both graph-timed"},
     }
     if not args.no_probe:
         from mamba_state_replay_amd import binding as rb

@@ -113,11 +113,24 @@ int gdn_commit(const gdn_config *cfg, const gdn_state *st, const int32_t *accept
    left alone). */
 int gdn_flush(const gdn_config *cfg, const gdn_state *st, void *stream);
 
-/* Conventional GDN step (the in-library baseline): per token, read the full state,
-   apply the gated delta rule, write the state back and read o from it.
-   state [batch][nv][dv][dk] fp32, updated in place; T must be 1. */
-int gdn_conventional_update(const gdn_config *cfg, float *state, const gdn_tokens *tok, float *o,
-                            void *stream);
+/* Conventional GDN step (the in-library baseline; blog section "Why SSM layers can become a
+   decoding bottleneck": every token loads, updates and stores the full state): per token,
+   S k, u = beta (v - alpha S k), S <- alpha S + u k^T, o = S q.
+   states: [batch][nslots][nv][dv][dk] fp32.
+   nslots == 1: tok->T must be 1 and the state is updated in place; slot may be NULL.
+   nslots > 1 (speculative verification with one state snapshot per draft, blog section
+     "Rollback for speculative decoding"): slot[b] (device int32 [batch]) names the current
+     state; draft q's state is written to slot (slot[b] + 1 + q) % nslots, 1 <= T < nslots,
+     T <= RSSM_MAX_DRAFTS.  A slot index out of range sets RSSM_STATUS_SLOT, writes NaN
+     outputs and leaves that sequence alone.
+   o: [batch][T][nv][dv] fp32. */
+int gdn_conventional_update(const gdn_config *cfg, float *states, int32_t nslots, const int32_t *slot,
+                            int32_t *status, const gdn_tokens *tok, float *o, void *stream);
+
+/* Baseline commit after a snapshot verification: slot[b] = (slot[b] + accepted[b]) % nslots,
+   0 <= accepted[b] <= T (else RSSM_STATUS_ACCEPT and the sequence is left alone). */
+int gdn_conventional_commit(const gdn_config *cfg, int32_t *slot, int32_t nslots, const int32_t *accepted,
+                            int32_t T, int32_t *status, void *stream);
 
 #ifdef __cplusplus
 }

@@ -43,8 +43,10 @@ _SIGS = {
     "gdn_commit": (ctypes.c_int, [_P(gdn_config), _P(gdn_state), ctypes.c_void_p, ctypes.c_int32,
                                   ctypes.c_void_p]),
     "gdn_flush": (ctypes.c_int, [_P(gdn_config), _P(gdn_state), ctypes.c_void_p]),
-    "gdn_conventional_update": (ctypes.c_int, [_P(gdn_config), ctypes.c_void_p, _P(gdn_tokens),
-                                               ctypes.c_void_p, ctypes.c_void_p]),
+    "gdn_conventional_update": (ctypes.c_int, [_P(gdn_config), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                               ctypes.c_void_p, _P(gdn_tokens), ctypes.c_void_p, ctypes.c_void_p]),
+    "gdn_conventional_commit": (ctypes.c_int, [_P(gdn_config), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
 }
 _LIB = None
 
@@ -192,12 +194,31 @@ def gdn_flush(cfg: GdnConfig, state: GdnState, stream=None):
     _check("gdn_flush", lib().gdn_flush(ctypes.byref(c), ctypes.byref(s), _stream(stream)))
 
 
-def gdn_conventional_update(cfg: GdnConfig, state: torch.Tensor, tokens: GdnTokens, o: torch.Tensor,
-                            stream=None):
-    dev = state.device
-    _expect("state", state, (cfg.batch, cfg.nv, cfg.dv, cfg.dk), torch.float32, dev)
+def gdn_conventional_update(cfg: GdnConfig, states: torch.Tensor, tokens: GdnTokens, o: torch.Tensor,
+                            nslots: int = 1, slot: torch.Tensor | None = None,
+                            status: torch.Tensor | None = None, stream=None):
+    """states: [batch][nv][dv][dk] (nslots 1, updated in place) or
+    [batch][nslots][nv][dv][dk] with slot [batch] int32 (one snapshot per draft)."""
+    dev = states.device
+    shape = (cfg.batch, cfg.nv, cfg.dv, cfg.dk) if nslots == 1 else (cfg.batch, nslots, cfg.nv, cfg.dv, cfg.dk)
+    _expect("states", states, shape, torch.float32, dev)
     tokens.validate(cfg, dev)
     _expect("o", o, (cfg.batch, tokens.T, cfg.nv, cfg.dv), torch.float32, dev)
+    if nslots > 1:
+        _expect("slot", slot, (cfg.batch,), torch.int32, dev)
+    if status is not None:
+        _expect("status", status, (1,), torch.int32, dev)
     c, t = cfg.c(), tokens.c()
     _check("gdn_conventional_update", lib().gdn_conventional_update(
-        ctypes.byref(c), _ptr(state), ctypes.byref(t), _ptr(o), _stream(stream)))
+        ctypes.byref(c), _ptr(states), int(nslots), _ptr(slot) if nslots > 1 else None, _ptr(status),
+        ctypes.byref(t), _ptr(o), _stream(stream)))
+
+
+def gdn_conventional_commit(cfg: GdnConfig, slot: torch.Tensor, nslots: int, accepted: torch.Tensor, T: int,
+                            status: torch.Tensor | None = None, stream=None):
+    dev = slot.device
+    _expect("slot", slot, (cfg.batch,), torch.int32, dev)
+    _expect("accepted", accepted, (cfg.batch,), torch.int32, dev)
+    c = cfg.c()
+    _check("gdn_conventional_commit", lib().gdn_conventional_commit(
+        ctypes.byref(c), _ptr(slot), int(nslots), _ptr(accepted), int(T), _ptr(status), _stream(stream)))

@@ -486,21 +486,51 @@ int gdn_commit(const gdn_config* cfg, const gdn_state* st, const int32_t* accept
     return launched(rssm::launch_replay_commit(a, static_cast<hipStream_t>(stream)), "gdn_commit");
 }
 
-int gdn_conventional_update(const gdn_config* cfg, float* state, const gdn_tokens* tok, float* o, void* stream) {
+int gdn_conventional_update(const gdn_config* cfg, float* states, int32_t nslots, const int32_t* slot,
+                            int32_t* status, const gdn_tokens* tok, float* o, void* stream) {
     int rc = gdn_check_config(cfg);
     if (rc) return rc;
     if (cfg->batch == 0) return RSSM_OK;
-    if (!state) return fail(RSSM_ERR_NULL, "state is NULL");
-    if (!aligned(state, 16)) return fail(RSSM_ERR_SHAPE, "state must be 16-byte aligned");
-    rc = gdn_check_tokens(tok, o, 1, 1);
+    if (!states) return fail(RSSM_ERR_NULL, "states is NULL");
+    if (!aligned(states, 16)) return fail(RSSM_ERR_SHAPE, "states must be 16-byte aligned");
+    if (nslots < 1) return fail(RSSM_ERR_SHAPE, "nslots %d < 1", nslots);
+    if (nslots > 1 && !slot) return fail(RSSM_ERR_NULL, "slot is required when nslots > 1");
+    if ((slot && !aligned(slot, 4)) || (status && !aligned(status, 4)))
+        return fail(RSSM_ERR_SHAPE, "misaligned slot or status");
+    const int tmax = nslots == 1 ? 1 : (nslots - 1 < RSSM_MAX_DRAFTS ? nslots - 1 : RSSM_MAX_DRAFTS);
+    rc = gdn_check_tokens(tok, o, 1, tmax);
     if (rc) return rc;
     gdn_state s;
     std::memset(&s, 0, sizeof s);
-    s.ckpt = state;
-    const rssm::GdnArgs a = gdn_args(cfg, &s, tok, o, rssm::MODE_DECODE);
+    s.ckpt = states;
+    s.status = status;
+    rssm::GdnArgs a = gdn_args(cfg, &s, tok, o, rssm::MODE_DECODE);
+    a.nslots = nslots;
+    a.slot = nslots > 1 ? slot : nullptr;
     return launched(rssm::launch_gdn_conventional(a, cfg->dk, cfg->in_dtype == RSSM_BF16 ? rssm::IN_BF16 : rssm::IN_F32,
                                                   static_cast<hipStream_t>(stream)),
                     "gdn_conventional_update");
+}
+
+int gdn_conventional_commit(const gdn_config* cfg, int32_t* slot, int32_t nslots, const int32_t* accepted,
+                            int32_t T, int32_t* status, void* stream) {
+    if (!cfg) return fail(RSSM_ERR_NULL, "config is NULL");
+    if (cfg->batch < 0) return fail(RSSM_ERR_SHAPE, "batch %d < 0", cfg->batch);
+    if (nslots < 2) return fail(RSSM_ERR_SHAPE, "nslots %d < 2", nslots);
+    if (T < 1 || T >= nslots) return fail(RSSM_ERR_DRAFTS, "T = %d outside 1..%d", T, nslots - 1);
+    if (cfg->batch == 0) return RSSM_OK;
+    if (!slot || !accepted) return fail(RSSM_ERR_NULL, "slot and accepted are required");
+    if (!aligned(slot, 4) || !aligned(accepted, 4) || (status && !aligned(status, 4)))
+        return fail(RSSM_ERR_SHAPE, "misaligned slot, accepted or status");
+    rssm::CommitArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.slot = slot;
+    a.accepted = accepted;
+    a.status = status;
+    a.batch = cfg->batch;
+    a.T = T;
+    a.nslots = nslots;
+    return launched(rssm::launch_conventional_commit(a, static_cast<hipStream_t>(stream)), "gdn_conventional_commit");
 }
 
 const char* replayssm_last_error(void) { return g_err; }

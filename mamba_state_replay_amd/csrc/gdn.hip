@@ -414,8 +414,11 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     }
 }
 
-// Conventional GDN step: read the tile, S k, u = beta (v - alpha S k),
-// S <- alpha S + u k^T, o = S q, store the tile.
+// Conventional GDN step (the in-library baseline): read the tile, then per
+// token S k, u = beta (v - alpha S k), S <- alpha S + u k^T, o = S q, store.
+// With nslots > 1 (speculative verification with one snapshot per draft, blog
+// section "Rollback for speculative decoding") the current slot is read once
+// and draft q's state is written to slot (slot + 1 + q) % nslots.
 template <int DK, typename InT>
 __global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_conventional_kernel(const GdnArgs a) {
     constexpr int ROWS = GdnGeo<DK>::ROWS;
@@ -426,9 +429,11 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_conventional_kernel(con
     constexpr int KV = DK / EPV;
     constexpr int RV = ROWS / EPV;
     extern __shared__ float smem[];
-    float* const kk = smem;             // [DK]
-    float* const qq = smem + DK;        // [DK]
-    float* const vv = smem + 2 * DK;    // [ROWS]
+    const int T = a.T;
+    float* const kk = smem;                     // [T][DK]
+    float* const qq = smem + T * DK;            // [T][DK]
+    float* const vv = smem + 2 * T * DK;        // [T][ROWS]
+    float* const gb = vv + T * ROWS;            // [T][2]: g, beta
 
     const int tid = threadIdx.x;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -437,66 +442,95 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_conventional_kernel(con
     const int b = bh / a.nv;
     const int h = bh % a.nv;
     const int kh = h / (a.nv / a.nk);
+    const int nslots = a.nslots;
+    const int s0 = nslots > 1 ? a.slot[b] : 0;
+    if (s0 < 0 || s0 >= nslots) {
+        if (tid == 0 && h == 0 && p == 0 && a.status) atomicOr(a.status, (int)kStatusSlot);
+        for (int i = tid; i < T * ROWS; i += NT)
+            a.o[((size_t)(b * T + i / ROWS) * a.nv + h) * a.dv + p * ROWS + i % ROWS] = __builtin_nanf("");
+        return;
+    }
+    const size_t per_slot = (size_t)a.nv * a.dv * DK;
+    float* const seq = a.ckpt + (size_t)b * nslots * per_slot + ((size_t)h * a.dv + p * ROWS) * DK;
 
-    float* const tile_p = a.ckpt + ((size_t)bh * a.dv + p * ROWS) * DK;
     v4f raw[Geo::NV];
+    {
+        const v4u* src = reinterpret_cast<const v4u*>(seq + s0 * per_slot);
 #pragma unroll
-    for (int s = 0; s < Geo::NV; ++s)
-        raw[s] = __builtin_bit_cast(v4f, __builtin_nontemporal_load(reinterpret_cast<const v4u*>(tile_p) +
-                                                                    Geo::vec(tid, s)));
-    for (int i = tid; i < 2 * KV + RV; i += NT) {
-        if (i < 2 * KV) {
-            const bool isq = i >= KV;
-            const int e = isq ? i - KV : i;
-            const InT* src = static_cast<const InT*>(isq ? a.q : a.k) + ((size_t)b * a.nk + kh) * DK;
-            widen16<InT>(reinterpret_cast<const uint4*>(src)[e], (isq ? qq : kk) + e * EPV);
+        for (int s = 0; s < Geo::NV; ++s)
+            raw[s] = __builtin_bit_cast(v4f, __builtin_nontemporal_load(src + Geo::vec(tid, s)));
+    }
+    for (int i = tid; i < T * (2 * KV + RV); i += NT) {
+        const int q = i / (2 * KV + RV);
+        const int r = i - q * (2 * KV + RV);
+        if (r < 2 * KV) {
+            const bool isq = r >= KV;
+            const int e = isq ? r - KV : r;
+            const InT* src = static_cast<const InT*>(isq ? a.q : a.k) + ((size_t)(b * T + q) * a.nk + kh) * DK;
+            widen16<InT>(reinterpret_cast<const uint4*>(src)[e], (isq ? qq : kk) + q * DK + e * EPV);
         } else {
-            const int e = i - 2 * KV;
-            const InT* src = static_cast<const InT*>(a.v) + ((size_t)b * a.nv + h) * a.dv + p * ROWS;
-            widen16<InT>(reinterpret_cast<const uint4*>(src)[e], vv + e * EPV);
+            const int e = r - 2 * KV;
+            const InT* src = static_cast<const InT*>(a.v) + ((size_t)(b * T + q) * a.nv + h) * a.dv + p * ROWS;
+            widen16<InT>(reinterpret_cast<const uint4*>(src)[e], vv + q * ROWS + e * EPV);
         }
     }
+    if (tid < T) {
+        const size_t ti = (size_t)(b * T + tid) * a.nv + h;
+        gb[2 * tid] = a.g[ti];
+        gb[2 * tid + 1] = a.beta[ti];
+    }
     __syncthreads();
-    const float alpha = __expf(a.g[(size_t)b * a.nv + h]);
-    const float beta = a.beta[(size_t)b * a.nv + h];
     const int row0 = Geo::row0(tid);
     const int lane = tid % W;
 
-    float sk[Geo::NI];
+    for (int q = 0; q < T; ++q) {
+        const float alpha = __expf(gb[2 * q]);
+        const float beta = gb[2 * q + 1];
+        const float* kq = kk + q * DK;
+        const float* qv = qq + q * DK;
+        float sk[Geo::NI];
 #pragma unroll
-    for (int r = 0; r < Geo::NI; ++r) sk[r] = 0.0f;
+        for (int r = 0; r < Geo::NI; ++r) sk[r] = 0.0f;
 #pragma unroll
-    for (int s = 0; s < Geo::NV; ++s) {
-        const int vc = lane + W * (s % Geo::VPL);
-        sk[s / Geo::VPL] += dot4(raw[s], *reinterpret_cast<const float4*>(kk + 4 * vc));
-    }
-    float u[Geo::NI];
+        for (int s = 0; s < Geo::NV; ++s) {
+            const int vc = lane + W * (s % Geo::VPL);
+            sk[s / Geo::VPL] += dot4(raw[s], *reinterpret_cast<const float4*>(kq + 4 * vc));
+        }
+        float u[Geo::NI];
 #pragma unroll
-    for (int r = 0; r < Geo::NI; ++r) u[r] = beta * (vv[row0 + r] - alpha * group_sum<W>(sk[r]));
-    float o[Geo::NI];
+        for (int r = 0; r < Geo::NI; ++r) u[r] = beta * (vv[q * ROWS + row0 + r] - alpha * group_sum<W>(sk[r]));
+        float o[Geo::NI];
 #pragma unroll
-    for (int r = 0; r < Geo::NI; ++r) o[r] = 0.0f;
+        for (int r = 0; r < Geo::NI; ++r) o[r] = 0.0f;
 #pragma unroll
-    for (int s = 0; s < Geo::NV; ++s) {
-        const int r = s / Geo::VPL;
-        const int vc = lane + W * (s % Geo::VPL);
-        const float4 k4 = *reinterpret_cast<const float4*>(kk + 4 * vc);
-        v4f x = raw[s];
-        x[0] = fmaf(alpha, x[0], u[r] * k4.x);
-        x[1] = fmaf(alpha, x[1], u[r] * k4.y);
-        x[2] = fmaf(alpha, x[2], u[r] * k4.z);
-        x[3] = fmaf(alpha, x[3], u[r] * k4.w);
-        raw[s] = x;
-        o[r] += dot4(x, *reinterpret_cast<const float4*>(qq + 4 * vc));
-    }
+        for (int s = 0; s < Geo::NV; ++s) {
+            const int r = s / Geo::VPL;
+            const int vc = lane + W * (s % Geo::VPL);
+            const float4 k4 = *reinterpret_cast<const float4*>(kq + 4 * vc);
+            v4f x = raw[s];
+            x[0] = fmaf(alpha, x[0], u[r] * k4.x);
+            x[1] = fmaf(alpha, x[1], u[r] * k4.y);
+            x[2] = fmaf(alpha, x[2], u[r] * k4.z);
+            x[3] = fmaf(alpha, x[3], u[r] * k4.w);
+            raw[s] = x;
+            o[r] += dot4(x, *reinterpret_cast<const float4*>(qv + 4 * vc));
+        }
+        int dst = s0;
+        if (nslots > 1) {
+            dst = s0 + 1 + q;
+            dst -= dst >= nslots ? nslots : 0;
+        }
+        v4u* const out = reinterpret_cast<v4u*>(seq + dst * per_slot);
 #pragma unroll
-    for (int s = 0; s < Geo::NV; ++s)
-        __builtin_nontemporal_store(__builtin_bit_cast(v4u, raw[s]), reinterpret_cast<v4u*>(tile_p) + Geo::vec(tid, s));
+        for (int s = 0; s < Geo::NV; ++s)
+            __builtin_nontemporal_store(__builtin_bit_cast(v4u, raw[s]), out + Geo::vec(tid, s));
 #pragma unroll
-    for (int r = 0; r < Geo::NI; ++r) o[r] = group_sum<W>(o[r]);
-    if (lane == 0) {
+        for (int r = 0; r < Geo::NI; ++r) o[r] = group_sum<W>(o[r]);
+        if (lane == 0) {
 #pragma unroll
-        for (int r = 0; r < Geo::NI; ++r) a.o[((size_t)b * a.nv + h) * a.dv + p * ROWS + row0 + r] = o[r];
+            for (int r = 0; r < Geo::NI; ++r)
+                a.o[((size_t)(b * T + q) * a.nv + h) * a.dv + p * ROWS + row0 + r] = o[r];
+        }
     }
 }
 
@@ -513,7 +547,7 @@ hipError_t launch_replay_t(const GdnArgs& a, hipStream_t stream) {
 template <int DK, typename InT>
 hipError_t launch_conv_t(const GdnArgs& a, hipStream_t stream) {
     constexpr int ROWS = GdnGeo<DK>::ROWS, NT = GdnGeo<DK>::NT;
-    const size_t lds = (size_t)(2 * DK + ROWS) * 4;
+    const size_t lds = (size_t)a.T * (2 * DK + ROWS + 2) * 4;
     const int nwg = a.batch * a.nv * a.parts;
     hipLaunchKernelGGL((gdn_conventional_kernel<DK, InT>), dim3(nwg), dim3(NT), lds, stream, a);
     return hipGetLastError();

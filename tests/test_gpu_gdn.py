@@ -121,6 +121,47 @@ def test_gdn_verify_commit(shape, T, rounds, in_dtype, dev):
     assert int(st.status.cpu()[0]) == 0
 
 
+@pytest.mark.parametrize("shape,T,rounds,in_dtype", [(TINY, 3, 7, "f32"), (LAYER_SMALL, 3, 6, "bf16"),
+                                                     (LAYER_SMALL, 2, 6, "bf16")],
+                         ids=["tiny-T3", "layer-T3", "layer-T2"])
+def test_gdn_snapshot_verify_baseline(shape, T, rounds, in_dtype, dev):
+    """The conventional kernel with one snapshot per draft (nslots = T + 1) and
+    its slot commit: draft outputs and the committed slot's state match the
+    oracle stepping the accepted tokens."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    w = sg.gdn_workload(shape, rounds, 55 + T, in_dtype, T=T)
+    acc = w.extra["accepted"]
+    cfg = _cfg(shape, T, in_dtype)
+    ns = T + 1
+    states = torch.zeros((shape.batch, ns, shape.nv, shape.dv, shape.dk), device=dev)
+    states[:, 0] = torch.from_numpy(w.S0).to(dev)
+    slot = torch.zeros(shape.batch, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ts = GdnTokenStream(w.steps, dev, T)
+    acc_d = torch.from_numpy(acc).to(dev)
+    o = torch.empty((rounds, shape.batch, T, shape.nv, shape.dv), device=dev)
+    say(f"gdn snapshot verify {shape} T={T}")
+    for r in range(rounds):
+        bg.gdn_conventional_update(cfg, states, ts.call(r), o[r], nslots=ns, slot=slot, status=status)
+        bg.gdn_conventional_commit(cfg, slot, ns, acc_d[r], T, status)
+    torch.cuda.synchronize()
+    tk = w.steps
+    S = w.S0.astype(np.float64)
+    oref = np.zeros((rounds, T, shape.batch, shape.nv, shape.dv))
+    for r in range(rounds):
+        sl = slice(r * T, (r + 1) * T)
+        args = (tk.q[sl], tk.k[sl], tk.v[sl], tk.g[sl], tk.beta[sl])
+        _, oref[r] = ogdn.conventional(S, *args)
+        S, _ = ogdn.conventional(S, *args, nsteps=acc[r])
+    assert_rows_close(np.swapaxes(o.cpu().numpy(), 1, 2), oref, what="gdn snapshot-verify outputs")
+    cur = slot.cpu().numpy()
+    assert np.array_equal(cur, np.sum(acc, axis=0) % ns)
+    got = states.cpu().numpy()[np.arange(shape.batch), cur]
+    assert state_err(got, S).max() <= TOL
+    assert int(status.cpu()[0]) == 0
+
+
 @pytest.mark.parametrize("shape,in_dtype", [(TINY, "f32"), (LAYER_SMALL, "bf16")], ids=["tiny", "layer"])
 def test_gdn_conventional_kernel(shape, in_dtype, dev):
     """The conventional GDN step (baseline) matches the oracle step by step."""
@@ -289,3 +330,59 @@ def test_gdn_fullsize_verify_sampled(dev):
     assert_rows_close(og, oref, what="gdn full-size draft outputs (sampled)")
     assert state_err(st.ckpt[torch.from_numpy(sl).to(dev)].cpu().numpy(), S).max() <= TOL
     assert int(st.status.cpu()[0]) == 0
+
+
+def _clone_gdn(st):
+    bg = _bg()
+    return bg.GdnState(**{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in vars(st).items()})
+
+
+def test_gdn_graph_replays_match_eager(dev):
+    """GDN decode steps (flushes included) and verify + commit rounds captured
+    in one HIP graph: three replays, each after eager launches of the same
+    tokens on a twin state and a synchronisation, reproduce the eager results
+    bit for bit (the entry points only launch kernels on the caller's stream)."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    shape = sg.GdnShape(batch=4, nv=32, nk=16, dk=128, dv=128, window=4)
+    K, T, R = 9, 3, 3
+    w = sg.gdn_workload(shape, K, 91)
+    vw = sg.gdn_workload(shape, R, 92, T=T)
+    cfg1, cfgT = _cfg(shape, 1, "bf16"), _cfg(shape, T, "bf16")
+    ts, vts = GdnTokenStream(w.steps, dev), GdnTokenStream(vw.steps, dev, T)
+    acc = torch.from_numpy(vw.extra["accepted"]).to(dev)
+    d_e, d_g = _state(cfg1, w.S0, dev), None
+    d_g = _clone_gdn(d_e)
+    v_e = _state(cfgT, vw.S0, dev)
+    v_g = _clone_gdn(v_e)
+    o_e = torch.empty((K, shape.batch, 1, shape.nv, shape.dv), device=dev)
+    o_g = torch.empty_like(o_e)
+    vo_e = torch.empty((R, shape.batch, T, shape.nv, shape.dv), device=dev)
+    vo_g = torch.empty_like(vo_e)
+
+    def run(dstate, vstate, o, vo):
+        for t in range(K):
+            bg.gdn_decode_step(cfg1, dstate, ts.call(t), o[t])
+        for r in range(R):
+            bg.gdn_verify_drafts(cfgT, vstate, vts.call(r), vo[r])
+            bg.gdn_commit(cfgT, vstate, acc[r], T)
+
+    say("capture GDN decode and verify + commit")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(d_g, v_g, o_g, vo_g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"GDN eager pass {rep}")
+        run(d_e, v_e, o_e, vo_e)
+        torch.cuda.synchronize()
+        say(f"GDN graph replay {rep}")
+        o_g.fill_(float("nan"))
+        vo_g.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e) and torch.equal(vo_g, vo_e), f"replay {rep} differs"
+        for a, b in ((d_g, d_e), (v_g, v_e)):
+            assert torch.equal(a.ckpt, b.ckpt) and torch.equal(a.meta, b.meta)
+            assert torch.equal(a.buf_u, b.buf_u) and torch.equal(a.buf_k, b.buf_k)
+    assert int(d_g.status.cpu()[0]) == 0 and int(v_g.status.cpu()[0]) == 0
