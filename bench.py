@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--no-conventional", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU sample")
-    ap.add_argument("--config", choices=["decode", "verify", "verify_sweep", "sweep", "dual", "gdn"], default="decode",
+    ap.add_argument("--config", choices=["decode", "verify", "verify_sweep", "sweep", "dual", "gdn",
+                                         "gdn_verify_sweep"], default="decode",
                     help="decode: the headline line (default); verify: speculative rounds at batch 512, "
                          "T=3; verify_sweep: the same for T in 1, 2, 3, 4, 8; sweep: batch x window grid; "
                          "dual: FP32 / bf16 / e4m3 read copies over 4096 steps; gdn: Gated DeltaNet layer "
@@ -127,7 +128,7 @@ def main():
         sys.exit(2)
     if args.config != "decode":
         {"verify": bench_verify, "verify_sweep": bench_verify_sweep, "sweep": bench_sweep,
-         "dual": bench_dual, "gdn": bench_gdn}[args.config](args)
+         "dual": bench_dual, "gdn": bench_gdn, "gdn_verify_sweep": bench_gdn_verify_sweep}[args.config](args)
         return
 
     import torch
@@ -418,6 +419,56 @@ def bench_gdn(args):
     if not args.no_cpu:
         result["cpu_baseline"] = gdn_cpu_baseline(w, step_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def bench_gdn_verify_sweep(args):
+    """GDN speculative rounds at batch --gdn-batch, L = 16, for T = 1, 2, 3, 4, 8:
+    replay verify + commit against the conventional GDN kernel writing one FP32
+    snapshot per draft + slot commit (both graph-timed, 8 rounds of seeded
+    drafts with U{0..T} acceptance cycled); one JSON line with the table."""
+    torch, dev = _device()
+    from mamba_state_replay_amd import binding_gdn as bg
+    from mamba_state_replay_amd import staging, synth_gdn, traffic
+
+    batch, L = args.gdn_batch, args.window
+    rows = []
+    for T in (1, 2, 3, 4, 8):
+        shape = synth_gdn.GdnShape(batch=batch, window=L, max_drafts=T, **GDN_LAYER)
+        R = 8
+        w = synth_gdn.gdn_workload(shape, R, seed=2100 + T, T=T)
+        cfg = bg.GdnConfig(batch, shape.nv, shape.nk, shape.dk, shape.dv, L, T, "bf16")
+        st = bg.GdnState.allocate(cfg, dev)
+        st.ckpt.copy_(torch.from_numpy(w.S0).to(dev))
+        toks = staging.GdnTokenStream(w.steps, dev, T)
+        acc = torch.from_numpy(w.extra["accepted"]).to(dev)
+        o = torch.empty((batch, T, shape.nv, shape.dv), device=dev)
+        rnd = lambda r: (bg.gdn_verify_drafts(cfg, st, toks.call(r % R), o), bg.gdn_commit(cfg, st, acc[r % R], T))
+        for r in range(2 * R):
+            rnd(r)
+        K = 32
+        rep_ms = graph_time(lambda r: rnd(r), K, torch)
+        assert int(st.status.cpu()[0]) == 0 and bool(torch.isfinite(o).all())
+        del st
+        snap = torch.empty((batch, T + 1, shape.nv, shape.dv, shape.dk), device=dev)
+        snap[:, 0] = torch.from_numpy(w.S0).to(dev)
+        slot = torch.zeros(batch, dtype=torch.int32, device=dev)
+        srnd = lambda r: (bg.gdn_conventional_update(cfg, snap, toks.call(r % R), o, nslots=T + 1, slot=slot),
+                          bg.gdn_conventional_commit(cfg, slot, T + 1, acc[r % R], T))
+        for r in range(4):
+            srnd(r)
+        snap_ms = graph_time(lambda r: srnd(r), K, torch)
+        sz = traffic.gdn_sizes(shape.nv, shape.nk, shape.dk, shape.dv)
+        del snap, toks
+        rows.append({"T": T, "replay_us_per_round": round(rep_ms * 1e3 / K, 2),
+                     "snapshot_us_per_round": round(snap_ms * 1e3 / K, 2),
+                     "speedup": round(snap_ms / rep_ms, 3),
+                     "snapshot_algorithmic_gb_per_round": round(traffic.snapshot_verify_bytes(sz, batch, T) / 1e9, 3)})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({"config": "gdn_verify_sweep", "batch": batch, "window": L,
+                      "workload": "Gated DeltaNet layer, 32 value heads over 16 key heads, dk = dv = 128, bf16 "
+                                  "inputs, FP32 checkpoint; U{0..T} acceptance",
+                      "timing": "32 rounds captured in one HIP graph, one replay timed after a warm replay",
+                      "rows": rows}), flush=True)
 
 
 def gdn_cpu_baseline(w, gpu_bytes_per_step, target_s):
