@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--window", type=int, default=16)
     ap.add_argument("--read-copy", choices=["none", "bf16", "e4m3", "mxfp4", "mxfp8"], default="none")
+    ap.add_argument("--stagger", action="store_true",
+                    help="staggered phases: sequence b starts with 1 + (b mod L) committed records, so about "
+                         "1/L of the sequences flush in every step (default: all start with L and flush together)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-conventional", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
@@ -140,7 +143,8 @@ def main():
     read_copy = None if args.read_copy == "none" else args.read_copy
     shape = synth.LayerShape(batch=args.batch, nheads=128, headdim=64, dstate=128, ngroups=8, window=L)
     ntok = 64
-    work = synth.decode_workload(shape, ntok, seed=1001, n0=L)
+    work = synth.decode_workload(shape, ntok, seed=1001,
+                                 n0=synth.staggered_fill(shape.batch, L) if args.stagger else L)
     cfg = staging.config(shape, read_copy=read_copy)
     st = staging.replay_state(cfg, work, dev)
     p = staging.params(work, dev)
@@ -195,7 +199,8 @@ def main():
     traffic_bytes = None
     if COUNTERS.exists():
         c = json.loads(COUNTERS.read_text())
-        if c.get("source_hash") == source_hash(KERNEL_SOURCES) and c.get("batch") == shape.batch:
+        if (c.get("source_hash") == source_hash(KERNEL_SOURCES) and c.get("batch") == shape.batch
+                and c.get("window") == L and read_copy is None and not args.stagger):
             traffic_bytes = c.get("bytes_per_launch")
 
     result = {
@@ -218,8 +223,10 @@ def main():
             "workload": f"Nemotron-3-style Mamba-2 layer decode (ReplaySSM), batch {shape.batch}, "
                         f"nheads 128, headdim 64, dstate 128, ngroups 8, L={L}, bf16 x/B/C, fp32 dt, "
                         f"FP32 checkpoint" + (f" + {read_copy} read copy" if read_copy else "") +
-                        ", steady state (L committed records at start)",
+                        (", staggered phases (1 + b mod L committed records at start)" if args.stagger else
+                         ", steady state (L committed records at start)"),
             "batch": shape.batch, "window": L, "read_copy": read_copy or "none",
+            "phases": "staggered" if args.stagger else "aligned",
             "flush_launches_timed": folds,
         },
         "kernel_source_hash": source_hash(KERNEL_SOURCES),

@@ -386,3 +386,22 @@ def test_gdn_graph_replays_match_eager(dev):
             assert torch.equal(a.ckpt, b.ckpt) and torch.equal(a.meta, b.meta)
             assert torch.equal(a.buf_u, b.buf_u) and torch.equal(a.buf_k, b.buf_k)
     assert int(d_g.status.cpu()[0]) == 0 and int(v_g.status.cpu()[0]) == 0
+
+
+def test_gdn_long_run_no_drift(dev):
+    """160 decode steps at L = 16 (ten flushes) on the layer shape: the error
+    against the fp64 oracle stays at the fp32 level in every window, with no
+    growth from the first windows to the last."""
+    shape = sg.GdnShape(batch=2, nv=32, nk=16, dk=128, dv=128, window=16)
+    steps = 160
+    w, cfg, st, og = _decode(shape, steps, 97, "bf16", dev)
+    t = w.steps
+    _, oref = ogdn.conventional(w.S0, t.q, t.k, t.v, t.g, t.beta)
+    errs = []
+    for k in range(steps // 16):
+        sl = slice(16 * k, 16 * (k + 1))
+        from tests.gpu_util import head_err
+        errs.append(float(head_err(og[sl], oref[sl]).max()))
+    print(f"[gpu] gdn per-window max error: first {errs[:3]}, last {errs[-3:]}", flush=True)
+    assert max(errs) <= TOL
+    assert max(errs[-3:]) <= 4 * max(max(errs[:3]), 1e-7)
