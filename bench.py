@@ -64,6 +64,8 @@ def parse():
                          "dual: FP32 / bf16 / e4m3 read copies over 4096 steps; gdn: Gated DeltaNet layer "
                          "decode and verify (batch --gdn-batch)")
     ap.add_argument("--gdn-batch", type=int, default=512)
+    ap.add_argument("--gdn-ckpt", choices=["f32", "f16"], default="f32",
+                    help="GDN checkpoint: FP32, or FP16 written with stochastic rounding")
     ap.add_argument("--summarize-configs", nargs="+", metavar="LOG",
                     help="write the tables of bench logs of the non-default configs into profiles/ and exit")
     ap.add_argument("--ingest-gdn-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
@@ -305,12 +307,14 @@ def bench_gdn(args):
     shape = synth_gdn.GdnShape(batch=batch, window=L, **GDN_LAYER)
     ntok = 32
     w = synth_gdn.gdn_workload(shape, ntok, seed=2001)
-    cfg = bg.GdnConfig(batch, shape.nv, shape.nk, shape.dk, shape.dv, L, 1, "bf16")
+    ck = args.gdn_ckpt
+    cfg = bg.GdnConfig(batch, shape.nv, shape.nk, shape.dk, shape.dv, L, 1, "bf16", ck)
     st = bg.GdnState.allocate(cfg, dev)
-    st.ckpt.copy_(torch.from_numpy(w.S0).to(dev))
+    st.ckpt.copy_(torch.from_numpy(w.S0).to(dev).to(cfg.ckpt_torch))
     toks = staging.GdnTokenStream(w.steps, dev)
     o = torch.empty((batch, 1, shape.nv, shape.dv), device=dev)
-    sz = traffic.gdn_sizes(shape.nv, shape.nk, shape.dk, shape.dv)
+    sz = traffic.gdn_sizes(shape.nv, shape.nk, shape.dk, shape.dv, ckpt_bytes=2 if ck == "f16" else 4)
+    csz = traffic.gdn_sizes(shape.nv, shape.nk, shape.dk, shape.dv)
     W, K = max(args.warmup, L + 1), args.steps
     for i in range(W):
         bg.gdn_decode_step(cfg, st, toks.call(i % ntok), o)
@@ -334,16 +338,17 @@ def bench_gdn(args):
     traffic_bytes = None
     if gdn_counters.exists():
         c = json.loads(gdn_counters.read_text())
-        if c.get("source_hash") == gdn_hash and c.get("batch") == batch and c.get("window") == L:
+        if c.get("source_hash") == gdn_hash and c.get("batch") == batch and c.get("window") == L and ck == "f32":
             traffic_bytes = c.get("bytes_per_launch")
 
     S = torch.from_numpy(w.S0).to(dev)
-    cstep = lambda i: bg.gdn_conventional_update(cfg, S, toks.call(i % ntok), o)  # nslots 1: in place
+    ccfg = bg.GdnConfig(batch, shape.nv, shape.nk, shape.dk, shape.dv, L, 1, "bf16")   # FP32 state
+    cstep = lambda i: bg.gdn_conventional_update(ccfg, S, toks.call(i % ntok), o)  # nslots 1: in place
     for i in range(4):
         cstep(i)
     ceager, cper = timed_launches(cstep, K, torch)
     ctot = graph_time(cstep, K, torch)
-    cbytes = traffic.conventional_step_bytes(sz, batch)
+    cbytes = traffic.conventional_step_bytes(csz, batch)
     c_us = ctot * 1e3 / K
     del S
 
@@ -355,10 +360,11 @@ def bench_gdn(args):
     # speculative rounds: T = 3 drafts, U{0..3} accepted, verify + commit
     rounds = 32
     vw = synth_gdn.gdn_workload(shape, rounds, seed=2003, T=T, ckpt_std=0.0)
-    vcfg = bg.GdnConfig(batch, shape.nv, shape.nk, shape.dk, shape.dv, L, T, "bf16")
+    vcfg = bg.GdnConfig(batch, shape.nv, shape.nk, shape.dk, shape.dv, L, T, "bf16", ck)
+    scfg = bg.GdnConfig(batch, shape.nv, shape.nk, shape.dk, shape.dv, L, T, "bf16")
     del st, toks
     vst = bg.GdnState.allocate(vcfg, dev)
-    vst.ckpt.copy_(torch.from_numpy(w.S0).to(dev))
+    vst.ckpt.copy_(torch.from_numpy(w.S0).to(dev).to(vcfg.ckpt_torch))
     vtoks = staging.GdnTokenStream(vw.steps, dev, T)
     acc = torch.from_numpy(vw.extra["accepted"]).to(dev)
     vo = torch.empty((batch, T, shape.nv, shape.dv), device=dev)
@@ -368,8 +374,8 @@ def bench_gdn(args):
         vround(r)
     v_ms = graph_time(lambda r: vround(8 + r), rounds, torch)
     assert int(vst.status.cpu()[0]) == 0 and bool(torch.isfinite(vo).all())
-    sround = lambda r: (bg.gdn_conventional_update(vcfg, snap, vtoks.call(r % rounds), vo, nslots=T + 1, slot=slot),
-                        bg.gdn_conventional_commit(vcfg, slot, T + 1, acc[r % rounds], T))
+    sround = lambda r: (bg.gdn_conventional_update(scfg, snap, vtoks.call(r % rounds), vo, nslots=T + 1, slot=slot),
+                        bg.gdn_conventional_commit(scfg, slot, T + 1, acc[r % rounds], T))
     for r in range(4):
         sround(r)
     s_ms = graph_time(lambda r: sround(4 + r), rounds, torch)
@@ -388,9 +394,10 @@ def bench_gdn(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"Gated DeltaNet layer decode (ReplaySSM), batch {batch}, 32 value heads over 16 "
-                               f"key heads, dk = dv = 128, L={L}, bf16 q/k/v, fp32 g/beta, FP32 checkpoint "
-                               f"(2 MiB per sequence), steady state",
-                   "batch": batch, "window": L, "flush_launches_timed": len(fold_ms)},
+                               f"key heads, dk = dv = 128, L={L}, bf16 q/k/v, fp32 g/beta, " +
+                               ("FP32 checkpoint (2 MiB per sequence)" if ck == "f32" else
+                                "FP16 checkpoint with stochastic rounding (1 MiB per sequence)") + ", steady state",
+                   "batch": batch, "window": L, "ckpt": ck, "flush_launches_timed": len(fold_ms)},
         "kernel_source_hash": gdn_hash,
         "roofline": {"bound": "hbm", "kernel": "gdn_replay_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
@@ -406,8 +413,9 @@ def bench_gdn(args):
         "speedup_vs_conventional": round(c_us / us_step, 3),
         "verify_T3": {"us_per_round": round(v_ms * 1e3 / rounds, 2), "rounds": rounds,
                       "snapshot_baseline_us_per_round": round(s_ms * 1e3 / rounds, 2),
+                      "snapshot_baseline_state": "FP32",
                       "speedup_vs_snapshot": round(s_ms / v_ms, 3),
-                      "algorithmic_bytes_snapshot_per_round": traffic.snapshot_verify_bytes(sz, batch, T),
+                      "algorithmic_bytes_snapshot_per_round": traffic.snapshot_verify_bytes(csz, batch, T),
                       "note": "verify + commit per round vs the conventional kernel writing one FP32 snapshot "
                               "per draft + slot commit, both graph-timed"},
     }

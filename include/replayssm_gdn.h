@@ -58,6 +58,15 @@ typedef struct {
     int32_t window;      /* L: a call that starts with >= L committed records flushes first */
     int32_t max_drafts;  /* T_max */
     int32_t in_dtype;    /* RSSM_F32 or RSSM_BF16: tokens q, k, v and the k records */
+    int32_t ckpt_dtype;  /* RSSM_F32 (0): FP32 checkpoint.  RSSM_F16: half-precision recurrence
+                            checkpoint (blog section "Benefit 3": an FP16 recurrence with stochastic
+                            rounding tracks FP32): every call widens the fp16 checkpoint to fp32
+                            registers; a flush folds there and writes fp16 with stochastic rounding
+                            (random words as for the Mamba-2 FP16 checkpoint in replayssm.h: Philox4x32-10,
+                            element 4v+e takes word e at counter (v low, v high, 0, 0) under the key
+                            sr_seed, v the 4-element vector index over [batch][nv][dv][dk]); the
+                            flushing call's outputs and records come from the fp32 registers.
+                            gdn_conventional_* need RSSM_F32. */
 } gdn_config;
 
 /* Number of row blocks (workgroups) per value head: dv/16 for dk = 16, dv/64 for dk = 128. */
@@ -68,7 +77,7 @@ int gdn_row_blocks(const gdn_config *cfg);
  * per sequence, used as a ring (record c of the window in slot (start + c) % cap).
  */
 typedef struct {
-    float *ckpt;      /* [batch][nv][dv][dk] fp32 checkpoint S_s */
+    void *ckpt;       /* [batch][nv][dv][dk] checkpoint S_s: fp32, or fp16 bits with RSSM_F16 */
     void *buf_k;      /* [batch][nk][cap][dk] in_dtype: keys of the records */
     float *buf_u;     /* [batch][nv][cap][dv] fp32: corrected values u of the records */
     float *buf_g;     /* [batch][nv][cap] fp32: log decays g of the records */
@@ -84,6 +93,8 @@ typedef struct {
     const void *q, *k, *v;
     const float *g, *beta;
     int32_t T;
+    uint64_t sr_seed;   /* RSSM_F16 checkpoint: key of the stochastic rounding of a flush this call
+                           performs (vary it per call, e.g. a step counter); ignored for RSSM_F32 */
 } gdn_tokens;
 
 /* Byte sizes of ckpt, buf_k, buf_u, buf_g, meta (in that order) for cfg. */
@@ -110,8 +121,8 @@ int gdn_commit(const gdn_config *cfg, const gdn_state *st, const int32_t *accept
                void *stream);
 
 /* Fold every sequence's committed records into its checkpoint (those with none are
-   left alone). */
-int gdn_flush(const gdn_config *cfg, const gdn_state *st, void *stream);
+   left alone); sr_seed keys the stochastic rounding of an RSSM_F16 checkpoint. */
+int gdn_flush(const gdn_config *cfg, const gdn_state *st, uint64_t sr_seed, void *stream);
 
 /* Conventional GDN step (the in-library baseline; blog section "Why SSM layers can become a
    decoding bottleneck": every token loads, updates and stores the full state): per token,

@@ -19,7 +19,7 @@ GDN_NUM_BUFS = 5
 
 class gdn_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "batch", "nv", "nk", "dk", "dv", "window", "max_drafts", "in_dtype")]
+        "batch", "nv", "nk", "dk", "dv", "window", "max_drafts", "in_dtype", "ckpt_dtype")]
 
 
 class gdn_state(ctypes.Structure):
@@ -29,7 +29,8 @@ class gdn_state(ctypes.Structure):
 
 class gdn_tokens(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("T", ctypes.c_int32)]
+                ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("T", ctypes.c_int32),
+                ("sr_seed", ctypes.c_uint64)]
 
 
 _P = ctypes.POINTER
@@ -42,7 +43,7 @@ _SIGS = {
                                          ctypes.c_void_p]),
     "gdn_commit": (ctypes.c_int, [_P(gdn_config), _P(gdn_state), ctypes.c_void_p, ctypes.c_int32,
                                   ctypes.c_void_p]),
-    "gdn_flush": (ctypes.c_int, [_P(gdn_config), _P(gdn_state), ctypes.c_void_p]),
+    "gdn_flush": (ctypes.c_int, [_P(gdn_config), _P(gdn_state), ctypes.c_uint64, ctypes.c_void_p]),
     "gdn_conventional_update": (ctypes.c_int, [_P(gdn_config), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                                ctypes.c_void_p, _P(gdn_tokens), ctypes.c_void_p, ctypes.c_void_p]),
     "gdn_conventional_commit": (ctypes.c_int, [_P(gdn_config), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
@@ -73,6 +74,11 @@ class GdnConfig:
     window: int = 16
     max_drafts: int = 1
     in_dtype: str = "bf16"
+    ckpt_dtype: str = "f32"     # "f32", or "f16": FP16 checkpoint written with stochastic rounding
+
+    @property
+    def ckpt_torch(self) -> torch.dtype:
+        return torch.float16 if self.ckpt_dtype == "f16" else torch.float32
 
     @property
     def cap(self) -> int:
@@ -84,7 +90,8 @@ class GdnConfig:
 
     def c(self) -> gdn_config:
         return gdn_config(self.batch, self.nv, self.nk, self.dk, self.dv, self.window, self.max_drafts,
-                          _rb.RSSM_BF16 if self.in_dtype == "bf16" else _rb.RSSM_F32)
+                          _rb.RSSM_BF16 if self.in_dtype == "bf16" else _rb.RSSM_F32,
+                          _rb.RSSM_F16 if self.ckpt_dtype == "f16" else _rb.RSSM_F32)
 
 
 def gdn_row_blocks(cfg: GdnConfig) -> int:
@@ -101,7 +108,7 @@ def gdn_sizes(cfg: GdnConfig) -> list[int]:
 
 @dataclass
 class GdnState:
-    ckpt: torch.Tensor      # [batch][nv][dv][dk] fp32
+    ckpt: torch.Tensor      # [batch][nv][dv][dk] fp32 (fp16 with ckpt_dtype "f16")
     buf_k: torch.Tensor     # [batch][nk][cap][dk]
     buf_u: torch.Tensor     # [batch][nv][cap][dv] fp32
     buf_g: torch.Tensor     # [batch][nv][cap] fp32
@@ -114,7 +121,7 @@ class GdnState:
         b, nv, nk, dk, dv, cap = cfg.batch, cfg.nv, cfg.nk, cfg.dk, cfg.dv, cfg.cap
         parts = gdn_row_blocks(cfg)
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
-        st = cls(z((b, nv, dv, dk), torch.float32), z((b, nk, cap, dk), cfg.in_torch),
+        st = cls(z((b, nv, dv, dk), cfg.ckpt_torch), z((b, nk, cap, dk), cfg.in_torch),
                  z((b, nv, cap, dv), torch.float32), z((b, nv, cap), torch.float32),
                  z((b, nv, parts, 2), torch.int32), z((1,), torch.int32) if status else None)
         for i, t in enumerate([st.ckpt, st.buf_k, st.buf_u, st.buf_g, st.meta]):
@@ -124,7 +131,7 @@ class GdnState:
     def validate(self, cfg: GdnConfig):
         b, nv, nk, dk, dv, cap = cfg.batch, cfg.nv, cfg.nk, cfg.dk, cfg.dv, cfg.cap
         dev = self.ckpt.device
-        _expect("ckpt", self.ckpt, (b, nv, dv, dk), torch.float32, dev)
+        _expect("ckpt", self.ckpt, (b, nv, dv, dk), cfg.ckpt_torch, dev)
         _expect("buf_k", self.buf_k, (b, nk, cap, dk), cfg.in_torch, dev)
         _expect("buf_u", self.buf_u, (b, nv, cap, dv), torch.float32, dev)
         _expect("buf_g", self.buf_g, (b, nv, cap), torch.float32, dev)
@@ -146,6 +153,7 @@ class GdnTokens:
     v: torch.Tensor
     g: torch.Tensor
     beta: torch.Tensor
+    sr_seed: int = 0    # FP16 checkpoint: key of the call's stochastic rounding (vary it per call)
 
     @property
     def T(self) -> int:
@@ -160,7 +168,8 @@ class GdnTokens:
         _expect("beta", self.beta, (b, T, cfg.nv), torch.float32, device)
 
     def c(self) -> gdn_tokens:
-        return gdn_tokens(_ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.g), _ptr(self.beta), self.T)
+        return gdn_tokens(_ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.g), _ptr(self.beta), self.T,
+                          int(self.sr_seed) & 0xFFFFFFFFFFFFFFFF)
 
 
 def _run(name, cfg, state, tokens, o, stream):
@@ -188,10 +197,11 @@ def gdn_commit(cfg: GdnConfig, state: GdnState, accepted: torch.Tensor, T: int, 
                                           _stream(stream)))
 
 
-def gdn_flush(cfg: GdnConfig, state: GdnState, stream=None):
+def gdn_flush(cfg: GdnConfig, state: GdnState, sr_seed: int = 0, stream=None):
     state.validate(cfg)
     c, s = cfg.c(), state.c()
-    _check("gdn_flush", lib().gdn_flush(ctypes.byref(c), ctypes.byref(s), _stream(stream)))
+    _check("gdn_flush", lib().gdn_flush(ctypes.byref(c), ctypes.byref(s), int(sr_seed) & 0xFFFFFFFFFFFFFFFF,
+                                        _stream(stream)))
 
 
 def gdn_conventional_update(cfg: GdnConfig, states: torch.Tensor, tokens: GdnTokens, o: torch.Tensor,

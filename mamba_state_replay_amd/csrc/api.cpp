@@ -174,6 +174,8 @@ int gdn_check_config(const gdn_config* c) {
         return fail(RSSM_ERR_SHAPE, "batch * nv * row blocks too large");
     if (c->in_dtype != RSSM_F32 && c->in_dtype != RSSM_BF16)
         return fail(RSSM_ERR_DTYPE, "in_dtype must be RSSM_F32 or RSSM_BF16");
+    if (c->ckpt_dtype != RSSM_F32 && c->ckpt_dtype != RSSM_F16)
+        return fail(RSSM_ERR_DTYPE, "ckpt_dtype must be RSSM_F32 or RSSM_F16");
     if (c->window < 1 || c->window > RSSM_MAX_WINDOW)
         return fail(RSSM_ERR_SHAPE, "window %d outside 1..%d", c->window, RSSM_MAX_WINDOW);
     if (c->max_drafts < 1 || c->max_drafts > RSSM_MAX_DRAFTS)
@@ -210,7 +212,7 @@ rssm::GdnArgs gdn_args(const gdn_config* c, const gdn_state* s, const gdn_tokens
     rssm::GdnArgs a;
     std::memset(&a, 0, sizeof a);
     if (s) {
-        a.ckpt = s->ckpt;
+        a.ckpt = static_cast<float*>(s->ckpt);
         a.buf_k = s->buf_k;
         a.buf_u = s->buf_u;
         a.buf_g = s->buf_g;
@@ -224,6 +226,7 @@ rssm::GdnArgs gdn_args(const gdn_config* c, const gdn_state* s, const gdn_tokens
         a.g = t->g;
         a.beta = t->beta;
         a.T = t->T;
+        a.sr_seed = t->sr_seed;
     }
     a.o = o;
     a.batch = c->batch;
@@ -234,6 +237,7 @@ rssm::GdnArgs gdn_args(const gdn_config* c, const gdn_state* s, const gdn_tokens
     a.L = c->window;
     a.cap = c->window + 2 * c->max_drafts - 1;
     a.mode = mode;
+    a.ckpt16 = c->ckpt_dtype == RSSM_F16;
     return a;
 }
 
@@ -428,7 +432,7 @@ int gdn_sizes(const gdn_config* c, size_t bytes[GDN_NUM_BUFS]) {
     const size_t cap = (size_t)(c->window + 2 * c->max_drafts - 1);
     const size_t in_bytes = c->in_dtype == RSSM_BF16 ? 2 : 4;
     const size_t heads = (size_t)c->batch * c->nv;
-    bytes[0] = heads * c->dv * c->dk * 4;
+    bytes[0] = heads * c->dv * c->dk * (c->ckpt_dtype == RSSM_F16 ? 2 : 4);
     bytes[1] = (size_t)c->batch * c->nk * cap * c->dk * in_bytes;
     bytes[2] = heads * cap * c->dv * 4;
     bytes[3] = heads * cap * 4;
@@ -457,13 +461,17 @@ int gdn_verify_drafts(const gdn_config* cfg, const gdn_state* st, const gdn_toke
     return run_gdn(cfg, st, tok, o, rssm::MODE_VERIFY, stream, "gdn_verify_drafts");
 }
 
-int gdn_flush(const gdn_config* cfg, const gdn_state* st, void* stream) {
+int gdn_flush(const gdn_config* cfg, const gdn_state* st, uint64_t sr_seed, void* stream) {
     int rc = gdn_check_config(cfg);
     if (rc) return rc;
     if (cfg->batch == 0) return RSSM_OK;
     rc = gdn_check_state(st);
     if (rc) return rc;
-    return run_gdn(cfg, st, nullptr, nullptr, rssm::MODE_FLUSH, stream, "gdn_flush");
+    rssm::GdnArgs a = gdn_args(cfg, st, nullptr, nullptr, rssm::MODE_FLUSH);
+    a.sr_seed = sr_seed;
+    return launched(rssm::launch_gdn_replay(a, cfg->dk, cfg->in_dtype == RSSM_BF16 ? rssm::IN_BF16 : rssm::IN_F32,
+                                            static_cast<hipStream_t>(stream)),
+                    "gdn_flush");
 }
 
 int gdn_commit(const gdn_config* cfg, const gdn_state* st, const int32_t* accepted, int32_t T, void* stream) {
@@ -490,6 +498,7 @@ int gdn_conventional_update(const gdn_config* cfg, float* states, int32_t nslots
                             int32_t* status, const gdn_tokens* tok, float* o, void* stream) {
     int rc = gdn_check_config(cfg);
     if (rc) return rc;
+    if (cfg->ckpt_dtype != RSSM_F32) return fail(RSSM_ERR_DTYPE, "the conventional GDN state is fp32 (ckpt_dtype RSSM_F32)");
     if (cfg->batch == 0) return RSSM_OK;
     if (!states) return fail(RSSM_ERR_NULL, "states is NULL");
     if (!aligned(states, 16)) return fail(RSSM_ERR_SHAPE, "states must be 16-byte aligned");

@@ -85,7 +85,9 @@ __device__ __forceinline__ float dot4(const v4f a, const float4 b) {
     return fmaf(a[3], b.w, s);
 }
 
-template <int DK, typename InT>
+// F16: the checkpoint is fp16 (widened to fp32 registers after the loads, and
+// written with stochastic rounding by a flush).
+template <int DK, typename InT, bool F16>
 __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const GdnArgs a) {
     constexpr int ROWS = GdnGeo<DK>::ROWS;
     constexpr int NT = GdnGeo<DK>::NT;
@@ -214,12 +216,21 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
         bq = a.beta[ti];
     }
 
-    float* const tile_p = a.ckpt + ((size_t)bh * a.dv + p * ROWS) * DK;
+    const size_t tile_off = ((size_t)bh * a.dv + p * ROWS) * DK;   // first element of the tile
+    float* const tile_p = a.ckpt + tile_off;
+    uint16_t* const tile16 = reinterpret_cast<uint16_t*>(a.ckpt) + tile_off;
     v4f raw[Geo::NV];
+    v2u raw16[F16 ? Geo::NV : 1];
+    if constexpr (F16) {
 #pragma unroll
-    for (int s = 0; s < Geo::NV; ++s)
-        raw[s] = __builtin_bit_cast(v4f, __builtin_nontemporal_load(reinterpret_cast<const v4u*>(tile_p) +
-                                                                    Geo::vec(tid, s)));
+        for (int s = 0; s < Geo::NV; ++s)
+            raw16[s] = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(tile16) + Geo::vec(tid, s));
+    } else {
+#pragma unroll
+        for (int s = 0; s < Geo::NV; ++s)
+            raw[s] = __builtin_bit_cast(v4f, __builtin_nontemporal_load(reinterpret_cast<const v4u*>(tile_p) +
+                                                                        Geo::vec(tid, s)));
+    }
 
 #pragma unroll
     for (int j = 0; j < JOBS; ++j) {
@@ -252,6 +263,13 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
         smem[Ls.BE + tid] = bq;
     }
     __syncthreads();
+    if constexpr (F16) {
+#pragma unroll
+        for (int s = 0; s < Geo::NV; ++s) {
+            const uint32_t w0 = raw16[s][0], w1 = raw16[s][1];
+            raw[s] = v4f{f16lo_to_f32(w0), f16hi_to_f32(w0), f16lo_to_f32(w1), f16hi_to_f32(w1)};
+        }
+    }
 
     const int row0 = Geo::row0(tid);
     const int lane = tid % W;
@@ -290,10 +308,19 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
                 }
             }
         }
+        if constexpr (F16) {
+            const uint64_t v0 = tile_off / 4;                 // vector index of the tile's first element
 #pragma unroll
-        for (int s = 0; s < Geo::NV; ++s)
-            __builtin_nontemporal_store(__builtin_bit_cast(v4u, raw[s]),
-                                        reinterpret_cast<v4u*>(tile_p) + Geo::vec(tid, s));
+            for (int s = 0; s < Geo::NV; ++s) {
+                const uint2 hv = f32x4_to_f16x4_sr(raw[s], v0 + Geo::vec(tid, s), a.sr_seed);
+                __builtin_nontemporal_store(v2u{hv.x, hv.y}, reinterpret_cast<v2u*>(tile16) + Geo::vec(tid, s));
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < Geo::NV; ++s)
+                __builtin_nontemporal_store(__builtin_bit_cast(v4u, raw[s]),
+                                            reinterpret_cast<v4u*>(tile_p) + Geo::vec(tid, s));
+        }
         if (T == 0) {
             if (tid == 0) {
                 a.meta[2 * wg] = qstart;
@@ -540,7 +567,10 @@ hipError_t launch_replay_t(const GdnArgs& a, hipStream_t stream) {
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
     const size_t lds = (size_t)gdn_plan(DK, ROWS, a.cap, T).total * 4;
     const int nwg = a.batch * a.nv * a.parts;
-    hipLaunchKernelGGL((gdn_replay_kernel<DK, InT>), dim3(nwg), dim3(NT), lds, stream, a);
+    if (a.ckpt16)
+        hipLaunchKernelGGL((gdn_replay_kernel<DK, InT, true>), dim3(nwg), dim3(NT), lds, stream, a);
+    else
+        hipLaunchKernelGGL((gdn_replay_kernel<DK, InT, false>), dim3(nwg), dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
 

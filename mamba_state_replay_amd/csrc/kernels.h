@@ -80,7 +80,7 @@ hipError_t launch_conventional_commit(const CommitArgs& a, hipStream_t stream);
 // Gated DeltaNet layer (gdn.hip): one workgroup per (sequence, value head,
 // row block of ROWS value rows).
 struct GdnArgs {
-    float* ckpt;        // [batch][nv][dv][dk] fp32 (replay checkpoint, or the conventional state)
+    float* ckpt;        // [batch][nv][dv][dk] fp32, or fp16 bits (ckpt16); or the conventional states
     void* buf_k;        // [batch][nk][cap][dk] input type
     float* buf_u;       // [batch][nv][cap][dv]
     float* buf_g;       // [batch][nv][cap]
@@ -96,12 +96,14 @@ struct GdnArgs {
     int32_t nslots;        // conventional: state slots per sequence (1: in place)
     int32_t batch, nv, nk, dv, parts;
     int32_t L, cap, T, mode;
+    int32_t ckpt16;     // FP16 checkpoint written with stochastic rounding
+    uint64_t sr_seed;
 };
 
 bool gdn_shape_supported(int dk, int dv);
 int gdn_rows(int dk);   // value rows per workgroup
 size_t gdn_lds_bytes(int dk, int cap, int T);
-hipError_t launch_gdn_replay(const GdnArgs& a, int dk, int in_type, hipStream_t stream);
+hipError_t launch_gdn_replay(const GdnArgs& a, int dk, int in_type, hipStream_t stream);   // a.ckpt16 selects the FP16 kernel
 hipError_t launch_gdn_conventional(const GdnArgs& a, int dk, int in_type, hipStream_t stream);
 
 }  // namespace rssm

@@ -93,12 +93,13 @@ def snapshot_verify_bytes(sz: Sizes, batch: int, T: int) -> int:
     return batch * ((1 + T) * sz.S + T * (sz.TOK + sz.Y))
 
 
-def gdn_sizes(nv, nk, dk, dv, in_bytes=2) -> Sizes:
+def gdn_sizes(nv, nk, dk, dv, in_bytes=2, ckpt_bytes=4) -> Sizes:
     """Per-sequence sizes of a Gated DeltaNet layer in the same accounting:
-    S = nv*dv*dk*4; a record is the key (per key head, in the input type), the
-    corrected value u (per value head, fp32) and g (fp32); a token's inputs are
-    q, k (per key head), v (per value head), g and beta; outputs are fp32."""
-    S = nv * dv * dk * 4
+    S = nv*dv*dk*ckpt_bytes (4 FP32, 2 FP16); a record is the key (per key
+    head, in the input type), the corrected value u (per value head, fp32) and
+    g (fp32); a token's inputs are q, k (per key head), v (per value head), g
+    and beta; outputs are fp32."""
+    S = nv * dv * dk * ckpt_bytes
     R = nk * dk * in_bytes + nv * dv * 4 + nv * 4
     TOK = 2 * nk * dk * in_bytes + nv * dv * in_bytes + 2 * nv * 4
     Y = nv * dv * 4

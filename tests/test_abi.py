@@ -170,6 +170,10 @@ def test_gdn_sizes_and_rejections(rb):
     c = bg.GdnConfig(4, 32, 16, 128, 128).c()
     c.in_dtype = 7
     assert bg.lib().gdn_sizes(ctypes.byref(c), (ctypes.c_size_t * 5)()) == -3
+    c = bg.GdnConfig(4, 32, 16, 128, 128).c()
+    c.ckpt_dtype = 2
+    assert bg.lib().gdn_sizes(ctypes.byref(c), (ctypes.c_size_t * 5)()) == -3
+    assert bg.gdn_sizes(bg.GdnConfig(512, 32, 16, 128, 128, ckpt_dtype="f16"))[0] == 1 << 29
 
 
 def test_gdn_null_pointers_rejected_before_launch(rb):
@@ -180,7 +184,7 @@ def test_gdn_null_pointers_rejected_before_launch(rb):
     t = bg.gdn_tokens(None, None, None, None, None, 1)
     assert L.gdn_decode_step(ctypes.byref(c), ctypes.byref(s), ctypes.byref(t), None, None) == -1
     assert L.gdn_verify_drafts(ctypes.byref(c), ctypes.byref(s), ctypes.byref(t), None, None) == -1
-    assert L.gdn_flush(ctypes.byref(c), ctypes.byref(s), None) == -1
+    assert L.gdn_flush(ctypes.byref(c), ctypes.byref(s), 0, None) == -1
     assert L.gdn_commit(ctypes.byref(c), ctypes.byref(s), None, 3, None) == -4
     assert L.gdn_commit(ctypes.byref(c), ctypes.byref(s), None, 1, None) == -1
     assert L.gdn_conventional_update(ctypes.byref(c), None, 1, None, None, ctypes.byref(t), None, None) == -1

@@ -1,0 +1,158 @@
+"""GDN layer with an FP16 recurrence checkpoint written with stochastic
+rounding (ckpt_dtype "f16"): the flush writes the oracle's stochastic rounding
+(oracle/sr.py, from the generator's and the rounding's definitions) of the
+exact fold, and decoding through several flushes tracks the oracle that rounds
+its own exact folds with the same seeds."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gdn as ogdn
+from oracle import sr
+from mamba_state_replay_amd import synth_gdn as sg
+from tests.gpu_util import assert_rows_close, say
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = sg.GdnShape(batch=2, nv=32, nk=16, dk=128, dv=128, window=4)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _setup(steps, seed, dev, T=1):
+    from mamba_state_replay_amd import binding_gdn as bg
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    w = sg.gdn_workload(SHAPE, steps, seed)
+    S0h = w.S0.astype(np.float16)                 # the checkpoint holds fp16 values
+    cfg = bg.GdnConfig(SHAPE.batch, SHAPE.nv, SHAPE.nk, SHAPE.dk, SHAPE.dv, SHAPE.window, T, "bf16", "f16")
+    st = bg.GdnState.allocate(cfg, dev)
+    st.ckpt.copy_(torch.from_numpy(S0h).to(dev))
+    return bg, w, S0h.astype(np.float64), cfg, st, GdnTokenStream(w.steps, dev)
+
+
+def _neighbours(got, exact, spacings=1):
+    """|got - exact| minus `spacings` fp16 spacings at the element (the larger
+    spacing at a binade edge) and 1e-6 of the head's largest magnitude for the
+    fp32 fold's own rounding: <= 0 where got is that close to exact."""
+    g64 = got.astype(np.float64)
+    spacing = np.maximum(sr.f16_grid(np.abs(exact))[1], sr.f16_grid(np.abs(g64))[1])
+    slack = 1e-6 * np.abs(exact).max(axis=(-1, -2), keepdims=True)
+    return np.abs(g64 - exact) - spacings * spacing - slack
+
+
+def test_gdn_f16_flush_writes_stochastic_rounding_of_the_fold(dev):
+    bg, w, S0, cfg, st, ts = _setup(4, 3001, dev)
+    o = torch.empty((4, SHAPE.batch, 1, SHAPE.nv, SHAPE.dv), device=dev)
+    say("gdn f16 checkpoint: 4 decode steps, then a flush")
+    for t in range(4):
+        bg.gdn_decode_step(cfg, st, ts.call(t), o[t])
+    seed = 0x5EED0000D17A
+    bg.gdn_flush(cfg, st, seed)
+    torch.cuda.synchronize()
+    tk = w.steps
+    exact, oref = ogdn.conventional(S0, tk.q, tk.k, tk.v, tk.g, tk.beta)
+    assert_rows_close(o.cpu().numpy()[:, :, 0], oref, what="gdn f16 outputs before the flush")
+    got = st.ckpt.cpu().numpy()
+    want = sr.sr_checkpoint(exact, seed)
+    same = got.view(np.uint16) == want.astype(np.float16).view(np.uint16)
+    excess = _neighbours(got, exact)
+    print(f"[gpu] gdn f16 flush: {same.mean():.6f} of elements equal the oracle's rounding; "
+          f"largest excess over one spacing {excess.max():.3g}", flush=True)
+    assert (excess <= 0).all(), "an element left the fp16 neighbours of its fold"
+    assert same.mean() >= 0.999
+    assert np.all(st.meta.cpu().numpy()[..., 1] == 0)
+
+
+def test_gdn_f16_decode_through_flushes(dev):
+    """Decode 13 tokens at L = 4 (flushes at the starts of calls 4, 8 and 12,
+    each with its own seed).  The oracle composes the definition's stepping with
+    the same flush schedule: at a flush it folds exactly (fp64), the flushing
+    call's token reads the exact fold, and the checkpoint then becomes the
+    stochastic rounding of that fold with the call's seed."""
+    steps = 13
+    bg, w, S0, cfg, st, ts = _setup(steps, 3002, dev)
+    o = torch.empty((steps, SHAPE.batch, 1, SHAPE.nv, SHAPE.dv), device=dev)
+    say("gdn f16 checkpoint: 13 decode steps through three flushes")
+    for t in range(steps):
+        tok = ts.call(t)
+        tok.sr_seed = 9000 + t
+        bg.gdn_decode_step(cfg, st, tok, o[t])
+    torch.cuda.synchronize()
+    tk = w.steps
+    rep = ogdn.Replay(S0, SHAPE.nv, SHAPE.nk)
+    oref = np.zeros((steps, SHAPE.batch, SHAPE.nv, SHAPE.dv))
+    for t in range(steps):
+        flushing = [b for b in range(SHAPE.batch) if len(rep.records[b]) >= SHAPE.window]
+        for b in flushing:
+            rep.fold(b)
+        for b in range(SHAPE.batch):
+            oref[t, b] = rep.step(b, tk.q[t][b], tk.k[t][b], tk.v[t][b], tk.g[t][b], tk.beta[t][b])
+        if flushing:
+            rounded = sr.sr_checkpoint(rep.ckpt, 9000 + t)
+            for b in flushing:
+                rep.ckpt[b] = rounded[b]
+    assert_rows_close(o.cpu().numpy()[:, :, 0], oref, what="gdn f16 decode outputs")
+    # the checkpoint after the last flush (call 12) equals the oracle's almost
+    # everywhere.  Where a rounding decision went the other way (the kernel's
+    # fp32 fold and the oracle's fp64 fold straddle a threshold) the two differ
+    # by a spacing, and in GDN such a difference spreads along its row at the
+    # next tokens (u reads S k), so after three flushes the bound is on the
+    # head's scale: within four fp16 half-ulps (2^-11) of the head's largest value
+    got = st.ckpt.cpu().numpy()
+    diff = np.abs(got.astype(np.float64) - rep.ckpt).max(axis=(-1, -2))
+    scale = np.abs(rep.ckpt).max(axis=(-1, -2))
+    print(f"[gpu] gdn f16 checkpoint after three flushes: max difference per head "
+          f"{(diff / scale).max():.2e} of the head's largest value", flush=True)
+    assert (diff <= 4 * 2.0 ** -11 * scale).all()
+    same = got.view(np.uint16) == rep.ckpt.astype(np.float16).view(np.uint16)
+    print(f"[gpu] gdn f16 checkpoint after three flushes: {same.mean():.6f} equal", flush=True)
+    assert same.mean() >= 0.99
+    assert int(st.status.cpu()[0]) == 0
+
+
+def test_gdn_f16_verify_commit(dev):
+    """Speculative rounds over the FP16 checkpoint (T = 3, L = 4): outputs match
+    the oracle that follows the same flush schedule and rounding."""
+    from mamba_state_replay_amd import binding_gdn as bg
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    T, rounds = 3, 6
+    w = sg.gdn_workload(SHAPE, rounds, 3003, T=T)
+    acc = w.extra["accepted"]
+    S0 = w.S0.astype(np.float16)
+    cfg = bg.GdnConfig(SHAPE.batch, SHAPE.nv, SHAPE.nk, SHAPE.dk, SHAPE.dv, SHAPE.window, T, "bf16", "f16")
+    st = bg.GdnState.allocate(cfg, dev)
+    st.ckpt.copy_(torch.from_numpy(S0).to(dev))
+    ts = GdnTokenStream(w.steps, dev, T)
+    acc_d = torch.from_numpy(acc).to(dev)
+    o = torch.empty((rounds, SHAPE.batch, T, SHAPE.nv, SHAPE.dv), device=dev)
+    say("gdn f16 checkpoint: verify + commit rounds")
+    for r in range(rounds):
+        tok = ts.call(r)
+        tok.sr_seed = 7000 + r
+        bg.gdn_verify_drafts(cfg, st, tok, o[r])
+        bg.gdn_commit(cfg, st, acc_d[r], T)
+    torch.cuda.synchronize()
+    tk = w.steps
+    rep = ogdn.Replay(S0.astype(np.float64), SHAPE.nv, SHAPE.nk)
+    oref = np.zeros((rounds, T, SHAPE.batch, SHAPE.nv, SHAPE.dv))
+    for r in range(rounds):
+        flushing = [b for b in range(SHAPE.batch) if len(rep.records[b]) >= SHAPE.window]
+        for b in flushing:
+            rep.fold(b)
+        for b in range(SHAPE.batch):
+            drafts = [(tk.q[r * T + i][b], tk.k[r * T + i][b], tk.v[r * T + i][b], tk.g[r * T + i][b],
+                       tk.beta[r * T + i][b]) for i in range(T)]
+            outs, recs = rep.verify(b, drafts)
+            oref[r, :, b] = np.stack(outs)
+            rep.commit(b, recs, int(acc[r, b]))
+        if flushing:
+            rounded = sr.sr_checkpoint(rep.ckpt, 7000 + r)
+            for b in flushing:
+                rep.ckpt[b] = rounded[b]
+    assert_rows_close(np.swapaxes(o.cpu().numpy(), 1, 2), oref, what="gdn f16 draft outputs")
+    assert int(st.status.cpu()[0]) == 0
