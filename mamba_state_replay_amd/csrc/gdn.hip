@@ -85,6 +85,44 @@ __device__ __forceinline__ float dot4(const v4f a, const float4 b) {
     return fmaf(a[3], b.w, s);
 }
 
+// Step 4 of a call: one 8-lane group per (query q, window position c <= m_q =
+// np + q) forms the segment decay exp(sum_{c<i<=m_q} g_i) and the key-key and
+// key-query scores (k_c . k_q, k_c . q_q), which give ck[q][c] (c < m_q) and
+// cq[q][c]; then dd[q] = exp(sum_{i<=m_q} g_i).  Window positions below np are
+// committed records (K, G), the others the call's tokens (KQ, GQ).
+template <int DK, int NT>
+__device__ __forceinline__ void gdn_coefficients(float* smem, const GdnLds& Ls, int np, int T, int cap, int tid) {
+    const int m = np + T;                             // window positions of the call
+    const int grp = tid / 8, gl = tid % 8;
+    for (int idx = grp; idx < T * m; idx += NT / 8) {
+        const int q = idx / m, c = idx % m;
+        const int mq = np + q;
+        if (c > mq) continue;                         // the whole group skips together
+        const float* key = c < np ? smem + Ls.K + c * DK : smem + Ls.KQ + (c - np) * DK;
+        const float* kq = smem + Ls.KQ + q * DK;
+        const float* qq = smem + Ls.QQ + q * DK;
+        float sk = 0.0f, sq = 0.0f, seg = 0.0f;
+        for (int e = gl; e < DK; e += 8) {
+            sk = fmaf(key[e], kq[e], sk);
+            sq = fmaf(key[e], qq[e], sq);
+        }
+        for (int i = c + 1 + gl; i <= mq; i += 8) seg += i < np ? smem[Ls.G + i] : smem[Ls.GQ + i - np];
+        sk = group_sum<8>(sk);
+        sq = group_sum<8>(sq);
+        seg = group_sum<8>(seg);
+        if (gl == 0) {
+            const float w = __expf(seg);
+            smem[Ls.CK + q * cap + c] = c < mq ? w * sk : 0.0f;
+            smem[Ls.CQ + q * cap + c] = w * sq;
+        }
+    }
+    for (int q = tid; q < T; q += NT) {
+        float s = 0.0f;
+        for (int i = 0; i <= np + q; ++i) s += i < np ? smem[Ls.G + i] : smem[Ls.GQ + i - np];
+        smem[Ls.DD + q] = __expf(s);
+    }
+}
+
 // F16: the checkpoint is fp16 (widened to fp32 registers after the loads, and
 // written with stochastic rounding by a flush).
 template <int DK, typename InT, bool F16>
@@ -331,37 +369,7 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     }
 
     // 4. coefficients: one 8-lane group per (query q, window position c <= np + q)
-    {
-        const int m = np + T;                             // window positions of the call
-        const int grp = tid / 8, gl = tid % 8;
-        for (int idx = grp; idx < T * m; idx += NT / 8) {
-            const int q = idx / m, c = idx % m;
-            const int mq = np + q;
-            if (c > mq) continue;                         // the whole group skips together
-            const float* key = c < np ? smem + Ls.K + c * DK : smem + Ls.KQ + (c - np) * DK;
-            const float* kq = smem + Ls.KQ + q * DK;
-            const float* qq = smem + Ls.QQ + q * DK;
-            float sk = 0.0f, sq = 0.0f, seg = 0.0f;
-            for (int e = gl; e < DK; e += 8) {
-                sk = fmaf(key[e], kq[e], sk);
-                sq = fmaf(key[e], qq[e], sq);
-            }
-            for (int i = c + 1 + gl; i <= mq; i += 8) seg += i < np ? smem[Ls.G + i] : smem[Ls.GQ + i - np];
-            sk = group_sum<8>(sk);
-            sq = group_sum<8>(sq);
-            seg = group_sum<8>(seg);
-            if (gl == 0) {
-                const float w = __expf(seg);
-                smem[Ls.CK + q * cap + c] = c < mq ? w * sk : 0.0f;
-                smem[Ls.CQ + q * cap + c] = w * sq;
-            }
-        }
-        for (int q = tid; q < T; q += NT) {
-            float s = 0.0f;
-            for (int i = 0; i <= np + q; ++i) s += i < np ? smem[Ls.G + i] : smem[Ls.GQ + i - np];
-            smem[Ls.DD + q] = __expf(s);
-        }
-    }
+    gdn_coefficients<DK, NT>(smem, Ls, np, T, cap, tid);
     __syncthreads();
 
     // 5. per query, in order: the rows' share of S_s k_q and S_s q_q from the
@@ -438,6 +446,332 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     if (tid == 0) {
         a.meta[2 * wg] = qstart;
         a.meta[2 * wg + 1] = np + (a.mode == MODE_DECODE ? T : 0);
+    }
+}
+
+// FP16 checkpoint, one workgroup per 128 value rows (two 64-row blocks) of a
+// head with dk = 128.  The fp16 tile of 128 rows is 32 KiB, the register
+// footprint of one 64-row FP32 tile, so a workgroup streams as many bytes as
+// the FP32 kernel's instead of half of them.  The tile stays packed in
+// registers (TileGeo<128, 128, 256, 2>: 4 rows per thread, two 8-element
+// vectors per row) and is widened where it is read.  The steps are those of
+// gdn_replay_kernel with these differences: a flush folds one row at a time in
+// fp32, writes it with stochastic rounding and forms that row's query products
+// from the fp32 values; the products are reduced per row and staged in LDS,
+// and one thread per row then walks the queries in order (u_q, o_q).
+template <typename InT>
+__global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnArgs a) {
+    constexpr int DK = 128, ROWS = 128, NT = 256;
+    using Geo = TileGeo<ROWS, DK, NT, 2>;
+    static_assert(Geo::NI == 4 && Geo::VPL == 2 && Geo::W == 8 && Geo::NV == 8, "fp16 wide tile layout");
+    constexpr int W = Geo::W;
+    constexpr int EPV = InTraits<InT>::EPV;
+    constexpr int KV = DK / EPV;
+    constexpr int RV = ROWS / EPV;
+    constexpr int UV = ROWS / 4;
+    extern __shared__ float smem[];
+
+    const int tid = threadIdx.x;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);   // = (b * nv + h) * (parts / 2) + pw
+    const int pairs = a.parts / 2;
+    const int pw = wg % pairs;
+    const int bh = wg / pairs;
+    const int b = bh / a.nv;
+    const int h = bh % a.nv;
+    const int kh = h / (a.nv / a.nk);
+    const int cap = a.cap;
+    const int T = a.mode == MODE_FLUSH ? 0 : a.T;
+    const GdnLds Ls = gdn_plan(DK, ROWS, cap, T);
+    const int PK = Ls.total, PQ = Ls.total + T * ROWS;     // reduced products [q][row]
+    const int m0 = bh * a.parts + 2 * pw;                  // the pointer copies of the two row blocks
+
+    // 1. ring pointer (the copies of both row blocks are equal) and flush decision
+    const int start = a.meta[2 * m0];
+    const int n = a.meta[2 * m0 + 1];
+    const bool valid = start >= 0 && start < cap && n >= 0 && n <= cap && a.meta[2 * m0 + 2] == start &&
+                       a.meta[2 * m0 + 3] == n;
+    const bool fold = valid && (a.mode == MODE_FLUSH ? n > 0 : n >= a.L);
+    const int np = fold ? 0 : n;
+    if (!valid || np + T > cap) {
+        if (tid == 0 && a.status) atomicOr(a.status, (int)kStatusMeta);
+        for (int i = tid; i < T * ROWS; i += NT)
+            a.o[((size_t)(b * T + i / ROWS) * a.nv + h) * a.dv + pw * ROWS + i % ROWS] = __builtin_nanf("");
+        return;
+    }
+    if (!fold && T == 0) return;
+    int qstart = start + n;
+    qstart -= qstart >= cap ? cap : 0;
+    if (!fold) qstart = start;
+
+    // 2. staging (as in gdn_replay_kernel, for 128 rows)
+    const InT* kring = static_cast<const InT*>(a.buf_k) + (size_t)(b * a.nk + kh) * cap * DK;
+    const float* uring = a.buf_u + (size_t)bh * cap * a.dv + pw * ROWS;
+    const bool append_k = (h % (a.nv / a.nk)) == 0 && pw == 0;
+    const int nkv = n * KV, nuv = n * UV, ntk = T * KV;
+    const int total = nkv + nuv + 2 * ntk + T * RV;
+    auto job = [&](int i, const uint4*& src, float*& dst, bool& widen, uint4*& app) {
+        app = nullptr;
+        widen = true;
+        if (i < nkv) {
+            const int c = i / KV, e = i - c * KV;
+            int slot = start + c;
+            slot -= slot >= cap ? cap : 0;
+            src = reinterpret_cast<const uint4*>(kring + (size_t)slot * DK) + e;
+            dst = smem + Ls.K + c * DK + e * EPV;
+            return;
+        }
+        i -= nkv;
+        if (i < nuv) {
+            const int c = i / UV, e = i - c * UV;
+            int slot = start + c;
+            slot -= slot >= cap ? cap : 0;
+            src = reinterpret_cast<const uint4*>(uring + (size_t)slot * a.dv) + e;
+            dst = smem + Ls.U + c * Ls.US + 4 * e;
+            widen = false;
+            return;
+        }
+        i -= nuv;
+        if (i < 2 * ntk) {
+            const bool isq = i >= ntk;
+            const int r = isq ? i - ntk : i;
+            const int q = r / KV, e = r - q * KV;
+            src = reinterpret_cast<const uint4*>(static_cast<const InT*>(isq ? a.q : a.k) +
+                                                 ((size_t)(b * T + q) * a.nk + kh) * DK) + e;
+            dst = smem + (isq ? Ls.QQ : Ls.KQ) + q * DK + e * EPV;
+            if (!isq && append_k) {
+                int slot = qstart + np + q;
+                slot -= slot >= cap ? cap : 0;
+                app = reinterpret_cast<uint4*>(static_cast<InT*>(a.buf_k) +
+                                               ((size_t)(b * a.nk + kh) * cap + slot) * DK) + e;
+            }
+            return;
+        }
+        i -= 2 * ntk;
+        const int q = i / RV, e = i - q * RV;
+        src = reinterpret_cast<const uint4*>(static_cast<const InT*>(a.v) +
+                                             ((size_t)(b * T + q) * a.nv + h) * a.dv + pw * ROWS) + e;
+        dst = smem + Ls.V + q * ROWS + e * EPV;
+    };
+    auto put = [&](float* dst, bool widen, uint4* app, const uint4 v) {
+        if (app) *app = v;
+        if (widen) {
+            widen16<InT>(v, dst);
+        } else {
+            *reinterpret_cast<uint4*>(dst) = v;
+        }
+    };
+    constexpr int JOBS = 2;
+    uint4 jv[JOBS];
+#pragma unroll
+    for (int j = 0; j < JOBS; ++j) {
+        const int i = tid + j * NT;
+        if (i < total) {
+            const uint4* src;
+            float* dst;
+            bool widen;
+            uint4* app;
+            job(i, src, dst, widen, app);
+            jv[j] = *src;
+        }
+    }
+    float gv = 0.0f, gq = 0.0f, bq = 0.0f;
+    if (tid < n) {
+        int slot = start + tid;
+        slot -= slot >= cap ? cap : 0;
+        gv = a.buf_g[(size_t)bh * cap + slot];
+    }
+    if (tid < T) {
+        const size_t ti = (size_t)(b * T + tid) * a.nv + h;
+        gq = a.g[ti];
+        bq = a.beta[ti];
+    }
+
+    const size_t tile_off = ((size_t)bh * a.dv + pw * ROWS) * DK;
+    uint16_t* const tile16 = reinterpret_cast<uint16_t*>(a.ckpt) + tile_off;
+    v4u raw[Geo::NV];                                       // 8 fp16 values per vector
+#pragma unroll
+    for (int s = 0; s < Geo::NV; ++s)
+        raw[s] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(tile16) + Geo::vec(tid, s));
+
+#pragma unroll
+    for (int j = 0; j < JOBS; ++j) {
+        const int i = tid + j * NT;
+        if (i < total) {
+            const uint4* src;
+            float* dst;
+            bool widen;
+            uint4* app;
+            job(i, src, dst, widen, app);
+            put(dst, widen, app, jv[j]);
+        }
+    }
+    for (int i = tid + JOBS * NT; i < total; i += NT) {
+        const uint4* src;
+        float* dst;
+        bool widen;
+        uint4* app;
+        job(i, src, dst, widen, app);
+        put(dst, widen, app, *src);
+    }
+    if (tid < n) smem[Ls.G + tid] = gv;
+    for (int i = tid + NT; i < n; i += NT) {
+        int slot = start + i;
+        slot -= slot >= cap ? cap : 0;
+        smem[Ls.G + i] = a.buf_g[(size_t)bh * cap + slot];
+    }
+    if (tid < T) {
+        smem[Ls.GQ + tid] = gq;
+        smem[Ls.BE + tid] = bq;
+    }
+    __syncthreads();
+
+    const int row0 = Geo::row0(tid);
+    const int lane = tid % W;
+    // the 16 values of row r of this thread's share, widened: columns (lane + 8k) * 8 + e
+    auto widen_row = [&](int r, float (&f)[16]) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const v4u w = raw[r * Geo::VPL + k];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[8 * k + 2 * e] = f16lo_to_f32(w[e]);
+                f[8 * k + 2 * e + 1] = f16hi_to_f32(w[e]);
+            }
+        }
+    };
+    auto dot_row = [&](const float (&f)[16], const float* x) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float4 x0 = *reinterpret_cast<const float4*>(x + (lane + W * k) * 8);
+            const float4 x1 = *reinterpret_cast<const float4*>(x + (lane + W * k) * 8 + 4);
+            acc = fmaf(f[8 * k], x0.x, acc);
+            acc = fmaf(f[8 * k + 1], x0.y, acc);
+            acc = fmaf(f[8 * k + 2], x0.z, acc);
+            acc = fmaf(f[8 * k + 3], x0.w, acc);
+            acc = fmaf(f[8 * k + 4], x1.x, acc);
+            acc = fmaf(f[8 * k + 5], x1.y, acc);
+            acc = fmaf(f[8 * k + 6], x1.z, acc);
+            acc = fmaf(f[8 * k + 7], x1.w, acc);
+        }
+        return acc;
+    };
+
+    if (fold) {
+        // 3. flush weights, then per row: fold in fp32, write with stochastic rounding
+        for (int c = tid; c < n; c += NT) {
+            float sg = 0.0f;
+            for (int i = c + 1; i < n; ++i) sg += smem[Ls.G + i];
+            smem[Ls.WF + c] = __expf(sg);
+        }
+        if (tid == NT - 1) {
+            float sg = 0.0f;
+            for (int i = 0; i < n; ++i) sg += smem[Ls.G + i];
+            smem[Ls.DD + T] = __expf(sg);
+        }
+    }
+    // 4. coefficients
+    gdn_coefficients<DK, NT>(smem, Ls, np, T, cap, tid);
+    __syncthreads();
+
+    // 5. per row of this thread: the query products (from the fp32 fold on a
+    // flush call, else from the widened fp16 checkpoint) plus the committed
+    // records' terms, reduced over the row's lanes and staged in LDS
+    const float gf = fold ? smem[Ls.DD + T] : 1.0f;
+#pragma unroll
+    for (int r = 0; r < Geo::NI; ++r) {
+        const int row = row0 + r;
+        float f[16];
+        widen_row(r, f);
+        if (fold) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) f[e] *= gf;
+            for (int c = 0; c < n; ++c) {
+                const float cf = smem[Ls.WF + c] * smem[Ls.U + c * Ls.US + row];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const float* kc = smem + Ls.K + c * DK + (lane + W * k) * 8;
+                    const float4 k0 = *reinterpret_cast<const float4*>(kc);
+                    const float4 k1 = *reinterpret_cast<const float4*>(kc + 4);
+                    f[8 * k] = fmaf(cf, k0.x, f[8 * k]);
+                    f[8 * k + 1] = fmaf(cf, k0.y, f[8 * k + 1]);
+                    f[8 * k + 2] = fmaf(cf, k0.z, f[8 * k + 2]);
+                    f[8 * k + 3] = fmaf(cf, k0.w, f[8 * k + 3]);
+                    f[8 * k + 4] = fmaf(cf, k1.x, f[8 * k + 4]);
+                    f[8 * k + 5] = fmaf(cf, k1.y, f[8 * k + 5]);
+                    f[8 * k + 6] = fmaf(cf, k1.z, f[8 * k + 6]);
+                    f[8 * k + 7] = fmaf(cf, k1.w, f[8 * k + 7]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int s = r * Geo::VPL + k;
+                const uint64_t v0 = (tile_off + (size_t)row * DK + (size_t)(lane + W * k) * 8) / 4;
+                const uint2 h0 = f32x4_to_f16x4_sr(v4f{f[8 * k], f[8 * k + 1], f[8 * k + 2], f[8 * k + 3]}, v0,
+                                                   a.sr_seed);
+                const uint2 h1 = f32x4_to_f16x4_sr(v4f{f[8 * k + 4], f[8 * k + 5], f[8 * k + 6], f[8 * k + 7]},
+                                                   v0 + 1, a.sr_seed);
+                __builtin_nontemporal_store(v4u{h0.x, h0.y, h1.x, h1.y},
+                                            reinterpret_cast<v4u*>(tile16) + Geo::vec(tid, s));
+            }
+        }
+        for (int q = 0; q < T; ++q) {
+            const float d = smem[Ls.DD + q];
+            float pk = d * dot_row(f, smem + Ls.KQ + q * DK);
+            float pq = d * dot_row(f, smem + Ls.QQ + q * DK);
+            for (int c = lane; c < np; c += W) {
+                const float u = smem[Ls.U + c * Ls.US + row];
+                pk = fmaf(smem[Ls.CK + q * cap + c], u, pk);
+                pq = fmaf(smem[Ls.CQ + q * cap + c], u, pq);
+            }
+            pk = group_sum<W>(pk);
+            pq = group_sum<W>(pq);
+            if (lane == 0) {
+                smem[PK + q * ROWS + row] = pk;
+                smem[PQ + q * ROWS + row] = pq;
+            }
+        }
+    }
+    if (T == 0) {
+        if (tid < 2) {
+            a.meta[2 * (m0 + tid)] = qstart;
+            a.meta[2 * (m0 + tid) + 1] = 0;
+        }
+        return;
+    }
+    __syncthreads();
+
+    // 6. one thread per row walks the queries in order: u_q, then o_q
+    if (tid < ROWS) {
+        const int row = tid;
+        float* const uring_w = a.buf_u + (size_t)bh * cap * a.dv + pw * ROWS + row;
+        for (int q = 0; q < T; ++q) {
+            float sk = smem[PK + q * ROWS + row];
+            float o = smem[PQ + q * ROWS + row];
+            for (int dd = 0; dd < q; ++dd) {
+                const float ud = smem[Ls.UD + dd * ROWS + row];
+                sk = fmaf(smem[Ls.CK + q * cap + np + dd], ud, sk);
+                o = fmaf(smem[Ls.CQ + q * cap + np + dd], ud, o);
+            }
+            const float u = smem[Ls.BE + q] * (smem[Ls.V + q * ROWS + row] - sk);
+            o = fmaf(smem[Ls.CQ + q * cap + np + q], u, o);
+            smem[Ls.UD + q * ROWS + row] = u;
+            a.o[((size_t)(b * T + q) * a.nv + h) * a.dv + pw * ROWS + row] = o;
+            int slot = qstart + np + q;
+            slot -= slot >= cap ? cap : 0;
+            uring_w[(size_t)slot * a.dv] = u;
+        }
+    }
+    if (pw == 0 && tid >= ROWS && tid < ROWS + T) {
+        const int q = tid - ROWS;
+        int slot = qstart + np + q;
+        slot -= slot >= cap ? cap : 0;
+        a.buf_g[(size_t)bh * cap + slot] = smem[Ls.GQ + q];
+    }
+    // 7. ring pointers of both row blocks
+    if (tid < 2) {
+        a.meta[2 * (m0 + tid)] = qstart;
+        a.meta[2 * (m0 + tid) + 1] = np + (a.mode == MODE_DECODE ? T : 0);
     }
 }
 
@@ -567,6 +901,13 @@ hipError_t launch_replay_t(const GdnArgs& a, hipStream_t stream) {
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
     const size_t lds = (size_t)gdn_plan(DK, ROWS, a.cap, T).total * 4;
     const int nwg = a.batch * a.nv * a.parts;
+    if constexpr (DK == 128) {
+        const size_t lds2 = ((size_t)gdn_plan(DK, 128, a.cap, T).total + 2 * (size_t)T * 128) * 4;
+        if (a.ckpt16 && a.parts % 2 == 0 && lds2 <= 64 * 1024) {   // 128 rows per workgroup
+            hipLaunchKernelGGL((gdn_replay_f16_wide_kernel<InT>), dim3(nwg / 2), dim3(256), lds2, stream, a);
+            return hipGetLastError();
+        }
+    }
     if (a.ckpt16)
         hipLaunchKernelGGL((gdn_replay_kernel<DK, InT, true>), dim3(nwg), dim3(NT), lds, stream, a);
     else
