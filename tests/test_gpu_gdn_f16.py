@@ -15,6 +15,9 @@ from tests.gpu_util import assert_rows_close, say
 pytestmark = pytest.mark.gpu
 
 SHAPE = sg.GdnShape(batch=2, nv=32, nk=16, dk=128, dv=128, window=4)
+# dv = 128 runs the kernel with 128 rows per workgroup; dv = 64 and dk = 16 the 64- and 16-row one
+SHAPES = {"wide": SHAPE, "rows64": sg.GdnShape(batch=2, nv=8, nk=4, dk=128, dv=64, window=4),
+          "tiny": sg.GdnShape(batch=3, nv=4, nk=2, dk=16, dv=32, window=4)}
 
 
 @pytest.fixture(scope="module")
@@ -24,12 +27,12 @@ def dev():
     return torch.device("cuda", 0)
 
 
-def _setup(steps, seed, dev, T=1):
+def _setup(steps, seed, dev, T=1, shape=SHAPE):
     from mamba_state_replay_amd import binding_gdn as bg
     from mamba_state_replay_amd.staging import GdnTokenStream
-    w = sg.gdn_workload(SHAPE, steps, seed)
+    w = sg.gdn_workload(shape, steps, seed)
     S0h = w.S0.astype(np.float16)                 # the checkpoint holds fp16 values
-    cfg = bg.GdnConfig(SHAPE.batch, SHAPE.nv, SHAPE.nk, SHAPE.dk, SHAPE.dv, SHAPE.window, T, "bf16", "f16")
+    cfg = bg.GdnConfig(shape.batch, shape.nv, shape.nk, shape.dk, shape.dv, shape.window, T, "bf16", "f16")
     st = bg.GdnState.allocate(cfg, dev)
     st.ckpt.copy_(torch.from_numpy(S0h).to(dev))
     return bg, w, S0h.astype(np.float64), cfg, st, GdnTokenStream(w.steps, dev)
@@ -45,10 +48,12 @@ def _neighbours(got, exact, spacings=1):
     return np.abs(g64 - exact) - spacings * spacing - slack
 
 
-def test_gdn_f16_flush_writes_stochastic_rounding_of_the_fold(dev):
-    bg, w, S0, cfg, st, ts = _setup(4, 3001, dev)
-    o = torch.empty((4, SHAPE.batch, 1, SHAPE.nv, SHAPE.dv), device=dev)
-    say("gdn f16 checkpoint: 4 decode steps, then a flush")
+@pytest.mark.parametrize("which", sorted(SHAPES))
+def test_gdn_f16_flush_writes_stochastic_rounding_of_the_fold(which, dev):
+    shape = SHAPES[which]
+    bg, w, S0, cfg, st, ts = _setup(4, 3001, dev, shape=shape)
+    o = torch.empty((4, shape.batch, 1, shape.nv, shape.dv), device=dev)
+    say(f"gdn f16 checkpoint ({which}): 4 decode steps, then a flush")
     for t in range(4):
         bg.gdn_decode_step(cfg, st, ts.call(t), o[t])
     seed = 0x5EED0000D17A
@@ -68,16 +73,18 @@ def test_gdn_f16_flush_writes_stochastic_rounding_of_the_fold(dev):
     assert np.all(st.meta.cpu().numpy()[..., 1] == 0)
 
 
-def test_gdn_f16_decode_through_flushes(dev):
+@pytest.mark.parametrize("which", sorted(SHAPES))
+def test_gdn_f16_decode_through_flushes(which, dev):
     """Decode 13 tokens at L = 4 (flushes at the starts of calls 4, 8 and 12,
     each with its own seed).  The oracle composes the definition's stepping with
     the same flush schedule: at a flush it folds exactly (fp64), the flushing
     call's token reads the exact fold, and the checkpoint then becomes the
     stochastic rounding of that fold with the call's seed."""
     steps = 13
-    bg, w, S0, cfg, st, ts = _setup(steps, 3002, dev)
+    SHAPE = SHAPES[which]
+    bg, w, S0, cfg, st, ts = _setup(steps, 3002, dev, shape=SHAPE)
     o = torch.empty((steps, SHAPE.batch, 1, SHAPE.nv, SHAPE.dv), device=dev)
-    say("gdn f16 checkpoint: 13 decode steps through three flushes")
+    say(f"gdn f16 checkpoint ({which}): 13 decode steps through three flushes")
     for t in range(steps):
         tok = ts.call(t)
         tok.sr_seed = 9000 + t
