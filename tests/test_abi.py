@@ -174,6 +174,13 @@ def test_gdn_sizes_and_rejections(rb):
     c.ckpt_dtype = 2
     assert bg.lib().gdn_sizes(ctypes.byref(c), (ctypes.c_size_t * 5)()) == -3
     assert bg.gdn_sizes(bg.GdnConfig(512, 32, 16, 128, 128, ckpt_dtype="f16"))[0] == 1 << 29
+    # LDS bound: dk = 128 takes window 40 at 8 drafts and window 64 at 4, not window 48 or 64 at 8
+    bg.gdn_sizes(bg.GdnConfig(2, 32, 16, 128, 128, 40, 8))
+    bg.gdn_sizes(bg.GdnConfig(2, 32, 16, 128, 128, 64, 4))
+    for L in (48, 64):
+        with pytest.raises(rb.ReplaySSMError) as e:
+            bg.gdn_sizes(bg.GdnConfig(2, 32, 16, 128, 128, L, 8))
+        assert e.value.code == -2 and "LDS" in str(e.value)
 
 
 def test_gdn_null_pointers_rejected_before_launch(rb):

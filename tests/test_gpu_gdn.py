@@ -405,3 +405,39 @@ def test_gdn_long_run_no_drift(dev):
     print(f"[gpu] gdn per-window max error: first {errs[:3]}, last {errs[-3:]}", flush=True)
     assert max(errs) <= TOL
     assert max(errs[-3:]) <= 4 * max(max(errs[:3]), 1e-7)
+
+
+@pytest.mark.parametrize("shape,T,rounds", [
+    (sg.GdnShape(batch=2, nv=4, nk=2, dk=16, dv=32, window=64), 8, 14),        # RSSM_MAX_WINDOW, RSSM_MAX_DRAFTS
+    (sg.GdnShape(batch=2, nv=32, nk=16, dk=128, dv=128, window=40), 8, 9),     # largest window at T = 8 in 64 KiB LDS
+    (sg.GdnShape(batch=1, nv=32, nk=16, dk=128, dv=128, window=64), 4, 20),    # largest window at T = 4
+], ids=["tiny-L64-T8", "layer-L40-T8", "layer-L64-T4-batch1"])
+def test_gdn_window_and_draft_limits(shape, T, rounds, dev):
+    """Verify + commit at the largest windows and draft counts the library
+    accepts: outputs and the flushed state match the oracle."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    w = sg.gdn_workload(shape, rounds, 131 + T, "bf16", T=T)
+    acc = w.extra["accepted"]
+    cfg = _cfg(shape, T, "bf16")
+    st = _state(cfg, w.S0, dev)
+    ts = GdnTokenStream(w.steps, dev, T)
+    acc_d = torch.from_numpy(acc).to(dev)
+    o = torch.empty((rounds, shape.batch, T, shape.nv, shape.dv), device=dev)
+    say(f"gdn limits {shape} T={T} rounds={rounds}")
+    for r in range(rounds):
+        bg.gdn_verify_drafts(cfg, st, ts.call(r), o[r])
+        bg.gdn_commit(cfg, st, acc_d[r], T)
+    bg.gdn_flush(cfg, st)
+    torch.cuda.synchronize()
+    tk = w.steps
+    S = w.S0.astype(np.float64)
+    oref = np.zeros((rounds, T, shape.batch, shape.nv, shape.dv))
+    for r in range(rounds):
+        sl = slice(r * T, (r + 1) * T)
+        args = (tk.q[sl], tk.k[sl], tk.v[sl], tk.g[sl], tk.beta[sl])
+        _, oref[r] = ogdn.conventional(S, *args)
+        S, _ = ogdn.conventional(S, *args, nsteps=acc[r])
+    assert_rows_close(np.swapaxes(o.cpu().numpy(), 1, 2), oref, what="gdn outputs at the limits")
+    assert state_err(st.ckpt.cpu().numpy(), S).max() <= TOL
+    assert int(st.status.cpu()[0]) == 0
