@@ -58,7 +58,7 @@ def parse():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU sample")
     ap.add_argument("--config", choices=["decode", "verify", "verify_sweep", "sweep", "dual", "gdn",
-                                         "gdn_verify_sweep"], default="decode",
+                                         "gdn_verify_sweep", "gdn_sweep"], default="decode",
                     help="decode: the headline line (default); verify: speculative rounds at batch 512, "
                          "T=3; verify_sweep: the same for T in 1, 2, 3, 4, 8; sweep: batch x window grid; "
                          "dual: FP32 / bf16 / e4m3 read copies over 4096 steps; gdn: Gated DeltaNet layer "
@@ -133,7 +133,8 @@ def main():
         sys.exit(2)
     if args.config != "decode":
         {"verify": bench_verify, "verify_sweep": bench_verify_sweep, "sweep": bench_sweep,
-         "dual": bench_dual, "gdn": bench_gdn, "gdn_verify_sweep": bench_gdn_verify_sweep}[args.config](args)
+         "dual": bench_dual, "gdn": bench_gdn, "gdn_verify_sweep": bench_gdn_verify_sweep,
+         "gdn_sweep": bench_gdn_sweep}[args.config](args)
         return
 
     import torch
@@ -483,6 +484,63 @@ def bench_gdn_verify_sweep(args):
                       "workload": "Gated DeltaNet layer, 32 value heads over 16 key heads, dk = dv = 128, bf16 "
                                   "inputs, FP32 checkpoint; U{0..T} acceptance",
                       "timing": "32 rounds captured in one HIP graph, one replay timed after a warm replay",
+                      "rows": rows}), flush=True)
+
+
+def bench_gdn_sweep(args):
+    """GDN decode at batch 16, 64, 256 and 512 (L = --window): replay decode
+    steps against the conventional GDN step, both graph-timed.  Below about
+    1 GiB of state, R replicas of the layer's state are rotated (call i uses
+    replica i mod R) so that the steps stream from HBM rather than the 256 MB
+    Infinity Cache; each replica runs 16 steps after a 17-step warm-up (one
+    flush each).  One JSON line with the table."""
+    torch, dev = _device()
+    from mamba_state_replay_amd import binding_gdn as bg
+    from mamba_state_replay_amd import staging, synth_gdn, traffic
+
+    L = args.window
+    rows = []
+    for batch in (16, 64, 256, 512):
+        shape = synth_gdn.GdnShape(batch=batch, window=L, **GDN_LAYER)
+        state_bytes = batch * shape.nv * shape.dv * shape.dk * 4
+        R = max(1, -(-(1 << 30) // state_bytes))
+        w = synth_gdn.gdn_workload(shape, 32, seed=2200 + batch)
+        cfg = bg.GdnConfig(batch, shape.nv, shape.nk, shape.dk, shape.dv, L, 1, "bf16")
+        toks = staging.GdnTokenStream(w.steps, dev)
+        S0 = torch.from_numpy(w.S0).to(dev)
+        sts = []
+        for _ in range(R):
+            st = bg.GdnState.allocate(cfg, dev)
+            st.ckpt.copy_(S0)
+            sts.append(st)
+        o = torch.empty((batch, 1, shape.nv, shape.dv), device=dev)
+        step = lambda i: bg.gdn_decode_step(cfg, sts[i % R], toks.call((i // R) % 32), o)
+        W = 17 * R
+        for i in range(W):
+            step(i)
+        K = 16 * R
+        rep_ms = graph_time(lambda i: step(W + i), K, torch)
+        assert all(int(st.status.cpu()[0]) == 0 for st in sts)
+        del sts
+        convs = [S0.clone() for _ in range(R)]
+        cstep = lambda i: bg.gdn_conventional_update(cfg, convs[i % R], toks.call((i // R) % 32), o)
+        for i in range(R):
+            cstep(i)
+        conv_ms = graph_time(cstep, K, torch)
+        del convs, toks, S0
+        sz = traffic.gdn_sizes(shape.nv, shape.nk, shape.dk, shape.dv)
+        sched, _ = traffic.decode_schedule(np.zeros(batch, np.int64), L, 17 + 16)
+        alg = sum(traffic.decode_step_bytes(sz, n, f) for n, f in sched[17:]) / 16
+        r_us, c_us = rep_ms * 1e3 / K, conv_ms * 1e3 / K
+        rows.append({"batch": batch, "replicas": R, "replay_us_per_step": round(r_us, 2),
+                     "conventional_us_per_step": round(c_us, 2), "speedup": round(c_us / r_us, 3),
+                     "replay_gbs": round(alg / (r_us * 1e-6) / 1e9, 1),
+                     "conventional_gbs": round(traffic.conventional_step_bytes(sz, batch) / (c_us * 1e-6) / 1e9, 1)})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({"config": "gdn_sweep", "window": L,
+                      "workload": "Gated DeltaNet layer, 32 value heads over 16 key heads, dk = dv = 128, bf16 "
+                                  "inputs, FP32 checkpoint, steady state from an empty buffer",
+                      "timing": "16 steps per replica captured in one HIP graph, one replay timed after a warm one",
                       "rows": rows}), flush=True)
 
 
