@@ -85,6 +85,157 @@ __device__ __forceinline__ float dot4(const v4f a, const float4 b) {
     return fmaf(a[3], b.w, s);
 }
 
+// Step 2 of a call, shared by the replay kernels: the staging list of a
+// workgroup that serves ROWS value rows starting at row r0 of head h.  Vector
+// i of the list is a 16-byte vector of a committed record's key, of the
+// records' u rows, of a token's key or query, or of the tokens' v rows; `job`
+// names its source, its LDS destination, whether it is widened from InT (else
+// copied as fp32) and where a token key is appended to the key ring (or null).
+// `issue` loads the first JOBS vectors of each thread into registers, so the
+// kernel can issue the tile's loads behind them; `finish` stores them (and
+// loads and stores the rest of a long window).  The log decays g (records) and
+// g, beta (tokens) are scalars: `load_g` / `store_g`.
+template <int DK, int ROWS, int NT, typename InT>
+struct GdnStage {
+    static constexpr int EPV = InTraits<InT>::EPV;   // input elements per 16-byte vector
+    static constexpr int KV = DK / EPV;              // vectors per key / query
+    static constexpr int RV = ROWS / EPV;            // vectors per block of v rows
+    static constexpr int UV = ROWS / 4;              // fp32 vectors per block of u rows
+    static constexpr int JOBS = 2;
+
+    const GdnArgs& a;
+    float* smem;
+    const GdnLds& Ls;
+    const InT* kring;        // this key head's key ring
+    const float* uring;      // this head's u ring, at row r0
+    int b, h, kh, bh, r0, cap, T, start, n, np, qstart;
+    bool append_k;
+    int nkv, nuv, ntk, total;
+
+    __device__ GdnStage(const GdnArgs& a_, float* smem_, const GdnLds& Ls_, int b_, int h_, int kh_, int r0_,
+                        int T_, int start_, int n_, int np_, int qstart_, bool append_k_)
+        : a(a_), smem(smem_), Ls(Ls_), b(b_), h(h_), kh(kh_), bh(b_ * a_.nv + h_), r0(r0_), cap(a_.cap), T(T_),
+          start(start_), n(n_), np(np_), qstart(qstart_), append_k(append_k_) {
+        kring = static_cast<const InT*>(a.buf_k) + (size_t)(b * a.nk + kh) * cap * DK;
+        uring = a.buf_u + (size_t)bh * cap * a.dv + r0;
+        nkv = n * KV;
+        nuv = n * UV;
+        ntk = T * KV;
+        total = nkv + nuv + 2 * ntk + T * RV;
+    }
+
+    __device__ __forceinline__ int slot_of(int c) const {   // (start + c) mod cap, c < cap
+        const int s = start + c;
+        return s >= cap ? s - cap : s;
+    }
+
+    __device__ __forceinline__ void job(int i, const uint4*& src, float*& dst, bool& widen, uint4*& app) const {
+        app = nullptr;
+        widen = true;
+        if (i < nkv) {
+            const int c = i / KV, e = i - c * KV;
+            src = reinterpret_cast<const uint4*>(kring + (size_t)slot_of(c) * DK) + e;
+            dst = smem + Ls.K + c * DK + e * EPV;
+            return;
+        }
+        i -= nkv;
+        if (i < nuv) {
+            const int c = i / UV, e = i - c * UV;
+            src = reinterpret_cast<const uint4*>(uring + (size_t)slot_of(c) * a.dv) + e;
+            dst = smem + Ls.U + c * Ls.US + 4 * e;
+            widen = false;
+            return;
+        }
+        i -= nuv;
+        if (i < 2 * ntk) {
+            const bool isq = i >= ntk;
+            const int r = isq ? i - ntk : i;
+            const int q = r / KV, e = r - q * KV;
+            src = reinterpret_cast<const uint4*>(static_cast<const InT*>(isq ? a.q : a.k) +
+                                                 ((size_t)(b * T + q) * a.nk + kh) * DK) + e;
+            dst = smem + (isq ? Ls.QQ : Ls.KQ) + q * DK + e * EPV;
+            if (!isq && append_k) {
+                int slot = qstart + np + q;
+                slot -= slot >= cap ? cap : 0;
+                app = reinterpret_cast<uint4*>(static_cast<InT*>(a.buf_k) +
+                                               ((size_t)(b * a.nk + kh) * cap + slot) * DK) + e;
+            }
+            return;
+        }
+        i -= 2 * ntk;
+        const int q = i / RV, e = i - q * RV;
+        src = reinterpret_cast<const uint4*>(static_cast<const InT*>(a.v) +
+                                             ((size_t)(b * T + q) * a.nv + h) * a.dv + r0) + e;
+        dst = smem + Ls.V + q * ROWS + e * EPV;
+    }
+
+    __device__ __forceinline__ static void put(float* dst, bool widen, uint4* app, const uint4 v) {
+        if (app) *app = v;
+        if (widen) {
+            widen16<InT>(v, dst);
+        } else {
+            *reinterpret_cast<uint4*>(dst) = v;
+        }
+    }
+
+    __device__ __forceinline__ void issue(uint4 (&jv)[JOBS], int tid) const {
+#pragma unroll
+        for (int j = 0; j < JOBS; ++j) {
+            const int i = tid + j * NT;
+            if (i < total) {
+                const uint4* src;
+                float* dst;
+                bool widen;
+                uint4* app;
+                job(i, src, dst, widen, app);
+                jv[j] = *src;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void finish(const uint4 (&jv)[JOBS], int tid) const {
+#pragma unroll
+        for (int j = 0; j < JOBS; ++j) {
+            const int i = tid + j * NT;
+            if (i < total) {
+                const uint4* src;
+                float* dst;
+                bool widen;
+                uint4* app;
+                job(i, src, dst, widen, app);
+                put(dst, widen, app, jv[j]);
+            }
+        }
+        for (int i = tid + JOBS * NT; i < total; i += NT) {   // windows longer than JOBS vectors a thread
+            const uint4* src;
+            float* dst;
+            bool widen;
+            uint4* app;
+            job(i, src, dst, widen, app);
+            put(dst, widen, app, *src);
+        }
+    }
+
+    __device__ __forceinline__ void load_g(int tid, float& gv, float& gq, float& bq) const {
+        gv = gq = bq = 0.0f;
+        if (tid < n) gv = a.buf_g[(size_t)bh * cap + slot_of(tid)];
+        if (tid < T) {
+            const size_t ti = (size_t)(b * T + tid) * a.nv + h;
+            gq = a.g[ti];
+            bq = a.beta[ti];
+        }
+    }
+
+    __device__ __forceinline__ void store_g(int tid, float gv, float gq, float bq) const {
+        if (tid < n) smem[Ls.G + tid] = gv;
+        for (int i = tid + NT; i < n; i += NT) smem[Ls.G + i] = a.buf_g[(size_t)bh * cap + slot_of(i)];
+        if (tid < T) {
+            smem[Ls.GQ + tid] = gq;
+            smem[Ls.BE + tid] = bq;
+        }
+    }
+};
+
 // Step 4 of a call: one 8-lane group per (query q, window position c <= m_q =
 // np + q) forms the segment decay exp(sum_{c<i<=m_q} g_i) and the key-key and
 // key-query scores (k_c . k_q, k_c . q_q), which give ck[q][c] (c < m_q) and
@@ -131,10 +282,6 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     constexpr int NT = GdnGeo<DK>::NT;
     using Geo = TileGeo<ROWS, DK, NT, 4>;
     constexpr int W = Geo::W;
-    constexpr int EPV = InTraits<InT>::EPV;       // input elements per 16-byte vector
-    constexpr int KV = DK / EPV;                  // vectors per key / query
-    constexpr int RV = ROWS / EPV;                // vectors per block of v rows
-    constexpr int UV = ROWS / 4;                  // fp32 vectors per block of u rows
     extern __shared__ float smem[];
 
     const int tid = threadIdx.x;
@@ -169,90 +316,12 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     // registers first, the tile's loads are issued behind them, and the staged
     // vectors are stored to LDS while the tile is still in flight (loads
     // complete in order, so waiting for a staged vector never waits for the tile).
-    const InT* kring = static_cast<const InT*>(a.buf_k) + (size_t)(b * a.nk + kh) * cap * DK;
-    const float* uring = a.buf_u + (size_t)bh * cap * a.dv + p * ROWS;
-    const bool append_k = (h % (a.nv / a.nk)) == 0 && p == 0;
-    const int nkv = n * KV, nuv = n * UV, ntk = T * KV;
-    const int total = nkv + nuv + 2 * ntk + T * RV;
-    // Vector i of the staging list: its source, its LDS destination, whether it
-    // is widened from InT (else copied as fp32), and where a token key is
-    // appended to the key ring (or null).
-    auto job = [&](int i, const uint4*& src, float*& dst, bool& widen, uint4*& app) {
-        app = nullptr;
-        widen = true;
-        if (i < nkv) {
-            const int c = i / KV, e = i - c * KV;
-            int slot = start + c;
-            slot -= slot >= cap ? cap : 0;
-            src = reinterpret_cast<const uint4*>(kring + (size_t)slot * DK) + e;
-            dst = smem + Ls.K + c * DK + e * EPV;
-            return;
-        }
-        i -= nkv;
-        if (i < nuv) {
-            const int c = i / UV, e = i - c * UV;
-            int slot = start + c;
-            slot -= slot >= cap ? cap : 0;
-            src = reinterpret_cast<const uint4*>(uring + (size_t)slot * a.dv) + e;
-            dst = smem + Ls.U + c * Ls.US + 4 * e;
-            widen = false;
-            return;
-        }
-        i -= nuv;
-        if (i < 2 * ntk) {
-            const bool isq = i >= ntk;
-            const int r = isq ? i - ntk : i;
-            const int q = r / KV, e = r - q * KV;
-            src = reinterpret_cast<const uint4*>(static_cast<const InT*>(isq ? a.q : a.k) +
-                                                 ((size_t)(b * T + q) * a.nk + kh) * DK) + e;
-            dst = smem + (isq ? Ls.QQ : Ls.KQ) + q * DK + e * EPV;
-            if (!isq && append_k) {
-                int slot = qstart + np + q;
-                slot -= slot >= cap ? cap : 0;
-                app = reinterpret_cast<uint4*>(static_cast<InT*>(a.buf_k) +
-                                               ((size_t)(b * a.nk + kh) * cap + slot) * DK) + e;
-            }
-            return;
-        }
-        i -= 2 * ntk;
-        const int q = i / RV, e = i - q * RV;
-        src = reinterpret_cast<const uint4*>(static_cast<const InT*>(a.v) +
-                                             ((size_t)(b * T + q) * a.nv + h) * a.dv + p * ROWS) + e;
-        dst = smem + Ls.V + q * ROWS + e * EPV;
-    };
-    auto put = [&](float* dst, bool widen, uint4* app, const uint4 v) {
-        if (app) *app = v;
-        if (widen) {
-            widen16<InT>(v, dst);
-        } else {
-            *reinterpret_cast<uint4*>(dst) = v;
-        }
-    };
-    constexpr int JOBS = 2;
-    uint4 jv[JOBS];
-#pragma unroll
-    for (int j = 0; j < JOBS; ++j) {
-        const int i = tid + j * NT;
-        if (i < total) {
-            const uint4* src;
-            float* dst;
-            bool widen;
-            uint4* app;
-            job(i, src, dst, widen, app);
-            jv[j] = *src;
-        }
-    }
-    float gv = 0.0f, gq = 0.0f, bq = 0.0f;
-    if (tid < n) {
-        int slot = start + tid;
-        slot -= slot >= cap ? cap : 0;
-        gv = a.buf_g[(size_t)bh * cap + slot];
-    }
-    if (tid < T) {
-        const size_t ti = (size_t)(b * T + tid) * a.nv + h;
-        gq = a.g[ti];
-        bq = a.beta[ti];
-    }
+    const GdnStage<DK, ROWS, NT, InT> stage(a, smem, Ls, b, h, kh, p * ROWS, T, start, n, np, qstart,
+                                            (h % (a.nv / a.nk)) == 0 && p == 0);
+    uint4 jv[stage.JOBS];
+    stage.issue(jv, tid);
+    float gv, gq, bq;
+    stage.load_g(tid, gv, gq, bq);
 
     const size_t tile_off = ((size_t)bh * a.dv + p * ROWS) * DK;   // first element of the tile
     float* const tile_p = a.ckpt + tile_off;
@@ -270,36 +339,8 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
                                                                         Geo::vec(tid, s)));
     }
 
-#pragma unroll
-    for (int j = 0; j < JOBS; ++j) {
-        const int i = tid + j * NT;
-        if (i < total) {
-            const uint4* src;
-            float* dst;
-            bool widen;
-            uint4* app;
-            job(i, src, dst, widen, app);
-            put(dst, widen, app, jv[j]);
-        }
-    }
-    for (int i = tid + JOBS * NT; i < total; i += NT) {   // windows longer than JOBS vectors a thread
-        const uint4* src;
-        float* dst;
-        bool widen;
-        uint4* app;
-        job(i, src, dst, widen, app);
-        put(dst, widen, app, *src);
-    }
-    if (tid < n) smem[Ls.G + tid] = gv;
-    for (int i = tid + NT; i < n; i += NT) {
-        int slot = start + i;
-        slot -= slot >= cap ? cap : 0;
-        smem[Ls.G + i] = a.buf_g[(size_t)bh * cap + slot];
-    }
-    if (tid < T) {
-        smem[Ls.GQ + tid] = gq;
-        smem[Ls.BE + tid] = bq;
-    }
+    stage.finish(jv, tid);
+    stage.store_g(tid, gv, gq, bq);
     __syncthreads();
     if constexpr (F16) {
 #pragma unroll
@@ -465,10 +506,6 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
     using Geo = TileGeo<ROWS, DK, NT, 2>;
     static_assert(Geo::NI == 4 && Geo::VPL == 2 && Geo::W == 8 && Geo::NV == 8, "fp16 wide tile layout");
     constexpr int W = Geo::W;
-    constexpr int EPV = InTraits<InT>::EPV;
-    constexpr int KV = DK / EPV;
-    constexpr int RV = ROWS / EPV;
-    constexpr int UV = ROWS / 4;
     extern __shared__ float smem[];
 
     const int tid = threadIdx.x;
@@ -504,87 +541,12 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
     if (!fold) qstart = start;
 
     // 2. staging (as in gdn_replay_kernel, for 128 rows)
-    const InT* kring = static_cast<const InT*>(a.buf_k) + (size_t)(b * a.nk + kh) * cap * DK;
-    const float* uring = a.buf_u + (size_t)bh * cap * a.dv + pw * ROWS;
-    const bool append_k = (h % (a.nv / a.nk)) == 0 && pw == 0;
-    const int nkv = n * KV, nuv = n * UV, ntk = T * KV;
-    const int total = nkv + nuv + 2 * ntk + T * RV;
-    auto job = [&](int i, const uint4*& src, float*& dst, bool& widen, uint4*& app) {
-        app = nullptr;
-        widen = true;
-        if (i < nkv) {
-            const int c = i / KV, e = i - c * KV;
-            int slot = start + c;
-            slot -= slot >= cap ? cap : 0;
-            src = reinterpret_cast<const uint4*>(kring + (size_t)slot * DK) + e;
-            dst = smem + Ls.K + c * DK + e * EPV;
-            return;
-        }
-        i -= nkv;
-        if (i < nuv) {
-            const int c = i / UV, e = i - c * UV;
-            int slot = start + c;
-            slot -= slot >= cap ? cap : 0;
-            src = reinterpret_cast<const uint4*>(uring + (size_t)slot * a.dv) + e;
-            dst = smem + Ls.U + c * Ls.US + 4 * e;
-            widen = false;
-            return;
-        }
-        i -= nuv;
-        if (i < 2 * ntk) {
-            const bool isq = i >= ntk;
-            const int r = isq ? i - ntk : i;
-            const int q = r / KV, e = r - q * KV;
-            src = reinterpret_cast<const uint4*>(static_cast<const InT*>(isq ? a.q : a.k) +
-                                                 ((size_t)(b * T + q) * a.nk + kh) * DK) + e;
-            dst = smem + (isq ? Ls.QQ : Ls.KQ) + q * DK + e * EPV;
-            if (!isq && append_k) {
-                int slot = qstart + np + q;
-                slot -= slot >= cap ? cap : 0;
-                app = reinterpret_cast<uint4*>(static_cast<InT*>(a.buf_k) +
-                                               ((size_t)(b * a.nk + kh) * cap + slot) * DK) + e;
-            }
-            return;
-        }
-        i -= 2 * ntk;
-        const int q = i / RV, e = i - q * RV;
-        src = reinterpret_cast<const uint4*>(static_cast<const InT*>(a.v) +
-                                             ((size_t)(b * T + q) * a.nv + h) * a.dv + pw * ROWS) + e;
-        dst = smem + Ls.V + q * ROWS + e * EPV;
-    };
-    auto put = [&](float* dst, bool widen, uint4* app, const uint4 v) {
-        if (app) *app = v;
-        if (widen) {
-            widen16<InT>(v, dst);
-        } else {
-            *reinterpret_cast<uint4*>(dst) = v;
-        }
-    };
-    constexpr int JOBS = 2;
-    uint4 jv[JOBS];
-#pragma unroll
-    for (int j = 0; j < JOBS; ++j) {
-        const int i = tid + j * NT;
-        if (i < total) {
-            const uint4* src;
-            float* dst;
-            bool widen;
-            uint4* app;
-            job(i, src, dst, widen, app);
-            jv[j] = *src;
-        }
-    }
-    float gv = 0.0f, gq = 0.0f, bq = 0.0f;
-    if (tid < n) {
-        int slot = start + tid;
-        slot -= slot >= cap ? cap : 0;
-        gv = a.buf_g[(size_t)bh * cap + slot];
-    }
-    if (tid < T) {
-        const size_t ti = (size_t)(b * T + tid) * a.nv + h;
-        gq = a.g[ti];
-        bq = a.beta[ti];
-    }
+    const GdnStage<DK, ROWS, NT, InT> stage(a, smem, Ls, b, h, kh, pw * ROWS, T, start, n, np, qstart,
+                                            (h % (a.nv / a.nk)) == 0 && pw == 0);
+    uint4 jv[stage.JOBS];
+    stage.issue(jv, tid);
+    float gv, gq, bq;
+    stage.load_g(tid, gv, gq, bq);
 
     const size_t tile_off = ((size_t)bh * a.dv + pw * ROWS) * DK;
     uint16_t* const tile16 = reinterpret_cast<uint16_t*>(a.ckpt) + tile_off;
@@ -593,36 +555,8 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
     for (int s = 0; s < Geo::NV; ++s)
         raw[s] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(tile16) + Geo::vec(tid, s));
 
-#pragma unroll
-    for (int j = 0; j < JOBS; ++j) {
-        const int i = tid + j * NT;
-        if (i < total) {
-            const uint4* src;
-            float* dst;
-            bool widen;
-            uint4* app;
-            job(i, src, dst, widen, app);
-            put(dst, widen, app, jv[j]);
-        }
-    }
-    for (int i = tid + JOBS * NT; i < total; i += NT) {
-        const uint4* src;
-        float* dst;
-        bool widen;
-        uint4* app;
-        job(i, src, dst, widen, app);
-        put(dst, widen, app, *src);
-    }
-    if (tid < n) smem[Ls.G + tid] = gv;
-    for (int i = tid + NT; i < n; i += NT) {
-        int slot = start + i;
-        slot -= slot >= cap ? cap : 0;
-        smem[Ls.G + i] = a.buf_g[(size_t)bh * cap + slot];
-    }
-    if (tid < T) {
-        smem[Ls.GQ + tid] = gq;
-        smem[Ls.BE + tid] = bq;
-    }
+    stage.finish(jv, tid);
+    stage.store_g(tid, gv, gq, bq);
     __syncthreads();
 
     const int row0 = Geo::row0(tid);
