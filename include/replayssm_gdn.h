@@ -36,7 +36,9 @@
  * bits in *status, leave the state untouched and write NaN outputs).
  * Compiled shapes: dk = 16 with dv % 16 == 0, and dk = 128 with dv % 64 == 0;
  * nv % nk == 0.  Each value head's state is split into dv/16 (dk = 16) or
- * dv/64 (dk = 128) row blocks of 16 x 16 or 64 x 128 fp32, one workgroup each.
+ * dv/64 (dk = 128) row blocks of 16 x 16 or 64 x 128 elements, each with its
+ * own copy of the ring pointer; a workgroup serves one block (two with an FP16
+ * checkpoint, dk = 128 and dv % 128 == 0).
  * Token, record and state pointers must be 16-byte aligned.
  */
 #ifndef REPLAYSSM_GDN_H

@@ -1,6 +1,7 @@
 // Gated DeltaNet (GDN) layer in ReplaySSM form on gfx950: the decode / verify /
-// flush kernel over an FP32 checkpoint plus corrected-value records, and the
-// conventional GDN step (the in-library baseline).
+// flush kernels over an FP32 (or FP16, stochastically rounded) checkpoint plus
+// corrected-value records, and the conventional GDN step (the in-library
+// baseline, with one state snapshot per draft for verification).
 //
 // Method: NVIDIA Developer blog "ReplaySSM: Rethinking State Storage for Faster
 // Hybrid-Model Decoding".  Its section "Why SSM layers can become a decoding
@@ -17,7 +18,10 @@
 // Row i of u_t needs only row i of S_{t-1}, so the rows of a value head's state
 // are independent: a head's dv x dk state is split into blocks of ROWS rows,
 // one workgroup each, streaming one ROWS x DK fp32 tile (64 x 128 = 32 KiB)
-// with the thread layout of TileGeo (8 lanes per row, 16-byte loads).
+// with the thread layout of TileGeo (8 lanes per row, 16-byte loads).  An FP16
+// checkpoint with dk = 128 and dv a multiple of 128 has its own kernel
+// (gdn_replay_f16_wide_kernel) that serves two row blocks per workgroup, so a
+// workgroup still streams 32 KiB.
 //
 // One call of gdn_replay_kernel, workgroup = (sequence b, value head h, row block p):
 //  1. read the workgroup's ring pointer {start, n}; decide the flush (n >= L,
