@@ -375,6 +375,12 @@ def bench_gdn(args):
         vround(r)
     v_ms = graph_time(lambda r: vround(8 + r), rounds, torch)
     assert int(vst.status.cpu()[0]) == 0 and bool(torch.isfinite(vo).all())
+    # the commit of round r - 1 fused into the verification of round r: one launch per round
+    fround = lambda r: bg.gdn_commit_verify(vcfg, vst, acc[(r - 1) % rounds], T, vtoks.call(r % rounds), vo)
+    for r in range(4):
+        fround(40 + r)
+    f_ms = graph_time(lambda r: fround(44 + r), rounds, torch)
+    assert int(vst.status.cpu()[0]) == 0 and bool(torch.isfinite(vo).all())
     sround = lambda r: (bg.gdn_conventional_update(scfg, snap, vtoks.call(r % rounds), vo, nslots=T + 1, slot=slot),
                         bg.gdn_conventional_commit(scfg, slot, T + 1, acc[r % rounds], T))
     for r in range(4):
@@ -413,6 +419,7 @@ def bench_gdn(args):
                          "algorithmic_bytes_per_launch": cbytes},
         "speedup_vs_conventional": round(c_us / us_step, 3),
         "verify_T3": {"us_per_round": round(v_ms * 1e3 / rounds, 2), "rounds": rounds,
+                      "fused_commit_us_per_round": round(f_ms * 1e3 / rounds, 2),
                       "snapshot_baseline_us_per_round": round(s_ms * 1e3 / rounds, 2),
                       "snapshot_baseline_state": "FP32",
                       "speedup_vs_snapshot": round(s_ms / v_ms, 3),

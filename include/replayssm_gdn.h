@@ -116,6 +116,14 @@ int gdn_decode_step(const gdn_config *cfg, const gdn_state *st, const gdn_tokens
 int gdn_verify_drafts(const gdn_config *cfg, const gdn_state *st, const gdn_tokens *tok, float *o,
                       void *stream);
 
+/* gdn_commit of the previous round (accepted_prev, T_prev) fused into this round's
+   gdn_verify_drafts: one launch per speculative round.  Equivalent, bit for bit, to
+   gdn_commit(cfg, st, accepted_prev, T_prev) followed by gdn_verify_drafts(cfg, st, tok, o);
+   an accepted count outside 0..T_prev sets RSSM_STATUS_ACCEPT, leaves that sequence alone and
+   writes NaN to its outputs. */
+int gdn_commit_verify(const gdn_config *cfg, const gdn_state *st, const int32_t *accepted_prev,
+                      int32_t T_prev, const gdn_tokens *tok, float *o, void *stream);
+
 /* Commit accepted[b] (device int32 [batch], 0..T) of the last T drafts: the committed
    length grows by accepted[b]; nothing else moves.  An accepted count outside 0..T (or
    past the ring) sets RSSM_STATUS_ACCEPT and leaves that sequence alone. */

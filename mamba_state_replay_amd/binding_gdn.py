@@ -44,6 +44,8 @@ _SIGS = {
     "gdn_commit": (ctypes.c_int, [_P(gdn_config), _P(gdn_state), ctypes.c_void_p, ctypes.c_int32,
                                   ctypes.c_void_p]),
     "gdn_flush": (ctypes.c_int, [_P(gdn_config), _P(gdn_state), ctypes.c_uint64, ctypes.c_void_p]),
+    "gdn_commit_verify": (ctypes.c_int, [_P(gdn_config), _P(gdn_state), ctypes.c_void_p, ctypes.c_int32,
+                                         _P(gdn_tokens), ctypes.c_void_p, ctypes.c_void_p]),
     "gdn_conventional_update": (ctypes.c_int, [_P(gdn_config), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                                ctypes.c_void_p, _P(gdn_tokens), ctypes.c_void_p, ctypes.c_void_p]),
     "gdn_conventional_commit": (ctypes.c_int, [_P(gdn_config), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
@@ -187,6 +189,18 @@ def gdn_decode_step(cfg: GdnConfig, state: GdnState, tokens: GdnTokens, o: torch
 
 def gdn_verify_drafts(cfg: GdnConfig, state: GdnState, tokens: GdnTokens, o: torch.Tensor, stream=None):
     _run("gdn_verify_drafts", cfg, state, tokens, o, stream)
+
+
+def gdn_commit_verify(cfg: GdnConfig, state: GdnState, accepted_prev: torch.Tensor, T_prev: int,
+                      tokens: GdnTokens, o: torch.Tensor, stream=None):
+    """gdn_commit(accepted_prev, T_prev) fused into this round's gdn_verify_drafts."""
+    dev = state.validate(cfg)
+    tokens.validate(cfg, dev)
+    _expect("o", o, (cfg.batch, tokens.T, cfg.nv, cfg.dv), torch.float32, dev)
+    _expect("accepted_prev", accepted_prev, (cfg.batch,), torch.int32, dev)
+    c, s, t = cfg.c(), state.c(), tokens.c()
+    _check("gdn_commit_verify", lib().gdn_commit_verify(ctypes.byref(c), ctypes.byref(s), _ptr(accepted_prev),
+                                                        int(T_prev), ctypes.byref(t), _ptr(o), _stream(stream)))
 
 
 def gdn_commit(cfg: GdnConfig, state: GdnState, accepted: torch.Tensor, T: int, stream=None):

@@ -461,6 +461,26 @@ int gdn_verify_drafts(const gdn_config* cfg, const gdn_state* st, const gdn_toke
     return run_gdn(cfg, st, tok, o, rssm::MODE_VERIFY, stream, "gdn_verify_drafts");
 }
 
+int gdn_commit_verify(const gdn_config* cfg, const gdn_state* st, const int32_t* accepted_prev, int32_t T_prev,
+                      const gdn_tokens* tok, float* o, void* stream) {
+    int rc = gdn_check_config(cfg);
+    if (rc) return rc;
+    if (T_prev < 1 || T_prev > cfg->max_drafts)
+        return fail(RSSM_ERR_DRAFTS, "T_prev = %d outside 1..%d", T_prev, cfg->max_drafts);
+    if (cfg->batch == 0) return RSSM_OK;
+    if (!accepted_prev) return fail(RSSM_ERR_NULL, "accepted_prev is required");
+    if (!aligned(accepted_prev, 4)) return fail(RSSM_ERR_SHAPE, "misaligned accepted_prev");
+    rc = gdn_check_state(st);
+    if (!rc) rc = gdn_check_tokens(tok, o, 1, cfg->max_drafts);
+    if (rc) return rc;
+    rssm::GdnArgs a = gdn_args(cfg, st, tok, o, rssm::MODE_VERIFY);
+    a.accepted_prev = accepted_prev;
+    a.T_prev = T_prev;
+    return launched(rssm::launch_gdn_replay(a, cfg->dk, cfg->in_dtype == RSSM_BF16 ? rssm::IN_BF16 : rssm::IN_F32,
+                                            static_cast<hipStream_t>(stream)),
+                    "gdn_commit_verify");
+}
+
 int gdn_flush(const gdn_config* cfg, const gdn_state* st, uint64_t sr_seed, void* stream) {
     int rc = gdn_check_config(cfg);
     if (rc) return rc;

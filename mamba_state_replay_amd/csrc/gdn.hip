@@ -299,14 +299,23 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
     const GdnLds Ls = gdn_plan(DK, ROWS, cap, T);
 
-    // 1. ring pointer and flush decision (every thread reads the workgroup's copy)
+    // 1. ring pointer (every thread reads the workgroup's copy), the fused commit
+    // of the previous verification if any (len += accepted_prev[b]), and the
+    // flush decision
     const int start = a.meta[2 * wg];
-    const int n = a.meta[2 * wg + 1];
-    const bool valid = start >= 0 && start < cap && n >= 0 && n <= cap;
+    const int n_stored = a.meta[2 * wg + 1];
+    int acc_prev = 0;
+    bool acc_ok = true;
+    if (a.accepted_prev) {
+        acc_prev = a.accepted_prev[b];
+        acc_ok = acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap;
+    }
+    const int n = n_stored + acc_prev;
+    const bool valid = acc_ok && start >= 0 && start < cap && n >= 0 && n <= cap;
     const bool fold = valid && (a.mode == MODE_FLUSH ? n > 0 : n >= a.L);
     const int np = fold ? 0 : n;                          // committed records seen by the queries
     if (!valid || np + T > cap) {
-        if (tid == 0 && a.status) atomicOr(a.status, (int)kStatusMeta);
+        if (tid == 0 && a.status) atomicOr(a.status, (int)(acc_ok ? kStatusMeta : kStatusAccept));
         for (int i = tid; i < T * ROWS; i += NT)
             a.o[((size_t)(b * T + i / ROWS) * a.nv + h) * a.dv + p * ROWS + i % ROWS] = __builtin_nanf("");
         return;
@@ -526,15 +535,23 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
     const int PK = Ls.total, PQ = Ls.total + T * ROWS;     // reduced products [q][row]
     const int m0 = bh * a.parts + 2 * pw;                  // the pointer copies of the two row blocks
 
-    // 1. ring pointer (the copies of both row blocks are equal) and flush decision
+    // 1. ring pointer (the copies of both row blocks are equal), the fused
+    // commit if any, and the flush decision
     const int start = a.meta[2 * m0];
-    const int n = a.meta[2 * m0 + 1];
-    const bool valid = start >= 0 && start < cap && n >= 0 && n <= cap && a.meta[2 * m0 + 2] == start &&
-                       a.meta[2 * m0 + 3] == n;
+    const int n_stored = a.meta[2 * m0 + 1];
+    int acc_prev = 0;
+    bool acc_ok = true;
+    if (a.accepted_prev) {
+        acc_prev = a.accepted_prev[b];
+        acc_ok = acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap;
+    }
+    const int n = n_stored + acc_prev;
+    const bool valid = acc_ok && start >= 0 && start < cap && n >= 0 && n <= cap &&
+                       a.meta[2 * m0 + 2] == start && a.meta[2 * m0 + 3] == n_stored;
     const bool fold = valid && (a.mode == MODE_FLUSH ? n > 0 : n >= a.L);
     const int np = fold ? 0 : n;
     if (!valid || np + T > cap) {
-        if (tid == 0 && a.status) atomicOr(a.status, (int)kStatusMeta);
+        if (tid == 0 && a.status) atomicOr(a.status, (int)(acc_ok ? kStatusMeta : kStatusAccept));
         for (int i = tid; i < T * ROWS; i += NT)
             a.o[((size_t)(b * T + i / ROWS) * a.nv + h) * a.dv + pw * ROWS + i % ROWS] = __builtin_nanf("");
         return;

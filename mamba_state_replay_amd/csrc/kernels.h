@@ -92,6 +92,8 @@ struct GdnArgs {
     const float* g;     // [batch][T][nv]
     const float* beta;
     float* o;           // [batch][T][nv][dv]
+    const int32_t* accepted_prev;   // fused commit of the previous verification, or null
+    int32_t T_prev;
     const int32_t* slot;   // conventional with snapshots: current slot per sequence, or null
     int32_t nslots;        // conventional: state slots per sequence (1: in place)
     int32_t batch, nv, nk, dv, parts;

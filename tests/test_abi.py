@@ -199,5 +199,7 @@ def test_gdn_null_pointers_rejected_before_launch(rb):
     assert L.gdn_conventional_commit(ctypes.byref(c), None, 4, None, 4, None, None) == -4
     assert L.gdn_conventional_commit(ctypes.byref(c), None, 4, None, 3, None, None) == -1
     assert L.gdn_decode_step(None, None, None, None, None) == -1
+    assert L.gdn_commit_verify(ctypes.byref(c), ctypes.byref(s), None, 1, ctypes.byref(t), None, None) == -1
+    assert L.gdn_commit_verify(ctypes.byref(c), ctypes.byref(s), None, 3, ctypes.byref(t), None, None) == -4
     zero = bg.GdnConfig(0, 32, 16, 128, 128).c()
     assert L.gdn_decode_step(ctypes.byref(zero), None, None, None, None) == 0   # batch 0: nothing to do

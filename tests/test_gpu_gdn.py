@@ -441,3 +441,49 @@ def test_gdn_window_and_draft_limits(shape, T, rounds, dev):
     assert_rows_close(np.swapaxes(o.cpu().numpy(), 1, 2), oref, what="gdn outputs at the limits")
     assert state_err(st.ckpt.cpu().numpy(), S).max() <= TOL
     assert int(st.status.cpu()[0]) == 0
+
+
+@pytest.mark.parametrize("ckpt", ["f32", "f16"])
+def test_gdn_commit_verify_equals_commit_then_verify(ckpt, dev):
+    """The fused entry point (commit of round r-1 inside verify of round r) gives
+    bit-identical outputs, checkpoints and rings to commit + verify; an accepted
+    count above T_prev is flagged and that sequence's outputs are NaN."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    shape = sg.GdnShape(batch=3, nv=32, nk=16, dk=128, dv=128, window=4)
+    T, rounds = 3, 7
+    w = sg.gdn_workload(shape, rounds, 151, "bf16", T=T)
+    cfg = bg.GdnConfig(shape.batch, shape.nv, shape.nk, shape.dk, shape.dv, shape.window, T, "bf16", ckpt)
+    S0 = torch.from_numpy(w.S0).to(dev).to(cfg.ckpt_torch)
+    a, f = bg.GdnState.allocate(cfg, dev), bg.GdnState.allocate(cfg, dev)
+    a.ckpt.copy_(S0)
+    f.ckpt.copy_(S0)
+    ts = GdnTokenStream(w.steps, dev, T)
+    acc = torch.from_numpy(w.extra["accepted"]).to(dev)
+    oa = torch.empty((rounds, shape.batch, T, shape.nv, shape.dv), device=dev)
+    of = torch.empty_like(oa)
+    say(f"gdn commit+verify fused vs separate ({ckpt})")
+    for r in range(rounds):
+        tok = ts.call(r)
+        tok.sr_seed = 40 + r
+        if r == 0:
+            bg.gdn_verify_drafts(cfg, f, tok, of[r])
+        else:
+            bg.gdn_commit_verify(cfg, f, acc[r - 1], T, tok, of[r])
+        bg.gdn_verify_drafts(cfg, a, tok, oa[r])
+        bg.gdn_commit(cfg, a, acc[r], T)
+    bg.gdn_commit(cfg, f, acc[rounds - 1], T)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, of)
+    for x, y in ((a.ckpt, f.ckpt), (a.meta, f.meta), (a.buf_u, f.buf_u), (a.buf_k, f.buf_k), (a.buf_g, f.buf_g)):
+        assert torch.equal(x, y)
+    assert int(a.status.cpu()[0]) == 0 and int(f.status.cpu()[0]) == 0
+    bad = torch.tensor([1, T + 1, 0], dtype=torch.int32, device=dev)
+    o1 = torch.zeros((shape.batch, T, shape.nv, shape.dv), device=dev)
+    meta_before = f.meta.clone()
+    say("gdn commit+verify with an accepted count above T_prev")
+    bg.gdn_commit_verify(cfg, f, bad, T, ts.call(0), o1)
+    torch.cuda.synchronize()
+    assert int(f.status.cpu()[0]) & 2
+    assert torch.isnan(o1[1]).all() and torch.isfinite(o1[[0, 2]]).all()
+    assert torch.equal(f.meta[1], meta_before[1])
