@@ -163,3 +163,44 @@ def test_gdn_f16_verify_commit(dev):
                 rep.ckpt[b] = rounded[b]
     assert_rows_close(np.swapaxes(o.cpu().numpy(), 1, 2), oref, what="gdn f16 draft outputs")
     assert int(st.status.cpu()[0]) == 0
+
+
+def test_gdn_f16_tracks_fp32_over_2048_steps(dev):
+    """2048 decode steps at L = 16 with the FP16 checkpoint (128 flushes, each
+    with its own rounding seed) beside the FP32 checkpoint, both against the
+    exact fp64 recurrence from the same fp16-valued start (the replay form in
+    fp64, pinned to the definition by the oracle tests).  The FP16 error sits
+    at the fp16 level and does not grow from the first windows to the last."""
+    from mamba_state_replay_amd import binding_gdn as bg
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    from tests.gpu_util import head_err
+    shape = sg.GdnShape(batch=2, nv=8, nk=4, dk=128, dv=128, window=16)
+    steps = 2048
+    w = sg.gdn_workload(shape, steps, 3050)
+    S0h = w.S0.astype(np.float16)
+    ts = GdnTokenStream(w.steps, dev)
+    outs = {}
+    for ck in ("f32", "f16"):
+        cfg = bg.GdnConfig(shape.batch, shape.nv, shape.nk, shape.dk, shape.dv, shape.window, 1, "bf16", ck)
+        st = bg.GdnState.allocate(cfg, dev)
+        st.ckpt.copy_(torch.from_numpy(S0h).to(dev).to(cfg.ckpt_torch))
+        o = torch.empty((steps, shape.batch, 1, shape.nv, shape.dv), device=dev)
+        say(f"gdn {ck} checkpoint: {steps} decode steps")
+        for t in range(steps):
+            tok = ts.call(t)
+            tok.sr_seed = 123456 + t
+            bg.gdn_decode_step(cfg, st, tok, o[t])
+        torch.cuda.synchronize()
+        assert int(st.status.cpu()[0]) == 0
+        outs[ck] = o.cpu().numpy()[:, :, 0]
+    tk = w.steps
+    _, oref = ogdn.replay_decode(S0h.astype(np.float64), tk.q, tk.k, tk.v, tk.g, tk.beta, shape.window)
+    win = 128
+    errs = {ck: np.array([head_err(outs[ck][i:i + win], oref[i:i + win]).max() for i in range(0, steps, win)])
+            for ck in outs}
+    q = len(errs["f16"]) // 4
+    print(f"[gpu] gdn 2048 steps, max error per window: fp32 {errs['f32'].max():.2e}; fp16 first quarter "
+          f"{errs['f16'][:q].max():.2e}, last quarter {errs['f16'][-q:].max():.2e}", flush=True)
+    assert errs["f32"].max() <= 1e-4
+    assert errs["f16"].max() <= 2e-3                       # fp16 state: a few 2^-11 half-ulps
+    assert errs["f16"][-q:].max() <= 2 * errs["f16"][:q].max()
