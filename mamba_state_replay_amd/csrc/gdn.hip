@@ -61,11 +61,13 @@ struct GdnLds {
     int K, KQ, QQ, U, US, V, G, GQ, BE, CK, CQ, DD, WF, UD, total;
 };
 
-__host__ __device__ inline GdnLds gdn_plan(int DK, int ROWS, int cap, int T) {
+// kbytes: bytes per element of the committed records' keys in LDS (they stay
+// in the input type: 2 for bf16, 4 for fp32).
+__host__ __device__ inline GdnLds gdn_plan(int DK, int ROWS, int cap, int T, int kbytes = 4) {
     GdnLds l;
     int o = 0;
     l.US = ROWS + 4;                // u row stride: lanes reading different records hit different banks
-    l.K = o;  o += cap * DK;        // committed records' keys
+    l.K = o;  o += (cap * DK * kbytes + 15) / 16 * 4;   // committed records' keys, input type
     l.KQ = o; o += T * DK;          // tokens' keys
     l.QQ = o; o += T * DK;          // tokens' queries
     l.U = o;  o += cap * l.US;      // committed records' u, this block's rows
@@ -80,6 +82,23 @@ __host__ __device__ inline GdnLds gdn_plan(int DK, int ROWS, int cap, int T) {
     l.UD = o; o += T * ROWS;        // the tokens' u
     l.total = (o + 3) & ~3;
     return l;
+}
+
+// One input-type element (fp32, or bf16 bits) as fp32.
+__device__ __forceinline__ float in_to_f32(float v) { return v; }
+__device__ __forceinline__ float in_to_f32(uint16_t v) { return bf16_to_f32(v); }
+
+// Four consecutive key elements starting at element e of an LDS array held in
+// the input type, as fp32.
+template <typename InT>
+__device__ __forceinline__ float4 key4(const float* base, int e) {
+    if constexpr (sizeof(InT) == 4) {
+        return *reinterpret_cast<const float4*>(base + e);
+    } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + e);
+        return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                           __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+    }
 }
 
 __device__ __forceinline__ float dot4(const v4f a, const float4 b) {
@@ -139,7 +158,8 @@ struct GdnStage {
         if (i < nkv) {
             const int c = i / KV, e = i - c * KV;
             src = reinterpret_cast<const uint4*>(kring + (size_t)slot_of(c) * DK) + e;
-            dst = smem + Ls.K + c * DK + e * EPV;
+            dst = reinterpret_cast<float*>(reinterpret_cast<InT*>(smem + Ls.K) + c * DK + e * EPV);
+            widen = false;                               // kept in the input type
             return;
         }
         i -= nkv;
@@ -245,7 +265,7 @@ struct GdnStage {
 // key-query scores (k_c . k_q, k_c . q_q), which give ck[q][c] (c < m_q) and
 // cq[q][c]; then dd[q] = exp(sum_{i<=m_q} g_i).  Window positions below np are
 // committed records (K, G), the others the call's tokens (KQ, GQ).
-template <int DK, int NT>
+template <int DK, int NT, typename InT>
 __device__ __forceinline__ void gdn_coefficients(float* smem, const GdnLds& Ls, int np, int T, int cap, int tid) {
     const int m = np + T;                             // window positions of the call
     const int grp = tid / 8, gl = tid % 8;
@@ -253,13 +273,22 @@ __device__ __forceinline__ void gdn_coefficients(float* smem, const GdnLds& Ls, 
         const int q = idx / m, c = idx % m;
         const int mq = np + q;
         if (c > mq) continue;                         // the whole group skips together
-        const float* key = c < np ? smem + Ls.K + c * DK : smem + Ls.KQ + (c - np) * DK;
         const float* kq = smem + Ls.KQ + q * DK;
         const float* qq = smem + Ls.QQ + q * DK;
         float sk = 0.0f, sq = 0.0f, seg = 0.0f;
-        for (int e = gl; e < DK; e += 8) {
-            sk = fmaf(key[e], kq[e], sk);
-            sq = fmaf(key[e], qq[e], sq);
+        if (c < np) {                                 // a committed record's key, input type
+            const InT* key = reinterpret_cast<const InT*>(smem + Ls.K) + c * DK;
+            for (int e = gl; e < DK; e += 8) {
+                const float kv = in_to_f32(key[e]);
+                sk = fmaf(kv, kq[e], sk);
+                sq = fmaf(kv, qq[e], sq);
+            }
+        } else {
+            const float* key = smem + Ls.KQ + (c - np) * DK;
+            for (int e = gl; e < DK; e += 8) {
+                sk = fmaf(key[e], kq[e], sk);
+                sq = fmaf(key[e], qq[e], sq);
+            }
         }
         for (int i = c + 1 + gl; i <= mq; i += 8) seg += i < np ? smem[Ls.G + i] : smem[Ls.GQ + i - np];
         sk = group_sum<8>(sk);
@@ -297,7 +326,7 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     const int kh = h / (a.nv / a.nk);
     const int cap = a.cap;
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
-    const GdnLds Ls = gdn_plan(DK, ROWS, cap, T);
+    const GdnLds Ls = gdn_plan(DK, ROWS, cap, T, sizeof(InT));
 
     // 1. ring pointer (every thread reads the workgroup's copy), the fused commit
     // of the previous verification if any (len += accepted_prev[b]), and the
@@ -389,7 +418,7 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
             for (int r = 0; r < Geo::NI; ++r) cf[r] = wc * smem[Ls.U + c * Ls.US + row0 + r];
 #pragma unroll
             for (int k = 0; k < Geo::VPL; ++k) {
-                const float4 kc = *reinterpret_cast<const float4*>(smem + Ls.K + c * DK + 4 * (lane + W * k));
+                const float4 kc = key4<InT>(smem + Ls.K, c * DK + 4 * (lane + W * k));
 #pragma unroll
                 for (int r = 0; r < Geo::NI; ++r) {
                     v4f& x = raw[r * Geo::VPL + k];
@@ -423,7 +452,7 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     }
 
     // 4. coefficients: one 8-lane group per (query q, window position c <= np + q)
-    gdn_coefficients<DK, NT>(smem, Ls, np, T, cap, tid);
+    gdn_coefficients<DK, NT, InT>(smem, Ls, np, T, cap, tid);
     __syncthreads();
 
     // 5. per query, in order: the rows' share of S_s k_q and S_s q_q from the
@@ -531,7 +560,7 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
     const int kh = h / (a.nv / a.nk);
     const int cap = a.cap;
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
-    const GdnLds Ls = gdn_plan(DK, ROWS, cap, T);
+    const GdnLds Ls = gdn_plan(DK, ROWS, cap, T, sizeof(InT));
     const int PK = Ls.total, PQ = Ls.total + T * ROWS;     // reduced products [q][row]
     const int m0 = bh * a.parts + 2 * pw;                  // the pointer copies of the two row blocks
 
@@ -626,7 +655,7 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
         }
     }
     // 4. coefficients
-    gdn_coefficients<DK, NT>(smem, Ls, np, T, cap, tid);
+    gdn_coefficients<DK, NT, InT>(smem, Ls, np, T, cap, tid);
     __syncthreads();
 
     // 5. per row of this thread: the query products (from the fp32 fold on a
@@ -645,9 +674,8 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
                 const float cf = smem[Ls.WF + c] * smem[Ls.U + c * Ls.US + row];
 #pragma unroll
                 for (int k = 0; k < 2; ++k) {
-                    const float* kc = smem + Ls.K + c * DK + (lane + W * k) * 8;
-                    const float4 k0 = *reinterpret_cast<const float4*>(kc);
-                    const float4 k1 = *reinterpret_cast<const float4*>(kc + 4);
+                    const float4 k0 = key4<InT>(smem + Ls.K, c * DK + (lane + W * k) * 8);
+                    const float4 k1 = key4<InT>(smem + Ls.K, c * DK + (lane + W * k) * 8 + 4);
                     f[8 * k] = fmaf(cf, k0.x, f[8 * k]);
                     f[8 * k + 1] = fmaf(cf, k0.y, f[8 * k + 1]);
                     f[8 * k + 2] = fmaf(cf, k0.z, f[8 * k + 2]);
@@ -854,10 +882,10 @@ template <int DK, typename InT>
 hipError_t launch_replay_t(const GdnArgs& a, hipStream_t stream) {
     constexpr int ROWS = GdnGeo<DK>::ROWS, NT = GdnGeo<DK>::NT;
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
-    const size_t lds = (size_t)gdn_plan(DK, ROWS, a.cap, T).total * 4;
+    const size_t lds = (size_t)gdn_plan(DK, ROWS, a.cap, T, sizeof(InT)).total * 4;
     const int nwg = a.batch * a.nv * a.parts;
     if constexpr (DK == 128) {
-        const size_t lds2 = ((size_t)gdn_plan(DK, 128, a.cap, T).total + 2 * (size_t)T * 128) * 4;
+        const size_t lds2 = ((size_t)gdn_plan(DK, 128, a.cap, T, sizeof(InT)).total + 2 * (size_t)T * 128) * 4;
         if (a.ckpt16 && a.parts % 2 == 0 && lds2 <= 64 * 1024) {   // 128 rows per workgroup
             hipLaunchKernelGGL((gdn_replay_f16_wide_kernel<InT>), dim3(nwg / 2), dim3(256), lds2, stream, a);
             return hipGetLastError();
