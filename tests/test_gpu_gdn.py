@@ -61,8 +61,8 @@ def _decode(shape, steps, seed, in_dtype, dev):
 
 
 @pytest.mark.parametrize("shape,steps,in_dtype", [(TINY, 23, "f32"), (TINY, 23, "bf16"),
-                                                  (LAYER_SMALL, 37, "bf16")],
-                         ids=["tiny-f32", "tiny-bf16", "layer-bf16"])
+                                                  (LAYER_SMALL, 37, "bf16"), (LAYER_SMALL, 21, "f32")],
+                         ids=["tiny-f32", "tiny-bf16", "layer-bf16", "layer-f32"])
 def test_gdn_decode_and_flush(shape, steps, in_dtype, dev):
     """Decode from an empty buffer through several flushes; outputs and, after
     a final flush, the checkpoint match stepping the gated delta rule."""
@@ -84,8 +84,9 @@ def test_gdn_decode_and_flush(shape, steps, in_dtype, dev):
 
 @pytest.mark.parametrize("shape,T,rounds,in_dtype", [(TINY, 3, 9, "f32"), (TINY, 2, 9, "bf16"),
                                                      (LAYER_SMALL, 3, 12, "bf16"),
-                                                     (LAYER_SMALL, 1, 20, "bf16")],
-                         ids=["tiny-T3-f32", "tiny-T2-bf16", "layer-T3", "layer-T1"])
+                                                     (LAYER_SMALL, 1, 20, "bf16"),
+                                                     (LAYER_SMALL, 4, 8, "f32")],
+                         ids=["tiny-T3-f32", "tiny-T2-bf16", "layer-T3", "layer-T1", "layer-T4-f32"])
 def test_gdn_verify_commit(shape, T, rounds, in_dtype, dev):
     """Speculative rounds: every draft's output equals stepping the accepted
     tokens so far and then the drafts; rollback is a pointer move, so the
