@@ -915,6 +915,9 @@ bool gdn_shape_supported(int dk, int dv) {
 
 int gdn_rows(int dk) { return dk == 16 ? GdnGeo<16>::ROWS : GdnGeo<128>::ROWS; }
 
+// LDS of the 64-row (or 16-row) replay kernel with fp32 keys: an upper bound
+// for every replay kernel the library picks for these sizes (bf16 keys take
+// less; the 128-row FP16 kernel is used only where its plan fits 64 KiB).
 size_t gdn_lds_bytes(int dk, int cap, int T) {
     return (size_t)gdn_plan(dk, gdn_rows(dk), cap, T).total * 4;
 }

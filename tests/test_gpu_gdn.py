@@ -7,7 +7,7 @@ import torch
 
 from oracle import gdn as ogdn
 from mamba_state_replay_amd import synth_gdn as sg
-from tests.gpu_util import TOL, assert_rows_close, say
+from tests.gpu_util import TOL, assert_rows_close, head_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -401,7 +401,6 @@ def test_gdn_long_run_no_drift(dev):
     errs = []
     for k in range(steps // 16):
         sl = slice(16 * k, 16 * (k + 1))
-        from tests.gpu_util import head_err
         errs.append(float(head_err(og[sl], oref[sl]).max()))
     print(f"[gpu] gdn per-window max error: first {errs[:3]}, last {errs[-3:]}", flush=True)
     assert max(errs) <= TOL
