@@ -487,3 +487,43 @@ def test_gdn_commit_verify_equals_commit_then_verify(ckpt, dev):
     assert int(f.status.cpu()[0]) & 2
     assert torch.isnan(o1[1]).all() and torch.isfinite(o1[[0, 2]]).all()
     assert torch.equal(f.meta[1], meta_before[1])
+
+
+@pytest.mark.parametrize("policy", ["all", "none", "alternate"])
+def test_gdn_acceptance_extremes(policy, dev):
+    """Every draft accepted each round (the ring at its fullest: L - 1 + T
+    committed records before a flush), none ever accepted (the drafts' slots
+    rewritten every round, the checkpoint never moves), and alternating T / 0:
+    outputs and final state against the oracle."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    shape = sg.GdnShape(batch=2, nv=32, nk=16, dk=128, dv=128, window=5)
+    T, rounds = 3, 10
+    w = sg.gdn_workload(shape, rounds, 171, "bf16", T=T)
+    acc = {"all": np.full((rounds, shape.batch), T), "none": np.zeros((rounds, shape.batch)),
+           "alternate": np.array([[T if (r + b) % 2 == 0 else 0 for b in range(shape.batch)]
+                                  for r in range(rounds)])}[policy].astype(np.int32)
+    cfg = _cfg(shape, T, "bf16")
+    st = _state(cfg, w.S0, dev)
+    ts = GdnTokenStream(w.steps, dev, T)
+    acc_d = torch.from_numpy(acc).to(dev)
+    o = torch.empty((rounds, shape.batch, T, shape.nv, shape.dv), device=dev)
+    say(f"gdn acceptance policy {policy}")
+    for r in range(rounds):
+        bg.gdn_verify_drafts(cfg, st, ts.call(r), o[r])
+        bg.gdn_commit(cfg, st, acc_d[r], T)
+    bg.gdn_flush(cfg, st)
+    torch.cuda.synchronize()
+    tk = w.steps
+    S = w.S0.astype(np.float64)
+    oref = np.zeros((rounds, T, shape.batch, shape.nv, shape.dv))
+    for r in range(rounds):
+        sl = slice(r * T, (r + 1) * T)
+        args = (tk.q[sl], tk.k[sl], tk.v[sl], tk.g[sl], tk.beta[sl])
+        _, oref[r] = ogdn.conventional(S, *args)
+        S, _ = ogdn.conventional(S, *args, nsteps=acc[r])
+    assert_rows_close(np.swapaxes(o.cpu().numpy(), 1, 2), oref, what=f"gdn outputs ({policy})")
+    assert state_err(st.ckpt.cpu().numpy(), S).max() <= TOL
+    if policy == "none":
+        assert np.array_equal(st.ckpt.cpu().numpy(), w.S0)        # nothing committed: checkpoint untouched
+    assert int(st.status.cpu()[0]) == 0
