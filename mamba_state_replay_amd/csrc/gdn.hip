@@ -276,19 +276,23 @@ __device__ __forceinline__ void gdn_coefficients(float* smem, const GdnLds& Ls, 
         const float* kq = smem + Ls.KQ + q * DK;
         const float* qq = smem + Ls.QQ + q * DK;
         float sk = 0.0f, sq = 0.0f, seg = 0.0f;
-        if (c < np) {                                 // a committed record's key, input type
-            const InT* key = reinterpret_cast<const InT*>(smem + Ls.K) + c * DK;
-            for (int e = gl; e < DK; e += 8) {
-                const float kv = in_to_f32(key[e]);
-                sk = fmaf(kv, kq[e], sk);
-                sq = fmaf(kv, qq[e], sq);
-            }
-        } else {
-            const float* key = smem + Ls.KQ + (c - np) * DK;
-            for (int e = gl; e < DK; e += 8) {
-                sk = fmaf(key[e], kq[e], sk);
-                sq = fmaf(key[e], qq[e], sq);
-            }
+        // lane gl takes the 4-element chunks gl, gl + 8, ... (16-byte reads; the
+        // group's lanes read consecutive chunks; not unrolled, so that only one
+        // chunk's values are live beside the tile's registers)
+#pragma unroll 1
+        for (int j4 = gl; j4 < DK / 4; j4 += 8) {
+            const float4 kv = c < np ? key4<InT>(smem + Ls.K, c * DK + 4 * j4)   // committed key, input type
+                                     : *reinterpret_cast<const float4*>(smem + Ls.KQ + (c - np) * DK + 4 * j4);
+            const float4 a = *reinterpret_cast<const float4*>(kq + 4 * j4);
+            const float4 bq = *reinterpret_cast<const float4*>(qq + 4 * j4);
+            sk = fmaf(kv.x, a.x, sk);
+            sk = fmaf(kv.y, a.y, sk);
+            sk = fmaf(kv.z, a.z, sk);
+            sk = fmaf(kv.w, a.w, sk);
+            sq = fmaf(kv.x, bq.x, sq);
+            sq = fmaf(kv.y, bq.y, sq);
+            sq = fmaf(kv.z, bq.z, sq);
+            sq = fmaf(kv.w, bq.w, sq);
         }
         for (int i = c + 1 + gl; i <= mq; i += 8) seg += i < np ? smem[Ls.G + i] : smem[Ls.GQ + i - np];
         sk = group_sum<8>(sk);
