@@ -504,22 +504,36 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
         slot -= slot >= cap ? cap : 0;
         const float bet = smem[Ls.BE + q];
         const float cself = smem[Ls.CQ + q * cap + np + q];
+        // One transposed reduction of the 2 NI sums over the row's W lanes
+        // (halving stages, as the Mamba-2 kernel reduces its rows): lane j of
+        // the group ends with the full sum of value idx(j), where values
+        // 0 .. NI-1 are S k of the thread's rows and NI .. 2 NI-1 their S q.
+        // A lane holding S k of a row and the lane holding S q of the same row
+        // differ in bit 0: the first forms u, passes it to the second, which
+        // forms o.
+        constexpr int NV2 = 2 * Geo::NI;
+        static_assert(NV2 <= W, "transposed reduction needs 2 NI <= W");
+        float red[16];
 #pragma unroll
         for (int r = 0; r < Geo::NI; ++r) {
-            const int row = row0 + r;
-            float sk = group_sum<W>(pk[r]);
-            float o = group_sum<W>(pq[r]);
-            for (int dd = 0; dd < q; ++dd) {
-                const float ud = smem[Ls.UD + dd * ROWS + row];
-                sk = fmaf(smem[Ls.CK + q * cap + np + dd], ud, sk);
-                o = fmaf(smem[Ls.CQ + q * cap + np + dd], ud, o);
-            }
-            const float u = bet * (smem[Ls.V + q * ROWS + row] - sk);
-            o = fmaf(cself, u, o);
-            if (q + 1 < T) smem[Ls.UD + q * ROWS + row] = u;
-            if (lane == r) {
-                a.o[((size_t)(b * T + q) * a.nv + h) * a.dv + p * ROWS + row] = o;
+            red[r] = pk[r];
+            red[Geo::NI + r] = pq[r];
+        }
+        int idx;
+        float acc = transpose_reduce<NV2, W>(red, lane, idx);
+        const bool is_k = idx < Geo::NI;
+        const int row = row0 + (is_k ? idx : idx - Geo::NI);
+        for (int dd = 0; dd < q; ++dd)
+            acc = fmaf(smem[(is_k ? Ls.CK : Ls.CQ) + q * cap + np + dd], smem[Ls.UD + dd * ROWS + row], acc);
+        const float u = bet * (smem[Ls.V + q * ROWS + row] - acc);     // meaningful where is_k
+        const float u_row = xor_shfl<1>(u);                            // the S q lane gets its row's u
+        const float o = fmaf(cself, u_row, acc);                       // meaningful where !is_k
+        if ((lane & (W - 1)) < NV2) {                                  // lanes holding distinct values
+            if (is_k) {
+                if (q + 1 < T) smem[Ls.UD + q * ROWS + row] = u;
                 uring_w[(size_t)slot * a.dv + row] = u;
+            } else {
+                a.o[((size_t)(b * T + q) * a.nv + h) * a.dv + p * ROWS + row] = o;
             }
         }
     }
