@@ -118,7 +118,9 @@ __device__ __forceinline__ float dot4(const v4f a, const float4 b) {
 // kernel can issue the tile's loads behind them; `finish` stores them (and
 // loads and stores the rest of a long window).  The log decays g (records) and
 // g, beta (tokens) are scalars: `load_g` / `store_g`.
-template <int DK, int ROWS, int NT, typename InT>
+// KEYS_F32: the committed records' keys are widened to fp32 in LDS (else kept
+// in the input type).
+template <int DK, int ROWS, int NT, typename InT, bool KEYS_F32 = false>
 struct GdnStage {
     static constexpr int EPV = InTraits<InT>::EPV;   // input elements per 16-byte vector
     static constexpr int KV = DK / EPV;              // vectors per key / query
@@ -158,8 +160,12 @@ struct GdnStage {
         if (i < nkv) {
             const int c = i / KV, e = i - c * KV;
             src = reinterpret_cast<const uint4*>(kring + (size_t)slot_of(c) * DK) + e;
-            dst = reinterpret_cast<float*>(reinterpret_cast<InT*>(smem + Ls.K) + c * DK + e * EPV);
-            widen = false;                               // kept in the input type
+            if constexpr (KEYS_F32) {
+                dst = smem + Ls.K + c * DK + e * EPV;
+            } else {
+                dst = reinterpret_cast<float*>(reinterpret_cast<InT*>(smem + Ls.K) + c * DK + e * EPV);
+                widen = false;                           // kept in the input type
+            }
             return;
         }
         i -= nkv;
@@ -578,7 +584,7 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
     const int kh = h / (a.nv / a.nk);
     const int cap = a.cap;
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
-    const GdnLds Ls = gdn_plan(DK, ROWS, cap, T, sizeof(InT));
+    const GdnLds Ls = gdn_plan(DK, ROWS, cap, T, 4);   // keys widened to fp32: the row-by-row fold reads each one per row
     const int PK = Ls.total, PQ = Ls.total + T * ROWS;     // reduced products [q][row]
     const int m0 = bh * a.parts + 2 * pw;                  // the pointer copies of the two row blocks
 
@@ -609,7 +615,7 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
     if (!fold) qstart = start;
 
     // 2. staging (as in gdn_replay_kernel, for 128 rows)
-    const GdnStage<DK, ROWS, NT, InT> stage(a, smem, Ls, b, h, kh, pw * ROWS, T, start, n, np, qstart,
+    const GdnStage<DK, ROWS, NT, InT, true> stage(a, smem, Ls, b, h, kh, pw * ROWS, T, start, n, np, qstart,
                                             (h % (a.nv / a.nk)) == 0 && pw == 0);
     uint4 jv[stage.JOBS];
     stage.issue(jv, tid);
@@ -673,7 +679,7 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
         }
     }
     // 4. coefficients
-    gdn_coefficients<DK, NT, InT>(smem, Ls, np, T, cap, tid);
+    gdn_coefficients<DK, NT, float>(smem, Ls, np, T, cap, tid);
     __syncthreads();
 
     // 5. per row of this thread: the query products (from the fp32 fold on a
@@ -692,8 +698,8 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
                 const float cf = smem[Ls.WF + c] * smem[Ls.U + c * Ls.US + row];
 #pragma unroll
                 for (int k = 0; k < 2; ++k) {
-                    const float4 k0 = key4<InT>(smem + Ls.K, c * DK + (lane + W * k) * 8);
-                    const float4 k1 = key4<InT>(smem + Ls.K, c * DK + (lane + W * k) * 8 + 4);
+                    const float4 k0 = key4<float>(smem + Ls.K, c * DK + (lane + W * k) * 8);
+                    const float4 k1 = key4<float>(smem + Ls.K, c * DK + (lane + W * k) * 8 + 4);
                     f[8 * k] = fmaf(cf, k0.x, f[8 * k]);
                     f[8 * k + 1] = fmaf(cf, k0.y, f[8 * k + 1]);
                     f[8 * k + 2] = fmaf(cf, k0.z, f[8 * k + 2]);
@@ -903,7 +909,7 @@ hipError_t launch_replay_t(const GdnArgs& a, hipStream_t stream) {
     const size_t lds = (size_t)gdn_plan(DK, ROWS, a.cap, T, sizeof(InT)).total * 4;
     const int nwg = a.batch * a.nv * a.parts;
     if constexpr (DK == 128) {
-        const size_t lds2 = ((size_t)gdn_plan(DK, 128, a.cap, T, sizeof(InT)).total + 2 * (size_t)T * 128) * 4;
+        const size_t lds2 = ((size_t)gdn_plan(DK, 128, a.cap, T, 4).total + 2 * (size_t)T * 128) * 4;
         if (a.ckpt16 && a.parts % 2 == 0 && lds2 <= 64 * 1024) {   // 128 rows per workgroup
             hipLaunchKernelGGL((gdn_replay_f16_wide_kernel<InT>), dim3(nwg / 2), dim3(256), lds2, stream, a);
             return hipGetLastError();
