@@ -7,8 +7,8 @@
  *
  * Method: NVIDIA Developer blog "ReplaySSM: Rethinking State Storage for Faster
  * Hybrid-Model Decoding".  Section "Why SSM layers can become a decoding
- * bottleneck" says GDN's delta-rule update can be written in the same
- * outer-product form as Mamba-2's, so the checkpoint-plus-buffer state of
+ * bottleneck" states that GDN's update, delta-rule correction included, keeps
+ * Mamba-2's decay-plus-rank-1 structure, so the checkpoint-plus-buffer state of
  * section "How ReplaySSM represents the state" applies; section "Benefit 2"
  * says GDN can use output-only evaluation.  The GDN recurrence is the gated
  * delta rule (Yang, Kautz and Hatamizadeh, "Gated Delta Networks", ICLR 2025),

@@ -5,8 +5,8 @@
 //
 // Method: NVIDIA Developer blog "ReplaySSM: Rethinking State Storage for Faster
 // Hybrid-Model Decoding".  Its section "Why SSM layers can become a decoding
-// bottleneck" says GDN's delta-rule update can be written in Mamba-2's
-// outer-product form, so the checkpoint-plus-buffer state (section "How
+// bottleneck" states that GDN's update, delta-rule correction included, has
+// the decay-plus-rank-1 structure of Mamba-2's, so the checkpoint-plus-buffer state (section "How
 // ReplaySSM represents the state") and output-only evaluation (section
 // "Benefit 2") carry over.  The gated delta rule (Yang, Kautz and Hatamizadeh,
 // "Gated Delta Networks", ICLR 2025), S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T)

@@ -6,9 +6,9 @@ with the HIP path.
 
 The ReplaySSM page (NVIDIA Developer blog "ReplaySSM: Rethinking State Storage
 for Faster Hybrid-Model Decoding", section "Why SSM layers can become a decoding
-bottleneck") names GDN as one of the SSM layers the method covers: GDN adds a
-delta-rule correction to the decay-plus-rank-1 update, and its update can be
-written in the same outer-product form.  The page prints no GDN formula; the
+bottleneck") names GDN as one of the SSM layers the method covers and states
+that its update, which corrects the decay-plus-rank-1 step with the delta rule,
+keeps that step's structure.  The page prints no GDN formula; the
 definition used here is the gated delta rule of Yang, Kautz and Hatamizadeh,
 "Gated Delta Networks: Improving Mamba2 with Delta Rule" (ICLR 2025), per
 sequence b and value head h (key head kh(h)):
@@ -29,7 +29,7 @@ Readings taken where the page is silent:
 `conventional` is the definition, written as the matrix product of the
 formula (S_{t-1} times the dk x dk transition matrix).  `Replay` is an
 independent fp64 form of the page's checkpoint-plus-buffer representation
-for this layer (the reading of "the same outer-product form"): expanding the
+for this layer (the reading of that statement): expanding the
 product gives S_t = alpha_t S_{t-1} + u_t k_t^T with the corrected value
 u_t = beta_t (v_t - alpha_t S_{t-1} k_t), so a record holds (k_t, u_t, g_t),
 a flush folds the records exactly as for Mamba-2 and a non-flush step needs

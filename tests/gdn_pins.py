@@ -4,8 +4,8 @@ Each pin takes the oracle module (so that planted mistakes in a copy of it can
 be run through the same pins) and raises AssertionError on a mismatch.  The
 facts are those of the gated delta rule (Yang, Kautz and Hatamizadeh, "Gated
 Delta Networks: Improving Mamba2 with Delta Rule", ICLR 2025) and of the
-ReplaySSM page's statement that GDN's update has the same outer-product form
-as Mamba-2's (NVIDIA Developer blog "ReplaySSM ...", section "Why SSM layers can
+ReplaySSM page's statement that GDN's update keeps Mamba-2's decay-plus-rank-1
+structure (NVIDIA Developer blog "ReplaySSM ...", section "Why SSM layers can
 become a decoding bottleneck"):
 
 * delta-rule write: with no decay, beta = 1 and a unit key, the state maps the
