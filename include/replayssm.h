@@ -83,8 +83,9 @@ typedef struct {
     int32_t read_copy;  /* RSSM_NONE, RSSM_BF16, RSSM_FP8_E4M3, RSSM_MXFP4 or RSSM_MXFP8 (the MX modes
                            need dstate % 32 == 0) */
     int32_t ckpt_dtype; /* RSSM_F32 (0): FP32 checkpoint.  RSSM_F16: half-precision recurrence
-                           checkpoint (blog section "Benefit 3": an FP16 recurrence with stochastic
-                           rounding tracks FP32): each flush computes the new state in fp32
+                           checkpoint (blog section "Benefit 3": a half-precision recurrence state
+                           stays close to FP32 when its writes round stochastically): each flush
+                           computes the new state in fp32
                            registers, writes it to fp16 with stochastic rounding (see
                            rssm_params.sr_seed) and casts the read copy from the same registers;
                            non-flush calls read the fp16 checkpoint itself when read_copy is

@@ -61,8 +61,9 @@ typedef struct {
     int32_t max_drafts;  /* T_max */
     int32_t in_dtype;    /* RSSM_F32 or RSSM_BF16: tokens q, k, v and the k records */
     int32_t ckpt_dtype;  /* RSSM_F32 (0): FP32 checkpoint.  RSSM_F16: half-precision recurrence
-                            checkpoint (blog section "Benefit 3": an FP16 recurrence with stochastic
-                            rounding tracks FP32): every call widens the fp16 checkpoint to fp32
+                            checkpoint (blog section "Benefit 3": a half-precision recurrence state
+                            stays close to FP32 when its writes round stochastically): every call
+                            widens the fp16 checkpoint to fp32
                             registers; a flush folds there and writes fp16 with stochastic rounding
                             (random words as for the Mamba-2 FP16 checkpoint in replayssm.h: Philox4x32-10,
                             element 4v+e takes word e at counter (v low, v high, 0, 0) under the key

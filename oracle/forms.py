@@ -16,8 +16,8 @@ stripped from the pages, against the step-by-step definition in oracle.c:
   verification");
 * ReplayModel: a checkpoint + record list driven by decode / verify / commit /
   flush with the flush taken at the start of a call once L records are
-  committed (the pages only say "when the buffer of L records fills" and that a
-  flush folds only committed records).
+  committed (the pages only place the flush at the point where the buffer holds
+  L records, and let it fold committed records alone).
 
 Every function works on one (sequence, head) tile:
   Hs [headdim][dstate]; records x [n][headdim], B [n][dstate], dt [n];

@@ -9,8 +9,8 @@ Storage for Faster Hybrid-Model Decoding", section "Why SSM layers can become a
 decoding bottleneck").  The scenario helpers below only compose calls of it:
 
 * decode: step the committed buffer records from the checkpoint, then every
-  decode token (section "How ReplaySSM represents the state": replay outputs
-  match conventional decoding up to floating-point differences);
+  decode token (section "How ReplaySSM represents the state": the replayed
+  outputs equal the stepped ones except for rounding);
 * verify: the outputs of T drafts are those of stepping them one by one from
   the committed state, and committing `a` of them equals having stepped only
   those `a` (section "Benefit 2: Simplify rollback and speed up verification").

@@ -1,7 +1,8 @@
 """GPU tests of the FP16 recurrence checkpoint written with stochastic rounding
 (NVIDIA Developer blog "ReplaySSM: Rethinking State Storage for Faster
 Hybrid-Model Decoding", section "Benefit 3: Limit error accumulation with
-separate precisions": an FP16 recurrence with stochastic rounding tracks FP32).
+separate precisions": a half-precision recurrence state stays close to FP32 when
+its writes round stochastically).
 
 * the kernel's rounding, through the probe entry point, equals the host
   definition (oracle/sr.py) bit for bit;

@@ -1,7 +1,7 @@
 """fp64 self-checks of the replay readings against the step-by-step definition.
 
-* replay form == conventional outputs (the pages: outputs match conventional
-  decoding up to floating-point differences)
+* replay form == conventional outputs (the pages: the replayed outputs equal the
+  stepped ones except for rounding)
 * fold(checkpoint, records) == the stepped state
 * output-only matrix form == replay form
 * checkpoint + buffer driven by decode/verify/commit/flush == stepping only the
