@@ -527,3 +527,38 @@ def test_gdn_acceptance_extremes(policy, dev):
     if policy == "none":
         assert np.array_equal(st.ckpt.cpu().numpy(), w.S0)        # nothing committed: checkpoint untouched
     assert int(st.status.cpu()[0]) == 0
+
+
+@pytest.mark.parametrize("nv,nk", [(8, 1), (4, 4), (16, 2)], ids=["8-per-key", "1-per-key", "8-per-key-2"])
+def test_gdn_head_grouping(nv, nk, dev):
+    """Value heads per key head from 1 to 8 (the key ring is appended by the
+    first row block of each key head's first value head and read by all of
+    them): verify + commit rounds and the flushed state against the oracle."""
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    bg = _bg()
+    shape = sg.GdnShape(batch=2, nv=nv, nk=nk, dk=128, dv=128, window=4)
+    T, rounds = 2, 8
+    w = sg.gdn_workload(shape, rounds, 191 + nv + nk, "bf16", T=T)
+    acc = w.extra["accepted"]
+    cfg = _cfg(shape, T, "bf16")
+    st = _state(cfg, w.S0, dev)
+    ts = GdnTokenStream(w.steps, dev, T)
+    acc_d = torch.from_numpy(acc).to(dev)
+    o = torch.empty((rounds, shape.batch, T, shape.nv, shape.dv), device=dev)
+    say(f"gdn head grouping nv={nv} nk={nk}")
+    for r in range(rounds):
+        bg.gdn_verify_drafts(cfg, st, ts.call(r), o[r])
+        bg.gdn_commit(cfg, st, acc_d[r], T)
+    bg.gdn_flush(cfg, st)
+    torch.cuda.synchronize()
+    tk = w.steps
+    S = w.S0.astype(np.float64)
+    oref = np.zeros((rounds, T, shape.batch, shape.nv, shape.dv))
+    for r in range(rounds):
+        sl = slice(r * T, (r + 1) * T)
+        args = (tk.q[sl], tk.k[sl], tk.v[sl], tk.g[sl], tk.beta[sl])
+        _, oref[r] = ogdn.conventional(S, *args)
+        S, _ = ogdn.conventional(S, *args, nsteps=acc[r])
+    assert_rows_close(np.swapaxes(o.cpu().numpy(), 1, 2), oref, what=f"gdn outputs nv={nv} nk={nk}")
+    assert state_err(st.ckpt.cpu().numpy(), S).max() <= TOL
+    assert int(st.status.cpu()[0]) == 0
