@@ -204,3 +204,50 @@ def test_gdn_f16_tracks_fp32_over_2048_steps(dev):
     assert errs["f32"].max() <= 1e-4
     assert errs["f16"].max() <= 2e-3                       # fp16 state: a few 2^-11 half-ulps
     assert errs["f16"][-q:].max() <= 2 * errs["f16"][:q].max()
+
+
+def test_gdn_f16_fullsize_decode_sampled(dev):
+    """The benchmarked FP16-checkpoint launch (batch 512, 32 value heads over
+    16 key heads, dk = dv = 128, L = 16; the 128-row kernel): 17 decode steps,
+    the flush at the start of call 16 with that call's seed.  Sampled sequences'
+    outputs against the oracle, and their checkpoint after the flush against
+    the stochastic rounding of the exact fold, taken at the elements' flat
+    indices in the whole checkpoint (the generator's counters)."""
+    from mamba_state_replay_amd import binding_gdn as bg
+    from mamba_state_replay_amd.staging import GdnTokenStream
+    shape = sg.GdnShape(batch=512, nv=32, nk=16, dk=128, dv=128, window=16)
+    steps, fseed = 17, 0xF16F0000 + 16
+    sample = np.array([0, 137, 300, 511])
+    w = sg.gdn_workload(shape, steps, 2001)
+    S0h = w.S0.astype(np.float16)
+    cfg = bg.GdnConfig(shape.batch, shape.nv, shape.nk, shape.dk, shape.dv, shape.window, 1, "bf16", "f16")
+    st = bg.GdnState.allocate(cfg, dev)
+    st.ckpt.copy_(torch.from_numpy(S0h).to(dev))
+    ts = GdnTokenStream(w.steps, dev)
+    o = torch.empty((steps, shape.batch, 1, shape.nv, shape.dv), device=dev)
+    say("gdn f16 checkpoint, batch 512: 17 decode steps, one flush")
+    for t in range(steps):
+        tok = ts.call(t)
+        tok.sr_seed = fseed if t == 16 else 1 + t
+        bg.gdn_decode_step(cfg, st, tok, o[t])
+    torch.cuda.synchronize()
+    tk = w.steps
+    S0 = S0h[sample].astype(np.float64)
+    args = [a[:, sample] for a in (tk.q, tk.k, tk.v, tk.g, tk.beta)]
+    exact, oref = ogdn.conventional(S0, *[a[:16] for a in args])
+    _, o16 = ogdn.conventional(exact, *[a[16:] for a in args])      # call 16 reads the exact fold
+    oref = np.concatenate([oref, o16])
+    assert_rows_close(o.cpu().numpy()[:, sample, 0], oref, what="gdn f16 batch-512 outputs (sampled)")
+    per_seq = shape.nv * shape.dv * shape.dk
+    idx = (sample.astype(np.uint64)[:, None] * np.uint64(per_seq)
+           + np.arange(per_seq, dtype=np.uint64)[None, :]).reshape(exact.shape)
+    want = sr.f16_sr(exact.astype(np.float32), sr.words(idx, fseed))
+    got = st.ckpt[torch.from_numpy(sample).to(dev)].cpu().numpy()
+    same = got.view(np.uint16) == want.astype(np.float16).view(np.uint16)
+    excess = _neighbours(got, exact)
+    print(f"[gpu] gdn f16 batch-512 flush: {same.mean():.6f} of sampled elements equal the oracle's "
+          f"rounding; largest excess over one spacing {excess.max():.3g}", flush=True)
+    assert (excess <= 0).all()
+    assert same.mean() >= 0.999
+    assert np.all(st.meta.cpu().numpy()[..., 1] == 1)
+    assert int(st.status.cpu()[0]) == 0
