@@ -242,3 +242,55 @@ def test_stochastic_rounding_tracks_where_nearest_stagnates():
     assert abs(e_rn.mean()) > 10                          # the case does stagnate under nearest rounding
     assert abs(e_sr.mean()) < 0.25
     assert np.sqrt((e_sr ** 2).mean()) < 6
+
+
+def test_f16_checkpoint_full_batch_sampled():
+    """The benchmarked layer (batch 256, 128 heads, headdim 64, dstate 128,
+    L = 16) with an FP16 checkpoint: 16 decode steps from 16 committed records,
+    so call 0 flushes (with its seed) and calls 1 .. 15 read the fp16
+    checkpoint.  Sampled sequences: the flushed checkpoint against the
+    stochastic rounding of the exact fold at the elements' flat indices in the
+    whole checkpoint, call 0's output against the exact fold, and the later
+    outputs against the oracle stepped from the kernel's own checkpoint."""
+    dev = device()
+    L, steps = 16, 16
+    shape = synth.LayerShape(batch=256, window=L, **NEMO)
+    work = _f16_work(shape, steps, 1031, n0=L)
+    cfg = staging.config(shape, ckpt_dtype="f16")
+    st = staging.replay_state(cfg, work, dev)
+    p = staging.params(work, dev)
+    toks = staging.TokenStream(work.steps, dev)
+    y = torch.empty((steps, shape.batch, 1, 128, 64), device=dev)
+    seed = 0xF16F00000100
+    say("f16 checkpoint decode, batch 256, 16 steps (flush at call 0)")
+    for t in range(steps):
+        p.sr_seed = seed + t
+        rb.replayssm_decode_step(cfg, st, p, toks.call(t), y[t])
+        if t == 0:
+            sample = np.array([0, 77, 128, 255])
+            ck = host(st.ckpt[torch.from_numpy(sample).to(dev)])
+    torch.cuda.synchronize()
+    exact = orc_mod.committed_state(work, seqs=sample)
+    per_seq = 128 * 64 * 128
+    idx = (sample.astype(np.uint64)[:, None] * np.uint64(per_seq)
+           + np.arange(per_seq, dtype=np.uint64)[None, :]).reshape(exact.shape)
+    want = sr.f16_sr(exact.astype(np.float32), sr.words(idx, seed))
+    same = _bits_equal(ck, want)
+    g64 = ck.astype(np.float64)
+    spacing = np.maximum(sr.f16_grid(np.abs(exact))[1], sr.f16_grid(np.abs(g64))[1])
+    slack = 1e-6 * np.abs(exact).max(axis=(-1, -2), keepdims=True)
+    excess = np.abs(g64 - exact) - spacing - slack
+    print(f"[gpu] f16 batch-256 flush: {same.mean():.6f} of sampled elements equal the oracle's "
+          f"rounding; largest excess over one spacing {excess.max():.3g}", flush=True)
+    assert (excess <= 0).all()
+    assert same.mean() >= 0.999
+    tok = work.steps
+    yg = host(y)[:, sample, 0]
+    args = (tok.x[:1][:, sample], tok.B[:1][:, sample], tok.C[:1][:, sample], tok.dt[:1][:, sample])
+    _, y0 = orc_mod.conventional(exact, *args, work.A, work.D)
+    _, yr = orc_mod.conventional(g64, tok.x[:, sample], tok.B[:, sample], tok.C[:, sample],
+                                 tok.dt[:, sample], work.A, work.D)
+    assert_rows_close(yg[:1], y0, what="f16 batch-256 flushing call's outputs (sampled)")
+    assert_rows_close(yg[1:], yr[1:], what="f16 batch-256 non-flush outputs (sampled)")
+    assert np.all(host(st.meta)[:, :, 1] == steps)
+    assert host(st.status)[0] == 0
