@@ -534,3 +534,44 @@ def test_copy_verify_rounds(copy, tile, T):
             seg[b] += dt[r * T:r * T + a_r[b], b].sum(axis=0)
         n = n + a_r
     print(f"[gpu] {copy} {tile} T={T}: worst error/bound {worst:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4", "mxfp8"])
+def test_dual_full_batch_sampled(copy):
+    """The benchmarked layer (batch 256, L = 16) with each read copy, 40 steps
+    (flushes at the starts of steps 16 and 32): the FP32 checkpoint and the
+    ring pointers are bit-identical to an FP32-only run over the whole batch;
+    on sampled sequences the non-flush outputs stay within the read bound of
+    test_dual_precision_error_bound and the flushing steps meet the FP32
+    tolerance."""
+    dev = device()
+    L, steps = 16, 40
+    shape = synth.NEMOTRON3
+    work = synth.decode_workload(shape, steps, seed=1012, n0=L)
+    say(f"dual precision {copy}, batch 256, {steps} steps")
+    _, st32, _ = _run_dual(staging.config(shape), work, dev, steps)
+    yc, stc, scales = _run_dual(staging.config(shape, read_copy=copy), work, dev, steps)
+    assert torch.equal(st32.ckpt, stc.ckpt), "read copy changed the FP32 recurrence"
+    assert torch.equal(st32.meta, stc.meta)
+    del st32
+    seqs = np.array([0, 77, 128, 255])
+    yc = yc[:, seqs]
+    yref, _ = orc_mod.decode(work, nsteps=steps, seqs=seqs)
+    flush_steps = [16, 32]
+    scale = np.abs(yref).max(axis=(0, 3))
+    worst = 0.0
+    for tf in [0] + flush_steps:
+        _, Hs = orc_mod.decode(work, nsteps=tf, seqs=seqs)
+        for t in range(tf, min(tf + L, steps)):
+            if t in flush_steps:
+                continue
+            dec = np.exp(work.A[None, :] * work.steps.dt[tf:t + 1][:, seqs].astype(np.float64).sum(0))
+            Cg = np.repeat(work.steps.C[t][seqs].astype(np.float64), shape.nheads // shape.ngroups, axis=1)
+            sc = scales[max(x for x in [0] + flush_steps if x <= t)][seqs] if copy != "bf16" else None
+            term = UNIT[copy] * np.abs(Hs) + read_delta(copy, sc, shape.headdim, shape.dstate)
+            bound = dec[:, :, None] * np.einsum("bhij,bhj->bhi", term, np.abs(Cg)) + 1e-4 * scale[:, :, None]
+            worst = max(worst, float((np.abs(yc[t] - yref[t]) / bound).max()))
+    print(f"[gpu] {copy} batch 256: worst error/bound {worst:.3f}", flush=True)
+    assert worst <= 1.0
+    assert_rows_close(yc[flush_steps], yref[flush_steps], what=f"{copy} batch-256 flushing-step outputs")
+    assert host(stc.status)[0] == 0
