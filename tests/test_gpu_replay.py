@@ -415,3 +415,35 @@ def test_rollback_equals_decoding_the_accepted_prefix(read_copy):
     print(f"[gpu] rollback: max output difference {err.max():.2e} of scale", flush=True)
     assert err.max() <= 1e-6
     assert tile_err(h_a, h_b).max() <= 1e-6
+
+
+def test_verify_full_batch_sampled():
+    """The benchmarked verification workload (batch 512, T = 3 drafts,
+    accepted U{0..3}, L = 16, initial fill U{0..15}, the bench's seed), 12
+    rounds through the fused commit + verify entry point: sampled sequences'
+    draft outputs and, after the last commit and a flush, their state."""
+    dev = device()
+    T, rounds = 3, 12
+    shape = synth.LayerShape(batch=512, window=16, max_drafts=T, **NEMO)
+    work = synth.verify_workload(shape, rounds, T, seed=1003)
+    cfg = staging.config(shape)
+    st = staging.replay_state(cfg, work, dev)
+    p = staging.params(work, dev)
+    stream = staging.TokenStream(work.steps, dev, T=T)
+    acc = torch.from_numpy(work.extra["accepted"]).to(dev)
+    y = torch.empty((rounds, shape.batch, T, cfg.nheads, cfg.headdim), device=dev)
+    say(f"verify full batch 512, T={T}, {rounds} rounds (fused commit)")
+    for r in range(rounds):
+        if r == 0:
+            rb.replayssm_verify_drafts(cfg, st, p, stream.call(r), y[r])
+        else:
+            rb.replayssm_commit_verify(cfg, st, p, acc[r - 1], T, stream.call(r), y[r])
+    rb.replayssm_commit(cfg, st, acc[rounds - 1], T)
+    rb.replayssm_flush(cfg, st, p)
+    torch.cuda.synchronize()
+    seqs = np.array([0, 100, 300, 511])
+    yref, Href = orc_mod.verify_rounds(work, seqs=seqs)
+    assert_rows_close(np.swapaxes(host(y)[:, seqs], 1, 2), yref, what="full-batch verify outputs (sampled)")
+    assert tile_err(host(st.ckpt[torch.from_numpy(seqs).to(dev)]), Href).max() <= TOL
+    assert np.all(host(st.meta)[:, :, 1] == 0)
+    assert host(st.status)[0] == 0
