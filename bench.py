@@ -131,13 +131,17 @@ def main():
         print("bench.py measures one GPU: the decode path shards by sequence or head group with no "
               "exchange, so only --gpus 1 is run here.", file=sys.stderr)
         sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py times the HIP kernels on an MI355X and has no CPU path: no HIP device is "
+              "visible.", file=sys.stderr)
+        sys.exit(1)
     if args.config != "decode":
         {"verify": bench_verify, "verify_sweep": bench_verify_sweep, "sweep": bench_sweep,
          "dual": bench_dual, "gdn": bench_gdn, "gdn_verify_sweep": bench_gdn_verify_sweep,
          "gdn_sweep": bench_gdn_sweep}[args.config](args)
         return
 
-    import torch
     from mamba_state_replay_amd import binding as rb
     from mamba_state_replay_amd import staging, synth, traffic
 
