@@ -3,6 +3,7 @@ host-side checks reject bad arguments before anything reaches the GPU."""
 import ctypes
 import re
 import subprocess
+import sys
 from pathlib import Path
 
 import pytest
@@ -203,3 +204,23 @@ def test_gdn_null_pointers_rejected_before_launch(rb):
     assert L.gdn_commit_verify(ctypes.byref(c), ctypes.byref(s), None, 3, ctypes.byref(t), None, None) == -4
     zero = bg.GdnConfig(0, 32, 16, 128, 128).c()
     assert L.gdn_decode_step(ctypes.byref(zero), None, None, None, None) == 0   # batch 0: nothing to do
+
+
+def test_missing_library_raises():
+    """With no built library every entry point raises at once: there is no
+    fallback path (run in a child process so the loaded library of this one
+    is left alone)."""
+    code = (
+        "import pathlib, pytest\n"
+        "from mamba_state_replay_amd import binding as rb, binding_gdn as bg\n"
+        "rb.LIBRARY = pathlib.Path('/nonexistent/libreplayssm.so')\n"
+        "rb._LIB = None\n"
+        "bg._LIB = None\n"
+        "with pytest.raises(RuntimeError, match='is missing'):\n"
+        "    rb.lib()\n"
+        "with pytest.raises(RuntimeError, match='is missing'):\n"
+        "    bg.gdn_row_blocks(bg.GdnConfig(1, 2, 1, 128, 128, 16, 1, 'bf16'))\n"
+        "print('ok')\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                         cwd=Path(__file__).resolve().parent.parent)
+    assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stderr[-1500:]
