@@ -122,22 +122,24 @@ def test_gdn_f16_decode_through_flushes(which, dev):
     assert int(st.status.cpu()[0]) == 0
 
 
-def test_gdn_f16_verify_commit(dev):
+@pytest.mark.parametrize("which", sorted(SHAPES))
+def test_gdn_f16_verify_commit(which, dev):
     """Speculative rounds over the FP16 checkpoint (T = 3, L = 4): outputs match
     the oracle that follows the same flush schedule and rounding."""
     from mamba_state_replay_amd import binding_gdn as bg
     from mamba_state_replay_amd.staging import GdnTokenStream
+    shape = SHAPES[which]
     T, rounds = 3, 6
-    w = sg.gdn_workload(SHAPE, rounds, 3003, T=T)
+    w = sg.gdn_workload(shape, rounds, 3003, T=T)
     acc = w.extra["accepted"]
     S0 = w.S0.astype(np.float16)
-    cfg = bg.GdnConfig(SHAPE.batch, SHAPE.nv, SHAPE.nk, SHAPE.dk, SHAPE.dv, SHAPE.window, T, "bf16", "f16")
+    cfg = bg.GdnConfig(shape.batch, shape.nv, shape.nk, shape.dk, shape.dv, shape.window, T, "bf16", "f16")
     st = bg.GdnState.allocate(cfg, dev)
     st.ckpt.copy_(torch.from_numpy(S0).to(dev))
     ts = GdnTokenStream(w.steps, dev, T)
     acc_d = torch.from_numpy(acc).to(dev)
-    o = torch.empty((rounds, SHAPE.batch, T, SHAPE.nv, SHAPE.dv), device=dev)
-    say("gdn f16 checkpoint: verify + commit rounds")
+    o = torch.empty((rounds, shape.batch, T, shape.nv, shape.dv), device=dev)
+    say(f"gdn f16 checkpoint ({which}): verify + commit rounds")
     for r in range(rounds):
         tok = ts.call(r)
         tok.sr_seed = 7000 + r
@@ -145,13 +147,13 @@ def test_gdn_f16_verify_commit(dev):
         bg.gdn_commit(cfg, st, acc_d[r], T)
     torch.cuda.synchronize()
     tk = w.steps
-    rep = ogdn.Replay(S0.astype(np.float64), SHAPE.nv, SHAPE.nk)
-    oref = np.zeros((rounds, T, SHAPE.batch, SHAPE.nv, SHAPE.dv))
+    rep = ogdn.Replay(S0.astype(np.float64), shape.nv, shape.nk)
+    oref = np.zeros((rounds, T, shape.batch, shape.nv, shape.dv))
     for r in range(rounds):
-        flushing = [b for b in range(SHAPE.batch) if len(rep.records[b]) >= SHAPE.window]
+        flushing = [b for b in range(shape.batch) if len(rep.records[b]) >= shape.window]
         for b in flushing:
             rep.fold(b)
-        for b in range(SHAPE.batch):
+        for b in range(shape.batch):
             drafts = [(tk.q[r * T + i][b], tk.k[r * T + i][b], tk.v[r * T + i][b], tk.g[r * T + i][b],
                        tk.beta[r * T + i][b]) for i in range(T)]
             outs, recs = rep.verify(b, drafts)
@@ -161,7 +163,7 @@ def test_gdn_f16_verify_commit(dev):
             rounded = sr.sr_checkpoint(rep.ckpt, 7000 + r)
             for b in flushing:
                 rep.ckpt[b] = rounded[b]
-    assert_rows_close(np.swapaxes(o.cpu().numpy(), 1, 2), oref, what="gdn f16 draft outputs")
+    assert_rows_close(np.swapaxes(o.cpu().numpy(), 1, 2), oref, what=f"gdn f16 draft outputs ({which})")
     assert int(st.status.cpu()[0]) == 0
 
 
