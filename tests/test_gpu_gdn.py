@@ -338,7 +338,8 @@ def _clone_gdn(st):
     return bg.GdnState(**{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in vars(st).items()})
 
 
-def test_gdn_graph_replays_match_eager(dev):
+@pytest.mark.parametrize("ckpt", ["f32", "f16"])
+def test_gdn_graph_replays_match_eager(ckpt, dev):
     """GDN decode steps (flushes included) and verify + commit rounds captured
     in one HIP graph: three replays, each after eager launches of the same
     tokens on a twin state and a synchronisation, reproduce the eager results
@@ -349,7 +350,8 @@ def test_gdn_graph_replays_match_eager(dev):
     K, T, R = 9, 3, 3
     w = sg.gdn_workload(shape, K, 91)
     vw = sg.gdn_workload(shape, R, 92, T=T)
-    cfg1, cfgT = _cfg(shape, 1, "bf16"), _cfg(shape, T, "bf16")
+    cfg1, cfgT = (bg.GdnConfig(shape.batch, shape.nv, shape.nk, shape.dk, shape.dv, shape.window, t, "bf16", ckpt)
+                  for t in (1, T))
     ts, vts = GdnTokenStream(w.steps, dev), GdnTokenStream(vw.steps, dev, T)
     acc = torch.from_numpy(vw.extra["accepted"]).to(dev)
     d_e, d_g = _state(cfg1, w.S0, dev), None
@@ -368,7 +370,7 @@ def test_gdn_graph_replays_match_eager(dev):
             bg.gdn_verify_drafts(cfgT, vstate, vts.call(r), vo[r])
             bg.gdn_commit(cfgT, vstate, acc[r], T)
 
-    say("capture GDN decode and verify + commit")
+    say(f"capture GDN decode and verify + commit ({ckpt} checkpoint)")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         run(d_g, v_g, o_g, vo_g)
