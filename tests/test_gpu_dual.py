@@ -459,14 +459,16 @@ COPY_VERIFY_SHAPES = {
 @pytest.mark.parametrize("tile", list(COPY_VERIFY_SHAPES))
 @pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4", "mxfp8"])
 def test_copy_verify_rounds(copy, tile, T):
-    """Speculative rounds (verify + commit) with a read copy against the same
-    rounds in FP32-only mode, on the same GPU: the FP32 checkpoint and ring
-    pointers stay bit-identical; outputs of rounds that flush (computed from
-    fresh FP32 registers) match to 1e-6; in the other rounds the difference is
-    the copy's read error alone, d_q (H_copy - H_s) C_q, and must lie within
-    d_q sum_j |C_q[j]| (u |H_s[i,j]| + delta) per element (u and delta as in
-    the dual-precision bound), with H_s the FP32 checkpoint of that round and
-    d_q the decay since the last flush, both taken from the run itself."""
+    """Speculative rounds (verify + commit) with a read copy beside the same
+    rounds in FP32-only mode: the FP32 checkpoint and ring pointers of the two
+    runs stay bit-identical (the copy never enters the recurrence).  Against
+    the fp64 oracle's verification rounds: outputs of rounds that flush
+    (computed from fresh FP32 registers) meet the FP32 tolerance; in the other
+    rounds the error is the copy's read error plus the FP32 one and must lie
+    within d_q sum_j |C_q[j]| (u |H_s[i,j]| + delta) + 1e-4 of the head's
+    output scale per element (u and delta as in the dual-precision bound,
+    delta from the copy's scales), with H_s the oracle's state at the
+    sequence's last flush and d_q the decay since then."""
     dev = device()
     L, rounds = 8, 14
     shape = synth.LayerShape(batch=2, window=L, max_drafts=T, **COPY_VERIFY_SHAPES[tile])
@@ -495,12 +497,16 @@ def test_copy_verify_rounds(copy, tile, T):
         runs[mode] = (ys, hs, scs, metas)
     y32, h32, _, m32 = runs[None]
     yc, hc, scc, mc = runs[copy]
+    yref, _ = orc_mod.verify_rounds(work)                  # [rounds][T][batch][nheads][headdim]
+    # the oracle's state after the commits of the first r rounds: H_s of a flush at the start of round r
+    Hr = [orc_mod.verify_rounds(work, rounds=r)[1] for r in range(rounds)]
     A = work.A.astype(np.float64)
     hpg = shape.nheads // shape.ngroups
     dt = work.steps.dt.astype(np.float64)                  # [rounds * T][batch][nheads]
     C = work.steps.C.astype(np.float64)                    # [rounds * T][batch][ngroups][dstate]
     n = np.zeros(shape.batch, np.int64)                    # committed records since the last flush
     seg = np.zeros((shape.batch, shape.nheads))            # sum of their dt
+    last = np.zeros(shape.batch, np.int64)                 # round of the last flush (0: the explicit one)
     worst = 0.0
     for r in range(rounds):
         assert np.array_equal(hc[r], h32[r]), f"round {r}: read copy changed the FP32 checkpoint"
@@ -508,24 +514,25 @@ def test_copy_verify_rounds(copy, tile, T):
         flushed = n >= L
         n = np.where(flushed, 0, n)
         seg = np.where(flushed[:, None], 0.0, seg)
-        scale = np.abs(y32[r]).max(axis=(1, 3))            # per (seq, head)
+        last = np.where(flushed, r, last)
+        scale = np.abs(yref[r]).max(axis=(0, 3))           # per (seq, head)
         for b in range(shape.batch):
             d_run = seg[b].copy()
             for q in range(T):
                 t = r * T + q
                 d_run = d_run + dt[t, b]
-                diff = np.abs(yc[r][b, q].astype(np.float64) - y32[r][b, q].astype(np.float64))   # [h][hd]
+                diff = np.abs(yc[r][b, q].astype(np.float64) - yref[r][q, b])    # [h][hd]
                 if flushed[b]:
-                    assert float((diff.max(axis=-1) / scale[b]).max()) <= 1e-6, f"round {r} seq {b}: flush outputs"
+                    assert float((diff.max(axis=-1) / scale[b]).max()) <= TOL, f"round {r} seq {b}: flush outputs"
                     continue
-                Cq = np.repeat(np.abs(C[t, b]), hpg, axis=0)                                       # [h][ds]
-                Hs = np.abs(hc[r][b])                                                              # [h][hd][ds]
+                Cq = np.repeat(np.abs(C[t, b]), hpg, axis=0)                     # [h][ds]
+                Hs = np.abs(Hr[last[b]][b])                                      # [h][hd][ds]
                 read = UNIT[copy] * np.einsum("hij,hj->hi", Hs, Cq)
                 if copy == "e4m3":
                     read = read + (scc[r][b] * 2.0 ** -10 * 1.001)[:, None] * Cq.sum(-1)[:, None]
                 elif copy in MX:
                     read = read + np.einsum("hij,hj->hi", read_delta(copy, scc[r][b], 0, 0), Cq)
-                bound = np.exp(A * d_run)[:, None] * read * 1.001 + 1e-6 * scale[b][:, None]
+                bound = np.exp(A * d_run)[:, None] * read * 1.001 + TOL * scale[b][:, None]
                 ratio = float((diff / bound).max())
                 worst = max(worst, ratio)
                 assert ratio <= 1.0, f"round {r} seq {b} draft {q}: error / bound {ratio:.3f}"
