@@ -25,10 +25,13 @@
  *   - Return value: RSSM_OK or a negative RSSM_ERR_* code; the message is in
  *     replayssm_last_error() (per calling thread).  On an error nothing is
  *     enqueued.
- *   - Errors a kernel finds in the data (a corrupt ring pointer, an accepted
- *     count out of range) OR a bit into *status (when status is not NULL),
- *     leave the state of the heads concerned untouched and write NaN to their
- *     outputs.
+ *   - Errors a kernel finds in the data (a ring pointer out of range, a head's
+ *     copy of it disagreeing with the sequence's first copy, a call whose
+ *     committed records plus its tokens would not fit the ring, an accepted
+ *     count out of range) OR a bit into *status (when status is not NULL; every
+ *     workgroup that finds one reports it), leave the state of the heads
+ *     concerned untouched and write NaN to their outputs; the other heads and
+ *     sequences proceed unaffected.
  *   - batch == 0: only the config is checked and nothing is enqueued.
  *   - Calls that share buffers must be ordered on one stream.
  *   - Tile shapes compiled in: (headdim, dstate) = (16, 16), (64, 64),
@@ -98,8 +101,11 @@ typedef struct {
  * sequence, used as a ring: record k of the window lives in slot
  * (start + k) % cap.  Every head keeps its own copy of the ring pointer
  * {start, len}; all copies of a sequence hold the same values (initialise them
- * together; the library keeps them equal).  A workgroup then reads and writes
- * only the copies of the heads it owns and never waits on another workgroup.
+ * together; the library keeps them equal).  A workgroup then writes only the
+ * copies of the heads it owns and never waits on another workgroup; it also
+ * reads the sequence's first copy and reports RSSM_STATUS_META when that copy
+ * holds neither its own pair nor the pair it is about to write.  Each copy is
+ * read and written as one 8-byte word (meta must be 8-byte aligned).
  */
 typedef struct {
     void *ckpt;         /* [batch][nheads][headdim][dstate] checkpoint H_s: fp32, or fp16 bits with

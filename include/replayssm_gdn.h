@@ -85,7 +85,8 @@ typedef struct {
     float *buf_u;     /* [batch][nv][cap][dv] fp32: corrected values u of the records */
     float *buf_g;     /* [batch][nv][cap] fp32: log decays g of the records */
     int32_t *meta;    /* [batch][nv][row_blocks][2] = {ring start, committed length}: one copy per
-                         workgroup, all copies of a sequence equal (initialise them together) */
+                         workgroup, all copies of a sequence equal (initialise them together);
+                         a copy disagreeing with the sequence's first one sets RSSM_STATUS_META */
     int32_t *status;  /* sticky RSSM_STATUS_* bits, or NULL */
 } gdn_state;
 

@@ -225,6 +225,37 @@ __device__ __forceinline__ float transpose_reduce(float (&v)[16], int lane, int&
     return s;
 }
 
+// ---------------------------------------------------------------------------
+// Ring pointers.  A sequence keeps several copies of its pointer {start, n}
+// (one per head, or per workgroup), each read and rewritten only by its owner.
+// A copy is one 64-bit word (start in the low half), loaded and stored whole,
+// so another workgroup that reads it while its owner rewrites it sees either
+// the old pair or the new one, never a mix of the two.
+// ---------------------------------------------------------------------------
+struct RingPtr {
+    int start, n;
+    __device__ __forceinline__ bool operator==(const RingPtr& o) const { return start == o.start && n == o.n; }
+};
+
+__device__ __forceinline__ RingPtr load_ring_ptr(const int32_t* meta, size_t copy) {
+    const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(meta) + copy, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return RingPtr{(int)(uint32_t)w, (int)(uint32_t)(w >> 32)};
+}
+
+__device__ __forceinline__ void store_ring_ptr(int32_t* meta, size_t copy, RingPtr p) {
+    const uint64_t w = (uint64_t)(uint32_t)p.start | ((uint64_t)(uint32_t)p.n << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(meta) + copy, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whether a workgroup's copy agrees with the sequence's reference copy (the
+// first one), which its owner may rewrite during the same launch: the
+// reference must hold the pair this copy holds now or the pair it will hold
+// after the call (own_new), which the owner of the reference computes alike.
+__device__ __forceinline__ bool ring_ptr_agrees(RingPtr ref, RingPtr own, RingPtr own_new) {
+    return ref == own || ref == own_new;
+}
+
 // Remap the linear workgroup id so that each of the 8 XCDs (which receive
 // workgroups round-robin) processes one contiguous block of tiles; the heads
 // of a group then share B/C records through that XCD's L2.

@@ -159,18 +159,25 @@ hipError_t conv_shape(const ConvArgs& a, int in_type, hipStream_t stream) {
 }
 
 // Commit kernels.  Replay: one thread per (sequence, head) copy of the ring
-// pointer; conventional: one thread per sequence.
+// pointer (nheads = copies per sequence), each checked against the sequence's
+// first copy as that copy stands before or after its own thread commits;
+// conventional: one thread per sequence.
 __global__ void replay_commit_kernel(const CommitArgs a) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= a.batch * a.nheads) return;
     const int b = t / a.nheads;
     const int acc = a.accepted[b];
-    const int n = a.meta[2 * t + 1];
-    if (acc < 0 || acc > a.T || n < 0 || n + acc > a.cap) {
+    const RingPtr own = load_ring_ptr(a.meta, t);
+    const RingPtr after{own.start, own.n + acc};
+    if (t != b * a.nheads && !ring_ptr_agrees(load_ring_ptr(a.meta, (size_t)b * a.nheads), own, after)) {
+        if (a.status) atomicOr(a.status, (int)kStatusMeta);
+        return;
+    }
+    if (acc < 0 || acc > a.T || own.n < 0 || own.n + acc > a.cap) {
         if (a.status) atomicOr(a.status, (int)kStatusAccept);
         return;
     }
-    a.meta[2 * t + 1] = n + acc;
+    store_ring_ptr(a.meta, t, after);
 }
 
 __global__ void conventional_commit_kernel(const CommitArgs a) {

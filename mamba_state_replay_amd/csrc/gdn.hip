@@ -338,11 +338,14 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
     const GdnLds Ls = gdn_plan(DK, ROWS, cap, T, sizeof(InT));
 
-    // 1. ring pointer (every thread reads the workgroup's copy), the fused commit
-    // of the previous verification if any (len += accepted_prev[b]), and the
-    // flush decision
-    const int start = a.meta[2 * wg];
-    const int n_stored = a.meta[2 * wg + 1];
+    // 1. ring pointer (every thread reads the workgroup's copy, checked against
+    // the sequence's first copy), the fused commit of the previous verification
+    // if any (len += accepted_prev[b]), and the flush decision
+    const RingPtr own = load_ring_ptr(a.meta, wg);
+    const size_t ref_copy = (size_t)b * a.nv * a.parts;
+    const RingPtr ref = load_ring_ptr(a.meta, ref_copy);
+    const int start = own.start;
+    const int n_stored = own.n;
     int acc_prev = 0;
     bool acc_ok = true;
     if (a.accepted_prev) {
@@ -350,10 +353,15 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
         acc_ok = acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap;
     }
     const int n = n_stored + acc_prev;
-    const bool valid = acc_ok && start >= 0 && start < cap && n >= 0 && n <= cap;
-    const bool fold = valid && (a.mode == MODE_FLUSH ? n > 0 : n >= a.L);
+    const bool fold = a.mode == MODE_FLUSH ? n > 0 : n >= a.L;
     const int np = fold ? 0 : n;                          // committed records seen by the queries
-    if (!valid || np + T > cap) {
+    // the pointer this call leaves (the drafts of a folding call go to the T
+    // slots after the n folded ones, so n + T must fit the ring whether or not
+    // the call folds)
+    const RingPtr after{fold ? (start + n) % cap : start, np + (a.mode == MODE_DECODE ? T : 0)};
+    const bool agree = (size_t)wg == ref_copy || ring_ptr_agrees(ref, own, after);
+    const bool valid = acc_ok && agree && start >= 0 && start < cap && n >= 0 && n + T <= cap;
+    if (!valid) {
         if (tid == 0 && a.status) atomicOr(a.status, (int)(acc_ok ? kStatusMeta : kStatusAccept));
         for (int i = tid; i < T * ROWS; i += NT)
             a.o[((size_t)(b * T + i / ROWS) * a.nv + h) * a.dv + p * ROWS + i % ROWS] = __builtin_nanf("");
@@ -453,10 +461,7 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
                                             reinterpret_cast<v4u*>(tile_p) + Geo::vec(tid, s));
         }
         if (T == 0) {
-            if (tid == 0) {
-                a.meta[2 * wg] = qstart;
-                a.meta[2 * wg + 1] = 0;
-            }
+            if (tid == 0) store_ring_ptr(a.meta, wg, after);
             return;
         }
     }
@@ -550,10 +555,7 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     }
 
     // 6. ring pointer: verify leaves the length, decode commits its token
-    if (tid == 0) {
-        a.meta[2 * wg] = qstart;
-        a.meta[2 * wg + 1] = np + (a.mode == MODE_DECODE ? T : 0);
-    }
+    if (tid == 0) store_ring_ptr(a.meta, wg, after);
 }
 
 // FP16 checkpoint, one workgroup per 128 value rows (two 64-row blocks) of a
@@ -588,10 +590,13 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
     const int PK = Ls.total, PQ = Ls.total + T * ROWS;     // reduced products [q][row]
     const int m0 = bh * a.parts + 2 * pw;                  // the pointer copies of the two row blocks
 
-    // 1. ring pointer (the copies of both row blocks are equal), the fused
-    // commit if any, and the flush decision
-    const int start = a.meta[2 * m0];
-    const int n_stored = a.meta[2 * m0 + 1];
+    // 1. ring pointer (the copies of both row blocks are equal, and agree with
+    // the sequence's first copy), the fused commit if any, and the flush decision
+    const RingPtr own = load_ring_ptr(a.meta, m0);
+    const size_t ref_copy = (size_t)b * a.nv * a.parts;
+    const RingPtr ref = load_ring_ptr(a.meta, ref_copy);
+    const int start = own.start;
+    const int n_stored = own.n;
     int acc_prev = 0;
     bool acc_ok = true;
     if (a.accepted_prev) {
@@ -599,11 +604,13 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
         acc_ok = acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap;
     }
     const int n = n_stored + acc_prev;
-    const bool valid = acc_ok && start >= 0 && start < cap && n >= 0 && n <= cap &&
-                       a.meta[2 * m0 + 2] == start && a.meta[2 * m0 + 3] == n_stored;
-    const bool fold = valid && (a.mode == MODE_FLUSH ? n > 0 : n >= a.L);
+    const bool fold = a.mode == MODE_FLUSH ? n > 0 : n >= a.L;
     const int np = fold ? 0 : n;
-    if (!valid || np + T > cap) {
+    const RingPtr after{fold ? (start + n) % cap : start, np + (a.mode == MODE_DECODE ? T : 0)};
+    const bool agree = load_ring_ptr(a.meta, m0 + 1) == own &&
+                       ((size_t)m0 == ref_copy || ring_ptr_agrees(ref, own, after));
+    const bool valid = acc_ok && agree && start >= 0 && start < cap && n >= 0 && n + T <= cap;
+    if (!valid) {
         if (tid == 0 && a.status) atomicOr(a.status, (int)(acc_ok ? kStatusMeta : kStatusAccept));
         for (int i = tid; i < T * ROWS; i += NT)
             a.o[((size_t)(b * T + i / ROWS) * a.nv + h) * a.dv + pw * ROWS + i % ROWS] = __builtin_nanf("");
@@ -740,10 +747,7 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
         }
     }
     if (T == 0) {
-        if (tid < 2) {
-            a.meta[2 * (m0 + tid)] = qstart;
-            a.meta[2 * (m0 + tid) + 1] = 0;
-        }
+        if (tid < 2) store_ring_ptr(a.meta, m0 + tid, after);
         return;
     }
     __syncthreads();
@@ -776,10 +780,7 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
         a.buf_g[(size_t)bh * cap + slot] = smem[Ls.GQ + q];
     }
     // 7. ring pointers of both row blocks
-    if (tid < 2) {
-        a.meta[2 * (m0 + tid)] = qstart;
-        a.meta[2 * (m0 + tid) + 1] = np + (a.mode == MODE_DECODE ? T : 0);
-    }
+    if (tid < 2) store_ring_ptr(a.meta, m0 + tid, after);
 }
 
 // Conventional GDN step (the in-library baseline): read the tile, then per

@@ -475,6 +475,7 @@ struct WgCtx {
     int b, h0, g, hpg;      // sequence, first head, group, heads per group
     int start, n_stored, n; // ring start, records stored, records counted (with a fused commit)
     bool flush_call;
+    RingPtr after;          // the ring pointer the call leaves
 };
 
 // Steps 1-6 of a decode / verify / flush call for one workgroup; FOLD: the call
@@ -799,12 +800,7 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
     }
 
     // ---- 6. advance the heads' ring pointers -----------------------------------------
-    const int new_start = fold && n > 0 ? (start + n) % cap : start;
-    const int new_n = (fold ? 0 : n) + (a.mode == MODE_DECODE ? 1 : 0);
-    if ((new_start != start || new_n != n_stored) && tid < HPW) {
-        a.meta[2 * (tile0 + tid)] = new_start;
-        a.meta[2 * (tile0 + tid) + 1] = new_n;
-    }
+    if (!(ctx.after == RingPtr{start, n_stored}) && tid < HPW) store_ring_ptr(a.meta, tile0 + tid, ctx.after);
 }
 
 // 8 waves per SIMD (64 VGPRs).  The MXFP4 kernels get 5 (96 VGPRs): their
@@ -827,13 +823,15 @@ __global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 5 : 8) void replay_kernel(co
     const size_t tile0 = (size_t)b * a.nheads + h0;
 
     // Every head keeps its own copy of the ring pointer; those of a workgroup's
-    // heads must agree.
-    const int start = a.meta[2 * tile0];
-    const int n_stored = a.meta[2 * tile0 + 1];
+    // heads must agree with each other and with the copy of the sequence's
+    // first head (read as it stands before or after this launch rewrites it).
+    const RingPtr own = load_ring_ptr(a.meta, tile0);
+    const RingPtr ref = load_ring_ptr(a.meta, (size_t)b * a.nheads);
+    const int start = own.start;
+    const int n_stored = own.n;
     bool same = true;
 #pragma unroll
-    for (int hh = 1; hh < HPW; ++hh)
-        same = same && a.meta[2 * (tile0 + hh)] == start && a.meta[2 * (tile0 + hh) + 1] == n_stored;
+    for (int hh = 1; hh < HPW; ++hh) same = same && load_ring_ptr(a.meta, tile0 + hh) == own;
     // Fused commit of the previous verification: len += accepted_prev[b].
     int acc_prev = 0;
     bool acc_ok = true;
@@ -842,9 +840,15 @@ __global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 5 : 8) void replay_kernel(co
         acc_ok = acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap;
     }
     const int n = n_stored + acc_prev;
+    const bool flush_call = a.mode == MODE_FLUSH;
+    const bool cast_only = flush_call && n == 0 && (a.flags & kFlushForceCast) && RM != READ_F32 && RM != READ_F16;
+    const bool fold = flush_call ? (n > 0 || cast_only) : (n >= a.L);
+    // the pointer this call leaves: past the folded records, and the decode token committed
+    const RingPtr after{fold && n > 0 ? (start + n) % cap : start, (fold ? 0 : n) + (a.mode == MODE_DECODE ? 1 : 0)};
+    const bool agree = h0 == 0 || ring_ptr_agrees(ref, own, after);
 
-    if (!(same && acc_ok && start >= 0 && start < cap && n >= 0 && n + T <= cap)) {
-        if (tid == 0 && h0 == 0 && a.status) atomicOr(a.status, (int)(acc_ok ? kStatusMeta : kStatusAccept));
+    if (!(same && agree && acc_ok && start >= 0 && start < cap && n >= 0 && n + T <= cap)) {
+        if (tid == 0 && a.status) atomicOr(a.status, (int)(acc_ok ? kStatusMeta : kStatusAccept));
         for (int o = tid; o < HPW * T * HD; o += NT) {
             const int hh = o / (T * HD), r = o - hh * T * HD;
             const int q = r / HD, i = r - q * HD;
@@ -853,13 +857,10 @@ __global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 5 : 8) void replay_kernel(co
         return;
     }
 
-    const bool flush_call = a.mode == MODE_FLUSH;
-    const bool cast_only = flush_call && n == 0 && (a.flags & kFlushForceCast) && RM != READ_F32 && RM != READ_F16;
-    const bool fold = flush_call ? (n > 0 || cast_only) : (n >= a.L);
     if (flush_call && !fold) return;
     // One body per case, so that the registers of the FP32 tile a flush holds
     // are not kept live across the read-copy path.
-    const WgCtx ctx{tile0, b, h0, g, hpg, start, n_stored, n, flush_call};
+    const WgCtx ctx{tile0, b, h0, g, hpg, start, n_stored, n, flush_call, after};
     if (fold)
         replay_body<HD, DS, NT, InT, RM, HPW, CK, true>(a, ctx, lds);
     else

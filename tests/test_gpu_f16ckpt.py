@@ -11,7 +11,9 @@ its writes round stochastically).
   rounding threshold, and there a neighbouring one;
 * decoding through several flushes equals the oracle that composes the same
   flush schedule on its own state (exact fold, then stochastic rounding with
-  the call's seed) to the FP32 tolerance;
+  the call's seed) to the FP32 tolerance per row, plus what one fp16 spacing
+  per checkpoint element (where a rounding decision went the other way) can
+  move an output;
 * with an MXFP4 read copy the fp16 checkpoints are bit-identical to a run
   without one, and the outputs stay within the copy's read bound of that
   oracle;
@@ -81,6 +83,34 @@ def _f16_work(shape, steps, seed, n0, in_dtype="bf16"):
     return dataclasses.replace(work, h0=work.h0.astype(np.float16).astype(np.float32))
 
 
+def _spacing_allowance(H, C, nheads):
+    """Per-output allowance [batch][nheads][headdim] for reading a checkpoint that
+    may differ from the oracle's H by one fp16 spacing per element:
+    sum_j |C[b, g(h), j]| * 2 * spacing16(|H[b, h, i, j]|).  Where the kernel's
+    fp32 fold and the oracle's fp64 fold straddle a rounding threshold the two
+    stochastic roundings are neighbours on the fp16 grid (one spacing of the
+    larger value's binade, at most twice the spacing at |H|); later folds decay
+    that difference (decays are <= 1) and round it again with the same random
+    bits, so it never exceeds one spacing.  C is [batch][ngroups][dstate]."""
+    _, sp = sr.f16_grid(np.abs(np.asarray(H, np.float64)))
+    Cg = np.repeat(np.abs(np.asarray(C, np.float64)), nheads // C.shape[1], axis=1)
+    return np.einsum("bhij,bhj->bhi", 2.0 * sp, Cg)
+
+
+def _window_allowances(C, cks, L, steps, nheads):
+    """Allowances [steps][batch][nheads][headdim] for a decode run whose call tf
+    (tf a multiple of L) flushes: the calls after tf read the oracle's rounded
+    checkpoint cks[tf]; the flushing call tf > 0 folds the previous one,
+    cks[tf - L]; call 0 folds the exact initial checkpoint (no allowance)."""
+    out = np.zeros((steps,) + cks[0].shape[:3])
+    for t in range(steps):
+        tf = t - t % L
+        H = cks[tf] if t > tf else cks.get(tf - L)
+        if H is not None:
+            out[t] = _spacing_allowance(H, C[t], nheads)
+    return out
+
+
 def test_flush_writes_the_stochastic_rounding_of_the_fold():
     dev = device()
     shape = synth.LayerShape(batch=3, window=16, **NEMO)
@@ -124,8 +154,9 @@ def test_decode_reads_the_f16_checkpoint(in_dtype):
     state element separate, so where a rounding decision went the other way
     (the kernel's fp32 fold and the oracle's fp64 fold straddle a threshold)
     the two checkpoints differ by one fp16 spacing at that element only; the
-    outputs meet the FP32 tolerance, and the final checkpoints agree on at
-    least 99.9% of their elements."""
+    outputs meet the FP32 tolerance per row plus what such a spacing can move
+    them (_spacing_allowance), and the final checkpoints agree on at least
+    99.9% of their elements."""
     dev = device()
     L, steps = 8, 40
     shape = synth.LayerShape(batch=4, window=L, **NEMO)
@@ -143,16 +174,18 @@ def test_decode_reads_the_f16_checkpoint(in_dtype):
     yg = host(y)[:, :, 0]
     tok = work.steps
     ref = np.zeros(yg.shape)
+    cks = {}
     H = orc_mod.committed_state(work)                     # the exact fold of call 0
     for tf in range(0, steps, L):                         # call tf flushes first
         t1 = min(tf + L, steps)
         win = (tok.x[tf:t1], tok.B[tf:t1], tok.C[tf:t1], tok.dt[tf:t1], work.A, work.D)
         _, yx = orc_mod.conventional(H, *win)
-        ck = sr.sr_checkpoint(H, 1000 + tf)
+        ck = cks[tf] = sr.sr_checkpoint(H, 1000 + tf)
         H, yc = orc_mod.conventional(ck, *win)            # H: the exact fold of the next flush
         ref[tf] = yx[0]
         ref[tf + 1:t1] = yc[1:]
-    assert_rows_close(yg, ref, what="f16-checkpoint decode outputs")
+    assert_rows_close(yg, ref, what="f16-checkpoint decode outputs",
+                      allowance=_window_allowances(tok.C, cks, L, steps, shape.nheads))
     same = _bits_equal(host(st.ckpt), ck)
     print(f"[gpu] f16 checkpoint after five flushes: {same.mean():.6f} equal to the oracle's", flush=True)
     assert same.mean() >= 0.999
@@ -207,7 +240,8 @@ def test_mxfp4_copy_over_an_f16_checkpoint():
         H, yo = orc_mod.conventional(cks[tf], *win)
         ref[tf] = yx[0]
         ref[tf + 1:t1] = yo[1:]
-    assert_rows_close(y16, ref, what="f16-checkpoint outputs without a copy")
+    assert_rows_close(y16, ref, what="f16-checkpoint outputs without a copy",
+                      allowance=_window_allowances(tok.C, cks, L, steps, shape.nheads))
     A = work.A.astype(np.float64)
     hpg = shape.nheads // shape.ngroups
     worst = 0.0
@@ -324,6 +358,7 @@ def test_f16_checkpoint_full_batch_sampled():
     _, yr = orc_mod.conventional(want, tok.x[:, sample], tok.B[:, sample], tok.C[:, sample],
                                  tok.dt[:, sample], work.A, work.D)
     assert_rows_close(yg[:1], y0, what="f16 batch-256 flushing call's outputs (sampled)")
-    assert_rows_close(yg[1:], yr[1:], what="f16 batch-256 non-flush outputs (sampled)")
+    allow = np.stack([_spacing_allowance(want, tok.C[t][sample], shape.nheads) for t in range(1, steps)])
+    assert_rows_close(yg[1:], yr[1:], what="f16 batch-256 non-flush outputs (sampled)", allowance=allow)
     assert np.all(host(st.meta)[:, :, 1] == steps)
     assert host(st.status)[0] == 0
