@@ -191,6 +191,18 @@ def main():
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
     del g
+    # Steady state beside the K-step figure: a whole number of windows (one
+    # flush per L calls exactly), captured and timed the same way, so the
+    # µs/step does not depend on how K lines up with L.
+    ss_steps = L * max(1, -(-64 // L))
+    ss_first = W + 3 * K
+    ss_ms = graph_time(lambda i: rb.replayssm_decode_step(cfg, st, p, toks.call((ss_first + i) % ntok), y),
+                       ss_steps, torch)
+    # graph_time replays the capture twice (a warm replay, then the timed one)
+    ss_sched, n_end = traffic.decode_schedule(work.n0, L, ss_first + 2 * ss_steps)
+    ss_sched = ss_sched[ss_first + ss_steps:]
+    ss_bytes = sum(traffic.decode_step_bytes(sz, n, f) for n, f in ss_sched)
+    ss_folds = sum(int(f.any()) for _, f in ss_sched)
     meta = st.meta.cpu().numpy()
     assert np.all(meta[:, :, 1] == n_end[:, None]), "ring pointers disagree with the flush schedule"
     assert int(st.status.cpu()[0]) == 0 and bool(torch.isfinite(y).all())
@@ -221,6 +233,10 @@ def main():
         "us_per_step": round(us_step, 2),
         "timing": "K steps captured in one HIP graph, one replay timed with HIP events after a warm replay",
         "eager_us_per_step": round(eager_ms * 1e3 / K, 2),
+        "steady_state": {"us_per_step": round(ss_ms * 1e3 / ss_steps, 2),
+                         "gbs": round(ss_bytes / (ss_ms * 1e-3) / 1e9, 1),
+                         "steps": ss_steps, "flush_calls": ss_folds,
+                         "note": "a whole number of windows, one flushing call per L (graph-timed)"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -574,7 +590,11 @@ def gdn_cpu_baseline(w, gpu_bytes_per_step, target_s):
         passes += 1
     el = time.perf_counter() - t0
     step_s = el / (passes * nsteps) * w.shape.batch / nseq
-    return {"value": round(gpu_bytes_per_step / step_s / 1e9, 4), "unit": "GB/s",
+    sh = w.shape
+    host_bytes = 2 * sh.batch * sh.nv * sh.dv * sh.dk * 8        # the fp64 state read and written per step
+    return {"value": round(host_bytes / step_s / 1e9, 3), "unit": "GB/s",
+            "bytes_counted": "fp64 state read + written per step (2 x 4 MiB per sequence)",
+            "gpu_bytes_rate_gbs": round(gpu_bytes_per_step / step_s / 1e9, 4),
             "us_per_step": round(step_s * 1e6, 1), "cores": threads, "kind": "oracle",
             "sample": f"{nseq} sequences x 32 heads x {nsteps} tokens, {passes} pass(es), {el:.1f} s "
                       f"(fp64 gated delta rule, numpy), scaled to {w.shape.batch} sequences",
@@ -582,12 +602,14 @@ def gdn_cpu_baseline(w, gpu_bytes_per_step, target_s):
 
 
 def cpu_baseline(work, gpu_bytes_per_step, target_s):
-    """The fp64 oracle on a bounded sample of the same workload, scaled to GB/s.
+    """The fp64 oracle on a bounded sample of the same workload.
 
     The oracle steps every sequence (all heads) of the workload through its 64
-    decode tokens, repeated until about `target_s` seconds have passed; the
-    value is the GPU step's algorithmic bytes divided by the oracle's time per
-    step (so the GPU/CPU value ratio is the step-rate ratio)."""
+    decode tokens, repeated until about `target_s` seconds have passed.  value:
+    host GB/s of the fp64 state it reads and writes per step (2 x 8 MiB per
+    sequence); us_per_step is the figure to compare with the GPU's step time,
+    and gpu_bytes_rate_gbs the GPU step's algorithmic bytes over the oracle's
+    step time (the step-rate ratio in GB/s)."""
     from oracle import oracle as orc
     o = orc.default()
     cores = o.num_threads()
@@ -603,10 +625,14 @@ def cpu_baseline(work, gpu_bytes_per_step, target_s):
     # one thread, 8 sequences (all heads), scaled to the whole batch
     few = np.arange(min(8, batch))
     one_s = orc.time_decode(work, few, nsteps, threads=1) / nsteps * batch / len(few)
+    sh = work.shape
+    host_bytes = 2 * batch * sh.nheads * sh.headdim * sh.dstate * 8   # the fp64 state read and written per step
     return {
-        "value": round(gpu_bytes_per_step / step_s / 1e9, 4),
+        "value": round(host_bytes / step_s / 1e9, 3),
         "unit": "GB/s",
+        "bytes_counted": "fp64 state read + written per step (2 x 8 MiB per sequence)",
         "us_per_step": round(step_s * 1e6, 1),
+        "gpu_bytes_rate_gbs": round(gpu_bytes_per_step / step_s / 1e9, 4),
         "cores": cores,
         "kind": "oracle",
         "sample": f"all {batch} sequences x 128 heads x {nsteps} decode tokens of the same workload, "

@@ -91,6 +91,27 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float out[4]) {
     out[3] = hi[1];
 }
 
+// Two bf16 values packed in a word (low half first), as the operand type of
+// gfx950's bf16 dot instruction.  The word goes through a copy: bit-casting an
+// element of an ext_vector_type vector straight to the pair type was seen to
+// compile to the vector's first element for every index.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) {
+    bf16x2_t r;
+    __builtin_memcpy(&r, &u, 4);
+    return r;
+}
+
+// c + a.lo * b.lo + a.hi * b.hi with v_dot2c_f32_bf16 (the products of two
+// bf16 values are exact in fp32).
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, as_bf16x2(b), c, false);
+}
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return dot2_bf16(as_bf16x2(a), b, c);
+}
+
 // MX block scale (E8M0 byte e: 2^(e - 127), e = 255 NaN) as fp32.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     return e == 255u ? __builtin_nanf("") : e == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);
@@ -228,9 +249,12 @@ __device__ __forceinline__ float transpose_reduce(float (&v)[16], int lane, int&
 // ---------------------------------------------------------------------------
 // Ring pointers.  A sequence keeps several copies of its pointer {start, n}
 // (one per head, or per workgroup), each read and rewritten only by its owner.
-// A copy is one 64-bit word (start in the low half), loaded and stored whole,
-// so another workgroup that reads it while its owner rewrites it sees either
-// the old pair or the new one, never a mix of the two.
+// A copy is one aligned 64-bit word (start in the low half), loaded and stored
+// as a single 8-byte access (an s_load_dwordx2 / global_store_dwordx2: the
+// memory system performs an aligned 8-byte access whole), so another workgroup
+// that reads it while its owner rewrites it sees either the old pair or the new
+// one, never a mix of the two.  The loads are plain so that the compiler keeps
+// them on the scalar unit, ahead of the tile loads that wait for them.
 // ---------------------------------------------------------------------------
 struct RingPtr {
     int start, n;
@@ -238,14 +262,12 @@ struct RingPtr {
 };
 
 __device__ __forceinline__ RingPtr load_ring_ptr(const int32_t* meta, size_t copy) {
-    const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(meta) + copy, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t w = reinterpret_cast<const uint64_t*>(meta)[copy];
     return RingPtr{(int)(uint32_t)w, (int)(uint32_t)(w >> 32)};
 }
 
 __device__ __forceinline__ void store_ring_ptr(int32_t* meta, size_t copy, RingPtr p) {
-    const uint64_t w = (uint64_t)(uint32_t)p.start | ((uint64_t)(uint32_t)p.n << 32);
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(meta) + copy, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    reinterpret_cast<uint64_t*>(meta)[copy] = (uint64_t)(uint32_t)p.start | ((uint64_t)(uint32_t)p.n << 32);
 }
 
 // Whether a workgroup's copy agrees with the sequence's reference copy (the

@@ -344,21 +344,22 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     const RingPtr own = load_ring_ptr(a.meta, wg);
     const size_t ref_copy = (size_t)b * a.nv * a.parts;
     const RingPtr ref = load_ring_ptr(a.meta, ref_copy);
+    const int acc_prev = a.accepted_prev ? a.accepted_prev[b] : 0;
+    // the loads in flight together (the reference is needed only after the
+    // flush decision; issued after it the latencies would add up)
+    asm volatile("" ::"s"(own.start), "s"(own.n), "s"(ref.start), "s"(ref.n), "s"(acc_prev));
     const int start = own.start;
     const int n_stored = own.n;
-    int acc_prev = 0;
-    bool acc_ok = true;
-    if (a.accepted_prev) {
-        acc_prev = a.accepted_prev[b];
-        acc_ok = acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap;
-    }
+    const bool acc_ok = !a.accepted_prev ||
+                        (acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap);
     const int n = n_stored + acc_prev;
     const bool fold = a.mode == MODE_FLUSH ? n > 0 : n >= a.L;
     const int np = fold ? 0 : n;                          // committed records seen by the queries
     // the pointer this call leaves (the drafts of a folding call go to the T
     // slots after the n folded ones, so n + T must fit the ring whether or not
     // the call folds)
-    const RingPtr after{fold ? (start + n) % cap : start, np + (a.mode == MODE_DECODE ? T : 0)};
+    const int wrapped = start + n >= cap ? start + n - cap : start + n;   // start + n < 2 cap when valid
+    const RingPtr after{fold ? wrapped : start, np + (a.mode == MODE_DECODE ? T : 0)};
     const bool agree = (size_t)wg == ref_copy || ring_ptr_agrees(ref, own, after);
     const bool valid = acc_ok && agree && start >= 0 && start < cap && n >= 0 && n + T <= cap;
     if (!valid) {
@@ -595,18 +596,19 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
     const RingPtr own = load_ring_ptr(a.meta, m0);
     const size_t ref_copy = (size_t)b * a.nv * a.parts;
     const RingPtr ref = load_ring_ptr(a.meta, ref_copy);
+    const int acc_prev = a.accepted_prev ? a.accepted_prev[b] : 0;
+    // the loads in flight together (the reference is needed only after the
+    // flush decision; issued after it the latencies would add up)
+    asm volatile("" ::"s"(own.start), "s"(own.n), "s"(ref.start), "s"(ref.n), "s"(acc_prev));
     const int start = own.start;
     const int n_stored = own.n;
-    int acc_prev = 0;
-    bool acc_ok = true;
-    if (a.accepted_prev) {
-        acc_prev = a.accepted_prev[b];
-        acc_ok = acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap;
-    }
+    const bool acc_ok = !a.accepted_prev ||
+                        (acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap);
     const int n = n_stored + acc_prev;
     const bool fold = a.mode == MODE_FLUSH ? n > 0 : n >= a.L;
     const int np = fold ? 0 : n;
-    const RingPtr after{fold ? (start + n) % cap : start, np + (a.mode == MODE_DECODE ? T : 0)};
+    const int wrapped = start + n >= cap ? start + n - cap : start + n;   // start + n < 2 cap when valid
+    const RingPtr after{fold ? wrapped : start, np + (a.mode == MODE_DECODE ? T : 0)};
     const bool agree = load_ring_ptr(a.meta, m0 + 1) == own &&
                        ((size_t)m0 == ref_copy || ring_ptr_agrees(ref, own, after));
     const bool valid = acc_ok && agree && start >= 0 && start < cap && n >= 0 && n + T <= cap;

@@ -20,7 +20,7 @@ namespace {
 // Per-head arrays are indexed [head][...]; B rows are the group's and shared
 // by the heads; the queries' C rows are widened to fp32.
 struct Lds {
-    int X, XS, K, SC, Cq, DT, AA, CO, DQ, WF, RED, total;
+    int X, XS, K, SC, Cq, Cb, DT, AA, CO, DQ, WF, RED, total;
 };
 
 constexpr int kRedSlots = 64;   // cross-wave reduction slots: [head][wave]
@@ -35,6 +35,7 @@ __host__ __device__ inline Lds lds_plan(int HD, int DS, int cap, int T, int HPW,
     l.K = o;  o += cap * DS * xbytes / 4;   // B of records then queries (input type)
     l.SC = o; o += HPW * mxbytes / 4;       // MX scale bytes of the heads' tiles
     l.Cq = o; o += T * DS;           // C of the queries
+    l.Cb = o; o += xbytes == 2 ? T * DS / 2 : 0;   // bf16 inputs: C of the queries as bf16 pairs too
     l.DT = o; o += HPW * cap;        // dt, window order, per head
     l.AA = o; o += HPW * cap;        // a = dt * A, per head
     l.CO = o; o += HPW * T * cap;    // co[h][q][c] = dt_c exp(sum_{c<i<=m_q} a_i) (B_c . C_q) [+ D at c = m_q]
@@ -121,9 +122,48 @@ struct TileRegs {
     // product runs over chunks of 4 columns: one float4 of C, then for every row
     // the 4 tile values under it (an fp32 quarter-vector, two bf16 words or
     // one e4m3 word, widened next to its use), so few values are live at once.
-    template <int EB, int OFF = 0, bool F16 = false>
-    __device__ __forceinline__ void dot(const float* cq, int j, float* v) const {
+    //
+    // DOT2 (bf16 inputs, 1- and 2-byte copy tiles): cb points at C as bf16
+    // pairs; a bf16 copy word is already a pair, and an e4m3 word becomes two
+    // pairs by gfx950's fp8 -> bf16 converter (exact, scale 1: the copy's scale
+    // is applied to the sum), so each pair of columns is one v_dot2c_f32_bf16
+    // (the products of two bf16 values are exact in fp32) instead of a widening
+    // step and two FMAs.
+    template <int EB, int OFF = 0, bool F16 = false, bool DOT2 = false>
+    __device__ __forceinline__ void dot(const float* cq, const uint32_t* cb, int j, float* v) const {
         using G = TileGeo<HD, DS, NT, EB>;
+        if constexpr (DOT2) {
+            static_assert((EB == 2 && !F16) || EB == 1, "pairs of bf16 or e4m3 codes");
+#pragma unroll
+            for (int k = 0; k < G::VPL; ++k) {
+                const uint4* cp = reinterpret_cast<const uint4*>(cb + (j + G::W * k) * G::EPV / 2);
+#pragma unroll
+                for (int h = 0; h < G::EPV / 8; ++h) {            // 8 columns (4 C pairs) at a time
+                    const uint4 c = cp[h];
+                    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+                    for (int r = 0; r < G::NI; ++r) {
+                        const v4u rv = __builtin_bit_cast(v4u, raw[OFF + r * G::VPL + k]);
+                        const uint32_t tw[4] = {rv.x, rv.y, rv.z, rv.w};
+                        float acc = v[r];
+                        if constexpr (EB == 2) {
+#pragma unroll
+                            for (int w = 0; w < 4; ++w) acc = dot2_bf16(tw[w], cw[w], acc);
+                        } else {
+#pragma unroll
+                            for (int w = 0; w < 2; ++w) {
+                                uint32_t code = tw[2 * h + w];
+                                asm volatile("" : "+v"(code));          // decode inside the query loop
+                                acc = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false), cw[2 * w], acc);
+                                acc = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, true), cw[2 * w + 1], acc);
+                            }
+                        }
+                        v[r] = acc;
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < G::VPL; ++k) {
 #pragma unroll
@@ -264,13 +304,17 @@ __device__ __forceinline__ StageJob stage_job(const StageMap& m, int v) {
     return j;
 }
 
+// A C vector (jb.wide) of bf16 inputs is stored widened at Cq and as it came
+// (bf16 pairs) at the same element offset in Cb.
 template <typename InT>
-__device__ __forceinline__ void stage_store(float* lds, const StageJob& jb, const uint4 v) {
+__device__ __forceinline__ void stage_store(float* lds, const StageJob& jb, const uint4 v, const Lds& L) {
     char* d = reinterpret_cast<char*>(lds) + jb.dst;
-    if (sizeof(InT) == 4 || !jb.wide)
+    if (sizeof(InT) == 4 || !jb.wide) {
         *reinterpret_cast<uint4*>(d) = v;
-    else
+    } else {
         widen16<InT>(v, reinterpret_cast<float*>(d));
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds) + L.Cb * 4 + (jb.dst - L.Cq * 4) / 2) = v;
+    }
 }
 
 // B_c[col .. col + 3] as fp32 from the B rows in LDS (input type).
@@ -305,7 +349,9 @@ __device__ __forceinline__ void queries_and_outputs(const TileRegs<HD, DS, NT>& 
         float v[16];
 #pragma unroll
         for (int r = 0; r < G::NI; ++r) v[r] = 0.f;
-        t.template dot<EB, OFF, F16>(lds + L.Cq + q * DS, j, v);
+        constexpr bool DOT2 = InTraits<InT>::EPV == 8 && (EB == 1 || (EB == 2 && !F16));
+        t.template dot<EB, OFF, F16, DOT2>(lds + L.Cq + q * DS,
+                                           reinterpret_cast<const uint32_t*>(lds + L.Cb) + q * DS / 2, j, v);
         const float dq = lds[hv.DQ + q];
 #pragma unroll
         for (int r = 0; r < G::NI; ++r) v[r] *= dq * rs[r];
@@ -390,24 +436,41 @@ __device__ __forceinline__ void mx_queries(const TileRegs<HD, DS, NT>& t, const 
         for (int q = 0; q < w.T; ++q) {
             float sq = bs;
             asm volatile("" : "+v"(sq));     // decode per query, not hoisted into registers
-            const float* cq = lds + L.Cq + q * DS + j * 32;
             float acc = 0.f;
+            if constexpr (InTraits<InT>::EPV == 8) {
+                // bf16 inputs: the converter writes two codes as a bf16 pair (times the
+                // block scale, exact), and one v_dot2c_f32_bf16 takes the pair with
+                // the matching pair of C (bf16 as staged)
+                const uint4* cp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint32_t*>(lds + L.Cb) +
+                                                                 q * DS / 2 + j * 16);
+                const uint32_t cwd[4] = {words.x, words.y, words.z, words.w};
 #pragma unroll
-            for (int ch = 0; ch < 8; ++ch) {
-                const float4 c = *reinterpret_cast<const float4*>(cq + 4 * ch);
-                f2 lo, hi;
-                if (ch % 2 == 0) {
-                    lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 0);
-                    hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 1);
-                } else {
-                    lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 2);
-                    hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 3);
+                for (int wq = 0; wq < 4; ++wq) {                  // code word wq: columns 8 wq .. 8 wq + 7
+                    const uint4 c = cp[wq];
+                    acc = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwd[wq], sq, 0), c.x, acc);
+                    acc = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwd[wq], sq, 1), c.y, acc);
+                    acc = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwd[wq], sq, 2), c.z, acc);
+                    acc = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwd[wq], sq, 3), c.w, acc);
                 }
-                acc = fmaf(lo[0], c.x, acc);
-                acc = fmaf(lo[1], c.y, acc);
-                acc = fmaf(hi[0], c.z, acc);
-                acc = fmaf(hi[1], c.w, acc);
-                if (ch % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // two chunks of C live at a time
+            } else {
+                const float* cq = lds + L.Cq + q * DS + j * 32;
+#pragma unroll
+                for (int ch = 0; ch < 8; ++ch) {
+                    const float4 c = *reinterpret_cast<const float4*>(cq + 4 * ch);
+                    f2 lo, hi;
+                    if (ch % 2 == 0) {
+                        lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 0);
+                        hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 1);
+                    } else {
+                        lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 2);
+                        hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[ch / 2], sq, 3);
+                    }
+                    acc = fmaf(lo[0], c.x, acc);
+                    acc = fmaf(lo[1], c.y, acc);
+                    acc = fmaf(hi[0], c.z, acc);
+                    acc = fmaf(hi[1], c.w, acc);
+                    if (ch % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // two chunks of C live at a time
+                }
             }
             acc = e == 255u ? __builtin_nanf("") : acc * lds[hv.DQ + q];
             const int m = w.n + q;
@@ -475,7 +538,6 @@ struct WgCtx {
     int b, h0, g, hpg;      // sequence, first head, group, heads per group
     int start, n_stored, n; // ring start, records stored, records counted (with a fused commit)
     bool flush_call;
-    RingPtr after;          // the ring pointer the call leaves
 };
 
 // Steps 1-6 of a decode / verify / flush call for one workgroup; FOLD: the call
@@ -572,14 +634,14 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
         if (v < nv) {
             const StageJob jb = stage_job<HD, DS, InT, HPW>(sm, v);
             if (jb.app) *jb.app = jv[j];
-            stage_store<InT>(lds, jb, jv[j]);
+            stage_store<InT>(lds, jb, jv[j], L);
         }
     }
     for (int v = tid + JOBS * NT; v < nv; v += NT) {   // windows too long for JOBS vectors a thread
         const StageJob jb = stage_job<HD, DS, InT, HPW>(sm, v);
         const uint4 val = *jb.src;
         if (jb.app) *jb.app = val;
-        stage_store<InT>(lds, jb, val);
+        stage_store<InT>(lds, jb, val, L);
     }
     for (int t = tid; t < HPW * rows; t += NT) {
         const int hh = block_of<HPW>(t, rows), c = t - hh * rows;
@@ -621,6 +683,7 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
             const int m = q < T ? n + q : n - 1;             // last record the weight spans
             float sc = 0.f;
             if (q < T) {
+                // (fp32 FMAs: v_dot2c_f32_bf16 on the bf16 B and C rows measured slower here)
                 for (int j4 = sub; j4 < DS / 4; j4 += 8) {
                     const float4 kb = load_b4<InT, DS>(lds, L.K, c, 4 * j4);
                     const float4 cq = *reinterpret_cast<const float4*>(lds + L.Cq + q * DS + 4 * j4);
@@ -800,14 +863,23 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
     }
 
     // ---- 6. advance the heads' ring pointers -----------------------------------------
-    if (!(ctx.after == RingPtr{start, n_stored}) && tid < HPW) store_ring_ptr(a.meta, tile0 + tid, ctx.after);
+    // (the pair the prologue checked the reference copy against)
+    const int wrapped = start + n >= cap ? start + n - cap : start + n;
+    const RingPtr after{fold && n > 0 ? wrapped : start, (fold ? 0 : n) + (a.mode == MODE_DECODE ? 1 : 0)};
+    if (!(after == RingPtr{start, n_stored}) && tid < HPW) store_ring_ptr(a.meta, tile0 + tid, after);
 }
 
-// 8 waves per SIMD (64 VGPRs).  The MXFP4 kernels get 5 (96 VGPRs): their
-// query loop decodes two fp4 codes per instruction into fp32 registers, and
-// at 64 VGPRs it spills.
+// Waves per SIMD: 8 (64 VGPRs), except for the MXFP4 kernels, whose flush
+// encodes and whose query loop decodes several heads' blocks: with bf16
+// inputs (codes decoded to bf16 pairs) 7 over an FP32 checkpoint and 6 over
+// an FP16 one; with fp32 inputs (codes decoded to fp32) 5.  Fewer would spill.
+template <int RM, typename InT, int CK>
+constexpr int replay_waves() {
+    return RM == READ_MXFP8 ? 7 : RM != READ_MXFP4 ? 8 : InTraits<InT>::EPV != 8 ? 5 : CK == 4 ? 7 : 6;
+}
+
 template <int HD, int DS, int NT, typename InT, int RM, int HPW, int CK>
-__global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 5 : 8) void replay_kernel(const ReplayArgs a) {
+__global__ __launch_bounds__(NT, (replay_waves<RM, InT, CK>())) void replay_kernel(const ReplayArgs a) {
     extern __shared__ float lds[];
 
     const int chunks = a.nheads / HPW;
@@ -825,26 +897,33 @@ __global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 5 : 8) void replay_kernel(co
     // Every head keeps its own copy of the ring pointer; those of a workgroup's
     // heads must agree with each other and with the copy of the sequence's
     // first head (read as it stands before or after this launch rewrites it).
-    const RingPtr own = load_ring_ptr(a.meta, tile0);
+    RingPtr cp[HPW];                                  // the copies of the workgroup's heads
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) cp[hh] = load_ring_ptr(a.meta, tile0 + hh);
+    const RingPtr own = cp[0];
     const RingPtr ref = load_ring_ptr(a.meta, (size_t)b * a.nheads);
+    // fused commit of the previous verification: len += accepted_prev[b]
+    const int acc_prev = a.accepted_prev ? a.accepted_prev[b] : 0;
+    // every load in flight together: the reference is needed only after the
+    // flush decision, and issued after it the latencies would add up
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) asm volatile("" ::"s"(cp[hh].start), "s"(cp[hh].n));
+    asm volatile("" ::"s"(ref.start), "s"(ref.n), "s"(acc_prev));
     const int start = own.start;
     const int n_stored = own.n;
     bool same = true;
 #pragma unroll
-    for (int hh = 1; hh < HPW; ++hh) same = same && load_ring_ptr(a.meta, tile0 + hh) == own;
-    // Fused commit of the previous verification: len += accepted_prev[b].
-    int acc_prev = 0;
-    bool acc_ok = true;
-    if (a.accepted_prev) {
-        acc_prev = a.accepted_prev[b];
-        acc_ok = acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap;
-    }
+    for (int hh = 1; hh < HPW; ++hh) same = same && cp[hh] == own;
+    const bool acc_ok = !a.accepted_prev ||
+                        (acc_prev >= 0 && acc_prev <= a.T_prev && n_stored >= 0 && n_stored + acc_prev <= cap);
     const int n = n_stored + acc_prev;
     const bool flush_call = a.mode == MODE_FLUSH;
     const bool cast_only = flush_call && n == 0 && (a.flags & kFlushForceCast) && RM != READ_F32 && RM != READ_F16;
     const bool fold = flush_call ? (n > 0 || cast_only) : (n >= a.L);
     // the pointer this call leaves: past the folded records, and the decode token committed
-    const RingPtr after{fold && n > 0 ? (start + n) % cap : start, (fold ? 0 : n) + (a.mode == MODE_DECODE ? 1 : 0)};
+    // (start + n < 2 cap for every pointer that passes the checks below)
+    const int wrapped = start + n >= cap ? start + n - cap : start + n;
+    const RingPtr after{fold && n > 0 ? wrapped : start, (fold ? 0 : n) + (a.mode == MODE_DECODE ? 1 : 0)};
     const bool agree = h0 == 0 || ring_ptr_agrees(ref, own, after);
 
     if (!(same && agree && acc_ok && start >= 0 && start < cap && n >= 0 && n + T <= cap)) {
@@ -860,7 +939,7 @@ __global__ __launch_bounds__(NT, RM == READ_MXFP4 ? 5 : 8) void replay_kernel(co
     if (flush_call && !fold) return;
     // One body per case, so that the registers of the FP32 tile a flush holds
     // are not kept live across the read-copy path.
-    const WgCtx ctx{tile0, b, h0, g, hpg, start, n_stored, n, flush_call, after};
+    const WgCtx ctx{tile0, b, h0, g, hpg, start, n_stored, n, flush_call};
     if (fold)
         replay_body<HD, DS, NT, InT, RM, HPW, CK, true>(a, ctx, lds);
     else
