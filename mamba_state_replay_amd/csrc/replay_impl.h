@@ -532,6 +532,29 @@ __device__ __forceinline__ void store_ckpt(void* ckpt, size_t tile, const v4f* f
     }
 }
 
+// Small batches: the launch is bound by its chain of dependent loads (ring
+// pointer, then the records it locates, then the tile), not by bytes.  The
+// eager variant (FP32 reads, one head per workgroup) issues, before the ring
+// pointer has arrived, the loads of every slot of the head's and group's
+// rings, of the call's tokens, of dt and of the FP32 tile; once the pointer
+// is known each thread routes its vectors to their window rows in LDS (a ring
+// slot s holds window position (s - start) mod cap, used if below n) and
+// appends the tokens' records.  It reads cap instead of n records, which
+// costs nothing where latency, not bandwidth, sets the time.
+constexpr int kEagerJobs = 4;   // 16-byte vectors per thread
+
+template <int NT>
+struct EagerRegs {
+    uint4 v[kEagerJobs];
+    float dt;
+};
+
+// Vectors of the eager list: x ring (cap x VR), B ring (cap x VS), then the
+// tokens' x (T x VR), B and C (T x VS each).
+__host__ __device__ inline int eager_count(int cap, int T, int VR, int VS) {
+    return cap * (VR + VS) + T * (VR + 2 * VS);
+}
+
 // Where a workgroup's call stands once its ring pointers are checked.
 struct WgCtx {
     size_t tile0;           // tile of the first head
@@ -543,8 +566,9 @@ struct WgCtx {
 // Steps 1-6 of a decode / verify / flush call for one workgroup; FOLD: the call
 // folds its window into the checkpoint (and rewrites the read copy); CK: the
 // checkpoint's element bytes (4: FP32; 2: FP16 written with stochastic rounding).
-template <int HD, int DS, int NT, typename InT, int RM, int HPW, int CK, bool FOLD>
-__device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ctx, float* lds) {
+template <int HD, int DS, int NT, typename InT, int RM, int HPW, int CK, bool FOLD, bool EAGER>
+__device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ctx, float* lds,
+                                            TileRegs<HD, DS, NT>& treg, const EagerRegs<NT>& er) {
     using G32 = TileGeo<HD, DS, NT, 4>;
     // read-tile element bytes (0: fp4); READ_F16 reads the FP16 checkpoint itself
     constexpr int EBC = RM == READ_MXFP4 ? 0 : (RM == READ_BF16 || RM == READ_F16) ? 2 : 1;
@@ -599,6 +623,65 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
     const StageMap sm{bx, bB, xt, Bt, Ct, start, n, cap, T, b, h0, g, a.nheads, a.ngroups,
                       nx, nb, rows, L.X, L.XS, L.K, L.Cq, append, append && writer,
                       reinterpret_cast<const uint8_t*>(a.ckpt_scale) + tile0 * MXB, nc, L.SC};
+  if constexpr (EAGER) {
+    static_assert(RM == READ_F32 && CK == 4 && HPW == 1, "eager loads: FP32 reads, one head");
+    // route the preloaded vectors (see EagerRegs) to their window rows
+    const int nring = cap * (VR + VS);
+    const int ne = eager_count(cap, T, VR, VS);
+    uint4* xring = reinterpret_cast<uint4*>(const_cast<InT*>(bx));
+    uint4* Bring = reinterpret_cast<uint4*>(const_cast<InT*>(bB));
+#pragma unroll
+    for (int j = 0; j < kEagerJobs; ++j) {
+        const int v = tid + j * NT;
+        if (v >= ne) continue;
+        int dst = -1;
+        bool wide = false;
+        uint4* app = nullptr;
+        if (v < cap * VR) {                                     // x ring slot s
+            const int s = v / VR, cv = v - s * VR;
+            const int c = s - start < 0 ? s - start + cap : s - start;
+            if (c < n) dst = L.X * 4 + (c * L.XS + cv * EPVIN) * (int)sizeof(InT);
+        } else if (v < nring) {                                 // B ring slot s
+            const int u = v - cap * VR;
+            const int s = u / VS, cv = u - s * VS;
+            const int c = s - start < 0 ? s - start + cap : s - start;
+            if (c < n) dst = L.K * 4 + (c * DS + cv * EPVIN) * (int)sizeof(InT);
+        } else if (v < nring + T * VR) {                        // x of query q
+            const int u = v - nring;
+            const int q = u / VR, cv = u - q * VR;
+            dst = L.X * 4 + ((n + q) * L.XS + cv * EPVIN) * (int)sizeof(InT);
+            if (append) app = xring + ring_slot(start, n + q, cap) * VR + cv;
+        } else if (v < nring + T * (VR + VS)) {                 // B of query q
+            const int u = v - nring - T * VR;
+            const int q = u / VS, cv = u - q * VS;
+            dst = L.K * 4 + ((n + q) * DS + cv * EPVIN) * (int)sizeof(InT);
+            if (append && writer) app = Bring + ring_slot(start, n + q, cap) * VS + cv;
+        } else {                                                // C of query q
+            const int u = v - nring - T * (VR + VS);
+            const int q = u / VS, cv = u - q * VS;
+            dst = (L.Cq + q * DS + cv * EPVIN) * 4;
+            wide = true;
+        }
+        if (app) *app = er.v[j];
+        if (dst >= 0) stage_store<InT>(lds, StageJob{nullptr, nullptr, dst, wide}, er.v[j], L);
+    }
+    if (tid < cap + T) {
+        float* const bdt = a.buf_dt + tile0 * cap;
+        const float d = er.dt;
+        int c;                                                  // window row, or past them
+        if (tid < cap) {                                        // ring slot tid: a committed record?
+            c = tid - start < 0 ? tid - start + cap : tid - start;
+            c = c < n ? c : rows;
+        } else {                                                // the token of query tid - cap
+            c = n + tid - cap;
+            if (append) bdt[ring_slot(start, c, cap)] = d;
+        }
+        if (c < rows) {
+            lds[L.DT + c] = d;
+            lds[L.AA + c] = d * Ah[0];
+        }
+    }
+  } else {
     uint4 jv[JOBS];
 #pragma unroll
     for (int j = 0; j < JOBS; ++j) {
@@ -611,14 +694,14 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
     float dtv = 0.f;
     if (tid < HPW * rows) {
         const int hh = block_of<HPW>(tid, rows), c = tid - hh * rows;
-        dtv = c < n ? bdt0[hh * cap + ring_slot(start, c, cap)] : a.dt[(size_t)(b * T + (c - n)) * a.nheads + h0 + hh];
+        dtv = c < n ? bdt0[hh * cap + ring_slot(start, c, cap)]
+                    : a.dt[(size_t)(b * T + (c - n)) * a.nheads + h0 + hh];
     }
 
     // The tile this call streams: FP32 when it flushes or has no read copy,
     // else the read copies of the workgroup's heads.  A flushing call with
     // several heads starts the first head's FP32 tile here and streams the
     // others in step 4.
-    TileRegs<HD, DS, NT> treg;
     if constexpr (FOLD) {
         load_ckpt<HD, DS, NT, CK>(treg, a.ckpt, tile0, tid);
     } else if constexpr (RM == READ_F32) {
@@ -647,7 +730,8 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
         const int hh = block_of<HPW>(t, rows), c = t - hh * rows;
         float d = dtv;
         if (t >= NT)                                        // windows longer than the workgroup
-            d = c < n ? bdt0[hh * cap + ring_slot(start, c, cap)] : a.dt[(size_t)(b * T + (c - n)) * a.nheads + h0 + hh];
+            d = c < n ? bdt0[hh * cap + ring_slot(start, c, cap)]
+                      : a.dt[(size_t)(b * T + (c - n)) * a.nheads + h0 + hh];
         if (append && c >= n) bdt0[hh * cap + ring_slot(start, c, cap)] = d;
         float ah = Ah[0];
 #pragma unroll
@@ -655,6 +739,7 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
         lds[L.DT + hh * cap + c] = d;
         lds[L.AA + hh * cap + c] = d * ah;
     }
+  }
     __syncthreads();
 
     // ---- 3. coefficients: one 8-lane group per (query, record) pair ---------------
@@ -878,8 +963,8 @@ constexpr int replay_waves() {
     return RM == READ_MXFP8 ? 7 : RM != READ_MXFP4 ? 8 : InTraits<InT>::EPV != 8 ? 5 : CK == 4 ? 7 : 6;
 }
 
-template <int HD, int DS, int NT, typename InT, int RM, int HPW, int CK>
-__global__ __launch_bounds__(NT, (replay_waves<RM, InT, CK>())) void replay_kernel(const ReplayArgs a) {
+template <int HD, int DS, int NT, typename InT, int RM, int HPW, int CK, bool EAGER>
+__global__ __launch_bounds__(NT, (EAGER ? 2 : replay_waves<RM, InT, CK>())) void replay_kernel(const ReplayArgs a) {
     extern __shared__ float lds[];
 
     const int chunks = a.nheads / HPW;
@@ -893,6 +978,42 @@ __global__ __launch_bounds__(NT, (replay_waves<RM, InT, CK>())) void replay_kern
     const int cap = a.cap;
     const int T = a.T;
     const size_t tile0 = (size_t)b * a.nheads + h0;
+
+    TileRegs<HD, DS, NT> treg;
+    EagerRegs<NT> er;
+    if constexpr (EAGER) {
+        // every slot of the rings, the tokens, dt and the FP32 tile, before the pointer
+        constexpr int EPVIN = InTraits<InT>::EPV;
+        constexpr int VR = HD / EPVIN, VS = DS / EPVIN;
+        const int ne = eager_count(cap, T, VR, VS), nring = cap * (VR + VS);
+        const uint4* xring = reinterpret_cast<const uint4*>(static_cast<const InT*>(a.buf_x) + tile0 * cap * HD);
+        const uint4* Bring =
+            reinterpret_cast<const uint4*>(static_cast<const InT*>(a.buf_B) + ((size_t)b * a.ngroups + g) * cap * DS);
+#pragma unroll
+        for (int j = 0; j < kEagerJobs; ++j) {
+            const int v = tid + j * NT;
+            if (v >= ne) continue;
+            const uint4* src;
+            if (v < cap * VR) {
+                src = xring + v;
+            } else if (v < nring) {
+                src = Bring + (v - cap * VR);
+            } else if (v < nring + T * VR) {
+                const int u = v - nring, q = u / VR;
+                src = reinterpret_cast<const uint4*>(a.x) + ((size_t)(b * T + q) * a.nheads + h0) * VR + (u - q * VR);
+            } else if (v < nring + T * (VR + VS)) {
+                const int u = v - nring - T * VR, q = u / VS;
+                src = reinterpret_cast<const uint4*>(a.B) + ((size_t)(b * T + q) * a.ngroups + g) * VS + (u - q * VS);
+            } else {
+                const int u = v - nring - T * (VR + VS), q = u / VS;
+                src = reinterpret_cast<const uint4*>(a.C) + ((size_t)(b * T + q) * a.ngroups + g) * VS + (u - q * VS);
+            }
+            er.v[j] = *src;
+        }
+        er.dt = tid < cap ? a.buf_dt[tile0 * cap + tid]
+                          : tid < cap + T ? a.dt[(size_t)(b * T + tid - cap) * a.nheads + h0] : 0.f;
+        treg.template load<4>(a.ckpt + tile0 * HD * DS, tid);
+    }
 
     // Every head keeps its own copy of the ring pointer; those of a workgroup's
     // heads must agree with each other and with the copy of the sequence's
@@ -941,9 +1062,9 @@ __global__ __launch_bounds__(NT, (replay_waves<RM, InT, CK>())) void replay_kern
     // are not kept live across the read-copy path.
     const WgCtx ctx{tile0, b, h0, g, hpg, start, n_stored, n, flush_call};
     if (fold)
-        replay_body<HD, DS, NT, InT, RM, HPW, CK, true>(a, ctx, lds);
+        replay_body<HD, DS, NT, InT, RM, HPW, CK, true, EAGER>(a, ctx, lds, treg, er);
     else
-        replay_body<HD, DS, NT, InT, RM, HPW, CK, false>(a, ctx, lds);
+        replay_body<HD, DS, NT, InT, RM, HPW, CK, false, EAGER>(a, ctx, lds, treg, er);
 }
 
 // MX scale bytes per head tile staged in LDS by the MX read modes.
@@ -984,9 +1105,21 @@ hipError_t launch_one(const ReplayArgs& a, hipStream_t stream) {
     const int nwg = a.batch * (a.nheads / HPW);
     const size_t lds =
         (size_t)lds_plan(HD, DS, a.cap, a.T, HPW, sizeof(InT), mx_bytes(HD, DS, RM)).total * sizeof(float);
-    hipLaunchKernelGGL((replay_kernel<HD, DS, NT, InT, RM, HPW, CK>), dim3(nwg), dim3(NT), lds, stream, a);
+    if constexpr (RM == READ_F32 && CK == 4 && HPW == 1) {
+        // small batches (fewer workgroups than two per compute unit): the eager variant,
+        // where its vectors fit kEagerJobs per thread
+        constexpr int EPVIN = InTraits<InT>::EPV;
+        if (nwg <= 512 && eager_count(a.cap, a.T, HD / EPVIN, DS / EPVIN) <= kEagerJobs * NT &&
+            a.cap + a.T <= NT && a.mode != MODE_FLUSH) {
+            hipLaunchKernelGGL((replay_kernel<HD, DS, NT, InT, RM, HPW, CK, true>), dim3(nwg), dim3(NT), lds,
+                               stream, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((replay_kernel<HD, DS, NT, InT, RM, HPW, CK, false>), dim3(nwg), dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
+
 
 // Read-copy launch with hpw heads per workgroup; the multi-head kernels are
 // compiled only where a copy tile leaves room for them (not 16 x 16).
