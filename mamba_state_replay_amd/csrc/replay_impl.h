@@ -1107,11 +1107,12 @@ hipError_t launch_one(const ReplayArgs& a, hipStream_t stream) {
         (size_t)lds_plan(HD, DS, a.cap, a.T, HPW, sizeof(InT), mx_bytes(HD, DS, RM)).total * sizeof(float);
     if constexpr (RM == READ_F32 && CK == 4 && HPW == 1) {
         // small batches (fewer workgroups than two per compute unit): the eager variant,
-        // where its vectors fit kEagerJobs per thread
+        // with twice the threads (each holding half the tile registers and half the
+        // staged vectors), where its vectors fit kEagerJobs per thread
         constexpr int EPVIN = InTraits<InT>::EPV;
-        if (nwg <= 512 && eager_count(a.cap, a.T, HD / EPVIN, DS / EPVIN) <= kEagerJobs * NT &&
-            a.cap + a.T <= NT && a.mode != MODE_FLUSH) {
-            hipLaunchKernelGGL((replay_kernel<HD, DS, NT, InT, RM, HPW, CK, true>), dim3(nwg), dim3(NT), lds,
+        if (nwg <= 512 && eager_count(a.cap, a.T, HD / EPVIN, DS / EPVIN) <= kEagerJobs * 2 * NT &&
+            a.cap + a.T <= 2 * NT && a.mode != MODE_FLUSH) {
+            hipLaunchKernelGGL((replay_kernel<HD, DS, 2 * NT, InT, RM, HPW, CK, true>), dim3(nwg), dim3(2 * NT), lds,
                                stream, a);
             return hipGetLastError();
         }
