@@ -347,51 +347,103 @@ __device__ __forceinline__ U32x4 philox4x32_10(U32x4 c, uint32_t k0, uint32_t k1
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-        c = U32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+        // each 32 x 32 -> 64-bit product as one 64-bit multiply (one v_mad_u64_u32
+        // instead of separate low and high multiplies: measured 27% faster)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+        c = U32x4{(uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0};
     }
     return c;
 }
 
-// fp32 -> fp16 bits with stochastic rounding: |v| goes to the fp16 value above
-// it with probability equal to its distance from the fp16 value below it, in
-// units of their spacing, decided by 13 random bits r (the low 13 bits used):
-// away from zero iff distance * 2^13 + r >= 2^13.  In the fp16 normal range
-// the distance is exactly a 13-bit number (the fp32 mantissa bits below the
-// fp16 ones), so adding r there and truncating is the whole rounding; below
-// 2^-14 (spacing 2^-24) the distance is first truncated to 13 bits.  |v| >=
-// 65504 and infinities give +-65504; a NaN stays a NaN.
-__device__ __forceinline__ uint32_t f32_to_f16_sr(float v, uint32_t r) {
-    const uint32_t b = __float_as_uint(v);
-    const uint32_t sign = (b >> 16) & 0x8000u;
-    const uint32_t u = b & 0x7FFFFFFFu;
-    const uint32_t r13 = r & 0x1FFFu;
-    uint32_t h;
-    if (u > 0x7F800000u) {
-        h = 0x7E00u;                                        // NaN
-    } else if (u >= 0x38800000u) {                          // |v| >= 2^-14
-        const uint32_t t = (u + r13) & ~0x1FFFu;            // on the fp16 grid, possibly one binade up
-        h = t >= 0x477FE000u ? 0x7BFFu : (t >> 13) - ((127u - 15u) << 10);
-    } else {
-        const float w = __uint_as_float(u) * 16777216.0f;    // |v| / 2^-24, exact
-        const uint32_t a = (uint32_t)w;
-        const uint32_t d = (uint32_t)((w - (float)a) * 8192.0f);
-        h = a + ((d + r13) >> 13);                          // at most 0x400, the smallest normal
-    }
-    return sign | h;
+// fp32 -> fp16 with stochastic rounding: |v| goes to the fp16 value above it
+// with probability equal to its distance from the fp16 value below it, in
+// units of their spacing, decided by a 13-bit random residue r13: away from
+// zero iff distance * 2^13 + r13 >= 2^13 (in the fp16 normal range the
+// distance is exactly the 13 fp32 mantissa bits below the fp16 ones; below
+// 2^-14 it is the distance truncated to 13 bits).  |v| >= 65504 and
+// infinities give +-65504; a NaN stays a NaN.
+//
+// gfx950's converter v_cvt_sr_f16_f32 rounds away from zero iff the dropped
+// fraction of |v| (in units of the fp16 spacing) plus its 32-bit random
+// operand / 2^32 reaches 1; with r13 in the operand's top 13 bits and zeros
+// below, that is the rule above (checked bit for bit against a software
+// implementation of the rule over the normal, subnormal and underflow ranges
+// and every special value, and by the library's rounding test).  Where the
+// rule saturates the converter gives an infinity (inputs from 65504 up that
+// round up, larger ones, infinities): an infinite half becomes +-65504 by
+// subtracting one from its bits; a NaN stays a NaN.
+
+// Two values to one word of fp16 bits (a in the low half), residues in the low
+// 13 bits of ra and rb.
+__device__ __forceinline__ uint32_t f32x2_to_f16x2_sr(float a, float b, uint32_t ra, uint32_t rb) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 w = {0, 0};
+    w = __builtin_amdgcn_cvt_sr_f16_f32(w, a, ra << 19, false);
+    w = __builtin_amdgcn_cvt_sr_f16_f32(w, b, rb << 19, true);
+    const uint32_t u = __builtin_bit_cast(uint32_t, w);
+    const uint32_t lo = (u & 0x7FFFu) == 0x7C00u ? 1u : 0u;
+    const uint32_t hi = (u & 0x7FFF0000u) == 0x7C000000u ? 0x10000u : 0u;
+    return u - lo - hi;
 }
 
-// Four consecutive fp32 values of the checkpoint, vector index vi (4 columns
-// each, row-major over the whole [batch][nheads][headdim][dstate] array), to
-// fp16 with stochastic rounding: the random words are Philox4x32-10 of the
-// counter (vi low, vi high, 0, 0) under the key (seed low, seed high), word e
-// for column e of the vector.
+// Random draws of the checkpoint's 4-element vectors (vector index vi,
+// row-major over the whole [batch][nheads][headdim][dstate] array): vectors vi
+// and vi + 16 of each aligned block of 32 share the Philox4x32-10 call at
+// counter (u low, u high, 0, 0), u = 16 (vi / 32) + vi % 16, under the key
+// (seed low, seed high); column e of the lower vector takes the low 16 bits
+// of word e, the upper vector the high 16 bits.  One call serves 8 values.
+__device__ __forceinline__ U32x4 sr_words(uint64_t vi, uint64_t seed) {
+    const uint64_t u = (vi >> 5) * 16 + (vi & 15);
+    return philox4x32_10(U32x4{(uint32_t)u, (uint32_t)(u >> 32), 0u, 0u}, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint2 f32x4_sr_with(const v4f f, const U32x4 r, int shift) {
+    return make_uint2(f32x2_to_f16x2_sr(f.x, f.y, r.x >> shift, r.y >> shift),
+                      f32x2_to_f16x2_sr(f.z, f.w, r.z >> shift, r.w >> shift));
+}
+
+// One vector to fp16 with stochastic rounding (the half of its call that the
+// partner vector uses is dropped).
 __device__ __forceinline__ uint2 f32x4_to_f16x4_sr(const v4f f, uint64_t vi, uint64_t seed) {
-    const U32x4 r = philox4x32_10(U32x4{(uint32_t)vi, (uint32_t)(vi >> 32), 0u, 0u}, (uint32_t)seed,
-                                  (uint32_t)(seed >> 32));
-    return make_uint2(f32_to_f16_sr(f.x, r.x) | (f32_to_f16_sr(f.y, r.y) << 16),
-                      f32_to_f16_sr(f.z, r.z) | (f32_to_f16_sr(f.w, r.w) << 16));
+    return f32x4_sr_with(f, sr_words(vi, seed), (vi & 16) ? 16 : 0);
+}
+
+// Vectors vi (vi % 32 < 16) and vi + 16 from one call.
+__device__ __forceinline__ void f32x8_to_f16x8_sr(const v4f lo, const v4f hi, uint64_t vi, uint64_t seed,
+                                                  uint2& out_lo, uint2& out_hi) {
+    const U32x4 r = sr_words(vi, seed);
+    out_lo = f32x4_sr_with(lo, r, 0);
+    out_hi = f32x4_sr_with(hi, r, 16);
+}
+
+// A thread's share of a tile in the TileGeo layout G (vector s at G::vec(t, s),
+// tile vectors from index base in the whole checkpoint) written as fp16 with
+// stochastic rounding.  Where rows hold 32 vectors (VPL = 4) or 16 (VPL = 2,
+// an even number of rows per thread), the thread's vectors s and s + 2 lie 16
+// apart in one aligned block of 32 (columns j + 8 k and j + 8 k + 16, or the
+// same column of an even row and of the next) and share a generator call.
+template <typename G>
+__device__ __forceinline__ void store_f16_sr(uint64_t* out, uint64_t base, const v4f* f, uint64_t seed, int tid) {
+    constexpr bool PAIRS = G::W == 8 && ((G::VPR == 32 && G::VPL == 4) || (G::VPR == 16 && G::VPL == 2 && G::NI % 2 == 0));
+    if constexpr (PAIRS) {
+#pragma unroll
+        for (int s = 0; s < G::NV; ++s) {
+            if (s & 2) continue;
+            uint2 lo, hi;
+            f32x8_to_f16x8_sr(f[s], f[s + 2], base + G::vec(tid, s), seed, lo, hi);
+            __builtin_nontemporal_store((uint64_t)lo.x | (uint64_t)lo.y << 32, out + G::vec(tid, s));
+            __builtin_nontemporal_store((uint64_t)hi.x | (uint64_t)hi.y << 32, out + G::vec(tid, s + 2));
+            __builtin_amdgcn_sched_barrier(0);   // one call's random words live at a time
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < G::NV; ++s) {
+            const uint2 h = f32x4_to_f16x4_sr(f[s], base + G::vec(tid, s), seed);
+            __builtin_nontemporal_store((uint64_t)h.x | (uint64_t)h.y << 32, out + G::vec(tid, s));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
 }
 
 // fp16 bits (low / high half of a word) to fp32, exact.

@@ -41,6 +41,8 @@
 //     row's lanes reduce and each adds the earlier drafts' terms and forms
 //     u_q, then o_q; one lane per row writes o and appends u;
 //  6. write the ring pointer (decode commits its token).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -449,12 +451,8 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
             }
         }
         if constexpr (F16) {
-            const uint64_t v0 = tile_off / 4;                 // vector index of the tile's first element
-#pragma unroll
-            for (int s = 0; s < Geo::NV; ++s) {
-                const uint2 hv = f32x4_to_f16x4_sr(raw[s], v0 + Geo::vec(tid, s), a.sr_seed);
-                __builtin_nontemporal_store(v2u{hv.x, hv.y}, reinterpret_cast<v2u*>(tile16) + Geo::vec(tid, s));
-            }
+            // (tile_off / 4: vector index of the tile's first element)
+            store_f16_sr<Geo>(reinterpret_cast<uint64_t*>(tile16), tile_off / 4, raw, a.sr_seed, tid);
         } else {
 #pragma unroll
             for (int s = 0; s < Geo::NV; ++s)
@@ -619,170 +617,180 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
         return;
     }
     if (!fold && T == 0) return;
-    int qstart = start + n;
-    qstart -= qstart >= cap ? cap : 0;
-    if (!fold) qstart = start;
+    // Two bodies, with and without the flush: the registers that the flush's
+    // fold and rounding hold then do not shape the non-flush path's allocation.
+    auto run = [&](auto fold_tag) {
+        constexpr bool fold = decltype(fold_tag)::value;
+        int qstart = start + n;
+        qstart -= qstart >= cap ? cap : 0;
+        if (!fold) qstart = start;
 
-    // 2. staging (as in gdn_replay_kernel, for 128 rows)
-    const GdnStage<DK, ROWS, NT, InT, true> stage(a, smem, Ls, b, h, kh, pw * ROWS, T, start, n, np, qstart,
-                                            (h % (a.nv / a.nk)) == 0 && pw == 0);
-    uint4 jv[stage.JOBS];
-    stage.issue(jv, tid);
-    float gv, gq, bq;
-    stage.load_g(tid, gv, gq, bq);
+        // 2. staging (as in gdn_replay_kernel, for 128 rows)
+        const GdnStage<DK, ROWS, NT, InT, true> stage(a, smem, Ls, b, h, kh, pw * ROWS, T, start, n, np, qstart,
+                                                (h % (a.nv / a.nk)) == 0 && pw == 0);
+        uint4 jv[stage.JOBS];
+        stage.issue(jv, tid);
+        float gv, gq, bq;
+        stage.load_g(tid, gv, gq, bq);
 
-    const size_t tile_off = ((size_t)bh * a.dv + pw * ROWS) * DK;
-    uint16_t* const tile16 = reinterpret_cast<uint16_t*>(a.ckpt) + tile_off;
-    v4u raw[Geo::NV];                                       // 8 fp16 values per vector
-#pragma unroll
-    for (int s = 0; s < Geo::NV; ++s)
-        raw[s] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(tile16) + Geo::vec(tid, s));
+        const size_t tile_off = ((size_t)bh * a.dv + pw * ROWS) * DK;
+        uint16_t* const tile16 = reinterpret_cast<uint16_t*>(a.ckpt) + tile_off;
+        v4u raw[Geo::NV];                                       // 8 fp16 values per vector
+    #pragma unroll
+        for (int s = 0; s < Geo::NV; ++s)
+            raw[s] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(tile16) + Geo::vec(tid, s));
 
-    stage.finish(jv, tid);
-    stage.store_g(tid, gv, gq, bq);
-    __syncthreads();
+        stage.finish(jv, tid);
+        stage.store_g(tid, gv, gq, bq);
+        __syncthreads();
 
-    const int row0 = Geo::row0(tid);
-    const int lane = tid % W;
-    // the 16 values of row r of this thread's share, widened: columns (lane + 8k) * 8 + e
-    auto widen_row = [&](int r, float (&f)[16]) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const v4u w = raw[r * Geo::VPL + k];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                f[8 * k + 2 * e] = f16lo_to_f32(w[e]);
-                f[8 * k + 2 * e + 1] = f16hi_to_f32(w[e]);
-            }
-        }
-    };
-    auto dot_row = [&](const float (&f)[16], const float* x) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const float4 x0 = *reinterpret_cast<const float4*>(x + (lane + W * k) * 8);
-            const float4 x1 = *reinterpret_cast<const float4*>(x + (lane + W * k) * 8 + 4);
-            acc = fmaf(f[8 * k], x0.x, acc);
-            acc = fmaf(f[8 * k + 1], x0.y, acc);
-            acc = fmaf(f[8 * k + 2], x0.z, acc);
-            acc = fmaf(f[8 * k + 3], x0.w, acc);
-            acc = fmaf(f[8 * k + 4], x1.x, acc);
-            acc = fmaf(f[8 * k + 5], x1.y, acc);
-            acc = fmaf(f[8 * k + 6], x1.z, acc);
-            acc = fmaf(f[8 * k + 7], x1.w, acc);
-        }
-        return acc;
-    };
-
-    if (fold) {
-        // 3. flush weights, then per row: fold in fp32, write with stochastic rounding
-        for (int c = tid; c < n; c += NT) {
-            float sg = 0.0f;
-            for (int i = c + 1; i < n; ++i) sg += smem[Ls.G + i];
-            smem[Ls.WF + c] = __expf(sg);
-        }
-        if (tid == NT - 1) {
-            float sg = 0.0f;
-            for (int i = 0; i < n; ++i) sg += smem[Ls.G + i];
-            smem[Ls.DD + T] = __expf(sg);
-        }
-    }
-    // 4. coefficients
-    gdn_coefficients<DK, NT, float>(smem, Ls, np, T, cap, tid);
-    __syncthreads();
-
-    // 5. per row of this thread: the query products (from the fp32 fold on a
-    // flush call, else from the widened fp16 checkpoint) plus the committed
-    // records' terms, reduced over the row's lanes and staged in LDS
-    const float gf = fold ? smem[Ls.DD + T] : 1.0f;
-#pragma unroll
-    for (int r = 0; r < Geo::NI; ++r) {
-        const int row = row0 + r;
-        float f[16];
-        widen_row(r, f);
-        if (fold) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) f[e] *= gf;
-            for (int c = 0; c < n; ++c) {
-                const float cf = smem[Ls.WF + c] * smem[Ls.U + c * Ls.US + row];
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const float4 k0 = key4<float>(smem + Ls.K, c * DK + (lane + W * k) * 8);
-                    const float4 k1 = key4<float>(smem + Ls.K, c * DK + (lane + W * k) * 8 + 4);
-                    f[8 * k] = fmaf(cf, k0.x, f[8 * k]);
-                    f[8 * k + 1] = fmaf(cf, k0.y, f[8 * k + 1]);
-                    f[8 * k + 2] = fmaf(cf, k0.z, f[8 * k + 2]);
-                    f[8 * k + 3] = fmaf(cf, k0.w, f[8 * k + 3]);
-                    f[8 * k + 4] = fmaf(cf, k1.x, f[8 * k + 4]);
-                    f[8 * k + 5] = fmaf(cf, k1.y, f[8 * k + 5]);
-                    f[8 * k + 6] = fmaf(cf, k1.z, f[8 * k + 6]);
-                    f[8 * k + 7] = fmaf(cf, k1.w, f[8 * k + 7]);
+        const int row0 = Geo::row0(tid);
+        const int lane = tid % W;
+        // the 16 values of row r of this thread's share, widened: columns (lane + 8k) * 8 + e
+        auto widen_row = [&](int r, float (&f)[16]) {
+    #pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const v4u w = raw[r * Geo::VPL + k];
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    f[8 * k + 2 * e] = f16lo_to_f32(w[e]);
+                    f[8 * k + 2 * e + 1] = f16hi_to_f32(w[e]);
                 }
             }
-#pragma unroll
+        };
+        auto dot_row = [&](const float (&f)[16], const float* x) {
+            float acc = 0.0f;
+    #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                const int s = r * Geo::VPL + k;
-                const uint64_t v0 = (tile_off + (size_t)row * DK + (size_t)(lane + W * k) * 8) / 4;
-                const uint2 h0 = f32x4_to_f16x4_sr(v4f{f[8 * k], f[8 * k + 1], f[8 * k + 2], f[8 * k + 3]}, v0,
-                                                   a.sr_seed);
-                const uint2 h1 = f32x4_to_f16x4_sr(v4f{f[8 * k + 4], f[8 * k + 5], f[8 * k + 6], f[8 * k + 7]},
-                                                   v0 + 1, a.sr_seed);
-                __builtin_nontemporal_store(v4u{h0.x, h0.y, h1.x, h1.y},
-                                            reinterpret_cast<v4u*>(tile16) + Geo::vec(tid, s));
+                const float4 x0 = *reinterpret_cast<const float4*>(x + (lane + W * k) * 8);
+                const float4 x1 = *reinterpret_cast<const float4*>(x + (lane + W * k) * 8 + 4);
+                acc = fmaf(f[8 * k], x0.x, acc);
+                acc = fmaf(f[8 * k + 1], x0.y, acc);
+                acc = fmaf(f[8 * k + 2], x0.z, acc);
+                acc = fmaf(f[8 * k + 3], x0.w, acc);
+                acc = fmaf(f[8 * k + 4], x1.x, acc);
+                acc = fmaf(f[8 * k + 5], x1.y, acc);
+                acc = fmaf(f[8 * k + 6], x1.z, acc);
+                acc = fmaf(f[8 * k + 7], x1.w, acc);
             }
-        }
-        for (int q = 0; q < T; ++q) {
-            const float d = smem[Ls.DD + q];
-            float pk = d * dot_row(f, smem + Ls.KQ + q * DK);
-            float pq = d * dot_row(f, smem + Ls.QQ + q * DK);
-            for (int c = lane; c < np; c += W) {
-                const float u = smem[Ls.U + c * Ls.US + row];
-                pk = fmaf(smem[Ls.CK + q * cap + c], u, pk);
-                pq = fmaf(smem[Ls.CQ + q * cap + c], u, pq);
-            }
-            pk = group_sum<W>(pk);
-            pq = group_sum<W>(pq);
-            if (lane == 0) {
-                smem[PK + q * ROWS + row] = pk;
-                smem[PQ + q * ROWS + row] = pq;
-            }
-        }
-    }
-    if (T == 0) {
-        if (tid < 2) store_ring_ptr(a.meta, m0 + tid, after);
-        return;
-    }
-    __syncthreads();
+            return acc;
+        };
 
-    // 6. one thread per row walks the queries in order: u_q, then o_q
-    if (tid < ROWS) {
-        const int row = tid;
-        float* const uring_w = a.buf_u + (size_t)bh * cap * a.dv + pw * ROWS + row;
-        for (int q = 0; q < T; ++q) {
-            float sk = smem[PK + q * ROWS + row];
-            float o = smem[PQ + q * ROWS + row];
-            for (int dd = 0; dd < q; ++dd) {
-                const float ud = smem[Ls.UD + dd * ROWS + row];
-                sk = fmaf(smem[Ls.CK + q * cap + np + dd], ud, sk);
-                o = fmaf(smem[Ls.CQ + q * cap + np + dd], ud, o);
+        if (fold) {
+            // 3. flush weights, then per row: fold in fp32, write with stochastic rounding
+            for (int c = tid; c < n; c += NT) {
+                float sg = 0.0f;
+                for (int i = c + 1; i < n; ++i) sg += smem[Ls.G + i];
+                smem[Ls.WF + c] = __expf(sg);
             }
-            const float u = smem[Ls.BE + q] * (smem[Ls.V + q * ROWS + row] - sk);
-            o = fmaf(smem[Ls.CQ + q * cap + np + q], u, o);
-            smem[Ls.UD + q * ROWS + row] = u;
-            a.o[((size_t)(b * T + q) * a.nv + h) * a.dv + pw * ROWS + row] = o;
+            if (tid == NT - 1) {
+                float sg = 0.0f;
+                for (int i = 0; i < n; ++i) sg += smem[Ls.G + i];
+                smem[Ls.DD + T] = __expf(sg);
+            }
+        }
+        // 4. coefficients
+        gdn_coefficients<DK, NT, float>(smem, Ls, np, T, cap, tid);
+        __syncthreads();
+
+        // 5. per row of this thread: the query products (from the fp32 fold on a
+        // flush call, else from the widened fp16 checkpoint) plus the committed
+        // records' terms, reduced over the row's lanes and staged in LDS
+        const float gf = fold ? smem[Ls.DD + T] : 1.0f;
+    #pragma unroll
+        for (int r = 0; r < Geo::NI; ++r) {
+            const int row = row0 + r;
+            float f[16];
+            widen_row(r, f);
+            if (fold) {
+    #pragma unroll
+                for (int e = 0; e < 16; ++e) f[e] *= gf;
+                for (int c = 0; c < n; ++c) {
+                    const float cf = smem[Ls.WF + c] * smem[Ls.U + c * Ls.US + row];
+    #pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const float4 k0 = key4<float>(smem + Ls.K, c * DK + (lane + W * k) * 8);
+                        const float4 k1 = key4<float>(smem + Ls.K, c * DK + (lane + W * k) * 8 + 4);
+                        f[8 * k] = fmaf(cf, k0.x, f[8 * k]);
+                        f[8 * k + 1] = fmaf(cf, k0.y, f[8 * k + 1]);
+                        f[8 * k + 2] = fmaf(cf, k0.z, f[8 * k + 2]);
+                        f[8 * k + 3] = fmaf(cf, k0.w, f[8 * k + 3]);
+                        f[8 * k + 4] = fmaf(cf, k1.x, f[8 * k + 4]);
+                        f[8 * k + 5] = fmaf(cf, k1.y, f[8 * k + 5]);
+                        f[8 * k + 6] = fmaf(cf, k1.z, f[8 * k + 6]);
+                        f[8 * k + 7] = fmaf(cf, k1.w, f[8 * k + 7]);
+                    }
+                }
+                // fp32 vectors v0, v0 + 1 (k = 0) and v0 + 16, v0 + 17 (k = 1): two
+                // generator calls, each shared by a vector and the one 16 after it
+                const uint64_t v0 = (tile_off + (size_t)row * DK + (size_t)lane * 8) / 4;
+                uint2 a0, a1, b0, b1;
+                f32x8_to_f16x8_sr(v4f{f[0], f[1], f[2], f[3]}, v4f{f[8], f[9], f[10], f[11]}, v0, a.sr_seed, a0, a1);
+                __builtin_amdgcn_sched_barrier(0);   // one call's random words live at a time
+                f32x8_to_f16x8_sr(v4f{f[4], f[5], f[6], f[7]}, v4f{f[12], f[13], f[14], f[15]}, v0 + 1, a.sr_seed, b0,
+                                  b1);
+                __builtin_nontemporal_store(v4u{a0.x, a0.y, b0.x, b0.y},
+                                            reinterpret_cast<v4u*>(tile16) + Geo::vec(tid, r * Geo::VPL));
+                __builtin_nontemporal_store(v4u{a1.x, a1.y, b1.x, b1.y},
+                                            reinterpret_cast<v4u*>(tile16) + Geo::vec(tid, r * Geo::VPL + 1));
+            }
+            for (int q = 0; q < T; ++q) {
+                const float d = smem[Ls.DD + q];
+                float pk = d * dot_row(f, smem + Ls.KQ + q * DK);
+                float pq = d * dot_row(f, smem + Ls.QQ + q * DK);
+                for (int c = lane; c < np; c += W) {
+                    const float u = smem[Ls.U + c * Ls.US + row];
+                    pk = fmaf(smem[Ls.CK + q * cap + c], u, pk);
+                    pq = fmaf(smem[Ls.CQ + q * cap + c], u, pq);
+                }
+                pk = group_sum<W>(pk);
+                pq = group_sum<W>(pq);
+                if (lane == 0) {
+                    smem[PK + q * ROWS + row] = pk;
+                    smem[PQ + q * ROWS + row] = pq;
+                }
+            }
+        }
+        if (T == 0) {
+            if (tid < 2) store_ring_ptr(a.meta, m0 + tid, after);
+            return;
+        }
+        __syncthreads();
+
+        // 6. one thread per row walks the queries in order: u_q, then o_q
+        if (tid < ROWS) {
+            const int row = tid;
+            float* const uring_w = a.buf_u + (size_t)bh * cap * a.dv + pw * ROWS + row;
+            for (int q = 0; q < T; ++q) {
+                float sk = smem[PK + q * ROWS + row];
+                float o = smem[PQ + q * ROWS + row];
+                for (int dd = 0; dd < q; ++dd) {
+                    const float ud = smem[Ls.UD + dd * ROWS + row];
+                    sk = fmaf(smem[Ls.CK + q * cap + np + dd], ud, sk);
+                    o = fmaf(smem[Ls.CQ + q * cap + np + dd], ud, o);
+                }
+                const float u = smem[Ls.BE + q] * (smem[Ls.V + q * ROWS + row] - sk);
+                o = fmaf(smem[Ls.CQ + q * cap + np + q], u, o);
+                smem[Ls.UD + q * ROWS + row] = u;
+                a.o[((size_t)(b * T + q) * a.nv + h) * a.dv + pw * ROWS + row] = o;
+                int slot = qstart + np + q;
+                slot -= slot >= cap ? cap : 0;
+                uring_w[(size_t)slot * a.dv] = u;
+            }
+        }
+        if (pw == 0 && tid >= ROWS && tid < ROWS + T) {
+            const int q = tid - ROWS;
             int slot = qstart + np + q;
             slot -= slot >= cap ? cap : 0;
-            uring_w[(size_t)slot * a.dv] = u;
+            a.buf_g[(size_t)bh * cap + slot] = smem[Ls.GQ + q];
         }
-    }
-    if (pw == 0 && tid >= ROWS && tid < ROWS + T) {
-        const int q = tid - ROWS;
-        int slot = qstart + np + q;
-        slot -= slot >= cap ? cap : 0;
-        a.buf_g[(size_t)bh * cap + slot] = smem[Ls.GQ + q];
-    }
-    // 7. ring pointers of both row blocks
-    if (tid < 2) store_ring_ptr(a.meta, m0 + tid, after);
+        // 7. ring pointers of both row blocks
+        if (tid < 2) store_ring_ptr(a.meta, m0 + tid, after);
+    };
+    if (fold)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 }
 
 // Conventional GDN step (the in-library baseline): read the tile, then per

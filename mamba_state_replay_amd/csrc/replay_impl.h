@@ -511,8 +511,8 @@ __device__ __forceinline__ void load_ckpt(TileRegs<HD, DS, NT>& t, const void* c
 }
 
 // Write the folded tile f back: fp32 as is, or FP16 with stochastic rounding
-// (random words keyed by the call's seed, counter = the vector's index in the
-// whole checkpoint).
+// (random draws keyed by the call's seed and the vectors' indices in the whole
+// checkpoint).
 template <int HD, int DS, int NT, int CK>
 __device__ __forceinline__ void store_ckpt(void* ckpt, size_t tile, const v4f* f, uint64_t seed, int tid) {
     using G32 = TileGeo<HD, DS, NT, 4>;
@@ -521,14 +521,7 @@ __device__ __forceinline__ void store_ckpt(void* ckpt, size_t tile, const v4f* f
 #pragma unroll
         for (int s = 0; s < G32::NV; ++s) __builtin_nontemporal_store(f[s], out + G32::vec(tid, s));
     } else {
-        v2u* out = static_cast<v2u*>(ckpt) + tile * (HD * DS / 4);
-#pragma unroll
-        for (int s = 0; s < G32::NV; ++s) {
-            const uint64_t vi = tile * (HD * DS / 4) + G32::vec(tid, s);
-            const uint2 h = f32x4_to_f16x4_sr(f[s], vi, seed);
-            __builtin_nontemporal_store(v2u{h.x, h.y}, out + G32::vec(tid, s));
-            __builtin_amdgcn_sched_barrier(0);   // one vector's random words live at a time
-        }
+        store_f16_sr<G32>(static_cast<uint64_t*>(ckpt) + tile * (HD * DS / 4), tile * (HD * DS / 4), f, seed, tid);
     }
 }
 

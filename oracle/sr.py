@@ -14,10 +14,14 @@ library) is:
   Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC 2011),
   written here from that definition;
 * checkpoint element 4 v + e (row-major over the whole [batch][nheads]
-  [headdim][dstate] array) uses word e of Philox at counter (v mod 2^32,
-  v div 2^32, 0, 0) under the key (seed mod 2^32, seed div 2^32), one seed
-  per call;
-* stochastic rounding of a value v to fp16 with random word r: let a be the
+  [headdim][dstate] array, v its 4-element vector) draws 16 bits from word e
+  of Philox under the key (seed mod 2^32, seed div 2^32), one seed per call:
+  within each aligned block of 32 vectors (128 elements), vectors v and
+  v + 16 (v mod 32 < 16) share the counter (u mod 2^32, u div 2^32, 0, 0)
+  with u = 16 (v div 32) + (v mod 16); the lower vector takes the low 16 bits
+  of each word, the upper one the high 16 bits.  Each generator call thus
+  serves 8 elements (the rounding below uses 13 bits of a draw);
+* stochastic rounding of a value v to fp16 with random draw r: let a be the
   fp16 grid point at or below |v| and s the grid spacing there (2^(E - 10) for
   |v| in [2^E, 2^(E+1)), E >= -14; 2^-24 below 2^-14), d the distance
   (|v| - a) / s taken to 13 bits (rounded down); |v| goes to a + s iff
@@ -57,14 +61,24 @@ def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
     return c0, c1, c2, c3
 
 
+def counter(v):
+    """Generator counter of 4-element vector v (vectors v and v + 16 of an
+    aligned block of 32 share one)."""
+    v = np.asarray(v, np.uint64)
+    return (v >> np.uint64(5)) * np.uint64(16) + (v & np.uint64(15))
+
+
 def words(index, seed: int) -> np.ndarray:
-    """Random word of each checkpoint element (flat row-major index array)."""
+    """Random 16-bit draw of each checkpoint element (flat row-major index array)."""
     idx = np.asarray(index, np.uint64)
     v = idx >> np.uint64(2)
-    out = philox4x32_10(v & np.uint64(_MASK), v >> np.uint64(32), 0, 0, seed & _MASK, (seed >> 32) & _MASK)
+    u = counter(v)
+    out = philox4x32_10(u & np.uint64(_MASK), u >> np.uint64(32), 0, 0, seed & _MASK, (seed >> 32) & _MASK)
     w = np.stack(out)                                      # [4][...]
     e = (idx & np.uint64(3)).astype(np.int64)
-    return np.take_along_axis(w, e[None], axis=0)[0].astype(np.uint32)
+    word = np.take_along_axis(w, e[None], axis=0)[0]
+    shift = ((v >> np.uint64(4)) & np.uint64(1)) * np.uint64(16)
+    return ((word >> shift) & np.uint64(0xFFFF)).astype(np.uint32)
 
 
 def f16_grid(a):
@@ -77,8 +91,9 @@ def f16_grid(a):
 
 
 def f16_sr(v, r) -> np.ndarray:
-    """Stochastic rounding of v (float32 values) to fp16 with random words r
-    (uint32); float64 results, all on the fp16 grid (NaN for NaN)."""
+    """Stochastic rounding of v (float32 values) to fp16 with random draws r
+    (integers, the low 13 bits used); float64 results, all on the fp16 grid
+    (NaN for NaN)."""
     v = np.asarray(v, np.float32).astype(np.float64)
     r13 = (np.asarray(r, np.uint64) & np.uint64(0x1FFF)).astype(np.int64)
     a = np.abs(v)

@@ -151,7 +151,10 @@ def test_gdn_f16_decode_through_flushes(which, dev):
 @pytest.mark.parametrize("which", sorted(SHAPES))
 def test_gdn_f16_verify_commit(which, dev):
     """Speculative rounds over the FP16 checkpoint (T = 3, L = 4): outputs match
-    the oracle that follows the same flush schedule and rounding."""
+    the oracle that follows the same flush schedule and rounding, within the
+    FP32 tolerance per row plus the allowance of the decode test above for
+    rounding decisions that went the other way (the drafts of a round read the
+    exact fold of its flush; the rounded checkpoint serves the later rounds)."""
     from mamba_state_replay_amd import binding_gdn as bg
     from mamba_state_replay_amd.staging import GdnTokenStream
     shape = SHAPES[which]
@@ -175,6 +178,9 @@ def test_gdn_f16_verify_commit(which, dev):
     tk = w.steps
     rep = ogdn.Replay(S0.astype(np.float64), shape.nv, shape.nk)
     oref = np.zeros((rounds, T, shape.batch, shape.nv, shape.dv))
+    grow = np.zeros((shape.batch, shape.nv, shape.dv))
+    allow = np.zeros(oref.shape)
+    hpk = shape.nv // shape.nk
     for r in range(rounds):
         flushing = [b for b in range(shape.batch) if len(rep.records[b]) >= shape.window]
         for b in flushing:
@@ -185,11 +191,17 @@ def test_gdn_f16_verify_commit(which, dev):
             outs, recs = rep.verify(b, drafts)
             oref[r, :, b] = np.stack(outs)
             rep.commit(b, recs, int(acc[r, b]))
+        for i in range(T):
+            qn = np.repeat(np.linalg.norm(np.asarray(tk.q[r * T + i], np.float64), axis=-1), hpk, axis=1)
+            allow[r, i] = grow * qn[:, :, None]
         if flushing:
             rounded = sr.sr_checkpoint(rep.ckpt, 7000 + r)
+            rows = _spacing_rows(rounded)
             for b in flushing:
                 rep.ckpt[b] = rounded[b]
-    assert_rows_close(np.swapaxes(o.cpu().numpy(), 1, 2), oref, what=f"gdn f16 draft outputs ({which})")
+                grow[b] += rows[b]
+    assert_rows_close(np.swapaxes(o.cpu().numpy(), 1, 2), oref, what=f"gdn f16 draft outputs ({which})",
+                      allowance=allow)
     assert int(st.status.cpu()[0]) == 0
 
 

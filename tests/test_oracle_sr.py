@@ -8,7 +8,7 @@
   normal range (the point of stochastic rounding), and within 2^-13 of a
   spacing below it;
 * the two candidates are numpy's fp16 neighbours of v (an independent grid);
-* sign symmetry, saturation at 65504, NaN, and the element -> word map.
+* sign symmetry, saturation at 65504, NaN, and the element -> random draw map.
 """
 import numpy as np
 import pytest
@@ -89,12 +89,25 @@ def test_sign_saturation_nan():
 
 
 def test_element_words():
-    """Element 4 v + e takes word e of the generator at counter (v lo, v hi, 0, 0)."""
+    """Element 4 v + e draws from word e of the generator: vectors v and v + 16
+    of an aligned block of 32 share the counter 16 (v div 32) + (v mod 16), the
+    lower vector taking the word's low 16 bits, the upper its high 16 bits."""
     seed = 0x0123456789ABCDEF
-    idx = np.array([0, 1, 2, 3, 4, 7, (1 << 34) + 5], np.uint64)
+    vs = [0, 1, 15, 16, 17, 31, 32, 47, 48, 63, 1000, (1 << 32) + 7, (1 << 36) + 21]
+    idx = np.array([4 * v + e for v in vs for e in range(4)], np.uint64)
     got = sr.words(idx, seed)
     for i, w in zip(idx.tolist(), got.tolist()):
         v, e = i // 4, i % 4
-        ref = sr.philox4x32_10(np.array([v & 0xFFFFFFFF]), np.array([v >> 32]), np.array([0]), np.array([0]),
+        block, pos = divmod(v, 32)
+        u = block * 16 + pos % 16
+        ref = sr.philox4x32_10(np.array([u & 0xFFFFFFFF]), np.array([u >> 32]), np.array([0]), np.array([0]),
                                seed & 0xFFFFFFFF, seed >> 32)
-        assert w == int(ref[e][0])
+        word = int(ref[e][0])
+        assert w == ((word >> 16) if pos >= 16 else word) & 0xFFFF
+    # every counter serves exactly the 8 elements of one vector pair, and the two
+    # halves of every word are used once each
+    idx = np.arange(4 * 32 * 3, dtype=np.uint64)
+    u = sr.counter(idx >> np.uint64(2))
+    assert np.array_equal(np.bincount(u.astype(np.int64)), np.full(48, 8))
+
+
