@@ -395,8 +395,11 @@ def bench_gdn(args):
         vround(r)
     v_ms = graph_time(lambda r: vround(8 + r), rounds, torch)
     assert int(vst.status.cpu()[0]) == 0 and bool(torch.isfinite(vo).all())
-    # the commit of round r - 1 fused into the verification of round r: one launch per round
+    # the commit of round r - 1 fused into the verification of round r: one launch per round,
+    # after a verification of round 39 that nothing has committed yet (every round above ended
+    # with its commit)
     fround = lambda r: bg.gdn_commit_verify(vcfg, vst, acc[(r - 1) % rounds], T, vtoks.call(r % rounds), vo)
+    bg.gdn_verify_drafts(vcfg, vst, vtoks.call(39 % rounds), vo)
     for r in range(4):
         fround(40 + r)
     f_ms = graph_time(lambda r: fround(44 + r), rounds, torch)
