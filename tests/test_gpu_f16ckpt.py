@@ -111,15 +111,28 @@ def _window_allowances(C, cks, L, steps, nheads):
     return out
 
 
-def test_flush_writes_the_stochastic_rounding_of_the_fold():
+# Every compiled tile shape: the flush's generator calls are shared by a thread's
+# vectors 16 apart in rows of 32 vectors (64 x 128, 128 x 128) and of 16 vectors
+# (64 x 64: the same column of an even row and the next), and taken per vector
+# where a thread holds one vector (16 x 16).
+TILES = {
+    "16x16": dict(nheads=4, headdim=16, dstate=16, ngroups=1),
+    "64x64": dict(nheads=16, headdim=64, dstate=64, ngroups=2),
+    "64x128": NEMO,
+    "128x128": dict(nheads=8, headdim=128, dstate=128, ngroups=1),
+}
+
+
+@pytest.mark.parametrize("tile", sorted(TILES))
+def test_flush_writes_the_stochastic_rounding_of_the_fold(tile):
     dev = device()
-    shape = synth.LayerShape(batch=3, window=16, **NEMO)
-    work = _f16_work(shape, 0, 1020, n0=7)
-    cfg = staging.config(shape, ckpt_dtype="f16")
+    shape = synth.LayerShape(batch=3, window=16, **TILES[tile])
+    work = _f16_work(shape, 0, 1020, n0=7, in_dtype="bf16" if tile != "16x16" else "f32")
+    cfg = staging.config(shape, ckpt_dtype="f16", in_dtype=work.steps.in_dtype)
     st = staging.replay_state(cfg, work, dev)
     seed = 0x5EED0000F16
     p = dataclasses.replace(staging.params(work, dev), sr_seed=seed)
-    say("f16 checkpoint flush, 7 records")
+    say(f"f16 checkpoint flush, {tile} tiles, 7 records")
     rb.replayssm_flush(cfg, st, p)
     torch.cuda.synchronize()
     got = host(st.ckpt)
