@@ -373,7 +373,7 @@ __device__ __forceinline__ U32x4 philox4x32_10(U32x4 c, uint32_t k0, uint32_t k1
 // rule saturates the converter gives an infinity (inputs from 65504 up that
 // round up, larger ones, infinities): an infinite half becomes +-65504 by
 // subtracting one from its bits; a NaN stays a NaN.
-
+//
 // Two values to one word of fp16 bits (a in the low half), residues in the low
 // 13 bits of ra and rb.
 __device__ __forceinline__ uint32_t f32x2_to_f16x2_sr(float a, float b, uint32_t ra, uint32_t rb) {
@@ -421,8 +421,9 @@ __device__ __forceinline__ void f32x8_to_f16x8_sr(const v4f lo, const v4f hi, ui
 // tile vectors from index base in the whole checkpoint) written as fp16 with
 // stochastic rounding.  Where rows hold 32 vectors (VPL = 4) or 16 (VPL = 2,
 // an even number of rows per thread), the thread's vectors s and s + 2 lie 16
-// apart in one aligned block of 32 (columns j + 8 k and j + 8 k + 16, or the
-// same column of an even row and of the next) and share a generator call.
+// apart in one aligned block of 32 (vector columns j + 8 k and j + 8 k + 16,
+// or the same column of an even row and of the next) and share a generator
+// call.
 template <typename G>
 __device__ __forceinline__ void store_f16_sr(uint64_t* out, uint64_t base, const v4f* f, uint64_t seed, int tid) {
     constexpr bool PAIRS = G::W == 8 && ((G::VPR == 32 && G::VPL == 4) || (G::VPR == 16 && G::VPL == 2 && G::NI % 2 == 0));
