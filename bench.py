@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-conventional", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="decode: skip the other workloads measured after the headline (verification at "
+                         "batch 512 with T = 3 and 8, the read copies and FP16 checkpoint, the GDN layer)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU sample")
     ap.add_argument("--config", choices=["decode", "verify", "verify_sweep", "sweep", "dual", "gdn",
                                          "gdn_verify_sweep", "gdn_sweep"], default="decode",
@@ -305,10 +308,47 @@ def main():
         result["roofline"]["frac_of_probe_read"] = round(achieved / read_gbs, 4)
         del src, dst, sink
 
+    if not args.no_extras:
+        result["also"] = extras(args)
+
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(work, total_bytes / K, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def extras(args):
+    """The other workloads, measured after the headline in the same run, each
+    in compact form (the --config runs give the full records): speculative
+    verification at batch 512 (T = 3 and 8, replay against FP32 snapshots),
+    decode with each read copy and with the FP16 checkpoint (batch 256,
+    L = 16, 256 steps = 16 whole windows), and the GDN layer (batch 512,
+    decode and T = 3 verification).  Times are graph-timed as in the --config
+    runs; launch times are HIP event pairs around eager launches."""
+    import torch
+    out = {}
+    torch.cuda.empty_cache()
+    for T in (3, 8):
+        pt = _verify_point(T, rounds=32)
+        out[f"verify_batch512_T{T}"] = {
+            "replay_us_per_round": pt["replay"]["us_per_round"], "replay_gbs": pt["replay"]["gbs"],
+            "fused_commit_us_per_round": pt["replay_fused_commit"]["us_per_round"],
+            "snapshot_us_per_round": pt["snapshot_baseline"]["us_per_round"],
+            "speedup_vs_snapshot": pt["speedup"], "rounds": 32}
+    out["read_copies_batch256_L16"] = {"steps": 256, "modes": dual_measure(256)}
+    g = gdn_measure(argparse.Namespace(window=16, gdn_batch=512, gdn_ckpt="f32", steps=64, warmup=16,
+                                       no_probe=True, no_cpu=True))
+    out["gdn_batch512_L16"] = {
+        "us_per_step": g["us_per_step"], "gbs": g["value"],
+        "nonflush_launch_us": g["roofline"]["nonflush_launch_us"],
+        "flush_launch_us": g["roofline"]["flush_launch_us"],
+        "conventional_us_per_step": g["conventional"]["us_per_step"],
+        "speedup_vs_conventional": g["speedup_vs_conventional"],
+        "verify_T3_us_per_round": g["verify_T3"]["us_per_round"],
+        "snapshot_T3_us_per_round": g["verify_T3"]["snapshot_baseline_us_per_round"],
+        "speedup_vs_snapshot": g["verify_T3"]["speedup_vs_snapshot"]}
+    torch.cuda.empty_cache()
+    return out
 
 
 GDN_LAYER = dict(nv=32, nk=16, dk=128, dv=128)
@@ -320,6 +360,11 @@ def bench_gdn(args):
     decode steps (steady state reached from an empty buffer during the
     warm-up) against the in-library conventional GDN step, then speculative
     rounds of T = 3 drafts with U{0..3} acceptance; one JSON line."""
+    print(json.dumps(gdn_measure(args)), flush=True)
+
+
+def gdn_measure(args):
+    """The measurements of bench_gdn, returned as its record."""
     torch, dev = _device()
     from mamba_state_replay_amd import binding_gdn as bg
     from mamba_state_replay_amd import staging, synth_gdn, traffic
@@ -452,7 +497,8 @@ def bench_gdn(args):
     }
     if not args.no_probe:
         from mamba_state_replay_amd import binding as rb
-        del vst, vtoks
+        vst = vtoks = None
+        torch.cuda.empty_cache()
         nbytes = 1 << 30
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_()
         dst = torch.empty_like(src)
@@ -464,7 +510,9 @@ def bench_gdn(args):
         del src, dst
     if not args.no_cpu:
         result["cpu_baseline"] = gdn_cpu_baseline(w, step_bytes, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    del vst, vtoks
+    torch.cuda.empty_cache()
+    return result
 
 
 def bench_gdn_verify_sweep(args):
@@ -880,10 +928,21 @@ def bench_dual(args):
     decode steps (token inputs cycle through 64 seeded steps).  The accuracy of
     the modes is tested on the GPU (tests/test_gpu_dual.py,
     tests/test_gpu_f16ckpt.py), not part of this timing."""
+    res = dual_measure(4096)
+    print(json.dumps({"metric": "dual-precision decode: us per step and HBM GB/s (batch 256, L=16, 4096 steps)",
+                      "config": {"workload": "Nemotron-3-style Mamba-2 layer, batch 256, L=16, 4096 decode steps"},
+                      "modes": res, "data": "synthetic", "n_gpus": 1}), flush=True)
+
+
+def dual_measure(steps):
+    """Decode with each read copy and with the FP16 checkpoint (batch 256,
+    L = 16, `steps` steps, a whole number of windows): per mode the graph-timed
+    step, its algorithmic GB/s, and the mean non-flush and flush launch."""
     torch, dev = _device()
     from mamba_state_replay_amd import binding as rb
     from mamba_state_replay_amd import staging, synth, traffic
-    L, steps = 16, 4096
+    L = 16
+    assert steps % L == 0
     res = {}
     shape = synth.LayerShape(batch=256, nheads=128, headdim=64, dstate=128, ngroups=8, window=L)
     work = synth.decode_workload(shape, 64, seed=1004, n0=L)
@@ -904,7 +963,7 @@ def bench_dual(args):
             p.sr_seed = i + 1                   # the FP16 checkpoint's rounding seed (unused for FP32)
             rb.replayssm_decode_step(cfg, st, p, toks.call(i % 64), y)
         ms, per = timed_launches(dstep, steps, torch)
-        gms = graph_time(dstep, steps, torch)          # 4096 steps = whole windows: same phase
+        gms = graph_time(dstep, steps, torch)          # whole windows: the replays start in the same phase
         per = np.array(per)
         folds = np.array([f.any() for _, f in sched])
         key = (mode or "fp32") if ck == "f32" else "f16 checkpoint" + (f" + {mode}" if mode else "")
@@ -915,18 +974,16 @@ def bench_dual(args):
                                "flush_launch_us": round(float(per[folds].mean()) * 1e3, 2)}
         del st
         torch.cuda.empty_cache()
-    print(json.dumps({"metric": "dual-precision decode: us per step and HBM GB/s (batch 256, L=16, 4096 steps)",
-                      "config": {"workload": "Nemotron-3-style Mamba-2 layer, batch 256, L=16, 4096 decode steps"},
-                      "modes": res, "data": "synthetic", "n_gpus": 1}), flush=True)
+    return res
 
 
 PROFILE_CMDS = {
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
-             "python -u bench.py --no-cpu --no-conventional --steps 16 --warmup 16",
+             "python -u bench.py --no-cpu --no-conventional --no-extras --steps 16 --warmup 16",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- "
-             "python -u bench.py --no-cpu --no-conventional --steps 16 --warmup 16",
+             "python -u bench.py --no-cpu --no-conventional --no-extras --steps 16 --warmup 16",
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof -o trace -- "
-             "python -u bench.py --no-cpu --steps 32 --warmup 16",
+             "python -u bench.py --no-cpu --no-extras --steps 32 --warmup 16",
 }
 
 
