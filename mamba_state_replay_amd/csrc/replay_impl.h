@@ -574,7 +574,10 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
     constexpr int VR = HD / EPVIN;                   // 16-byte vectors per x row
     constexpr int VS = DS / EPVIN;                   // 16-byte vectors per B/C row
     constexpr int NW = NT / 64;
-    constexpr int JOBS = 2;                          // staged vectors per thread issued up front
+    // staged vectors per thread issued up front: 4 on the non-folding calls of the
+    // 4-head MX workgroups (whose windows of x rows for four heads exceed two
+    // vectors a thread from about half a window on), 2 elsewhere (more spill)
+    constexpr int JOBS = !FOLD && HPW >= 4 && (RM == READ_MXFP4 || RM == READ_MXFP8) ? 4 : 2;
     static_assert(HPW == 1 || (RM != READ_F32 && HPW * GC::NV <= G32::NV && GC::ACTIVE == NT),
                   "several heads per workgroup only for read copies that fill the register array");
     static_assert(HPW * NW <= kRedSlots, "reduction slots");
