@@ -326,27 +326,38 @@ def extras(args):
     decode and T = 3 verification).  Times are graph-timed as in the --config
     runs; launch times are HIP event pairs around eager launches."""
     import torch
-    out = {}
-    torch.cuda.empty_cache()
-    for T in (3, 8):
+    import traceback
+
+    def verify(T):
         pt = _verify_point(T, rounds=32)
-        out[f"verify_batch512_T{T}"] = {
-            "replay_us_per_round": pt["replay"]["us_per_round"], "replay_gbs": pt["replay"]["gbs"],
-            "fused_commit_us_per_round": pt["replay_fused_commit"]["us_per_round"],
-            "snapshot_us_per_round": pt["snapshot_baseline"]["us_per_round"],
-            "speedup_vs_snapshot": pt["speedup"], "rounds": 32}
-    out["read_copies_batch256_L16"] = {"steps": 256, "modes": dual_measure(256)}
-    g = gdn_measure(argparse.Namespace(window=16, gdn_batch=512, gdn_ckpt="f32", steps=64, warmup=16,
-                                       no_probe=True, no_cpu=True))
-    out["gdn_batch512_L16"] = {
-        "us_per_step": g["us_per_step"], "gbs": g["value"],
-        "nonflush_launch_us": g["roofline"]["nonflush_launch_us"],
-        "flush_launch_us": g["roofline"]["flush_launch_us"],
-        "conventional_us_per_step": g["conventional"]["us_per_step"],
-        "speedup_vs_conventional": g["speedup_vs_conventional"],
-        "verify_T3_us_per_round": g["verify_T3"]["us_per_round"],
-        "snapshot_T3_us_per_round": g["verify_T3"]["snapshot_baseline_us_per_round"],
-        "speedup_vs_snapshot": g["verify_T3"]["speedup_vs_snapshot"]}
+        return {"replay_us_per_round": pt["replay"]["us_per_round"], "replay_gbs": pt["replay"]["gbs"],
+                "fused_commit_us_per_round": pt["replay_fused_commit"]["us_per_round"],
+                "snapshot_us_per_round": pt["snapshot_baseline"]["us_per_round"],
+                "speedup_vs_snapshot": pt["speedup"], "rounds": 32}
+
+    def gdn():
+        g = gdn_measure(argparse.Namespace(window=16, gdn_batch=512, gdn_ckpt="f32", steps=64, warmup=16,
+                                           no_probe=True, no_cpu=True))
+        return {"us_per_step": g["us_per_step"], "gbs": g["value"],
+                "nonflush_launch_us": g["roofline"]["nonflush_launch_us"],
+                "flush_launch_us": g["roofline"]["flush_launch_us"],
+                "conventional_us_per_step": g["conventional"]["us_per_step"],
+                "speedup_vs_conventional": g["speedup_vs_conventional"],
+                "verify_T3_us_per_round": g["verify_T3"]["us_per_round"],
+                "snapshot_T3_us_per_round": g["verify_T3"]["snapshot_baseline_us_per_round"],
+                "speedup_vs_snapshot": g["verify_T3"]["speedup_vs_snapshot"]}
+
+    out = {}
+    jobs = [("verify_batch512_T3", lambda: verify(3)), ("verify_batch512_T8", lambda: verify(8)),
+            ("read_copies_batch256_L16", lambda: {"steps": 256, "modes": dual_measure(256)}),
+            ("gdn_batch512_L16", gdn)]
+    for key, fn in jobs:
+        torch.cuda.empty_cache()
+        try:
+            out[key] = fn()
+        except Exception as e:          # a failed extra is reported in its place; the headline stands
+            traceback.print_exc()
+            out[key] = {"error": f"{type(e).__name__}: {e}"}
     torch.cuda.empty_cache()
     return out
 
