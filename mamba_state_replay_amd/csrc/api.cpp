@@ -107,6 +107,14 @@ int check_tokens(const rssm_tokens* t, const rssm_params* p, const float* y, int
     return RSSM_OK;
 }
 
+// log2 of a positive power of two, else -1.
+int log2_exact(int v) {
+    if (v <= 0 || (v & (v - 1)) != 0) return -1;
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
 rssm::ReplayArgs replay_args(const rssm_config* c, const rssm_state* s, const rssm_params* p) {
     rssm::ReplayArgs a;
     std::memset(&a, 0, sizeof a);
@@ -127,6 +135,8 @@ rssm::ReplayArgs replay_args(const rssm_config* c, const rssm_state* s, const rs
     a.ngroups = c->ngroups;
     a.L = c->window;
     a.cap = c->window + 2 * c->max_drafts - 1;
+    a.nheads_log2 = log2_exact(c->nheads);
+    a.hpg_log2 = c->ngroups > 0 && c->nheads % c->ngroups == 0 ? log2_exact(c->nheads / c->ngroups) : -1;
     return a;
 }
 
@@ -238,6 +248,9 @@ rssm::GdnArgs gdn_args(const gdn_config* c, const gdn_state* s, const gdn_tokens
     a.cap = c->window + 2 * c->max_drafts - 1;
     a.mode = mode;
     a.ckpt16 = c->ckpt_dtype == RSSM_F16;
+    a.parts_log2 = log2_exact(a.parts);
+    a.nv_log2 = log2_exact(c->nv);
+    a.hpk_log2 = c->nk > 0 && c->nv % c->nk == 0 ? log2_exact(c->nv / c->nk) : -1;
     return a;
 }
 

@@ -86,6 +86,35 @@ __host__ __device__ inline GdnLds gdn_plan(int DK, int ROWS, int cap, int T, int
     return l;
 }
 
+// A workgroup's place: wg = (b nv + h) span + part, span parts per (sequence,
+// value head), and the head's key head kh = h / (nv / nk); by shifts where
+// span, nv and nv / nk are powers of two (the host passes their logarithms,
+// span_log2 < 0 where it is not), else by divisions.
+struct GdnIdx {
+    int part, bh, b, h, kh;
+    bool key_writer;   // the first value head of its key head
+};
+__device__ __forceinline__ GdnIdx gdn_index(const GdnArgs& a, int wg, int span, int span_log2) {
+    GdnIdx x;
+    if (span_log2 >= 0 && a.nv_log2 >= 0 && a.hpk_log2 >= 0) {
+        x.part = wg & (span - 1);
+        x.bh = wg >> span_log2;
+        x.b = x.bh >> a.nv_log2;
+        x.h = x.bh & ((1 << a.nv_log2) - 1);
+        x.kh = x.h >> a.hpk_log2;
+        x.key_writer = (x.h & ((1 << a.hpk_log2) - 1)) == 0;
+    } else {
+        const int hpk = a.nv / a.nk;
+        x.part = wg % span;
+        x.bh = wg / span;
+        x.b = x.bh / a.nv;
+        x.h = x.bh - x.b * a.nv;
+        x.kh = x.h / hpk;
+        x.key_writer = x.h == x.kh * hpk;
+    }
+    return x;
+}
+
 // One input-type element (fp32, or bf16 bits) as fp32.
 __device__ __forceinline__ float in_to_f32(float v) { return v; }
 __device__ __forceinline__ float in_to_f32(uint16_t v) { return bf16_to_f32(v); }
@@ -331,11 +360,8 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
 
     const int tid = threadIdx.x;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);   // = (b * nv + h) * parts + p
-    const int p = wg % a.parts;
-    const int bh = wg / a.parts;
-    const int b = bh / a.nv;
-    const int h = bh % a.nv;
-    const int kh = h / (a.nv / a.nk);
+    const GdnIdx ix = gdn_index(a, wg, a.parts, a.parts_log2);
+    const int p = ix.part, bh = ix.bh, b = ix.b, h = ix.h, kh = ix.kh;
     const int cap = a.cap;
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
     const GdnLds Ls = gdn_plan(DK, ROWS, cap, T, sizeof(InT));
@@ -380,7 +406,7 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 7) void gdn_replay_kernel(const Gdn
     // vectors are stored to LDS while the tile is still in flight (loads
     // complete in order, so waiting for a staged vector never waits for the tile).
     const GdnStage<DK, ROWS, NT, InT> stage(a, smem, Ls, b, h, kh, p * ROWS, T, start, n, np, qstart,
-                                            (h % (a.nv / a.nk)) == 0 && p == 0);
+                                            ix.key_writer && p == 0);
     uint4 jv[stage.JOBS];
     stage.issue(jv, tid);
     float gv, gq, bq;
@@ -578,11 +604,8 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
     const int tid = threadIdx.x;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);   // = (b * nv + h) * (parts / 2) + pw
     const int pairs = a.parts / 2;
-    const int pw = wg % pairs;
-    const int bh = wg / pairs;
-    const int b = bh / a.nv;
-    const int h = bh % a.nv;
-    const int kh = h / (a.nv / a.nk);
+    const GdnIdx ix = gdn_index(a, wg, pairs, a.parts_log2 >= 1 ? a.parts_log2 - 1 : -1);
+    const int pw = ix.part, bh = ix.bh, b = ix.b, h = ix.h, kh = ix.kh;
     const int cap = a.cap;
     const int T = a.mode == MODE_FLUSH ? 0 : a.T;
     const GdnLds Ls = gdn_plan(DK, ROWS, cap, T, 4);   // keys widened to fp32: the row-by-row fold reads each one per row
@@ -627,7 +650,7 @@ __global__ __launch_bounds__(256, 7) void gdn_replay_f16_wide_kernel(const GdnAr
 
         // 2. staging (as in gdn_replay_kernel, for 128 rows)
         const GdnStage<DK, ROWS, NT, InT, true> stage(a, smem, Ls, b, h, kh, pw * ROWS, T, start, n, np, qstart,
-                                                (h % (a.nv / a.nk)) == 0 && pw == 0);
+                                                ix.key_writer && pw == 0);
         uint4 jv[stage.JOBS];
         stage.issue(jv, tid);
         float gv, gq, bq;
@@ -816,11 +839,8 @@ __global__ __launch_bounds__(GdnGeo<DK>::NT, 8) void gdn_conventional_kernel(con
 
     const int tid = threadIdx.x;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int p = wg % a.parts;
-    const int bh = wg / a.parts;
-    const int b = bh / a.nv;
-    const int h = bh % a.nv;
-    const int kh = h / (a.nv / a.nk);
+    const GdnIdx ix = gdn_index(a, wg, a.parts, a.parts_log2);
+    const int p = ix.part, bh = ix.bh, b = ix.b, h = ix.h, kh = ix.kh;
     const int nslots = a.nslots;
     const int s0 = nslots > 1 ? a.slot[b] : 0;
     if (s0 < 0 || s0 >= nslots) {

@@ -38,6 +38,8 @@ struct ReplayArgs {
     int32_t L, cap, T, T_prev;
     int32_t mode, flags;
     int32_t ckpt16;     // the checkpoint is FP16, written with stochastic rounding
+    int32_t nheads_log2, hpg_log2;   // log2 of nheads and of nheads / ngroups where they are
+                                     // powers of two (else -1): the kernel then shifts, not divides
     uint64_t sr_seed;   // key of the rounding's random words for this call
 };
 
@@ -99,6 +101,8 @@ struct GdnArgs {
     int32_t batch, nv, nk, dv, parts;
     int32_t L, cap, T, mode;
     int32_t ckpt16;     // FP16 checkpoint written with stochastic rounding
+    int32_t parts_log2, nv_log2, hpk_log2;   // log2 of parts, nv and nv / nk where they are powers
+                                             // of two (else -1): the kernels then shift, not divide
     uint64_t sr_seed;
 };
 

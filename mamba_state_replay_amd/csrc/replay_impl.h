@@ -611,7 +611,7 @@ __device__ __forceinline__ void replay_body(const ReplayArgs& a, const WgCtx& ct
     const InT* xt = reinterpret_cast<const InT*>(a.x);
     const InT* Bt = reinterpret_cast<const InT*>(a.B);
     const InT* Ct = reinterpret_cast<const InT*>(a.C);
-    const bool writer = (h0 % hpg) == 0;
+    const bool writer = h0 == g * hpg;             // the group's first head
     const int nx = HPW * rows * VR, nb = rows * VS, nc = T * VS;
     const int ns = fold ? 0 : HPW * MXB / 16;        // the copy's scale bytes, 16 per vector
     const int nv = nx + nb + nc + ns;
@@ -966,10 +966,22 @@ __global__ __launch_bounds__(NT, (EAGER ? 2 : replay_waves<RM, InT, CK>())) void
     const int chunks = a.nheads / HPW;
     const int nwg = a.batch * chunks;
     const int wg = xcd_remap(blockIdx.x, nwg);
-    const int b = wg / chunks;
-    const int h0 = (wg - b * chunks) * HPW;          // first head of this workgroup
-    const int hpg = a.nheads / a.ngroups;
-    const int g = h0 / hpg;
+    // sequence, first head of this workgroup, heads per group and group: by
+    // shifts where the head counts are powers of two, else by divisions
+    constexpr int LH = HPW == 4 ? 2 : HPW == 2 ? 1 : 0;
+    int b, h0, hpg, g;
+    if (a.nheads_log2 >= LH && a.hpg_log2 >= 0) {
+        const int cl = a.nheads_log2 - LH;
+        b = wg >> cl;
+        h0 = (wg - (b << cl)) * HPW;
+        hpg = 1 << a.hpg_log2;
+        g = h0 >> a.hpg_log2;
+    } else {
+        b = wg / chunks;
+        h0 = (wg - b * chunks) * HPW;
+        hpg = a.nheads / a.ngroups;
+        g = h0 / hpg;
+    }
     const int tid = threadIdx.x;
     const int cap = a.cap;
     const int T = a.T;
