@@ -75,6 +75,9 @@ def parse():
                     help="summarise rocprofv3 output of the GDN runs into profiles/ and exit")
     ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                     help="summarise rocprofv3 output of the counter runs into profiles/ and exit")
+    ap.add_argument("--ingest-sq-counters", action="store_true",
+                    help="summarise the rocprofv3 runs of SQ_PROFILE_CMDS (MXFP4 copy HBM and SQ counters, "
+                         "FP32 SQ counters) into profiles/ and exit")
     return ap.parse_args()
 
 
@@ -123,6 +126,9 @@ def main():
     args = parse()
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters)
+        return
+    if args.ingest_sq_counters:
+        ingest_sq_counters()
         return
     if args.ingest_gdn_counters:
         ingest_gdn_counters(*args.ingest_gdn_counters)
@@ -1172,6 +1178,97 @@ def ingest_gdn_counters(fetch_dir, write_dir, trace_dir):
            f"(ratio {(fetch_b + write_b) / alg:.4f}).", f"Kernel source hash {fl['kernel_source_hash']}."]
     (ROOT / "profiles" / "gdn_decode_batch512_L16.md").write_text("\n".join(md) + "\n")
     print(json.dumps(out))
+
+
+_SQ_SET = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_INSTS_VALU SQ_INSTS_SALU "
+           "SQ_INSTS_LDS")
+_MX_CMD = "python -u bench.py --read-copy mxfp4 --no-cpu --no-conventional --no-extras --steps 16 --warmup 16"
+SQ_PROFILE_CMDS = {
+    "fetch": f"rocprofv3 --pmc FETCH_SIZE -d gpurun_out/mx_fetch -o fetch -- {_MX_CMD}",
+    "write": f"rocprofv3 --pmc WRITE_SIZE -d gpurun_out/mx_write -o write -- {_MX_CMD}",
+    "sq": f"rocprofv3 --pmc {_SQ_SET} -d gpurun_out/mx_sq -o sq -- {_MX_CMD}",
+    "sq_f32": f"rocprofv3 --pmc {_SQ_SET} -d gpurun_out/f32_sq -o sq -- "
+              "python -u bench.py --no-cpu --no-conventional --no-extras --steps 16 --warmup 16",
+}
+
+
+def ingest_sq_counters():
+    """Summarise the runs of SQ_PROFILE_CMDS: per-dispatch HBM bytes of the
+    MXFP4 read-copy kernel (non-flush and flush dispatches apart, scaled by the
+    copy probe of the same run) and per-wave SQ counters of that kernel, the
+    FP32 kernel and the streaming read probe."""
+    import collections
+    import sqlite3
+    import statistics
+
+    def per_dispatch(d):
+        db = sorted(Path(d).rglob("*.db"))[0]
+        rows = sqlite3.connect(str(db)).execute(
+            "select dispatch_id, kernel_name, counter_name, value from counters_collection").fetchall()
+        vals = collections.defaultdict(lambda: collections.defaultdict(float))
+        names = {}
+        for did, kn, cn, v in rows:
+            vals[did][cn] += v
+            names[did] = kn
+        return vals, names
+
+    def ids(names, key):
+        return [d for d in sorted(names) if key in names[d]]
+
+    mx = "replay_kernel<64, 128, 256, unsigned short, 3, 4, 4, false>"
+    f32 = "replay_kernel<64, 128, 256, unsigned short, 0, 1, 4, false>"
+    f, fn = per_dispatch("gpurun_out/mx_fetch")
+    w, wn = per_dispatch("gpurun_out/mx_write")
+    fs = [f[d]["FETCH_SIZE"] for d in ids(fn, mx)]
+    ws = [w[d]["WRITE_SIZE"] for d in ids(wn, mx)]
+    med = statistics.median(fs)
+    flush_idx = [i for i, v in enumerate(fs) if v > 3 * med]     # they read the FP32 checkpoint
+    nonflush_idx = [i for i in range(len(fs)) if i not in set(flush_idx)]
+    fscale = round(1048576.0 / statistics.median(f[d]["FETCH_SIZE"] for d in ids(fn, "probe_copy_kernel")), 4)
+    wscale = round(1048576.0 / statistics.median(w[d]["WRITE_SIZE"] for d in ids(wn, "probe_copy_kernel")), 4)
+    rows = []
+    for label, idx in (("non-flush", nonflush_idx), ("flush", flush_idx)):
+        fk = sum(fs[i] for i in idx) / len(idx)
+        wk = sum(ws[i] for i in idx) / len(idx)
+        rows.append(f"| {label} ({len(idx)} dispatches) | {fk:.1f} | {wk:.1f} | "
+                    f"{(fk * fscale + wk * wscale) * 1024 / 1e9:.4f} |")
+
+    cols = ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_INSTS_VALU",
+            "SQ_INSTS_SALU", "SQ_INSTS_LDS"]
+    sqrows = []
+    for label, d, key, idx in (("MXFP4 copy, non-flush", "gpurun_out/mx_sq", mx, nonflush_idx),
+                               ("MXFP4 copy, flush", "gpurun_out/mx_sq", mx, flush_idx),
+                               ("FP32 checkpoint, all decode launches", "gpurun_out/f32_sq", f32, None),
+                               ("streaming read probe (1 GiB)", "gpurun_out/f32_sq", "probe_read_kernel", None)):
+        vals, names = per_dispatch(d)
+        sel = ids(names, key)
+        if idx is not None:                  # the same launch order as the HBM-counter runs
+            sel = [sel[i] for i in idx if i < len(sel)]
+        tot = collections.defaultdict(float)
+        for i in sel:
+            for k, v in vals[i].items():
+                tot[k] += v
+        per = {k: round(v / tot["SQ_WAVES"], 1) for k, v in tot.items() if k != "SQ_WAVES"}
+        sqrows.append(f"| {label} ({len(sel)}) | " + " | ".join(str(per.get(c, "")) for c in cols) + " |")
+
+    md = ["# Mamba-2 decode, batch 256, L = 16: HBM and SQ counters of the MXFP4 read-copy kernel "
+          "(and the FP32 kernel's SQ counters)", "", "Commands (one MI355X; one counter set per run):", "", "```"]
+    md += [SQ_PROFILE_CMDS[k] for k in ("fetch", "write", "sq", "sq_f32")]
+    md += ["```", "",
+           f"Kernel `{mx}` (sixth template argument: 4 heads per workgroup). Dispatches whose FETCH_SIZE "
+           "exceeds three times the median are the flushing calls (they read the FP32 checkpoint and write it "
+           "and the copy).",
+           f"Scale factors from the copy probe in the same runs (1 GiB read + 1 GiB written): FETCH_SIZE x "
+           f"{fscale}, WRITE_SIZE x {wscale}.", "",
+           "| dispatches | FETCH_SIZE KiB per dispatch | WRITE_SIZE KiB per dispatch | scaled HBM GB per dispatch |",
+           "|---|---|---|---|"] + rows
+    md += ["", "The non-flush calls' algorithmic bytes at the steady state's average of 8 committed records are "
+           "about 0.200 GB (codes, scale bytes, records, tokens, outputs; `mamba_state_replay_amd/traffic.py`).",
+           "", "SQ counters, per wave (cycle counters in the counter's own units):", "",
+           "| kernel (dispatches) | " + " | ".join(cols) + " |", "|---" * (len(cols) + 1) + "|"] + sqrows
+    out = ROOT / "profiles" / "replay_decode_batch256_L16_sq_counters.md"
+    out.write_text("\n".join(md) + "\n")
+    print(f"wrote {out}")
 
 
 def ingest_counters(fetch_dir, write_dir, trace_dir):
