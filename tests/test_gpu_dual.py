@@ -469,14 +469,29 @@ def test_copy_verify_rounds(copy, tile, T):
     output scale per element (u and delta as in the dual-precision bound,
     delta from the copy's scales), with H_s the oracle's state at the
     sequence's last flush and d_q the decay since then."""
+    _copy_verify(copy, tile, T, L=8, rounds=14)
+
+
+@pytest.mark.parametrize("copy", ["e4m3", "mxfp4", "mxfp8"])
+def test_copy_verify_long_window(copy):
+    """The same check at L = 16 with T = 8 drafts on the benchmarked layer:
+    windows of up to 23 rows, so the staging list of the 4-head copy
+    workgroups (x rows of four heads, the group's B rows, the drafts' C rows,
+    the MX scale bytes) outgrows the vectors each thread issues up front and
+    the rest goes through the staging loop."""
+    n_max = _copy_verify(copy, "64x128", 8, L=16, rounds=12)
+    # a round with 11 committed records stages 4 x 19 x 8 + 19 x 16 + 8 x 16 + 64 = 1104 vectors
+    assert n_max >= 11, f"no round reached 11 committed records (max {n_max})"
+
+
+def _copy_verify(copy, tile, T, L, rounds):
     dev = device()
-    L, rounds = 8, 14
     shape = synth.LayerShape(batch=2, window=L, max_drafts=T, **COPY_VERIFY_SHAPES[tile])
     work = synth.verify_workload(shape, rounds, T, seed=1015)
     acc = torch.from_numpy(work.extra["accepted"]).to(dev)
     p = staging.params(work, dev)
     stream = staging.TokenStream(work.steps, dev, T=T)
-    say(f"copy verify {copy} {tile} T={T}")
+    say(f"copy verify {copy} {tile} T={T} L={L}")
     runs = {}
     for mode in (None, copy):
         cfg = staging.config(shape, read_copy=mode)
@@ -508,10 +523,12 @@ def test_copy_verify_rounds(copy, tile, T):
     seg = np.zeros((shape.batch, shape.nheads))            # sum of their dt
     last = np.zeros(shape.batch, np.int64)                 # round of the last flush (0: the explicit one)
     worst = 0.0
+    n_max = 0                                              # most committed records a non-flushing round found
     for r in range(rounds):
         assert np.array_equal(hc[r], h32[r]), f"round {r}: read copy changed the FP32 checkpoint"
         assert np.array_equal(mc[r], m32[r])
         flushed = n >= L
+        n_max = max(n_max, int(np.where(flushed, 0, n).max()))
         n = np.where(flushed, 0, n)
         seg = np.where(flushed[:, None], 0.0, seg)
         last = np.where(flushed, r, last)
@@ -540,7 +557,9 @@ def test_copy_verify_rounds(copy, tile, T):
         for b in range(shape.batch):
             seg[b] += dt[r * T:r * T + a_r[b], b].sum(axis=0)
         n = n + a_r
-    print(f"[gpu] {copy} {tile} T={T}: worst error/bound {worst:.3f}", flush=True)
+    print(f"[gpu] {copy} {tile} T={T} L={L}: worst error/bound {worst:.3f}, most committed records {n_max}",
+          flush=True)
+    return n_max
 
 
 @pytest.mark.parametrize("copy", ["bf16", "e4m3", "mxfp4", "mxfp8"])
